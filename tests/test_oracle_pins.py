@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+* the hand-worked example in tests/golden/hand_example.json (values derived by hand);
+* the constants the pages print (tests/golden/page_constants.json);
+* closed forms (block sums of an arithmetic sequence, the 8x candidate-count ratio);
+* special cases that reduce to a library routine (dense causal attention = torch SDPA in fp64
+  with an explicit bottom-right causal mask; B = 1 = token-level top-k via heapq.nlargest);
+* brute force on tiny inputs (an O(n^2) rank count for the selection, independent of sorting);
+* invariants (nesting in k, permutation of index dims, positive scaling, constant values).
+"""
+import heapq
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sgqa_inputs import generate_small, get_workload
+
+
+# ----------------------------------------------------------------------------------------------
+# hand-worked example
+# ----------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def hand(golden_dir):
+    with open(os.path.join(golden_dir, "hand_example.json")) as f:
+        return json.load(f)
+
+
+def test_hand_compress(hand):
+    k_idx = np.array(hand["k_idx"], dtype=np.float64)[None]
+    kb = oracle.compress(k_idx, hand["block"])
+    assert kb.shape == (1, 5, 2)
+    np.testing.assert_array_equal(kb[0], np.array(hand["k_blk_by_hand"], dtype=np.float64))
+
+
+def test_hand_scores_and_selection(hand):
+    kb = oracle.compress(np.array(hand["k_idx"], dtype=np.float64)[None], hand["block"])[0]
+    for qd in hand["queries"]:
+        p = qd["position"]
+        o = p // hand["block"]
+        s = oracle.block_scores(qd["q_idx"], kb, o)
+        np.testing.assert_array_equal(s, np.array(qd["scores_by_hand"], dtype=np.float64))
+        sel = oracle.select_blocks(s, o, hand["n_sel"])
+        assert sel.tolist() == qd["sel"]
+        toks = oracle.attended_tokens(sel, hand["block"], p, hand["t_kv"])
+        assert toks.tolist() == qd["tokens"]
+
+
+@pytest.mark.parametrize("which", ["attention_uniform", "attention_weighted"])
+def test_hand_attention(hand, which):
+    t_kv = hand["t_kv"]
+    v = np.arange(t_kv, dtype=np.float64)[:, None]
+    if which == "attention_uniform":
+        q = np.zeros((1, 1))
+        k = np.ones((t_kv, 1))
+    else:
+        q = np.ones((1, 1))
+        k = np.log(np.arange(t_kv, dtype=np.float64) + 1.0)[:, None]
+    for qd in hand["queries"]:
+        num, den = hand[which]["expected"][str(qd["position"])]
+        out = oracle.gated_attention(q, k, v, np.zeros((1, 1)), np.array(qd["tokens"]), 1.0)
+        assert out.shape == (1, 1)
+        assert abs(out[0, 0] - num / den) < 1e-14
+
+
+def test_hand_forward_end_to_end(hand):
+    """The whole path on the hand example, through forward_rows."""
+    t_kv = hand["t_kv"]
+    pos = [q["position"] for q in hand["queries"]]
+    t_q = t_kv  # every position is a query; only the hand-worked ones are checked
+    q_idx = np.zeros((1, t_q, 1, 2))
+    for qd in hand["queries"]:
+        q_idx[0, qd["position"], 0] = qd["q_idx"]
+    inputs = {
+        "q_idx": q_idx,
+        "k_idx": np.array(hand["k_idx"], dtype=np.float64)[None],
+        "q": np.ones((1, t_q, 1, 1, 1)),
+        "k": np.log(np.arange(t_kv, dtype=np.float64) + 1.0)[None, None, :, None],
+        "v": np.arange(t_kv, dtype=np.float64)[None, None, :, None],
+        "gate": np.zeros((1, t_q, 1, 1, 1)),
+    }
+    sel, out, _ = oracle.forward_rows(inputs, hand["block"], hand["topk_tokens"], 1.0,
+                                      [(0, p) for p in pos])
+    for r, qd in enumerate(hand["queries"]):
+        assert sel[r, 0].tolist() == qd["sel"]
+        num, den = hand["attention_weighted"]["expected"][str(qd["position"])]
+        assert abs(out[r, 0, 0, 0] - num / den) < 1e-14
+
+
+# ----------------------------------------------------------------------------------------------
+# constants the pages print
+# ----------------------------------------------------------------------------------------------
+def test_page_constants(golden_dir):
+    with open(os.path.join(golden_dir, "page_constants.json")) as f:
+        c = json.load(f)
+    B, k = c["final_block_size"]["value"], c["final_topk_tokens"]["value"]
+    assert oracle.n_selected_blocks(k, B) == c["selected_blocks"]["value"]
+    # the workloads carry the pages' setting
+    for name in ("32k", "128k", "decode", "1m"):
+        w = get_workload(name)
+        assert (w.block, w.topk, w.n_sel) == (B, k, c["selected_blocks"]["value"])
+    assert get_workload("1m").t_kv == c["max_context_tokens"]["value"]
+
+
+def test_eightfold_candidate_reduction(golden_dir):
+    """Indexer/top-k work is the number of scored candidates; B=8 cuts it ~8x (pages' claim).
+
+    Closed form over a full 128K prefill: sum_p p / sum_p floor(p/8) = (N-1)/(N/8-1).
+    """
+    with open(os.path.join(golden_dir, "page_constants.json")) as f:
+        c = json.load(f)
+    N = 131072
+    b1 = sum(oracle.scored_candidates(p, c["reference_block_size"]["value"]) for p in range(N))
+    b8 = sum(oracle.scored_candidates(p, c["final_block_size"]["value"]) for p in range(N))
+    assert Fraction(b1, b8) == Fraction(N - 1, N // 8 - 1)
+    assert abs(b1 / b8 - c["indexer_topk_cost_reduction"]["value"]) < 1e-3
+
+
+# ----------------------------------------------------------------------------------------------
+# compression: closed forms and invariants
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T", [(8, 64), (8, 61), (3, 20), (1, 7), (16, 40)])
+def test_compress_arithmetic_sequence(B, T):
+    """k_idx[t] = (t, 1): block j sums to (sum of its token indices, its token count)."""
+    k_idx = np.stack([np.arange(T, dtype=np.float64), np.ones(T)], axis=1)[None]
+    kb = oracle.compress(k_idx, B)[0]
+    assert kb.shape[0] == math.ceil(T / B)
+    for j in range(kb.shape[0]):
+        lo, hi = j * B, min(j * B + B, T) - 1
+        n = hi - lo + 1
+        assert kb[j, 0] == (lo + hi) * n / 2      # arithmetic series
+        assert kb[j, 1] == n
+
+
+def test_compress_invariants():
+    rng = np.random.default_rng(1)
+    k_idx = rng.integers(-4, 5, size=(2, 53, 6)).astype(np.float64)
+    for B in (1, 2, 5, 8):
+        kb = oracle.compress(k_idx, B)
+        np.testing.assert_array_equal(kb.sum(axis=1), k_idx.sum(axis=1))
+    np.testing.assert_array_equal(oracle.compress(k_idx, 1), k_idx)
+
+
+# ----------------------------------------------------------------------------------------------
+# scores
+# ----------------------------------------------------------------------------------------------
+def test_scores_unit_queries_pick_columns():
+    rng = np.random.default_rng(2)
+    k_idx = rng.integers(-4, 5, size=(1, 40, 5)).astype(np.float64)
+    kb = oracle.compress(k_idx, 8)[0]
+    for c in range(5):
+        e = np.zeros(5)
+        e[c] = 1.0
+        s = oracle.block_scores(e, kb, 5)
+        # column c of the block sums of the raw keys
+        expect = [k_idx[0, 8 * j:8 * j + 8, c].sum() for j in range(5)]
+        np.testing.assert_array_equal(s, expect)
+
+
+def test_scores_bilinear_and_permutation_invariant():
+    rng = np.random.default_rng(3)
+    kb = rng.integers(-32, 33, size=(30, 7)).astype(np.float64)
+    a = rng.integers(-4, 5, size=7).astype(np.float64)
+    b = rng.integers(-4, 5, size=7).astype(np.float64)
+    np.testing.assert_array_equal(oracle.block_scores(a + 2 * b, kb, 30),
+                                  oracle.block_scores(a, kb, 30) + 2 * oracle.block_scores(b, kb, 30))
+    perm = rng.permutation(7)
+    np.testing.assert_array_equal(oracle.block_scores(a[perm], kb[:, perm], 30),
+                                  oracle.block_scores(a, kb, 30))
+
+
+# ----------------------------------------------------------------------------------------------
+# selection
+# ----------------------------------------------------------------------------------------------
+def _brute_force_selection(s, o, n_sel):
+    """Independent O(n^2) definition: j is chosen iff j == o, or fewer than n_sel-1 candidates beat
+    it, where j' beats j when s[j'] > s[j] or (s[j'] == s[j] and j' < j)."""
+    if o + 1 <= n_sel:
+        return list(range(o + 1))
+    chosen = [o]
+    for j in range(o):
+        beaten_by = sum(1 for jj in range(o) if s[jj] > s[j] or (s[jj] == s[j] and jj < j))
+        if beaten_by < n_sel - 1:
+            chosen.append(j)
+    return sorted(chosen)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
+def test_selection_brute_force(B):
+    rng = np.random.default_rng(10 + B)
+    T = 64
+    k_idx = rng.integers(-1, 2, size=(1, T, 3)).astype(np.float64)   # tiny range: many ties
+    kb = oracle.compress(k_idx, B)[0]
+    for p in range(T):
+        o = p // B
+        q = rng.integers(-1, 2, size=3).astype(np.float64)
+        s = oracle.block_scores(q, kb, o)
+        for n_sel in range(1, oracle.num_blocks(T, B) + 2):
+            sel = oracle.select_blocks(s, o, n_sel)
+            got = [j for j in sel.tolist() if j >= 0]
+            assert got == _brute_force_selection(s.tolist(), o, n_sel)
+            assert sel.tolist()[len(got):] == [-1] * (n_sel - len(got))
+
+
+def test_selection_b1_is_token_level_topk():
+    """B=1: own token plus the top k-1 past tokens, ties to the lower token (heapq, no sort)."""
+    rng = np.random.default_rng(4)
+    T, k = 300, 64
+    k_idx = rng.integers(-4, 5, size=(1, T, 8)).astype(np.float64)
+    kb = oracle.compress(k_idx, 1)[0]
+    for p in range(0, T, 7):
+        q = rng.integers(-4, 5, size=8).astype(np.float64)
+        s = k_idx[0, :p] @ q                      # token-level scores, computed directly
+        sel = oracle.select_blocks(oracle.block_scores(q, kb, p), p, k)
+        got = sorted(j for j in sel.tolist() if j >= 0)
+        if p + 1 <= k:
+            expect = list(range(p + 1))
+        else:
+            best = heapq.nlargest(k - 1, range(p), key=lambda j: (s[j], -j))
+            expect = sorted(best + [p])
+        assert got == expect
+
+
+def test_selection_dense_when_budget_covers_context():
+    rng = np.random.default_rng(5)
+    T, B = 96, 8
+    kb = oracle.compress(rng.integers(-4, 5, size=(1, T, 4)).astype(np.float64), B)[0]
+    nb = oracle.num_blocks(T, B)
+    for p in range(T):
+        o = p // B
+        s = oracle.block_scores(rng.integers(-4, 5, size=4), kb, o)
+        sel = oracle.select_blocks(s, o, nb)
+        assert [j for j in sel.tolist() if j >= 0] == list(range(o + 1))
+        assert oracle.attended_tokens(sel, B, p, T).tolist() == list(range(p + 1))
+
+
+def test_selection_nesting_and_shape():
+    rng = np.random.default_rng(6)
+    s = rng.integers(-3, 4, size=200).astype(np.float64)
+    o = 200
+    prev = set()
+    for n_sel in range(1, 210):
+        sel = oracle.select_blocks(s, o, n_sel)
+        cur = {j for j in sel.tolist() if j >= 0}
+        assert len(cur) == min(n_sel, o + 1)
+        assert o in cur and max(cur) == o and min(cur) >= 0
+        assert prev <= cur
+        assert sorted(cur) == [j for j in sel.tolist() if j >= 0]
+        prev = cur
+
+
+def test_selection_scale_invariance_and_negative_zero():
+    rng = np.random.default_rng(7)
+    s = rng.integers(-3, 4, size=50).astype(np.float64)
+    ref = oracle.select_blocks(s, 50, 11)
+    np.testing.assert_array_equal(oracle.select_blocks(3.0 * s, 50, 11), ref)
+    z = np.zeros(20)
+    z[::2] = -0.0
+    # -0.0 and +0.0 are equal scores: ties go to the lowest indices
+    assert oracle.select_blocks(z, 20, 6).tolist() == [0, 1, 2, 3, 4, 20]
+
+
+# ----------------------------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------------------------
+def _sdpa_reference(inp, mask, scale):
+    """torch SDPA in fp64 with an explicit boolean mask [T_q, T_kv], times sigmoid(gate)."""
+    q = inp["q"].to(torch.float64)                      # [Bt, Tq, G, h, d]
+    Bt, Tq, G, h, d = q.shape
+    k = inp["k"].to(torch.float64).repeat_interleave(h, dim=1)   # [Bt, G*h, Tkv, d]
+    v = inp["v"].to(torch.float64).repeat_interleave(h, dim=1)
+    qh = q.reshape(Bt, Tq, G * h, d).transpose(1, 2)             # [Bt, G*h, Tq, d]
+    o = torch.nn.functional.scaled_dot_product_attention(qh, k, v, attn_mask=mask, scale=scale)
+    o = o.transpose(1, 2).reshape(Bt, Tq, G, h, d)
+    return (o * torch.sigmoid(inp["gate"].to(torch.float64))).numpy()
+
+
+@pytest.mark.parametrize("t_q,t_kv", [(40, 40), (13, 40), (1, 33)])
+def test_attention_dense_equals_sdpa(t_q, t_kv):
+    w, inp = generate_small(t_q=t_q, t_kv=t_kv, groups=2, heads=3, head_dim=8, index_dim=4,
+                            block=8, topk=64, seed=3)
+    sel, out, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    pos = torch.arange(t_kv - t_q, t_kv)
+    mask = torch.arange(t_kv)[None, :] <= pos[:, None]            # bottom-right causal
+    ref = _sdpa_reference(inp, mask, w.softmax_scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_sparse_equals_masked_sdpa():
+    """A sparse selection equals dense SDPA under the selection's token mask (built from sel)."""
+    w, inp = generate_small(t_q=48, t_kv=80, groups=2, heads=2, head_dim=8, index_dim=4,
+                            block=4, topk=16, seed=9)
+    sel, out, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv)
+    for g in range(w.groups):
+        mask = torch.zeros(w.t_q, w.t_kv, dtype=torch.bool)
+        for i in range(w.t_q):
+            chosen = set(sel[0, i, g].tolist()) - {-1}
+            for t in range(w.t_kv):
+                mask[i, t] = bool((t // w.block) in chosen and t <= int(pos[i]))
+        sub = {n: inp[n][:, :, g:g + 1] for n in ("q", "gate")}
+        sub.update({n: inp[n][:, g:g + 1] for n in ("k", "v")})
+        ref = _sdpa_reference(sub, mask, w.softmax_scale)
+        np.testing.assert_allclose(out[:, :, g:g + 1], ref, rtol=0, atol=1e-12)
+        # the test is only meaningful if late queries really are sparse
+        assert (sel[0, -1, g] >= 0).sum() == w.n_sel
+
+
+def test_attention_constant_values_and_first_token():
+    rng = np.random.default_rng(8)
+    q = rng.normal(size=(4, 16))
+    k = rng.normal(size=(30, 16))
+    g = rng.normal(size=(4, 16))
+    c = rng.normal(size=16)
+    v = np.tile(c, (30, 1))
+    toks = np.array([0, 3, 4, 9, 17])
+    out = oracle.gated_attention(q, k, v, g, toks, 0.3)
+    np.testing.assert_allclose(out, c[None, :] / (1 + np.exp(-g)), rtol=1e-14, atol=1e-15)
+    v2 = rng.normal(size=(30, 16))
+    out0 = oracle.gated_attention(q, k, v2, g, np.array([0]), 0.3)
+    np.testing.assert_allclose(out0, v2[0][None, :] / (1 + np.exp(-g)), rtol=1e-14, atol=1e-15)
+
+
+def test_attention_token_order_invariant():
+    rng = np.random.default_rng(9)
+    q, k, v, g = (rng.normal(size=s) for s in ((2, 8), (40, 8), (40, 8), (2, 8)))
+    toks = np.array([1, 5, 6, 20, 33, 39])
+    a = oracle.gated_attention(q, k, v, g, toks, 0.5)
+    b = oracle.gated_attention(q, k, v, g, toks[::-1].copy(), 0.5)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------------------------
+# inclusion rate (measured property; parity unpinned) -- only its definition's edge cases
+# ----------------------------------------------------------------------------------------------
+def test_inclusion_rate_edge_cases():
+    w, inp = generate_small(t_q=64, t_kv=64, groups=2, index_dim=4, seed=2)
+    rows = [(0, i) for i in range(64)]
+    same = oracle.inclusion_rate(inp["q_idx"], inp["k_idx"], rows, 64, (1, 16), (1, 16))
+    assert np.all(same == 1.0)
+    dense = oracle.inclusion_rate(inp["q_idx"], inp["k_idx"], rows, 64, (8, 64), (1, 16))
+    assert np.all(dense == 1.0)          # a dense selection includes everything
+    r = oracle.inclusion_rate(inp["q_idx"], inp["k_idx"], rows, 64, (8, 16), (1, 16))
+    assert np.all((r >= 0) & (r <= 1)) and r.min() < 1.0
