@@ -1,0 +1,164 @@
+/*
+ * sgqa.h -- C ABI of the MI355X (gfx950) Sparse GQA forward path.
+ *
+ * Sparse GQA is the full-context attention layer of Step 5 Preview (Step 5 Preview summary on
+ * mo.ai.kr, section "모델 구조와 학습 안정성"; ai.info article, section "Sparse GQA punta a un
+ * contesto di 1 milione di token").  Per (query token, KV group) it
+ *   1. compresses the shared index keys into blocks of B tokens          (sgqa_index, k_idx != NULL)
+ *   2. scores the query's index vector against every causal past block   (sgqa_index)
+ *   3. keeps the top k/B blocks independently for each KV group          (sgqa_topk)
+ *   4. runs sigmoid-gated grouped-query attention over only those tokens (sgqa_attend)
+ * and sgqa_forward chains the four steps.
+ *
+ * Readings fixed where the pages are silent: a block key is the SUM of its B index keys; the score
+ * is the raw dot product; the query's own block o = p / B is always selected, counts toward the
+ * k/B budget and is causally masked inside (tokens t <= p); among past blocks higher scores win
+ * and equal scores go to the lower block index; when o + 1 <= k/B every causal block is taken;
+ * out = sigmoid(gate) * attention, elementwise; the softmax scale is an argument; query head j of
+ * group g attends with group g's keys and values; the t_q queries are the last t_q positions of
+ * the key stream, p = t_kv - t_q + i.
+ *
+ * Conventions (every call):
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA memory) of the current
+ *     device, contiguous row-major in the layout stated below, aligned to 16 bytes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; results are valid once the stream has been synchronised.
+ *   - The caller owns every buffer, workspaces included; the library allocates no device memory,
+ *     keeps no state between calls and never synchronises.  Inputs are read-only; outputs must not
+ *     alias inputs.  Concurrent calls need distinct outputs and workspaces.
+ *   - Arguments are validated on the host before anything is enqueued.  On any error the call
+ *     returns a non-zero sgqa_status, enqueues nothing and touches no output; sgqa_last_error()
+ *     then gives a human-readable detail (thread-local).  A failed launch returns SGQA_ERR_HIP.
+ *     Nothing aborts the process or throws across this boundary.
+ *   - NaN / Inf inputs are not detected and give unspecified results.
+ *
+ * Layouts (Bt = batch, Tq = t_q, Tk = t_kv, G = kv_groups, H = heads_per_group, D = head_dim,
+ * Di = index_dim, NB = ceil(Tk / B), NS = topk_tokens / B):
+ *   q, gate, out : [Bt, Tq, G, H, D]      dtype
+ *   k, v         : [Bt, G, Tk, D]         dtype
+ *   q_idx        : [Bt, Tq, G, Di]        index_dtype   (index query per token and KV group)
+ *   k_idx        : [Bt, Tk, Di]           index_dtype   (index key per token, shared by all groups)
+ *   k_blk        : [Bt, NB, Di]           index_dtype   (block keys; rounded to index_dtype)
+ *   scores       : [Bt, Tq, G, NB]        float32       (entry j valid for j < p / B only)
+ *   sel          : [Bt, Tq, G, NS]        int32         (selected blocks ascending, -1 padded)
+ */
+#ifndef SGQA_H_
+#define SGQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGQA_ABI_VERSION 1
+
+typedef enum {
+  SGQA_OK = 0,
+  SGQA_ERR_NULL = 1,         /* a required pointer is NULL                                   */
+  SGQA_ERR_SHAPE = 2,        /* an inconsistent or out-of-range size                          */
+  SGQA_ERR_UNSUPPORTED = 3,  /* valid, but outside what the kernels implement                 */
+  SGQA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                              */
+  SGQA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than sgqa_sizes() asks for        */
+  SGQA_ERR_HIP = 6           /* the HIP runtime reported an error (detail in sgqa_last_error) */
+} sgqa_status;
+
+typedef enum { SGQA_F32 = 0, SGQA_BF16 = 1 } sgqa_dtype;
+
+/* Problem descriptor; passed by const pointer, never retained. */
+typedef struct {
+  int64_t batch;            /* Bt >= 1                                                   */
+  int64_t t_q;              /* 1 <= t_q <= t_kv                                          */
+  int64_t t_kv;             /* >= 1                                                      */
+  int32_t kv_groups;        /* G >= 1                                                    */
+  int32_t heads_per_group;  /* H >= 1 (query heads of KV group g are g*H .. g*H+H-1)      */
+  int32_t head_dim;         /* D in {64, 128}                                            */
+  int32_t index_dim;        /* Di in {32, 64, 128}                                        */
+  int32_t block;            /* B >= 1                                                    */
+  int32_t topk_tokens;      /* k >= B, k % B == 0; NS = k / B <= 4096                     */
+  float softmax_scale;      /* > 0, finite (1/sqrt(D) in the usual setting)               */
+  int32_t dtype;            /* sgqa_dtype of q, k, v, gate, out                          */
+  int32_t index_dtype;      /* sgqa_dtype of q_idx, k_idx, k_blk                         */
+} sgqa_problem;
+
+/* Derived sizes (bytes unless stated). */
+typedef struct {
+  int64_t num_blocks;               /* NB                                                  */
+  int64_t n_sel;                    /* NS                                                  */
+  size_t k_blk_bytes;               /* k_blk buffer                                        */
+  size_t scores_bytes;              /* scores buffer for sgqa_index / sgqa_topk            */
+  size_t sel_bytes;                 /* sel buffer                                          */
+  size_t attend_workspace_bytes;    /* workspace sgqa_attend needs                         */
+  size_t forward_workspace_bytes;   /* workspace sgqa_forward needs (fixed size)           */
+} sgqa_sizes_t;
+
+/* ABI version of the loaded library (SGQA_ABI_VERSION when it matches this header). */
+int sgqa_abi_version(void);
+
+/* Static text for a status code. */
+const char* sgqa_status_string(sgqa_status status);
+
+/* Detail of the last error on the calling thread ("" after a successful call). */
+const char* sgqa_last_error(void);
+
+/* Validate `prob` and fill `out` with the derived sizes.  Host only; touches no device. */
+sgqa_status sgqa_sizes(const sgqa_problem* prob, sgqa_sizes_t* out);
+
+/*
+ * Steps 1-2: block compression and the indexer.
+ *   k_idx  : [Bt, Tk, Di] or NULL.  If non-NULL, k_blk is first written as the block sums of k_idx
+ *            (fp32 accumulation, rounded to index_dtype).  If NULL, k_blk is an INPUT holding block
+ *            keys computed earlier (a decode cache).
+ *   k_blk  : [Bt, NB, Di]
+ *   q_idx  : [Bt, Tq, G, Di]
+ *   scores : [Bt, Tq, G, NB] float32; scores[b,i,g,j] = q_idx[b,i,g,:] . k_blk[b,j,:] for every
+ *            j < p_i / B (p_i = Tk - Tq + i), accumulated in fp32.  Entries j >= p_i / B are left
+ *            untouched.  Integer-valued index data with |score| < 2^24 gives exact scores.
+ */
+sgqa_status sgqa_index(const sgqa_problem* prob, const void* q_idx, const void* k_idx,
+                       void* k_blk, float* scores, void* stream);
+
+/*
+ * Step 3: per-(query, KV group) block selection from stored scores.
+ *   scores : [Bt, Tq, G, NB] float32 as written by sgqa_index (only j < p/B is read).
+ *   sel    : [Bt, Tq, G, NS] int32.  With o = p / B: if o + 1 <= NS, sel = 0..o then -1s;
+ *            otherwise sel = {o} plus the NS-1 candidates j < o with the largest scores, equal
+ *            scores going to the lower j, listed ascending.  -0.0 and +0.0 are equal scores.
+ */
+sgqa_status sgqa_topk(const sgqa_problem* prob, const float* scores, int32_t* sel, void* stream);
+
+/*
+ * Step 4: gated grouped-query attention over the selected tokens.
+ *   q, gate : [Bt, Tq, G, H, D];  k, v : [Bt, G, Tk, D];  sel : [Bt, Tq, G, NS] (as sgqa_topk).
+ *   out     : [Bt, Tq, G, H, D]; for head j of group g, query i at p = Tk - Tq + i:
+ *             out = sigmoid(gate) * sum_t softmax_t(scale * q . k_t) v_t over the tokens t <= p
+ *             of the selected blocks.  fp32 accumulation; bf16 outputs are rounded to nearest even.
+ *   workspace: >= sizes.attend_workspace_bytes of device memory (a block-packed copy of v).
+ *   The attention kernels need B to divide 8 or be a multiple of 8; other block sizes return
+ *   SGQA_ERR_UNSUPPORTED (steps 1-3 accept any B).
+ */
+sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, const void* v,
+                        const void* gate, const int32_t* sel, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Steps 1-4 in one call.
+ *   k_idx   : as in sgqa_index (NULL = k_blk already holds the block keys).
+ *   k_blk   : [Bt, NB, Di] (written when k_idx != NULL).
+ *   sel_out : [Bt, Tq, G, NS] or NULL (the selection is then not returned).
+ *   out     : [Bt, Tq, G, H, D].
+ *   workspace: >= sizes.forward_workspace_bytes.  Scores are never stored in full: the selection
+ *   is computed from block scores recomputed in tiles and the surviving candidates only.
+ * Results equal sgqa_index + sgqa_topk + sgqa_attend on the same inputs (selection bit-exact).
+ */
+sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k, const void* v,
+                         const void* gate, const void* q_idx, const void* k_idx, void* k_blk,
+                         int32_t* sel_out, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* SGQA_H_ */

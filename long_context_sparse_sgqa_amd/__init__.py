@@ -1,0 +1,239 @@
+"""Sparse GQA forward path on MI355X (gfx950): Python binding of the libsgqa.so C ABI.
+
+Argument marshalling only.  Every step of the path (block compression, indexer, top-k selection,
+gated attention) runs in the library's HIP kernels; torch supplies device memory and the current
+stream.  There is no CPU fallback: if libsgqa.so is missing or cannot be loaded, importing the
+binding's functions raises.
+
+Layouts and semantics are those of include/sgqa.h:
+  q, gate, out : [Bt, Tq, G, H, D]       k, v : [Bt, G, Tk, D]
+  q_idx        : [Bt, Tq, G, Di]         k_idx: [Bt, Tk, Di]        k_blk: [Bt, NB, Di]
+  scores       : [Bt, Tq, G, NB] fp32    sel  : [Bt, Tq, G, NS] int32
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["Problem", "load_library", "library_path", "abi_version", "sizes", "index", "topk",
+           "attend", "forward", "SgqaError", "EXPORTED_SYMBOLS"]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libsgqa.so"
+
+SGQA_F32, SGQA_BF16 = 0, 1
+_DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
+
+EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
+                    "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward")
+
+
+class SgqaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"sgqa status {status}: {detail}")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("t_q", ctypes.c_int64), ("t_kv", ctypes.c_int64),
+                ("kv_groups", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("topk_tokens", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("index_dtype", ctypes.c_int32)]
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int64), ("n_sel", ctypes.c_int64),
+                ("k_blk_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t),
+                ("sel_bytes", ctypes.c_size_t), ("attend_workspace_bytes", ctypes.c_size_t),
+                ("forward_workspace_bytes", ctypes.c_size_t)]
+
+
+class Problem:
+    """Problem descriptor (sgqa_problem)."""
+
+    def __init__(self, batch, t_q, t_kv, kv_groups, heads_per_group, head_dim, index_dim, block,
+                 topk_tokens, softmax_scale=None, dtype=torch.bfloat16, index_dtype=torch.bfloat16):
+        self.batch, self.t_q, self.t_kv = int(batch), int(t_q), int(t_kv)
+        self.kv_groups, self.heads_per_group = int(kv_groups), int(heads_per_group)
+        self.head_dim, self.index_dim = int(head_dim), int(index_dim)
+        self.block, self.topk_tokens = int(block), int(topk_tokens)
+        self.softmax_scale = float(softmax_scale if softmax_scale is not None
+                                   else 1.0 / math.sqrt(head_dim))
+        self.dtype, self.index_dtype = dtype, index_dtype
+
+    @classmethod
+    def from_workload(cls, w, **overrides):
+        kw = dict(batch=w.batch, t_q=w.t_q, t_kv=w.t_kv, kv_groups=w.groups,
+                  heads_per_group=w.heads, head_dim=w.head_dim, index_dim=w.index_dim,
+                  block=w.block, topk_tokens=w.topk, softmax_scale=w.softmax_scale,
+                  dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                  index_dtype=torch.float32 if w.index_dtype == "f32" else torch.bfloat16)
+        kw.update(overrides)
+        return cls(**kw)
+
+    @property
+    def num_blocks(self):
+        return -(-self.t_kv // self.block)
+
+    @property
+    def n_sel(self):
+        return self.topk_tokens // self.block
+
+    def _c(self) -> _Problem:
+        return _Problem(self.batch, self.t_q, self.t_kv, self.kv_groups, self.heads_per_group,
+                        self.head_dim, self.index_dim, self.block, self.topk_tokens,
+                        self.softmax_scale, _DT.get(self.dtype, -1), _DT.get(self.index_dtype, -1))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_PKG_DIR, _LIB_NAME)
+
+
+def load_library():
+    """Load libsgqa.so (built in-tree by long_context_sparse_sgqa_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m long_context_sparse_sgqa_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    P = ctypes.POINTER(_Problem)
+    lib.sgqa_abi_version.restype = ctypes.c_int
+    lib.sgqa_status_string.restype = ctypes.c_char_p
+    lib.sgqa_status_string.argtypes = [ctypes.c_int]
+    lib.sgqa_last_error.restype = ctypes.c_char_p
+    lib.sgqa_sizes.argtypes = [P, ctypes.POINTER(_Sizes)]
+    lib.sgqa_index.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.sgqa_topk.argtypes = [P, vp, vp, vp]
+    lib.sgqa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sgqa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().sgqa_abi_version()
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise SgqaError(status, (lib.sgqa_last_error() or b"").decode())
+
+
+def sizes(prob: Problem) -> dict:
+    s = _Sizes()
+    _check(load_library().sgqa_sizes(ctypes.byref(prob._c()), ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in _Sizes._fields_}
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, shape, dtype):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _shapes(p: Problem):
+    Bt, Tq, Tk, G, H = p.batch, p.t_q, p.t_kv, p.kv_groups, p.heads_per_group
+    D, Di, NB, NS = p.head_dim, p.index_dim, p.num_blocks, p.n_sel
+    return dict(q=(Bt, Tq, G, H, D), k=(Bt, G, Tk, D), q_idx=(Bt, Tq, G, Di), k_idx=(Bt, Tk, Di),
+                k_blk=(Bt, NB, Di), scores=(Bt, Tq, G, NB), sel=(Bt, Tq, G, NS))
+
+
+def index(prob: Problem, q_idx, k_idx, k_blk=None, scores=None, stream=None):
+    """Steps 1-2.  k_idx=None scores against the given k_blk.  Returns (k_blk, scores)."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q_idx.device
+    if k_blk is None:
+        k_blk = torch.empty(sh["k_blk"], dtype=prob.index_dtype, device=dev)
+    if scores is None:
+        scores = torch.empty(sh["scores"], dtype=torch.float32, device=dev)
+    _check(lib.sgqa_index(ctypes.byref(prob._c()), _ptr(q_idx, "q_idx", sh["q_idx"], prob.index_dtype),
+                          _ptr(k_idx, "k_idx", sh["k_idx"], prob.index_dtype),
+                          _ptr(k_blk, "k_blk", sh["k_blk"], prob.index_dtype),
+                          _ptr(scores, "scores", sh["scores"], torch.float32), _stream(stream)))
+    return k_blk, scores
+
+
+def topk(prob: Problem, scores, sel=None, stream=None):
+    """Step 3.  Returns sel [Bt, Tq, G, NS] int32."""
+    lib = load_library()
+    sh = _shapes(prob)
+    if sel is None:
+        sel = torch.empty(sh["sel"], dtype=torch.int32, device=scores.device)
+    _check(lib.sgqa_topk(ctypes.byref(prob._c()), _ptr(scores, "scores", sh["scores"], torch.float32),
+                         _ptr(sel, "sel", sh["sel"], torch.int32), _stream(stream)))
+    return sel
+
+
+def attend(prob: Problem, q, k, v, gate, sel, out=None, workspace=None, stream=None):
+    """Step 4.  Returns out [Bt, Tq, G, H, D]."""
+    lib = load_library()
+    sh = _shapes(prob)
+    if out is None:
+        out = torch.empty(sh["q"], dtype=prob.dtype, device=q.device)
+    need = sizes(prob)["attend_workspace_bytes"]
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.sgqa_attend(ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype),
+                           _ptr(k, "k", sh["k"], prob.dtype), _ptr(v, "v", sh["k"], prob.dtype),
+                           _ptr(gate, "gate", sh["q"], prob.dtype),
+                           _ptr(sel, "sel", sh["sel"], torch.int32),
+                           _ptr(out, "out", sh["q"], prob.dtype),
+                           workspace.data_ptr() if workspace is not None else None,
+                           workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
+
+
+def forward(prob: Problem, q, k, v, gate, q_idx, k_idx, k_blk=None, out=None, sel=None,
+            return_sel=False, workspace=None, stream=None):
+    """Steps 1-4.  k_idx=None reuses the block keys in k_blk.  Returns out (and sel)."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q.device
+    if k_blk is None:
+        k_blk = torch.empty(sh["k_blk"], dtype=prob.index_dtype, device=dev)
+    if out is None:
+        out = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    if sel is None and return_sel:
+        sel = torch.empty(sh["sel"], dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(sizes(prob)["forward_workspace_bytes"], dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_forward(ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype),
+                            _ptr(k, "k", sh["k"], prob.dtype), _ptr(v, "v", sh["k"], prob.dtype),
+                            _ptr(gate, "gate", sh["q"], prob.dtype),
+                            _ptr(q_idx, "q_idx", sh["q_idx"], prob.index_dtype),
+                            _ptr(k_idx, "k_idx", sh["k_idx"], prob.index_dtype),
+                            _ptr(k_blk, "k_blk", sh["k_blk"], prob.index_dtype),
+                            _ptr(sel, "sel", sh["sel"], torch.int32),
+                            _ptr(out, "out", sh["q"], prob.dtype), workspace.data_ptr(),
+                            workspace.numel(), _stream(stream)))
+    return (out, sel) if return_sel else out

@@ -1,0 +1,497 @@
+// Step 4 -- gated grouped-query attention over the selected tokens.
+//
+// The Step 5 Preview pages (mo.ai.kr summary, section "모델 구조와 학습 안정성"; ai.info article,
+// section on the 3:1 layer mix) build Sparse GQA on Gated GQA and attend only over the selected
+// blocks; the same passage notes that adjacent tokens' selections overlap a lot and that batching
+// them raises GPU utilisation.  Readings fixed here: query head j of KV group g attends with group
+// g's keys and values; the attended set of a query at position p is every token t <= p of its
+// selected blocks; out = sigmoid(gate) * softmax(scale * q.k) v, elementwise in the gate.
+//
+// Matrix-core path (bf16, 8 heads per group, B dividing 8 or a multiple of 8):
+//   * one wavefront owns two adjacent query tokens of one KV group: 2 tokens x 8 heads = 16 rows,
+//     the M = 16 of v_mfma_f32_16x16x32_bf16.  The two tokens' selections are expanded into sorted
+//     lists of 8-token units (with per-token bitmasks) and merged into their union in LDS, so a unit
+//     both tokens chose is loaded and multiplied once (the overlap the pages exploit);
+//   * the union is consumed 4 units (32 tokens) at a time: S^T = K Q^T on 2 x D/32 MFMAs, with the
+//     K rows permuted so that every lane ends up holding the 8 scores of ONE unit for ONE row;
+//     masking (unit not chosen by the row's token, or t > p), an online softmax in the exp2 domain,
+//     then O^T += V^T P^T on D/16 MFMAs whose P operand is exactly the lane's 8 probabilities;
+//   * V is read from a unit-packed copy [.., unit, d, 8 tokens] so the V^T operand is one 16-byte
+//     load per lane;
+//   * the epilogue divides by the row sum and multiplies by sigmoid(gate) before a bf16 store.
+//   Workgroups are numbered with the KV group fastest, so with 8 groups every XCD (workgroups are
+//   dealt round-robin to the 8 XCDs) serves one group and its L2 holds only that group's K/V.
+// Plain path (fp32, or other head counts): one workgroup per (token, group), 32 lanes per head,
+// sequential online softmax over the attended tokens in fp32.
+#include "device_common.h"
+#include "sgqa_internal.h"
+
+namespace sgqa {
+namespace {
+
+constexpr int kMfmaWaves = 4;
+// Unit-list capacity per token on the matrix-core path (LDS: 4 waves x 24 bytes x units <= 96 KiB).
+constexpr int64_t kMaxUnits = 1024;
+
+// ------------------------------------------------------------------------------------------------
+// V packing: vp[b, g, u, d, e] = v[b, g, 8u + e, d] (zero past Tk)
+// ------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) pack_v_kernel(const T* __restrict__ v, T* __restrict__ vp,
+                                                     int64_t Tk, int64_t NU, int D, int64_t total) {
+  for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int d = static_cast<int>(id % D);
+    const int64_t u = (id / D) % NU;
+    const int64_t bg = id / (static_cast<int64_t>(D) * NU);
+    const T* src = v + bg * Tk * D + d;
+    T vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t t = u * 8 + e;
+      vals[e] = (t < Tk) ? src[t * D] : T(0);
+    }
+    T* dst = vp + ((bg * NU + u) * D + d) * 8;
+    if constexpr (sizeof(T) == 2) {
+      uint4 w;
+      w.x = vals[0] | (static_cast<uint32_t>(vals[1]) << 16);
+      w.y = vals[2] | (static_cast<uint32_t>(vals[3]) << 16);
+      w.z = vals[4] | (static_cast<uint32_t>(vals[5]) << 16);
+      w.w = vals[6] | (static_cast<uint32_t>(vals[7]) << 16);
+      *reinterpret_cast<uint4*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = vals[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Unit lists.  An entry is unit | (mask << 24): unit u covers tokens 8u .. 8u+7, mask bit e says
+// token 8u+e belongs to a selected block.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_lt_count(uint64_t bal, int lane) {
+  return __popcll(bal & ((1ull << lane) - 1ull));
+}
+
+// Expands one token's selection (NS entries; entries outside [0, o] are ignored) into its sorted
+// unit list; returns the entry count.  B is a multiple of 8 or divides 8.
+__device__ int build_units(const int32_t* __restrict__ selrow, int NS, int B, int64_t o,
+                           uint32_t* list, int lane) {
+  int running = 0;
+  if (B >= 8) {
+    const int U = B >> 3;
+    for (int base = 0; base < NS; base += 64) {
+      const int e = base + lane;
+      const int blk = (e < NS) ? selrow[e] : -1;
+      const bool valid = blk >= 0 && blk <= o;
+      const uint64_t bal = __ballot(valid);
+      if (valid) {
+        const int pos = running + U * lane_lt_count(bal, lane);
+        for (int u = 0; u < U; ++u) list[pos + u] = static_cast<uint32_t>(blk * U + u) | (0xffu << 24);
+      }
+      running += U * __popcll(bal);
+    }
+  } else {
+    const uint32_t bmask = (1u << B) - 1u;
+    for (int base = 0; base < NS; base += 64) {
+      const int e = base + lane;
+      const int blk = (e < NS) ? selrow[e] : -1;
+      const bool valid = blk >= 0 && blk <= o;
+      const int unit = (blk * B) >> 3;
+      bool head = false;
+      uint32_t mask = 0u;
+      if (valid) {
+        const int prev = (e > 0) ? selrow[e - 1] : -1;
+        const bool prev_valid = prev >= 0 && prev <= o;
+        head = !(prev_valid && ((prev * B) >> 3) == unit);
+        if (head) {
+          mask = bmask << ((blk * B) & 7);
+          for (int k2 = 1; k2 < 8 && e + k2 < NS; ++k2) {
+            const int nb2 = selrow[e + k2];
+            if (!(nb2 >= 0 && nb2 <= o) || ((nb2 * B) >> 3) != unit) break;
+            mask |= bmask << ((nb2 * B) & 7);
+          }
+        }
+      }
+      const uint64_t bal = __ballot(head);
+      if (head) list[running + lane_lt_count(bal, lane)] = static_cast<uint32_t>(unit) | (mask << 24);
+      running += __popcll(bal);
+    }
+  }
+  return running;
+}
+
+// Number of entries of a sorted unit list whose unit is <= last_unit.
+__device__ int count_units_upto(const uint32_t* list, int n, int64_t last_unit, int lane) {
+  int cnt = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int e = base + lane;
+    const bool keep = e < n && static_cast<int64_t>(list[e] & 0xffffffu) <= last_unit;
+    cnt += __popcll(__ballot(keep));
+  }
+  return cnt;
+}
+
+__device__ __forceinline__ int lower_bound_units(const uint32_t* list, int n, uint32_t unit) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((list[mid] & 0xffffffu) < unit) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Union of the two sorted unit lists: uunit[] ascending, umask[] = maskA | maskB << 8.
+__device__ int merge_units(const uint32_t* la, int na, const uint32_t* lb, int nb, int32_t* uunit,
+                           uint32_t* umask, int lane) {
+  int dups = 0;
+  for (int base = 0; base < na; base += 64) {
+    const int i = base + lane;
+    const uint32_t ea = (i < na) ? la[i] : 0u;
+    const uint32_t ua = ea & 0xffffffu;
+    const int x = (i < na) ? lower_bound_units(lb, nb, ua) : 0;
+    const bool eq = (i < na) && x < nb && (lb[x] & 0xffffffu) == ua;
+    const uint64_t bal = __ballot(eq);
+    if (i < na) {
+      const int pos = i + x - (dups + lane_lt_count(bal, lane));
+      uunit[pos] = static_cast<int32_t>(ua);
+      umask[pos] = (ea >> 24) | (eq ? ((lb[x] >> 24) << 8) : 0u);
+    }
+    dups += __popcll(bal);
+  }
+  int dups_b = 0;
+  for (int base = 0; base < nb; base += 64) {
+    const int j = base + lane;
+    const uint32_t eb = (j < nb) ? lb[j] : 0u;
+    const uint32_t ub = eb & 0xffffffu;
+    const int x = (j < nb) ? lower_bound_units(la, na, ub) : 0;
+    const bool eq = (j < nb) && x < na && (la[x] & 0xffffffu) == ub;
+    const uint64_t bal = __ballot(eq);
+    if (j < nb && !eq) {
+      const int pos = j + x - (dups_b + lane_lt_count(bal, lane));
+      uunit[pos] = static_cast<int32_t>(ub);
+      umask[pos] = (eb >> 24) << 8;
+    }
+    dups_b += __popcll(bal);
+  }
+  return na + nb - dups;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Matrix-core kernel: bf16, 8 heads per KV group
+// ------------------------------------------------------------------------------------------------
+struct MfmaArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* vp;
+  const bf16_t* gate;
+  const int32_t* sel;
+  bf16_t* out;
+  int64_t Tq, Tk, NU, pos0, pair_groups;   // pair_groups = ceil(ceil(Tq/2) / waves)
+  int G, NS, B, umax;
+  float scale_log2e;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
+  extern __shared__ uint32_t lds[];
+  constexpr int H = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = static_cast<int>(blockIdx.x % a.G);
+  const int64_t rest = blockIdx.x / a.G;
+  const int64_t pg = rest % a.pair_groups;
+  const int64_t b = rest / a.pair_groups;
+  const int64_t pair = pg * kMfmaWaves + wave;
+  const int64_t tokA = 2 * pair;
+  const bool validA = tokA < a.Tq;
+  const bool validB = tokA + 1 < a.Tq;
+
+  // wave-private LDS: listA[umax], listB[umax], uunit[2 umax], umask[2 umax]
+  uint32_t* listA = lds + static_cast<size_t>(wave) * 6 * a.umax;
+  uint32_t* listB = listA + a.umax;
+  int32_t* uunit = reinterpret_cast<int32_t*>(listB + a.umax);
+  uint32_t* umask = reinterpret_cast<uint32_t*>(uunit + 2 * a.umax);
+
+  const int64_t pA = a.pos0 + tokA, pB = pA + 1;
+  int na = 0, nb = 0;
+  if (validA)
+    na = build_units(a.sel + ((b * a.Tq + tokA) * a.G + g) * a.NS, a.NS, a.B, pA / a.B, listA, lane);
+  if (validB)
+    nb = build_units(a.sel + ((b * a.Tq + tokA + 1) * a.G + g) * a.NS, a.NS, a.B, pB / a.B, listB,
+                     lane);
+  __syncthreads();
+  // drop trailing units that start past the query (only the own block of a B > 8 selection has
+  // them); the lists are ascending, so the kept units are a prefix
+  na = count_units_upto(listA, na, pA >> 3, lane);
+  nb = count_units_upto(listB, nb, pB >> 3, lane);
+  const int nu = merge_units(listA, na, listB, nb, uunit, umask, lane);
+  __syncthreads();
+
+  const int lr = lane & 15, lg = lane >> 4;
+  const int X = lr >> 3;                           // which of the two tokens this lane's row is
+  const int head = lr & 7;
+  const int64_t tokX = tokA + X;
+  const bool rowvalid = X ? validB : validA;
+  const int64_t pX = a.pos0 + tokX;
+
+  // Q^T operand: lane holds q[row lr][32 kc + 8 lg .. +8]
+  bf16x8_t qf[D / 32];
+  const bf16_t* qrow = a.q + (((b * a.Tq + (rowvalid ? tokX : 0)) * a.G + g) * H + head) * D;
+#pragma unroll
+  for (int kc = 0; kc < D / 32; ++kc)
+    qf[kc] = rowvalid ? load_bf16x8(qrow + 32 * kc + 8 * lg) : zero_bf16x8();
+
+  const bf16_t* kg = a.k + (b * a.G + g) * a.Tk * D;
+  const bf16_t* vg = a.vp + (b * a.G + g) * a.NU * D * 8;
+
+  f32x4_t acc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -1e30f, l_run = 0.f;
+  const float ninf = -__builtin_inff();
+
+  for (int c0 = 0; c0 < nu; c0 += 4) {
+    const int eS = c0 + lg;                        // the unit whose scores this lane holds
+    int unitS = -1;
+    uint32_t msk = 0u;
+    if (eS < nu) {
+      unitS = uunit[eS];
+      msk = umask[eS];
+    }
+    const int eK = c0 + (lr >> 2);                 // the unit of this lane's K rows
+    const int unitK = (eK < nu) ? uunit[eK] : 0;
+    int64_t t1 = static_cast<int64_t>(unitK) * 8 + (lr & 3);
+    int64_t t2 = t1 + 4;
+    t1 = t1 < a.Tk ? t1 : a.Tk - 1;
+    t2 = t2 < a.Tk ? t2 : a.Tk - 1;
+
+    f32x4_t s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t s2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) {
+      const bf16x8_t k1 = load_bf16x8(kg + t1 * D + 32 * kc + 8 * lg);
+      const bf16x8_t k2 = load_bf16x8(kg + t2 * D + 32 * kc + 8 * lg);
+      s1 = mfma16x16x32(k1, qf[kc], s1);
+      s2 = mfma16x16x32(k2, qf[kc], s2);
+    }
+    // lane holds scores of unit unitS, tokens 0..3 (s1) and 4..7 (s2), for row lr
+    const uint32_t bits = X ? ((msk >> 8) & 0xffu) : (msk & 0xffu);
+    const int64_t tbase = static_cast<int64_t>(unitS) * 8;
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok0 = ((bits >> e) & 1u) && (tbase + e <= pX);
+      const bool ok1 = ((bits >> (e + 4)) & 1u) && (tbase + e + 4 <= pX);
+      sv[e] = ok0 ? s1[e] * a.scale_log2e : ninf;
+      sv[e + 4] = ok1 ? s2[e] * a.scale_log2e : ninf;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    uint32_t pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sv[2 * e] - m_new));
+      const bf16_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sv[2 * e + 1] - m_new));
+      psum += bf16_to_f32(p0) + bf16_to_f32(p1);
+      pw[e] = static_cast<uint32_t>(p0) | (static_cast<uint32_t>(p1) << 16);
+    }
+    l_run = l_run * alpha + psum;
+    const bf16x8_t pf = bf16x8_from_u4(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    const int unitV = unitS >= 0 ? unitS : 0;
+    const bf16_t* vrow = vg + (static_cast<int64_t>(unitV) * D + lr) * 8;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      acc[t] *= alpha;
+      const bf16x8_t vf = load_bf16x8(vrow + t * 16 * 8);
+      acc[t] = mfma16x16x32(vf, pf, acc[t]);
+    }
+  }
+
+  // epilogue: row sum over the 4 lane groups, normalise, gate, store
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (!rowvalid || nu == 0) return;
+  const float inv = 1.f / l_tot;
+  const int64_t obase = (((b * a.Tq + tokX) * a.G + g) * H + head) * D;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const int d0 = 16 * t + 4 * lg;
+    const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + obase + d0);
+    const float g0 = bf16_to_f32(static_cast<bf16_t>(gw.x & 0xffffu));
+    const float g1 = bf16_to_f32(static_cast<bf16_t>(gw.x >> 16));
+    const float g2 = bf16_to_f32(static_cast<bf16_t>(gw.y & 0xffffu));
+    const float g3 = bf16_to_f32(static_cast<bf16_t>(gw.y >> 16));
+    const float o0 = acc[t][0] * inv / (1.f + __expf(-g0));
+    const float o1 = acc[t][1] * inv / (1.f + __expf(-g1));
+    const float o2 = acc[t][2] * inv / (1.f + __expf(-g2));
+    const float o3 = acc[t][3] * inv / (1.f + __expf(-g3));
+    uint2 ow;
+    ow.x = pack_bf16x2(o0, o1);
+    ow.y = pack_bf16x2(o2, o3);
+    *reinterpret_cast<uint2*>(a.out + obase + d0) = ow;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Plain kernel: any dtype, any head count <= 32.  One workgroup per (b, i, g); 32 lanes per head.
+// ------------------------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(1024) attend_plain_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ gate, const int32_t* __restrict__ sel, T* __restrict__ out, int64_t Tq,
+    int64_t Tk, int G, int H, int NS, int B, int64_t pos0, float scale) {
+  constexpr int PER = D / 32;
+  const int g = static_cast<int>(blockIdx.x % G);
+  const int64_t bi = blockIdx.x / G;              // b * Tq + i
+  const int64_t i = bi % Tq;
+  const int64_t b = bi / Tq;
+  const int h = threadIdx.x >> 5;
+  const int l32 = threadIdx.x & 31;
+  const int64_t p = pos0 + i;
+  const int64_t o = p / B;
+  const int64_t row = ((bi * G + g) * H + h) * D;
+  float qv[PER], acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    qv[j] = Elem<T>::load(q + row + l32 + 32 * j);
+    acc[j] = 0.f;
+  }
+  const T* kg = k + (b * G + g) * Tk * D;
+  const T* vg = v + (b * G + g) * Tk * D;
+  const int32_t* selrow = sel + (bi * G + g) * NS;
+  float m = -__builtin_inff(), l = 0.f;
+  for (int e = 0; e < NS; ++e) {
+    const int64_t blk = selrow[e];
+    if (blk < 0 || blk > o) continue;
+    int64_t t_end = blk * B + B;
+    if (t_end > p + 1) t_end = p + 1;
+    for (int64_t t = blk * B; t < t_end; ++t) {
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) dot = fmaf(qv[j], Elem<T>::load(kg + t * D + l32 + 32 * j), dot);
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 32);
+      const float s = dot * scale;
+      const float m_new = fmaxf(m, s);
+      const float alpha = expf(m - m_new);
+      const float pw = expf(s - m_new);
+      l = l * alpha + pw;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        acc[j] = fmaf(pw, Elem<T>::load(vg + t * D + l32 + 32 * j), acc[j] * alpha);
+      m = m_new;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const float gt = Elem<T>::load(gate + row + l32 + 32 * j);
+    Elem<T>::store(out + row + l32 + 32 * j, acc[j] / l / (1.f + expf(-gt)));
+  }
+}
+
+}  // namespace
+
+bool attend_uses_mfma(const Dims& d) {
+  const bool block_ok = (d.B % 8 == 0) || (8 % d.B == 0);
+  return d.bf16 && d.H == 8 && block_ok && units_per_query(d) <= kMaxUnits;
+}
+
+int64_t units_per_query(const Dims& d) {
+  // a query's selection covers at most NS blocks of ceil(B/8) units, and at most the units of
+  // blocks 0..o, i.e. NU rounded up to whole blocks
+  const int64_t per_blk = d.B >= 8 ? d.B / 8 : 1;
+  const int64_t u = static_cast<int64_t>(d.NS) * per_blk;
+  const int64_t cap = d.NU + per_blk;
+  return u < cap ? u : cap;
+}
+
+size_t attend_packed_v_bytes(const Dims& d) {
+  if (!attend_uses_mfma(d)) return 0;
+  return static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
+}
+
+hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* gate, const int32_t* sel, void* out, void* packed_v,
+                         hipStream_t s) {
+  if (attend_uses_mfma(d)) {
+    const int64_t total = d.Bt * d.G * d.NU * d.D;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(packed_v), d.Tk, d.NU,
+                       d.D, total);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    MfmaArgs a;
+    a.q = static_cast<const bf16_t*>(q);
+    a.k = static_cast<const bf16_t*>(k);
+    a.vp = static_cast<const bf16_t*>(packed_v);
+    a.gate = static_cast<const bf16_t*>(gate);
+    a.sel = sel;
+    a.out = static_cast<bf16_t*>(out);
+    a.Tq = d.Tq;
+    a.Tk = d.Tk;
+    a.NU = d.NU;
+    a.pos0 = d.pos0;
+    const int64_t pairs = (d.Tq + 1) / 2;
+    a.pair_groups = (pairs + kMfmaWaves - 1) / kMfmaWaves;
+    a.G = d.G;
+    a.NS = d.NS;
+    a.B = d.B;
+    a.umax = static_cast<int>(units_per_query(d));
+    a.scale_log2e = d.scale * 1.4426950408889634f;
+    const size_t lds = static_cast<size_t>(kMfmaWaves) * 6 * a.umax * sizeof(uint32_t);
+    const int64_t grid = d.Bt * a.pair_groups * d.G;
+    if (d.D == 128)
+      hipLaunchKernelGGL(attend_mfma_h8_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256),
+                         lds, s, a);
+    else
+      hipLaunchKernelGGL(attend_mfma_h8_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256),
+                         lds, s, a);
+    return hipGetLastError();
+  }
+  const int64_t grid = d.Bt * d.Tq * d.G;
+  const dim3 block(32 * d.H);
+  if (d.bf16) {
+    auto* qq = static_cast<const bf16_t*>(q);
+    auto* kk = static_cast<const bf16_t*>(k);
+    auto* vv = static_cast<const bf16_t*>(v);
+    auto* gg = static_cast<const bf16_t*>(gate);
+    auto* oo = static_cast<bf16_t*>(out);
+    if (d.D == 128)
+      hipLaunchKernelGGL((attend_plain_kernel<bf16_t, 128>), dim3(static_cast<unsigned>(grid)), block,
+                         0, s, qq, kk, vv, gg, sel, oo, d.Tq, d.Tk, d.G, d.H, d.NS, d.B, d.pos0,
+                         d.scale);
+    else
+      hipLaunchKernelGGL((attend_plain_kernel<bf16_t, 64>), dim3(static_cast<unsigned>(grid)), block,
+                         0, s, qq, kk, vv, gg, sel, oo, d.Tq, d.Tk, d.G, d.H, d.NS, d.B, d.pos0,
+                         d.scale);
+  } else {
+    auto* qq = static_cast<const float*>(q);
+    auto* kk = static_cast<const float*>(k);
+    auto* vv = static_cast<const float*>(v);
+    auto* gg = static_cast<const float*>(gate);
+    auto* oo = static_cast<float*>(out);
+    if (d.D == 128)
+      hipLaunchKernelGGL((attend_plain_kernel<float, 128>), dim3(static_cast<unsigned>(grid)), block,
+                         0, s, qq, kk, vv, gg, sel, oo, d.Tq, d.Tk, d.G, d.H, d.NS, d.B, d.pos0,
+                         d.scale);
+    else
+      hipLaunchKernelGGL((attend_plain_kernel<float, 64>), dim3(static_cast<unsigned>(grid)), block,
+                         0, s, qq, kk, vv, gg, sel, oo, d.Tq, d.Tk, d.G, d.H, d.NS, d.B, d.pos0,
+                         d.scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sgqa

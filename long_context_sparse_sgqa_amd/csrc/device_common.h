@@ -1,0 +1,64 @@
+// Device helpers shared by the gfx950 kernels: bf16 storage, vector types, MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+typedef uint16_t bf16_t;  // bf16 held as its bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two fp32 -> packed pair of bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// 16-byte global load as the MFMA bf16x8 operand.
+__device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ bf16x8_t bf16x8_from_u4(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+  uint4 u = make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
+// Lane l supplies A[l % 16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l % 16]; it receives
+// C[4*(l/16) + i][l % 16] for i = 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace sgqa

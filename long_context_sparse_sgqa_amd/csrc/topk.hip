@@ -1,0 +1,254 @@
+// Step 3 -- per-(query, KV group) block selection.
+//
+// The Step 5 Preview pages (mo.ai.kr summary, section "모델 구조와 학습 안정성"; ai.info article,
+// section on Sparse GQA and the 1M context) let every KV group pick its own top-k past blocks, with
+// k = 4096 tokens = 512 blocks of 8.  Readings fixed here: the own block o = p/B is always selected
+// and counts toward the NS = k/B budget; of the candidates j < o the NS-1 with the highest scores
+// are taken, equal scores going to the lower j; when o + 1 <= NS every block 0..o is taken.  The
+// output lists the blocks ascending, padded with -1.
+//
+// One workgroup (256 threads) per row.  Scores become order-preserving 32-bit keys (-0.0 is folded
+// into +0.0 first).  The NS-1'th largest key tau is found by an exact 4-pass radix select (8-bit
+// digits, LDS histogram); every key > tau is taken, plus the lowest-indexed keys == tau until the
+// budget is met.  The emit pass walks candidates in index order with wavefront ballots and prefix
+// counts, so the output is ascending without a sort.
+//
+// Long rows first shrink the candidate set: a strided sample of 1024 scores gives a threshold whose
+// expected pass count is about twice the budget; one streaming pass keeps the (key, index) pairs at
+// or above it in per-wave LDS segments, in index order.  Every key of the true top NS-1 is >= that
+// threshold whenever at least NS-1 candidates pass, so the select then runs on the short list.  If
+// too few pass, or a segment overflows, the row is selected directly from the full score row
+// instead.  Either way the result is exact.
+#include "device_common.h"
+#include "sgqa_internal.h"
+
+namespace sgqa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kSegCap = 1024;                 // per-wave candidate capacity
+constexpr int kSample = 1024;                 // sampled scores of a long row
+constexpr int kDirectMax = 2048;              // rows this short are selected straight from scores
+
+struct TopkShared {
+  uint32_t hist[256];
+  int wave_cnt[kWaves];
+  int seg_cnt[kWaves];
+  int seg_off[kWaves + 1];
+  uint32_t pick_digit;
+  int pick_above;
+  int flag;
+  uint32_t key[kWaves * kSegCap];             // candidate keys (also the sample buffer)
+  int32_t idx[kWaves * kSegCap];              // candidate block indices
+};
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;                 // -0.0 and +0.0 are the same score
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Exclusive prefix of `flag` over the workgroup in thread order; *total gets the sum.
+__device__ __forceinline__ int block_flag_scan(bool flag, int* total, TopkShared& sh) {
+  const uint64_t bal = __ballot(flag);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) sh.wave_cnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = sh.wave_cnt[w];
+    off += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + in_wave;
+}
+
+// Candidate sources: key(x) and index(x) for x in [0, n).
+struct RowSource {       // the full score row of one (query, group)
+  const float* s;
+  __device__ __forceinline__ uint32_t key(int x) const { return order_key(s[x]); }
+  __device__ __forceinline__ int32_t index(int x) const { return x; }
+};
+struct SampleSource {    // sampled keys held in LDS
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t key(int x) const { return k[x]; }
+  __device__ __forceinline__ int32_t index(int x) const { return x; }
+};
+struct SegSource {       // per-wave candidate segments, concatenated in wave order
+  const TopkShared* sh;
+  __device__ __forceinline__ int slot(int x) const {
+    int w = 0;
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) w += (x >= sh->seg_off[v]) ? 1 : 0;
+    return w * kSegCap + (x - sh->seg_off[w]);
+  }
+  __device__ __forceinline__ uint32_t key(int x) const { return sh->key[slot(x)]; }
+  __device__ __forceinline__ int32_t index(int x) const { return sh->idx[slot(x)]; }
+};
+
+// The need-th largest key (1-based) of src[0, n): returns tau and *take_eq = how many keys equal
+// to tau belong to the top `need` (the others above it are exactly the keys > tau).
+template <class Src>
+__device__ uint32_t radix_select(const Src& src, int n, int need, int* take_eq, TopkShared& sh) {
+  uint32_t prefix = 0u, mask = 0u;
+  int rem = need;
+  const int t = threadIdx.x;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sh.hist[t] = 0u;                                  // kThreads == 256 bins
+    __syncthreads();
+    for (int x = t; x < n; x += kThreads) {
+      const uint32_t k = src.key(x);
+      if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // inclusive scan over digits from the top: thread t holds digit 255 - t
+    const int h = static_cast<int>(sh.hist[255 - t]);
+    int incl = h;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane_id() >= o) incl += y;
+    }
+    if (lane_id() == 63) sh.wave_cnt[t >> 6] = incl;
+    __syncthreads();
+    for (int w = 0; w < (t >> 6); ++w) incl += sh.wave_cnt[w];
+    if (incl >= rem && incl - h < rem) {
+      sh.pick_digit = static_cast<uint32_t>(255 - t);
+      sh.pick_above = incl - h;
+    }
+    __syncthreads();
+    prefix |= sh.pick_digit << shift;
+    mask |= 255u << shift;
+    rem -= sh.pick_above;
+    __syncthreads();
+  }
+  *take_eq = rem;
+  return prefix;
+}
+
+// Writes the selected indices of src[0, n) in index order: keys > tau, then keys == tau while fewer
+// than take_eq of them have been taken.  Returns the number written.
+template <class Src>
+__device__ int emit_selected(const Src& src, int n, uint32_t tau, int take_eq, int need,
+                             int32_t* out, TopkShared& sh) {
+  int written = 0, eq_seen = 0;
+  for (int base = 0; base < n && written < need; base += kThreads) {
+    const int x = base + threadIdx.x;
+    const uint32_t k = (x < n) ? src.key(x) : 0u;
+    const bool gt = (x < n) && k > tau;
+    const bool eq = (x < n) && k == tau;
+    int eq_total;
+    const int eq_rank = eq_seen + block_flag_scan(eq, &eq_total, sh);
+    const bool take = gt || (eq && eq_rank < take_eq);
+    int take_total;
+    const int pos = written + block_flag_scan(take, &take_total, sh);
+    if (take) out[pos] = src.index(x);
+    written += take_total;
+    eq_seen += eq_total;
+  }
+  return written;
+}
+
+__global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ scores,
+                                                        int32_t* __restrict__ sel, int64_t NB,
+                                                        int NS, int B, int G, int64_t Tq,
+                                                        int64_t pos0, int64_t b0, int64_t i0,
+                                                        int64_t ntok) {
+  __shared__ TopkShared sh;
+  const int64_t rr = blockIdx.x;
+  const int64_t tok = rr / G;
+  const int g = static_cast<int>(rr - tok * G);
+  const int64_t b = b0 + tok / ntok;
+  const int64_t i = i0 + tok % ntok;
+  const int64_t p = pos0 + i;
+  const int64_t o = p / B;
+  int32_t* out = sel + ((b * Tq + i) * G + g) * NS;
+  const int t = threadIdx.x;
+
+  if (o + 1 <= NS) {                                 // dense: every causal block
+    for (int x = t; x < NS; x += kThreads) out[x] = (x <= o) ? x : -1;
+    return;
+  }
+  const int n = static_cast<int>(o);                 // candidates 0..o-1
+  const int need = NS - 1;
+  const RowSource row{scores + rr * NB};
+  int take_eq = 0;
+  uint32_t tau;
+  bool done = false;
+
+  if (n > kDirectMax) {
+    // threshold from a strided sample, aiming at ~2x the budget passing
+    for (int s = t; s < kSample; s += kThreads)
+      sh.key[s] = row.key(static_cast<int>((static_cast<int64_t>(s) * n) / kSample));
+    __syncthreads();
+    int rs = static_cast<int>((2ll * need * kSample + n - 1) / n);
+    rs = rs < 1 ? 1 : (rs > kSample ? kSample : rs);
+    int dummy;
+    const uint32_t guess = radix_select(SampleSource{sh.key}, kSample, rs, &dummy, sh);
+    __syncthreads();                                 // sample buffer is reused below
+
+    // stream the row once; each wave keeps its contiguous quarter's survivors in order
+    const int wave = t >> 6, lane = lane_id();
+    const int per_wave = (n + kWaves - 1) / kWaves;
+    const int lo = wave * per_wave;
+    const int hi = min(n, lo + per_wave);
+    int cnt = 0;
+    for (int x0 = lo; x0 < hi; x0 += 64) {
+      const int x = x0 + lane;
+      const uint32_t k = (x < hi) ? row.key(x) : 0u;
+      const bool keep = (x < hi) && k >= guess;
+      const uint64_t bal = __ballot(keep);
+      const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (keep && pos < kSegCap) {
+        sh.key[wave * kSegCap + pos] = k;
+        sh.idx[wave * kSegCap + pos] = x;
+      }
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) sh.seg_cnt[wave] = cnt;
+    __syncthreads();
+    if (t == 0) {
+      int off = 0, ok = 1;
+      for (int w = 0; w < kWaves; ++w) {
+        sh.seg_off[w] = off;
+        off += sh.seg_cnt[w];
+        ok &= (sh.seg_cnt[w] <= kSegCap) ? 1 : 0;
+      }
+      sh.seg_off[kWaves] = off;
+      sh.flag = (ok && off >= need) ? off : -1;
+    }
+    __syncthreads();
+    const int m = sh.flag;
+    if (m >= 0) {
+      const SegSource seg{&sh};
+      tau = radix_select(seg, m, need, &take_eq, sh);
+      emit_selected(seg, m, tau, take_eq, need, out, sh);
+      done = true;
+    }
+  }
+  if (!done) {
+    tau = radix_select(row, n, need, &take_eq, sh);
+    emit_selected(row, n, tau, take_eq, need, out, sh);
+  }
+  if (t == 0) out[need] = static_cast<int32_t>(o);   // the own block, last in ascending order
+}
+
+}  // namespace
+
+hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const Chunk& c,
+                       hipStream_t s) {
+  const int64_t rows = c.rows(d.G);
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, s, scores,
+                     sel, d.NB, d.NS, d.B, d.G, d.Tq, d.pos0, c.b0, c.i0, c.ntok);
+  return hipGetLastError();
+}
+
+}  // namespace sgqa

@@ -175,10 +175,10 @@ def forward_rows(inputs, block: int, topk_tokens: int, scale: float, rows, k_blk
     inputs: dict with q [Bt,Tq,G,h,d], k, v [Bt,G,Tkv,d], gate [Bt,Tq,G,h,d], q_idx [Bt,Tq,G,di],
             k_idx [Bt,Tkv,di]  (numpy arrays or torch tensors, any float dtype).
     rows: iterable of (b, i) query tokens.
-    Returns (sel [n, G, n_sel] int64, out [n, G, h, d] float64, k_blk [Bt, NB, di] float64).
+    k_blk: optional precomputed block keys [Bt, NB, di]; otherwise each needed sequence's k_idx is
+           compressed here.
+    Returns (sel [n, G, n_sel] int64, out [n, G, h, d] float64, {b: K_blk[b]} float64).
     """
-    if k_blk is None:
-        k_blk = compress(_np64(inputs["k_idx"]), block)
     q_idx, q, k, v, gate = (inputs[n] for n in ("q_idx", "q", "k", "v", "gate"))
     t_q, G = q_idx.shape[1], q_idx.shape[2]
     t_kv = k.shape[2]
@@ -188,30 +188,37 @@ def forward_rows(inputs, block: int, topk_tokens: int, scale: float, rows, k_blk
     h, d = q.shape[3], q.shape[4]
     sel_out = np.full((len(rows), G, n_sel), -1, dtype=np.int64)
     out = np.zeros((len(rows), G, h, d), dtype=np.float64)
+    kblk = {}
     for r, (b, i) in enumerate(rows):
+        if b not in kblk:
+            kblk[b] = (_np64(k_blk[b]) if k_blk is not None
+                       else compress(_np64(inputs["k_idx"][b:b + 1]), block)[0])
         p = int(pos[i])
         o = p // block
         qi = _np64(q_idx[b, i])
         qb = _np64(q[b, i])
         gb = _np64(gate[b, i])
         for g in range(G):
-            s = block_scores(qi[g], k_blk[b], o)
+            s = block_scores(qi[g], kblk[b], o)
             sel = select_blocks(s, o, n_sel)
             sel_out[r, g] = sel
             toks = attended_tokens(sel, block, p, t_kv)
             kk = _rows64(k, b, g, toks)
             vv = _rows64(v, b, g, toks)
             out[r, g] = gated_attention(qb[g], kk, vv, gb[g], np.arange(toks.size), scale)
-    return sel_out, out, k_blk
+    return sel_out, out, kblk
 
 
 def forward(inputs, block: int, topk_tokens: int, scale: float):
-    """Every query token of every sequence (small inputs only)."""
+    """Every query token of every sequence (small inputs only).
+
+    Returns (sel [Bt, Tq, G, n_sel], out [Bt, Tq, G, h, d], K_blk [Bt, NB, di])."""
     bt, t_q = inputs["q_idx"].shape[0], inputs["q_idx"].shape[1]
     rows = [(b, i) for b in range(bt) for i in range(t_q)]
-    sel, out, k_blk = forward_rows(inputs, block, topk_tokens, scale, rows)
+    sel, out, kblk = forward_rows(inputs, block, topk_tokens, scale, rows)
     G, n_sel = sel.shape[1], sel.shape[2]
     h, d = out.shape[2], out.shape[3]
+    k_blk = np.stack([kblk[b] for b in range(bt)])
     return sel.reshape(bt, t_q, G, n_sel), out.reshape(bt, t_q, G, h, d), k_blk
 
 
@@ -226,22 +233,23 @@ def inclusion_rate(q_idx, k_idx, rows, t_kv: int, cfg_a=(8, 4096), cfg_b=(1, 204
     B=1, k=2048 (78.06 % vs 79.09 %) without naming the reference set; this takes the B=1, k=2048
     token set as the reference.  Returns float64 [n_rows, G].  Parity unpinned (a measured property).
     """
-    qi = _np64(q_idx)
-    ki = _np64(k_idx)
-    t_q = qi.shape[1]
+    t_q, G = q_idx.shape[1], q_idx.shape[2]
     pos = query_positions(t_q, t_kv)
     (ba, ka), (bb, kb) = cfg_a, cfg_b
-    kblk_a = compress(ki, ba)
-    kblk_b = compress(ki, bb)
     rows = list(rows)
-    G = qi.shape[2]
     rate = np.zeros((len(rows), G))
+    cache = {}
     for r, (b, i) in enumerate(rows):
+        if b not in cache:
+            kseq = _np64(k_idx[b:b + 1])
+            cache = {b: (compress(kseq, ba)[0], compress(kseq, bb)[0])}
+        kblk_a, kblk_b = cache[b]
+        qi = _np64(q_idx[b, i])
         p = int(pos[i])
         for g in range(G):
             oa, ob = p // ba, p // bb
-            sa = select_blocks(block_scores(qi[b, i, g], kblk_a[b], oa), oa, ka // ba)
-            sb = select_blocks(block_scores(qi[b, i, g], kblk_b[b], ob), ob, kb // bb)
+            sa = select_blocks(block_scores(qi[g], kblk_a, oa), oa, ka // ba)
+            sb = select_blocks(block_scores(qi[g], kblk_b, ob), ob, kb // bb)
             ta = attended_tokens(sa, ba, p, t_kv)
             tb = attended_tokens(sb, bb, p, t_kv)
             rate[r, g] = np.intersect1d(ta, tb).size / tb.size

@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same seeded inputs.
+
+Selections and block scores must be bit-exact (integer-valued index data makes them exact);
+outputs within max-abs 1e-5 (fp32) or 1e-2 (bf16).  Small cases are checked on every row; the
+full-size workloads on stratified sampled rows plus structural checks of every row's selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_sgqa_amd as sg
+import oracle
+from gpu_helpers import (check_out, check_sel_rows, oracle_rows, run_forward, run_split,
+                         sample_tokens, say, structural_check_sel, to_dev)
+from sgqa_inputs import generate, generate_small, get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load_library()     # fails loudly if the HIP library is missing
+
+
+# ----------------------------------------------------------------------------------------------
+# tiny workload (fp32): every row, every step
+# ----------------------------------------------------------------------------------------------
+def test_tiny_every_step_every_row():
+    w = get_workload("tiny")
+    say("case: tiny", w)
+    x = to_dev(generate(w, seed=0))
+    prob = sg.Problem.from_workload(w)
+    k_blk, scores, sel, out = run_split(prob, x)
+    sel_ref, out_ref, kblk_ref = oracle.forward(x, w.block, w.topk, w.softmax_scale)
+    np.testing.assert_array_equal(k_blk.cpu().double().numpy(), kblk_ref)
+    # every defined score (j < p/B) equals the oracle's exactly
+    sc = scores.cpu().double().numpy()
+    kb = kblk_ref[0]
+    qi = x["q_idx"].cpu().double().numpy()[0]
+    for i in range(0, w.t_q, 97):
+        o = i // w.block
+        for g in range(w.groups):
+            np.testing.assert_array_equal(sc[0, i, g, :o], oracle.block_scores(qi[i, g], kb, o))
+    check_sel_rows(sel, sel_ref)
+    check_out(out, out_ref, fp32=True, what="tiny split")
+    out2, sel2 = run_forward(prob, x)
+    assert torch.equal(sel2, sel)
+    check_out(out2, out_ref, fp32=True, what="tiny forward")
+
+
+# ----------------------------------------------------------------------------------------------
+# small bf16 cases through the matrix-core path: ragged shapes, several block sizes, every row
+# ----------------------------------------------------------------------------------------------
+SMALL_CASES = [
+    # t_q, t_kv, block, topk, groups, index_dim, sharp
+    (300, 1001, 8, 256, 2, 128, False),
+    (517, 517, 8, 128, 3, 64, False),
+    (517, 517, 8, 128, 2, 128, True),
+    (257, 700, 16, 256, 2, 32, False),
+    (401, 601, 4, 128, 2, 128, False),
+    (333, 333, 2, 64, 1, 128, True),
+    (1, 333, 8, 64, 2, 128, False),
+    (2, 2, 8, 64, 2, 128, False),
+    (64, 64, 8, 4096, 2, 128, False),        # budget covers the whole context: dense
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d-di%d%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "-sharp" if c[6] else ""))
+def test_small_bf16_every_row(case):
+    t_q, t_kv, B, k, G, di, sharp = case
+    say("case:", case)
+    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=128, index_dim=di,
+                          block=B, topk=k, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          needles=1 if (t_kv // B) >= 2 * G else 0, seed=11, device="cuda",
+                          sharp=sharp)
+    prob = sg.Problem.from_workload(w)
+    k_blk, scores, sel, out = run_split(prob, x)
+    sel_ref, out_ref, kblk_ref = oracle.forward(x, B, k, w.softmax_scale)
+    np.testing.assert_array_equal(k_blk.cpu().double().numpy(), kblk_ref)
+    check_sel_rows(sel, sel_ref)
+    structural_check_sel(sel, prob)
+    check_out(out, out_ref, fp32=False, what="split")
+    out2, sel2 = run_forward(prob, x)
+    assert torch.equal(sel2, sel)
+    assert torch.equal(out2, out)
+
+
+def test_block_one_selection_is_token_level():
+    """B = 1 (token-level, the pages' comparison setting) through index + top-k."""
+    w, x = generate_small(t_q=700, t_kv=900, groups=2, heads=8, head_dim=128, index_dim=128,
+                          block=1, topk=128, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=5, device="cuda")
+    prob = sg.Problem.from_workload(w)
+    _, scores = sg.index(prob, x["q_idx"], x["k_idx"])
+    sel = sg.topk(prob, scores)
+    torch.cuda.synchronize()
+    rows = [(0, i) for i in range(w.t_q)]
+    sel_ref, _, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0], sel_ref)
+
+
+def test_heavy_ties_and_negative_zero():
+    """Constant index keys: every candidate ties, so the lowest block indices must win."""
+    w, x = generate_small(t_q=600, t_kv=600, groups=2, heads=8, head_dim=128, index_dim=32,
+                          block=8, topk=128, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=3, device="cuda")
+    x["k_idx"].fill_(1.0)
+    x["q_idx"][:, :, 0].fill_(0.0)          # group 0: every score is +0.0
+    x["q_idx"][:, :, 1].fill_(-1.0)         # group 1: every score is -32 (all equal)
+    prob = sg.Problem.from_workload(w)
+    k_blk, scores, sel, out = run_split(prob, x)
+    sel_ref, out_ref, _ = oracle.forward(x, w.block, w.topk, w.softmax_scale)
+    check_sel_rows(sel, sel_ref)
+    check_out(out, out_ref, fp32=False, what="ties")
+
+
+def test_forward_chunked_workspace_matches():
+    """sgqa_forward with a workspace that forces many query-row chunks gives the same result."""
+    w, x = generate_small(t_q=900, t_kv=1200, groups=2, heads=8, head_dim=128, index_dim=128,
+                          block=8, topk=256, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          needles=2, seed=8, device="cuda")
+    prob = sg.Problem.from_workload(w)
+    out_a, sel_a = run_forward(prob, x)
+    s = sg.sizes(prob)
+    fixed = s["forward_workspace_bytes"] - ((s["scores_bytes"] + 255) // 256) * 256
+    small = fixed + 37 * w.groups * w.num_blocks * 4         # 37 query tokens per chunk
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    out_b, sel_b = run_forward(prob, x, workspace=ws)
+    assert torch.equal(sel_a, sel_b)
+    assert torch.equal(out_a, out_b)
+
+
+def test_run_to_run_bitwise():
+    w, x = generate_small(t_q=512, t_kv=800, groups=2, heads=8, head_dim=128, index_dim=128,
+                          block=8, topk=256, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=4, device="cuda")
+    prob = sg.Problem.from_workload(w)
+    a = run_forward(prob, x)
+    b = run_forward(prob, x)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------------------------------------------
+# full-size workloads: sampled rows against the oracle, structural checks on every row
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n_random", [("32k", 24), ("128k", 12), ("1m", 6)])
+def test_workload_sampled_rows(name, n_random):
+    w = get_workload(name)
+    say("case:", name)
+    x = generate(w, device="cuda", seed=0)
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    structural_check_sel(sel, prob)
+    toks = sample_tokens(w.t_q, w.t_kv, w.block, w.n_sel, n_random)
+    rows = [(0, i) for i in toks]
+    say(f"  oracle on {len(rows)} tokens x {w.groups} groups")
+    sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0, toks], sel_ref)
+    check_out(out[0, toks], out_ref, fp32=False, what=name)
+    # needles of a group are always among that group's picks for late queries
+    last = sel[0, -1].cpu().numpy()
+    for g in range(w.groups):
+        assert set(x["needle_blocks"][g].tolist()) <= set(last[g].tolist())
+    del x, out, sel
+    torch.cuda.empty_cache()
+
+
+def test_decode_sampled_sequences():
+    w = get_workload("decode")
+    say("case: decode")
+    x = generate(w, device="cuda", seed=0)
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    structural_check_sel(sel, prob)
+    rows = [(b, i) for b in (0, 37) for i in range(w.t_q)]
+    sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(torch.stack([sel[b, i] for b, i in rows]), sel_ref)
+    check_out(torch.stack([out[b, i] for b, i in rows]), out_ref, fp32=False, what="decode")
+    del x, out, sel
+    torch.cuda.empty_cache()
+
+
+def test_32k_split_equals_forward_and_coverage():
+    """Split calls equal the one-call forward on the 32K workload; the B=1, k=2048 selection is
+    run alongside and the token inclusion rate is reported (a measured property)."""
+    w = get_workload("32k")
+    x = generate(w, device="cuda", seed=0)
+    prob = sg.Problem.from_workload(w)
+    out_f, sel_f = run_forward(prob, x)
+    _, scores = sg.index(prob, x["q_idx"], x["k_idx"])
+    sel_s = sg.topk(prob, scores)
+    del scores
+    assert torch.equal(sel_s, sel_f)
+    out_s = sg.attend(prob, x["q"], x["k"], x["v"], x["gate"], sel_s)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_f)
+    # B = 1, k = 2048 on the same index data
+    p1 = sg.Problem.from_workload(w, block=1, topk_tokens=2048)
+    _, sc1 = sg.index(p1, x["q_idx"], x["k_idx"])
+    sel1 = sg.topk(p1, sc1)
+    del sc1
+    torch.cuda.synchronize()
+    toks = sample_tokens(w.t_q, w.t_kv, 1, 2048, 8, seed=1)
+    sel1_ref, _, _ = oracle_rows(p1, x, [(0, i) for i in toks])
+    check_sel_rows(sel1[0, toks], sel1_ref)
+    rate_ref = oracle.inclusion_rate(x["q_idx"], x["k_idx"], [(0, i) for i in toks[-4:]], w.t_kv)
+    say(f"  token inclusion (oracle, {len(toks[-4:])} late tokens): {rate_ref.mean():.4f}")
