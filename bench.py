@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Sparse GQA forward throughput on one MI355X: query-tokens/s at 128K context.
+
+One step = one sgqa_forward call (block compression + indexer + top-k + gated attention) over the
+whole 128K prefill (1 sequence x 131072 query tokens, 8 KV groups x 8 heads, d = 128, d_idx = 128,
+B = 8, k = 4096, bf16), with every input already resident in HBM.  W untimed warm-up steps, then K
+timed steps bracketed by device synchronisation; HIP events recorded by the library between its
+stages give the per-stage (per-kernel) durations on the stream the kernels run on.
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      : the dominant kernel's algorithmic work / measured duration against the MI355X peak
+  cpu_baseline  : the CPU oracle timed on a bounded sample of the same workload (this process, 1 core)
+  stages        : per-stage milliseconds and roofline fractions
+  parity        : the sampled rows of the last timed step against the oracle
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+STAGES = ("compress", "index_topk", "pack_v", "attention")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="128k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# algorithmic work of the workload (closed forms over the query positions)
+# ------------------------------------------------------------------------------------------------
+def algorithmic_counts(w):
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv, dtype=np.int64)
+    o = pos // w.block
+    pairs = int(o.sum()) * w.groups * w.batch                       # scored (query, group, block)
+    dense = o + 1 <= w.n_sel
+    n_att = np.where(dense, pos + 1, (w.n_sel - 1) * w.block + pos % w.block + 1)
+    att = int(n_att.sum()) * w.groups * w.batch                     # attended (query, group, token)
+    isz = 2 if w.index_dtype == "bf16" else 4
+    dsz = 2 if w.dtype == "bf16" else 4
+    rows = w.batch * w.t_q * w.groups
+    return {
+        "pairs": pairs,
+        "attended": att,
+        "compress_bytes": w.batch * (w.t_kv + w.num_blocks) * w.index_dim * isz,
+        "index_flops": 2 * w.index_dim * pairs,
+        "score_bytes": 4 * pairs,
+        "sel_bytes": 4 * rows * w.n_sel,
+        "attention_flops": 4 * w.head_dim * w.heads * att,
+        "pack_bytes": 2 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,
+        # compulsory attention traffic: q, gate, out once, plus each group's K/V once
+        "attention_min_bytes": 3 * rows * w.heads * w.head_dim * dsz
+                               + 2 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,
+    }
+
+
+# ------------------------------------------------------------------------------------------------
+# HIP events (the runtime torch already loaded)
+# ------------------------------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.events.append(ev)
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
+# ------------------------------------------------------------------------------------------------
+# traffic from committed rocprofv3 counter summaries
+# ------------------------------------------------------------------------------------------------
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "long_context_sparse_sgqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE), scaled by the
+    copy-kernel calibration; None if absent or if the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != kernel_source_digest(rec.get("sources", [])):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ------------------------------------------------------------------------------------------------
+def cpu_baseline(w, x, out_gpu, sel_gpu, target_s, seed):
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    torch.set_num_threads(1)
+    if threadpool_limits is not None:
+        threadpool_limits(limits=1)          # numpy BLAS on one thread for the whole run
+    rng = np.random.default_rng(seed)
+    pos0 = w.t_kv - w.t_q
+    # sample over the whole query range, weighted like the workload (uniform over tokens)
+    cpu = {n: x[n].to("cpu") for n in ("q", "k", "v", "gate", "q_idx", "k_idx")}
+    cand = rng.permutation(w.t_q)
+    toks, times = [], []
+    sels, outs = [], []
+    t_begin = time.perf_counter()
+    kblk = None
+    for i in cand:
+        t0 = time.perf_counter()
+        sel, out, kb = oracle.forward_rows(cpu, w.block, w.topk, w.softmax_scale, [(0, int(i))],
+                                           k_blk=kblk)
+        if kblk is None:
+            kblk = np.stack([kb[0]])        # compression done once, like one pass per forward
+        times.append(time.perf_counter() - t0)
+        toks.append(int(i))
+        sels.append(sel[0])
+        outs.append(out[0])
+        if time.perf_counter() - t_begin >= target_s and len(toks) >= 4:
+            break
+    elapsed = time.perf_counter() - t_begin
+    rate = len(toks) / elapsed
+    # parity of the sampled rows against the last GPU step
+    sel_ref = np.stack(sels)
+    out_ref = np.stack(outs)
+    sg = sel_gpu[0, toks].to("cpu").numpy().astype(np.int64)
+    og = out_gpu[0, toks].to("cpu", torch.float64).numpy()
+    parity = {"rows": len(toks) * w.groups,
+              "sel_mismatch_rows": int((sg != sel_ref).any(axis=-1).sum()),
+              "max_abs_err": float(np.abs(og - out_ref).max()),
+              "tolerance": 1e-2 if w.dtype == "bf16" else 1e-5}
+    late = sum(1 for i in toks if (pos0 + i) // w.block + 1 > w.n_sel)
+    base = {"value": rate, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(toks)} random query tokens of the {w.name} workload ({late} in the sparse "
+                      f"regime), all {w.groups} KV groups, block compression included once; "
+                      f"fp64 numpy oracle, 1 thread, {elapsed:.1f} s"}
+    return base, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import long_context_sparse_sgqa_amd as sg
+    from sgqa_inputs import generate, get_workload
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = sg.load_library()
+    x = generate(w, device=dev, seed=args.seed)
+    prob = sg.Problem.from_workload(w)
+    sz = sg.sizes(prob)
+    out = torch.empty(prob.batch, prob.t_q, prob.kv_groups, prob.heads_per_group, prob.head_dim,
+                      dtype=prob.dtype, device=dev)
+    sel = torch.empty(prob.batch, prob.t_q, prob.kv_groups, prob.n_sel, dtype=torch.int32, device=dev)
+    k_blk = torch.empty(prob.batch, prob.num_blocks, prob.index_dim, dtype=prob.index_dtype, device=dev)
+    ws = torch.empty(sz["forward_workspace_bytes"], dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"], k_blk=k_blk,
+                   out=out, sel=sel, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    marks = [[ev.create() for _ in range(5)] for _ in range(args.steps)]
+    arr_t = ctypes.c_void_p * 5
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        lib.sgqa_set_stage_events(arr_t(*[m.value for m in marks[k]]))
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.sgqa_set_stage_events(None)
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {s: 0.0 for s in STAGES}
+    gpu_ms = 0.0
+    for m in marks:
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += ev.elapsed_ms(m[j], m[j + 1]) / args.steps
+        gpu_ms += ev.elapsed_ms(m[0], m[4]) / args.steps
+    ev.destroy()
+
+    tokens = prob.batch * prob.t_q
+    value = tokens / (wall_ms / 1e3)
+    c = algorithmic_counts(w)
+    stages = {
+        "compress": {"ms": stage_ms["compress"], "bound": "hbm",
+                     "achieved_GBps": c["compress_bytes"] / (stage_ms["compress"] * 1e-3) / 1e9},
+        "index_topk": {"ms": stage_ms["index_topk"], "bound": "hbm",
+                       "achieved_GBps": 2 * c["score_bytes"] / (stage_ms["index_topk"] * 1e-3) / 1e9,
+                       "index_TFLOPs": c["index_flops"] / (stage_ms["index_topk"] * 1e-3) / 1e12},
+        "pack_v": {"ms": stage_ms["pack_v"], "bound": "hbm",
+                   "achieved_GBps": c["pack_bytes"] / max(stage_ms["pack_v"], 1e-9) / 1e6},
+        "attention": {"ms": stage_ms["attention"], "bound": "mfma",
+                      "achieved_TFLOPs": c["attention_flops"] / (stage_ms["attention"] * 1e-3) / 1e12},
+    }
+    for s in stages.values():
+        if "achieved_TFLOPs" in s:
+            s["frac"] = s["achieved_TFLOPs"] * 1e12 / PEAK_BF16_FLOPS
+        else:
+            s["frac"] = s["achieved_GBps"] * 1e9 / PEAK_HBM_BYTES
+    dominant = max(STAGES, key=lambda s: stage_ms[s])
+    if dominant == "attention":
+        ach = c["attention_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
+        roof = {"kernel": "attend_mfma_h8_kernel", "bound": "mfma", "achieved": ach,
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_BF16_FLOPS,
+                "traffic": load_traffic("attend", w.name),
+                "work_per_launch": f"{c['attention_flops']:.4e} FLOP = 4*d*h per attended "
+                                   f"(query, group, token) x {c['attended']:.4e}"}
+    else:
+        ms = stage_ms[dominant]
+        byts = {"index_topk": 2 * c["score_bytes"], "compress": c["compress_bytes"],
+                "pack_v": c["pack_bytes"]}[dominant]
+        ach = byts / (ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_BYTES / 1e9,
+                "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM_BYTES,
+                "traffic": load_traffic(dominant, w.name), "work_per_launch": f"{byts:.4e} B"}
+
+    cpu, parity = (None, None)
+    if args.cpu_seconds > 0:
+        cpu, parity = cpu_baseline(w, x, out, sel, args.cpu_seconds, args.seed)
+
+    rec = {
+        "metric": "Sparse-GQA prefill query-tokens/s at 128K ctx (index+topk+attn); % roofline",
+        "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; integer index data in [-4,4] with 64 needle blocks per group; "
+                "q,k,v ~ N(0,1)/sqrt(d); gate ~ N(0,1))",
+        "config": {"workload": w.name, "batch": w.batch, "t_q": w.t_q, "t_kv": w.t_kv,
+                   "kv_groups": w.groups, "heads_per_group": w.heads, "head_dim": w.head_dim,
+                   "index_dim": w.index_dim, "block": w.block, "topk_tokens": w.topk,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "parity": parity,
+        "algorithmic": c,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,7 +24,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; results are valid once the stream has been synchronised.
  *   - The caller owns every buffer, workspaces included; the library allocates no device memory,
- *     keeps no state between calls and never synchronises.  Inputs are read-only; outputs must not
+ *     keeps no state between calls (apart from the optional stage markers armed by
+ *     sgqa_set_stage_events) and never synchronises.  Inputs are read-only; outputs must not
  *     alias inputs.  Concurrent calls need distinct outputs and workspaces.
  *   - Arguments are validated on the host before anything is enqueued.  On any error the call
  *     returns a non-zero sgqa_status, enqueues nothing and touches no output; sgqa_last_error()
@@ -90,7 +91,9 @@ typedef struct {
   size_t scores_bytes;              /* scores buffer for sgqa_index / sgqa_topk            */
   size_t sel_bytes;                 /* sel buffer                                          */
   size_t attend_workspace_bytes;    /* workspace sgqa_attend needs                         */
-  size_t forward_workspace_bytes;   /* workspace sgqa_forward needs (fixed size)           */
+  size_t forward_workspace_bytes;   /* workspace for sgqa_forward with the default chunking */
+  size_t forward_workspace_min_bytes; /* smallest workspace sgqa_forward accepts (one query
+                                         token per chunk); any size in between also works   */
 } sgqa_sizes_t;
 
 /* ABI version of the loaded library (SGQA_ABI_VERSION when it matches this header). */
@@ -148,14 +151,33 @@ sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, 
  *   k_blk   : [Bt, NB, Di] (written when k_idx != NULL).
  *   sel_out : [Bt, Tq, G, NS] or NULL (the selection is then not returned).
  *   out     : [Bt, Tq, G, H, D].
- *   workspace: >= sizes.forward_workspace_bytes.  Scores are never stored in full: the selection
- *   is computed from block scores recomputed in tiles and the surviving candidates only.
+ *   workspace: >= sizes.forward_workspace_min_bytes; sizes.forward_workspace_bytes gives the
+ *   default chunking.  The workspace holds the packed V, an internal selection buffer and the
+ *   selection state of a chunk of query tokens: with bf16 index data and k/B <= 513 that state is
+ *   a short candidate list per (query, group) (the full score rows are never stored: candidate
+ *   scores at or above a sampled threshold are kept and the exact selection runs on them, falling
+ *   back to recomputed full rows when a list is too short or overflows); otherwise the chunk's full
+ *   score rows.  Larger workspaces mean fewer, larger chunks.
  * Results equal sgqa_index + sgqa_topk + sgqa_attend on the same inputs (selection bit-exact).
  */
 sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k, const void* v,
                          const void* gate, const void* q_idx, const void* k_idx, void* k_blk,
                          int32_t* sel_out, void* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * Profiling hook: stage markers for sgqa_forward.
+ *   events : SGQA_STAGE_EVENTS hipEvent_t handles (passed as void*) created by the caller, or NULL
+ *            to disarm.  The handles are copied; the array may be freed after the call.
+ * While armed, every sgqa_forward call on the calling thread records, on its stream,
+ *   events[0] before the first kernel, events[1] after block compression, events[2] after the
+ *   indexer and top-k of every query chunk, events[3] after the V packing, events[4] after the
+ *   attention kernel,
+ * so that hipEventElapsedTime between consecutive markers is the duration of that stage.  Arming
+ * costs nothing on the device; recording failures make sgqa_forward return SGQA_ERR_HIP.
+ */
+#define SGQA_STAGE_EVENTS 5
+sgqa_status sgqa_set_stage_events(void* const* events);
 
 #ifdef __cplusplus
 } /* extern "C" */

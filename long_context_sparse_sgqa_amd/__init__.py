@@ -29,7 +29,8 @@ SGQA_F32, SGQA_BF16 = 0, 1
 _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
-                    "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward")
+                    "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
+                    "sgqa_set_stage_events")
 
 
 class SgqaError(RuntimeError):
@@ -51,7 +52,8 @@ class _Sizes(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int64), ("n_sel", ctypes.c_int64),
                 ("k_blk_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t),
                 ("sel_bytes", ctypes.c_size_t), ("attend_workspace_bytes", ctypes.c_size_t),
-                ("forward_workspace_bytes", ctypes.c_size_t)]
+                ("forward_workspace_bytes", ctypes.c_size_t),
+                ("forward_workspace_min_bytes", ctypes.c_size_t)]
 
 
 class Problem:
@@ -118,7 +120,9 @@ def load_library():
     lib.sgqa_topk.argtypes = [P, vp, vp, vp]
     lib.sgqa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sgqa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward"):
+    lib.sgqa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
+                 "sgqa_set_stage_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

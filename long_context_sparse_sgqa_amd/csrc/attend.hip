@@ -19,8 +19,8 @@
 //   * V is read from a unit-packed copy [.., unit, d, 8 tokens] so the V^T operand is one 16-byte
 //     load per lane;
 //   * the epilogue divides by the row sum and multiplies by sigmoid(gate) before a bf16 store.
-//   Workgroups are numbered with the KV group fastest, so with 8 groups every XCD (workgroups are
-//   dealt round-robin to the 8 XCDs) serves one group and its L2 holds only that group's K/V.
+//   Workgroups are numbered with the token pairs fastest and the KV group next, so the GPU works
+//   through one group's K/V at a time (64 MiB at 128K), which stays resident in the Infinity Cache.
 // Plain path (fp32, or other head counts): one workgroup per (token, group), 32 lanes per head,
 // sequential online softmax over the attended tokens in fp32.
 #include "device_common.h"
@@ -199,10 +199,12 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
   constexpr int H = 8;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g = static_cast<int>(blockIdx.x % a.G);
-  const int64_t rest = blockIdx.x / a.G;
-  const int64_t pg = rest % a.pair_groups;
-  const int64_t b = rest / a.pair_groups;
+  // group-major order: the whole GPU sweeps one (sequence, KV group) at a time, so the K/V working
+  // set is one group's, which the Infinity Cache holds
+  const int64_t pg = blockIdx.x % a.pair_groups;
+  const int64_t bg = blockIdx.x / a.pair_groups;
+  const int g = static_cast<int>(bg % a.G);
+  const int64_t b = bg / a.G;
   const int64_t pair = pg * kMfmaWaves + wave;
   const int64_t tokA = 2 * pair;
   const bool validA = tokA < a.Tq;
@@ -243,8 +245,9 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
   for (int kc = 0; kc < D / 32; ++kc)
     qf[kc] = rowvalid ? load_bf16x8(qrow + 32 * kc + 8 * lg) : zero_bf16x8();
 
-  const bf16_t* kg = a.k + (b * a.G + g) * a.Tk * D;
-  const bf16_t* vg = a.vp + (b * a.G + g) * a.NU * D * 8;
+  // buffer resources of this (sequence, group): 32-bit offsets, out-of-range reads return 0
+  const BufRsrc krs = make_rsrc(a.k + (b * a.G + g) * a.Tk * D, a.Tk * D * 2);
+  const BufRsrc vrs = make_rsrc(a.vp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
 
   f32x4_t acc[D / 16];
 #pragma unroll
@@ -252,68 +255,84 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
   float m_run = -1e30f, l_run = 0.f;
   const float ninf = -__builtin_inff();
 
+  // K rows of a chunk for this lane: unit slot lr/4, tokens (lr%4) and (lr%4)+4 of that unit
+  auto k_offset = [&](int c0) -> int {
+    const int e = c0 + (lr >> 2);
+    const int u = (e < nu) ? uunit[e] : 0;
+    return ((u * 8 + (lr & 3)) * D + 8 * lg) * 2;
+  };
+  bf16x8_t k1[D / 32], k2[D / 32];
+  if (nu > 0) {
+    const int ko = k_offset(0);
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) {
+      k1[kc] = buffer_load_bf16x8(krs, ko + kc * 64);
+      k2[kc] = buffer_load_bf16x8(krs, ko + 4 * D * 2 + kc * 64);
+    }
+  }
+
   for (int c0 = 0; c0 < nu; c0 += 4) {
     const int eS = c0 + lg;                        // the unit whose scores this lane holds
-    int unitS = -1;
+    int unitS = 0;
     uint32_t msk = 0u;
     if (eS < nu) {
       unitS = uunit[eS];
       msk = umask[eS];
     }
-    const int eK = c0 + (lr >> 2);                 // the unit of this lane's K rows
-    const int unitK = (eK < nu) ? uunit[eK] : 0;
-    int64_t t1 = static_cast<int64_t>(unitK) * 8 + (lr & 3);
-    int64_t t2 = t1 + 4;
-    t1 = t1 < a.Tk ? t1 : a.Tk - 1;
-    t2 = t2 < a.Tk ? t2 : a.Tk - 1;
+    // V^T operand rows of this chunk (issued early, consumed after the softmax)
+    bf16x8_t vf[D / 16];
+    const int vo = (unitS * D + lr) * 16;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) vf[t] = buffer_load_bf16x8(vrs, vo + t * 256);
 
     f32x4_t s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t s2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
-      const bf16x8_t k1 = load_bf16x8(kg + t1 * D + 32 * kc + 8 * lg);
-      const bf16x8_t k2 = load_bf16x8(kg + t2 * D + 32 * kc + 8 * lg);
-      s1 = mfma16x16x32(k1, qf[kc], s1);
-      s2 = mfma16x16x32(k2, qf[kc], s2);
+      s1 = mfma16x16x32(k1[kc], qf[kc], s1);
+      s2 = mfma16x16x32(k2[kc], qf[kc], s2);
     }
-    // lane holds scores of unit unitS, tokens 0..3 (s1) and 4..7 (s2), for row lr
+    if (c0 + 4 < nu) {                             // prefetch the next chunk's K rows
+      const int ko = k_offset(c0 + 4);
+#pragma unroll
+      for (int kc = 0; kc < D / 32; ++kc) {
+        k1[kc] = buffer_load_bf16x8(krs, ko + kc * 64);
+        k2[kc] = buffer_load_bf16x8(krs, ko + 4 * D * 2 + kc * 64);
+      }
+    }
+
+    // valid tokens of the lane's unit for its row: chosen by the row's token and t <= p
     const uint32_t bits = X ? ((msk >> 8) & 0xffu) : (msk & 0xffu);
-    const int64_t tbase = static_cast<int64_t>(unitS) * 8;
+    const int64_t dlt = pX - static_cast<int64_t>(unitS) * 8;
+    const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
+    const uint32_t valid = bits & causal;
     float sv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ok0 = ((bits >> e) & 1u) && (tbase + e <= pX);
-      const bool ok1 = ((bits >> (e + 4)) & 1u) && (tbase + e + 4 <= pX);
-      sv[e] = ok0 ? s1[e] * a.scale_log2e : ninf;
-      sv[e + 4] = ok1 ? s2[e] * a.scale_log2e : ninf;
+      sv[e] = ((valid >> e) & 1u) ? s1[e] * a.scale_log2e : ninf;
+      sv[e + 4] = ((valid >> (e + 4)) & 1u) ? s2[e] * a.scale_log2e : ninf;
     }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    uint32_t pw[4];
-    float psum = 0.f;
+    if (__ballot(m_new > m_run)) {                 // some row's max grew: rescale (alpha = 1 elsewhere)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sv[2 * e] - m_new));
-      const bf16_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sv[2 * e + 1] - m_new));
-      psum += bf16_to_f32(p0) + bf16_to_f32(p1);
-      pw[e] = static_cast<uint32_t>(p0) | (static_cast<uint32_t>(p1) << 16);
+      for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
+      m_run = m_new;
     }
-    l_run = l_run * alpha + psum;
-    const bf16x8_t pf = bf16x8_from_u4(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-    const int unitV = unitS >= 0 ? unitS : 0;
-    const bf16_t* vrow = vg + (static_cast<int64_t>(unitV) * D + lr) * 8;
+    float pv[8];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      acc[t] *= alpha;
-      const bf16x8_t vf = load_bf16x8(vrow + t * 16 * 8);
-      acc[t] = mfma16x16x32(vf, pf, acc[t]);
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
+      l_run += pv[e];
     }
+    const bf16x8_t pf = pack8_bf16(pv);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[t] = mfma16x16x32(vf[t], pf, acc[t]);
   }
 
   // epilogue: row sum over the 4 lane groups, normalise, gate, store
@@ -403,7 +422,9 @@ __global__ void __launch_bounds__(1024) attend_plain_kernel(
 
 bool attend_uses_mfma(const Dims& d) {
   const bool block_ok = (d.B % 8 == 0) || (8 % d.B == 0);
-  return d.bf16 && d.H == 8 && block_ok && units_per_query(d) <= kMaxUnits;
+  // 32-bit buffer offsets: one (sequence, group) of packed V must stay below 2 GiB
+  const bool offsets_ok = d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31);
+  return d.bf16 && d.H == 8 && block_ok && offsets_ok && units_per_query(d) <= kMaxUnits;
 }
 
 int64_t units_per_query(const Dims& d) {
@@ -420,18 +441,21 @@ size_t attend_packed_v_bytes(const Dims& d) {
   return static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
 }
 
-hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* gate, const int32_t* sel, void* out, void* packed_v,
-                         hipStream_t s) {
+hipError_t launch_pack_v(const Dims& d, const void* v, void* packed_v, hipStream_t s) {
+  if (!attend_uses_mfma(d)) return hipSuccess;
+  const int64_t total = d.Bt * d.G * d.NU * d.D;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(packed_v), d.Tk, d.NU, d.D,
+                     total);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* gate, const int32_t* sel, void* out,
+                                const void* packed_v, hipStream_t s) {
   if (attend_uses_mfma(d)) {
-    const int64_t total = d.Bt * d.G * d.NU * d.D;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(v), static_cast<bf16_t*>(packed_v), d.Tk, d.NU,
-                       d.D, total);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     MfmaArgs a;
     a.q = static_cast<const bf16_t*>(q);
     a.k = static_cast<const bf16_t*>(k);
@@ -492,6 +516,14 @@ hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void
                          d.scale);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
+                         const void* gate, const int32_t* sel, void* out, void* packed_v,
+                         hipStream_t s) {
+  hipError_t e = launch_pack_v(d, v, packed_v, s);
+  if (e != hipSuccess) return e;
+  return launch_attend_packed(d, q, k, v, gate, sel, out, packed_v, s);
 }
 
 }  // namespace sgqa

@@ -57,6 +57,28 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Hardware round-to-nearest-even packing of 8 fp32 into the bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8_t pack8_bf16(const float* v) {
+  typedef float f32x8_t __attribute__((ext_vector_type(8)));
+  const f32x8_t x = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+  return __builtin_convertvector(x, bf16x8_t);
+}
+
+// Raw buffer access: wave-uniform base and size, 32-bit byte offsets, reads past `bytes` give 0.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ bf16x8_t buffer_load_bf16x8(BufRsrc r, int byte_offset) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

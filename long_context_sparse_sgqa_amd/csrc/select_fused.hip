@@ -1,0 +1,369 @@
+// Steps 2-3 fused for the one-call forward: indexer scores are never stored in full.
+//
+// Same method as index.hip + topk.hip (Step 5 Preview pages, mo.ai.kr summary, section
+// "모델 구조와 학습 안정성": every KV group scores the block-compressed shared index keys and keeps
+// its own top-k blocks; B = 8 makes this eight times cheaper than token-level scoring).  Readings:
+// raw dot-product scores of the strictly past blocks j < o = p/B, the own block always selected
+// and counted in the NS = k/B budget, ties to the lower block index, ascending output.
+//
+// filter kernel (one workgroup = 4 waves = 64 rows of one sequence; a row = (query, KV group)):
+//   1. sample: scores against 512 blocks at a fixed stride (v_mfma_f32_16x16x32_bf16); per row the
+//      r-th largest sampled score, r chosen so that about twice the budget is expected to pass, is
+//      the row's threshold (kept as the top 16 bits of the order-preserving key: any threshold is
+//      correct, it only sizes the candidate list);
+//   2. filter: every causal score, column tiles of K_blk staged in LDS (double-buffered) and
+//      shared by the 4 waves; a wave owns 16 whole rows, so its ballot-ordered appends keep each
+//      row's (key, block) candidates in ascending block order.
+// select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
+//   candidates held in registers, then an ordered ballot emit of keys > tau and the lowest-indexed
+//   keys == tau.  Exact whenever at least NS-1 candidates passed (every member of the top set is
+//   >= tau >= threshold); rows with too few or too many (> capacity) candidates are queued for the
+//   exact fallback in topk.hip, which recomputes the full score row.
+#include "device_common.h"
+#include "sgqa_internal.h"
+
+namespace sgqa {
+namespace {
+
+constexpr int kRows = 64;          // rows per workgroup
+constexpr int kSamp = 512;         // sampled blocks per row
+constexpr int kCols = 128;         // K_blk columns per staged tile
+
+__device__ __forceinline__ uint32_t order_key_f(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;                 // -0.0 and +0.0 are the same score
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+struct FilterArgs {
+  const bf16_t* q_idx;
+  const bf16_t* k_blk;
+  uint64_t* cand;              // [chunk rows][cap]
+  int32_t* cnt;                // [chunk rows]
+  int32_t* fail_count;         // zeroed here (block 0) for the select kernel that follows
+  int64_t b0, i0, ntok, Tq, pos0, NB, seq_rows, tiles_per_seq;
+  int G, B, NS, cap;
+};
+
+template <int DI>
+__global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
+  constexpr int kRowBytes = DI * 2 + 16;                  // padded LDS row of one K_blk block
+  constexpr int kTileBytes = kCols * kRowBytes;
+  constexpr int kSampBytes = kRows * kSamp * 2;
+  constexpr int kLds = (kSampBytes > 2 * kTileBytes) ? kSampBytes : 2 * kTileBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
+  __shared__ uint32_t s_thr[kRows];
+
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t seq = blockIdx.x / a.tiles_per_seq;
+  const int64_t row0 = (blockIdx.x - seq * a.tiles_per_seq) * kRows;      // within the sequence
+  const int64_t rows_here = min<int64_t>(kRows, a.seq_rows - row0);
+  const int64_t b = a.b0 + seq;
+  const bf16_t* kb = a.k_blk + b * a.NB * DI;
+
+  // o of a local row (rows of the tile hold consecutive tokens, so the last row has the largest)
+  auto row_o = [&](int local, int64_t* rr_out) -> int64_t {
+    const int64_t rl = row0 + local;
+    const int64_t tok = rl / a.G;
+    const int64_t i = a.i0 + tok;
+    if (rr_out) *rr_out = seq * a.seq_rows + rl;
+    return (a.pos0 + i) / a.B;
+  };
+  const int64_t o_max = row_o(static_cast<int>(rows_here) - 1, nullptr);
+
+  // this wave's 16 rows: A operand (q_idx) for every k-step, plus per-lane row facts for C rows
+  const int my_local_a = wave * 16 + lr;                  // A row held by this lane
+  const bool a_valid = my_local_a < rows_here;
+  bf16x8_t qa[DI / 32];
+  {
+    const int64_t rl = row0 + (a_valid ? my_local_a : 0);
+    const int64_t tok = rl / a.G;
+    const int g = static_cast<int>(rl - tok * a.G);
+    const bf16_t* qrow = a.q_idx + (((b * a.Tq) + a.i0 + tok) * a.G + g) * DI;
+#pragma unroll
+    for (int kc = 0; kc < DI / 32; ++kc) qa[kc] = a_valid ? load_bf16x8(qrow + kc * 32 + lg * 8) : zero_bf16x8();
+  }
+  int64_t c_rr[4], c_o[4];
+  bool c_valid[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int local = wave * 16 + lg * 4 + e;
+    c_valid[e] = local < rows_here;
+    c_o[e] = c_valid[e] ? row_o(local, &c_rr[e]) : 0;
+    if (!c_valid[e]) c_rr[e] = 0;
+  }
+
+  // ---------------- phase 1: sampled scores -> per-row threshold ----------------
+  const bool sampling = o_max > a.cap;
+  if (sampling) {
+    const int64_t stride = (o_max + kSamp - 1) / kSamp;
+    uint16_t* samp = reinterpret_cast<uint16_t*>(lds);
+    for (int n = 0; n < kSamp / 16; ++n) {
+      const int64_t col = (static_cast<int64_t>(n) * 16 + lr) * stride;
+      const bool ok = col < a.NB;
+      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < DI / 32; ++kc) {
+        const bf16x8_t bb = ok ? load_bf16x8(kb + col * DI + kc * 32 + lg * 8) : zero_bf16x8();
+        c = mfma16x16x32(qa[kc], bb, c);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        samp[(wave * 16 + lg * 4 + e) * kSamp + n * 16 + lr] =
+            static_cast<uint16_t>(order_key_f(c[e]) >> 16);
+    }
+    __syncthreads();
+    // per row: the r-th largest sampled key (top 16 bits), one row at a time per wave
+    for (int rloc = 0; rloc < 16; ++rloc) {
+      const int local = wave * 16 + rloc;
+      uint32_t thr = 0u;
+      if (local < rows_here) {
+        const int64_t o = row_o(local, nullptr);
+        if (o > a.cap && o + 1 > a.NS) {
+          const int nvalid = static_cast<int>((o + stride - 1) / stride);
+          const int need = a.NS - 1;
+          int r = static_cast<int>((2ll * need * nvalid + o - 1) / o);
+          r = r < 1 ? 1 : (r > nvalid ? nvalid : r);
+          uint32_t kv[kSamp / 64];
+#pragma unroll
+          for (int e = 0; e < kSamp / 64; ++e) {
+            const int s = e * 64 + lane;
+            kv[e] = s < nvalid ? samp[local * kSamp + s] : 0u;
+          }
+          uint32_t prefix = 0u;
+          for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t cand = prefix | (1u << bit);
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < kSamp / 64; ++e) c += kv[e] >= cand ? 1 : 0;
+            if (wave_sum(c) >= r) prefix = cand;
+          }
+          thr = prefix << 16;
+        }
+      }
+      if (lane == 0) s_thr[local] = thr;
+    }
+  } else {
+    if (threadIdx.x < kRows) s_thr[threadIdx.x] = 0u;
+  }
+  __syncthreads();
+  uint32_t c_thr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c_thr[e] = s_thr[wave * 16 + lg * 4 + e];
+
+  // ---------------- phase 2: every causal score, filtered, ordered appends ----------------
+  int count[4] = {0, 0, 0, 0};
+  const int64_t ntiles = (o_max + kCols - 1) / kCols;
+  // staging: 128 blocks x DI bf16 = 128 x (DI/8) 16-byte pieces over 256 threads; the next tile
+  // is fetched into registers before the current one is multiplied and written to LDS after it
+  constexpr int kPer = kCols * (DI / 8) / 256;
+  uint4 pre[kPer];
+  auto load_tile = [&](int64_t t) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int pc = threadIdx.x + k * 256;
+      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
+      const int64_t col = t * kCols + row;
+      pre[k] = col < a.NB ? *reinterpret_cast<const uint4*>(kb + col * DI + part * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* dst = lds + buf * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int pc = threadIdx.x + k * 256;
+      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
+      *reinterpret_cast<uint4*>(dst + row * kRowBytes + part * 16) = pre[k];
+    }
+  };
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int buf = static_cast<int>(t & 1);
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const unsigned char* src = lds + buf * kTileBytes;
+#pragma unroll 2
+    for (int n = 0; n < kCols / 16; ++n) {
+      const int64_t col = t * kCols + n * 16 + lr;
+      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < DI / 32; ++kc) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + (n * 16 + lr) * kRowBytes + kc * 64 + lg * 16);
+        c = mfma16x16x32(qa[kc], bf16x8_from_u4(u), c);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key_f(c[e]);
+        const bool pass = c_valid[e] && col < c_o[e] && key >= c_thr[e];
+        const uint64_t bal = __ballot(pass);
+        const uint32_t grp = static_cast<uint32_t>(bal >> (lg * 16)) & 0xffffu;
+        const int pos = count[e] + __popc(static_cast<uint32_t>((bal & lt_mask) >> (lg * 16)));
+        if (pass && pos < a.cap)
+          a.cand[c_rr[e] * a.cap + pos] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(col);
+        count[e] += __popc(grp);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier below in t-1
+    __syncthreads();
+  }
+  if (lr == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c_valid[e]) a.cnt[c_rr[e]] = count[e];
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// select: one wave per row over its candidate list
+// ------------------------------------------------------------------------------------------------
+struct SelectArgs {
+  const uint64_t* cand;
+  const int32_t* cnt;
+  int32_t* sel;
+  int32_t* fail_list;
+  int32_t* fail_count;
+  int64_t b0, i0, ntok, Tq, pos0, rows;
+  int G, B, NS, cap;
+};
+
+constexpr int kSelPer = 32;        // candidates per lane held in registers (cap <= 64 * kSelPer)
+
+__global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (rr >= a.rows) return;
+  const int64_t tok = rr / a.G;
+  const int g = static_cast<int>(rr - tok * a.G);
+  const int64_t bseq = a.b0 + tok / a.ntok;
+  const int64_t i = a.i0 + tok % a.ntok;
+  const int64_t o = (a.pos0 + i) / a.B;
+  int32_t* out = a.sel + ((bseq * a.Tq + i) * a.G + g) * a.NS;
+  if (o + 1 <= a.NS) {
+    for (int x = lane; x < a.NS; x += 64) out[x] = (x <= o) ? x : -1;
+    return;
+  }
+  const int need = a.NS - 1;
+  const int m = a.cnt[rr];
+  if (m < need || m > a.cap) {
+    if (lane == 0) a.fail_list[atomicAdd(a.fail_count, 1)] = static_cast<int32_t>(rr);
+    return;
+  }
+  const uint64_t* cr = a.cand + rr * a.cap;
+  uint32_t key[kSelPer];
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) {
+    const int x = e * 64 + lane;
+    key[e] = x < m ? static_cast<uint32_t>(cr[x] >> 32) : 0u;
+  }
+  // tau = the need-th largest key: the largest v with #(key >= v) >= need
+  uint32_t tau = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) c += key[e] >= cand ? 1 : 0;
+    if (wave_sum(c) >= need) tau = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) gt += key[e] > tau ? 1 : 0;
+  const int take_eq = need - wave_sum(gt);
+  // ordered emit (candidates are in ascending block order)
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  int written = 0, eq_seen = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) {
+    if (e * 64 >= m) break;
+    const int x = e * 64 + lane;
+    const bool valid = x < m;
+    const bool is_gt = valid && key[e] > tau;
+    const bool is_eq = valid && key[e] == tau;
+    const uint64_t beq = __ballot(is_eq);
+    const int eq_rank = eq_seen + __popcll(beq & lt_mask);
+    const bool take = is_gt || (is_eq && eq_rank < take_eq);
+    const uint64_t btk = __ballot(take);
+    if (take) out[written + __popcll(btk & lt_mask)] = static_cast<int32_t>(cr[x] & 0xffffffffu);
+    written += __popcll(btk);
+    eq_seen += __popcll(beq);
+  }
+  if (lane == 0) out[need] = static_cast<int32_t>(o);
+}
+
+}  // namespace
+
+int fused_select_capacity() { return 64 * kSelPer; }
+
+bool fused_select_supported(const Dims& d) {
+  // the candidate list holds about twice the budget: budgets up to 512 blocks
+  return d.idx_bf16 && d.NS <= 513 && (d.Di == 32 || d.Di == 64 || d.Di == 128);
+}
+
+hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
+                               int32_t* cnt, int32_t* fail_count, const Chunk& c, hipStream_t s) {
+  FilterArgs a;
+  a.q_idx = static_cast<const bf16_t*>(q_idx);
+  a.k_blk = static_cast<const bf16_t*>(k_blk);
+  a.cand = cand;
+  a.cnt = cnt;
+  a.fail_count = fail_count;
+  a.b0 = c.b0;
+  a.i0 = c.i0;
+  a.ntok = c.ntok;
+  a.Tq = d.Tq;
+  a.pos0 = d.pos0;
+  a.NB = d.NB;
+  a.seq_rows = c.ntok * d.G;
+  a.tiles_per_seq = (a.seq_rows + kRows - 1) / kRows;
+  a.G = d.G;
+  a.B = d.B;
+  a.NS = d.NS;
+  a.cap = fused_select_capacity();
+  const dim3 grid(static_cast<unsigned>(a.tiles_per_seq * c.nseq));
+  if (d.Di == 128)
+    hipLaunchKernelGGL(index_filter_kernel<128>, grid, dim3(256), 0, s, a);
+  else if (d.Di == 64)
+    hipLaunchKernelGGL(index_filter_kernel<64>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(index_filter_kernel<32>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
+                                    int32_t* sel, int32_t* fail_list, int32_t* fail_count,
+                                    const Chunk& c, hipStream_t s) {
+  SelectArgs a;
+  a.cand = cand;
+  a.cnt = cnt;
+  a.sel = sel;
+  a.fail_list = fail_list;
+  a.fail_count = fail_count;
+  a.b0 = c.b0;
+  a.i0 = c.i0;
+  a.ntok = c.ntok;
+  a.Tq = d.Tq;
+  a.pos0 = d.pos0;
+  a.rows = c.rows(d.G);
+  a.G = d.G;
+  a.B = d.B;
+  a.NS = d.NS;
+  a.cap = fused_select_capacity();
+  const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
+  hipLaunchKernelGGL(select_candidates_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sgqa

@@ -14,6 +14,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_events[SGQA_STAGE_EVENTS];
+thread_local bool g_stage_armed = false;
 
 sgqa_status fail(sgqa_status st, const char* fmt, ...) {
   char buf[512];
@@ -44,8 +46,9 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 size_t dtype_size(int32_t dt) { return dt == SGQA_BF16 ? 2 : 4; }
 
-// Query-token rectangle a fixed score budget holds in the forward workspace.
-constexpr size_t kForwardScoreBudget = size_t(4) << 30;   // 4 GiB of fp32 scores per chunk
+// Query tokens per chunk are bounded by a fixed budget of per-chunk selection state (stored score
+// rows on the split path, candidate lists on the fused path).
+constexpr size_t kForwardChunkBudget = size_t(2) << 30;   // 2 GiB
 
 struct Derived {
   sgqa::Dims d;
@@ -124,17 +127,65 @@ bool attend_block_ok(const sgqa::Dims& d) { return (d.B % 8 == 0) || (8 % d.B ==
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Forward workspace: [packed v][internal sel][score chunk]; the chunk holds `chunk_tok` tokens.
-size_t forward_fixed_bytes(const Derived& dv) {
-  return align_up(dv.packed_v_bytes) + align_up(dv.sel_bytes);
+// Forward workspace layout.
+//   fused path : [packed v][internal sel][fail count][fallback scratch][cand][cnt][fail list]
+//   split path : [packed v][internal sel][scores]
+// where the last group is sized per query token and repeats for `chunk_tok` tokens.
+struct ForwardLayout {
+  bool fused;
+  size_t off_sel, off_failcnt, off_scratch, off_chunk;
+  size_t fixed;           // bytes before the per-chunk area
+  size_t per_token;       // per-chunk bytes per query token (all groups)
+  size_t cand_bytes, cnt_bytes;   // per token, fused path
+};
+
+ForwardLayout forward_layout(const Derived& dv) {
+  ForwardLayout L{};
+  const sgqa::Dims& d = dv.d;
+  L.fused = sgqa::fused_select_supported(d);
+  size_t off = align_up(dv.packed_v_bytes);
+  L.off_sel = off;
+  off += align_up(dv.sel_bytes);
+  if (L.fused) {
+    L.off_failcnt = off;
+    off += kAlign;
+    L.off_scratch = off;
+    off += align_up(sgqa::select_fallback_scratch_bytes(d));
+    L.cand_bytes = static_cast<size_t>(d.G) * sgqa::fused_select_capacity() * sizeof(uint64_t);
+    L.cnt_bytes = static_cast<size_t>(d.G) * sizeof(int32_t);
+    L.per_token = L.cand_bytes + 2 * L.cnt_bytes;     // cand + cnt + fail list
+  } else {
+    L.per_token = dv.score_row_bytes;
+  }
+  L.off_chunk = off;
+  L.fixed = off;
+  return L;
+}
+
+// Bytes of the per-chunk area for `tok` tokens (each sub-array aligned).
+size_t chunk_bytes(const ForwardLayout& L, int64_t tok) {
+  const size_t t = static_cast<size_t>(tok);
+  if (L.fused) return align_up(t * L.cand_bytes) + 2 * align_up(t * L.cnt_bytes);
+  return align_up(t * L.per_token);
 }
 
 size_t forward_default_bytes(const Derived& dv) {
-  const size_t tokens = static_cast<size_t>(dv.d.Bt * dv.d.Tq);
-  size_t chunk = kForwardScoreBudget / dv.score_row_bytes;
+  const ForwardLayout L = forward_layout(dv);
+  const int64_t tokens = dv.d.Bt * dv.d.Tq;
+  int64_t chunk = static_cast<int64_t>(kForwardChunkBudget / L.per_token);
   if (chunk < 1) chunk = 1;
   if (chunk > tokens) chunk = tokens;
-  return forward_fixed_bytes(dv) + align_up(chunk * dv.score_row_bytes);
+  return L.fixed + chunk_bytes(L, chunk);
+}
+
+// Largest chunk (in query tokens) the given workspace holds; 0 if not even one token fits.
+int64_t forward_chunk_tokens(const Derived& dv, const ForwardLayout& L, size_t ws_bytes) {
+  if (ws_bytes < L.fixed) return 0;
+  const int64_t tokens = dv.d.Bt * dv.d.Tq;
+  int64_t chunk = static_cast<int64_t>((ws_bytes - L.fixed) / L.per_token);
+  if (chunk > tokens) chunk = tokens;
+  while (chunk > 0 && L.fixed + chunk_bytes(L, chunk) > ws_bytes) --chunk;
+  return chunk;
 }
 
 sgqa_status check_ptr(const void* p, const char* name) {
@@ -144,15 +195,23 @@ sgqa_status check_ptr(const void* p, const char* name) {
   return SGQA_OK;
 }
 
+// Records stage marker `i` when the profiling hook is armed.
+sgqa_status mark_stage(int i, hipStream_t s) {
+  if (!g_stage_armed) return SGQA_OK;
+  hipError_t e = hipEventRecord(g_stage_events[i], s);
+  if (e != hipSuccess) return hip_fail(e, "stage marker");
+  return SGQA_OK;
+}
+
 #define SGQA_CHECK(expr)                \
   do {                                  \
     sgqa_status _st = (expr);           \
     if (_st != SGQA_OK) return _st;     \
   } while (0)
 
-// Index + top-k over query-token rectangles of at most `chunk_tok` tokens.
-sgqa_status index_topk_chunked(const sgqa::Dims& d, const void* q_idx, const void* k_blk,
-                               float* scores, int32_t* sel, int64_t chunk_tok, hipStream_t s) {
+// Query-token rectangles of at most `chunk_tok` tokens covering every sequence.
+template <class F>
+sgqa_status for_each_chunk(const sgqa::Dims& d, int64_t chunk_tok, F&& fn) {
   for (int64_t b = 0; b < d.Bt;) {
     sgqa::Chunk c;
     if (chunk_tok >= d.Tq) {
@@ -161,10 +220,7 @@ sgqa_status index_topk_chunked(const sgqa::Dims& d, const void* q_idx, const voi
       if (c.nseq > d.Bt - b) c.nseq = d.Bt - b;
       c.i0 = 0;
       c.ntok = d.Tq;
-      hipError_t e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
-      if (e != hipSuccess) return hip_fail(e, "indexer launch");
-      e = sgqa::launch_topk(d, scores, sel, c, s);
-      if (e != hipSuccess) return hip_fail(e, "top-k launch");
+      SGQA_CHECK(fn(c));
       b += c.nseq;
     } else {
       for (int64_t i0 = 0; i0 < d.Tq; i0 += chunk_tok) {
@@ -172,15 +228,44 @@ sgqa_status index_topk_chunked(const sgqa::Dims& d, const void* q_idx, const voi
         c.nseq = 1;
         c.i0 = i0;
         c.ntok = (d.Tq - i0 < chunk_tok) ? d.Tq - i0 : chunk_tok;
-        hipError_t e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
-        if (e != hipSuccess) return hip_fail(e, "indexer launch");
-        e = sgqa::launch_topk(d, scores, sel, c, s);
-        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        SGQA_CHECK(fn(c));
       }
       b += 1;
     }
   }
   return SGQA_OK;
+}
+
+// Steps 2-3 of the forward, chunk by chunk, on either path.
+sgqa_status select_chunked(const sgqa::Dims& d, const ForwardLayout& L, char* ws, int64_t chunk_tok,
+                           const void* q_idx, const void* k_blk, int32_t* sel, hipStream_t s) {
+  char* area = ws + L.off_chunk;
+  if (!L.fused) {
+    float* scores = reinterpret_cast<float*>(area);
+    return for_each_chunk(d, chunk_tok, [&](const sgqa::Chunk& c) -> sgqa_status {
+      hipError_t e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
+      if (e != hipSuccess) return hip_fail(e, "indexer launch");
+      e = sgqa::launch_topk(d, scores, sel, c, s);
+      if (e != hipSuccess) return hip_fail(e, "top-k launch");
+      return SGQA_OK;
+    });
+  }
+  const size_t t = static_cast<size_t>(chunk_tok);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(area);
+  int32_t* cnt = reinterpret_cast<int32_t*>(area + align_up(t * L.cand_bytes));
+  int32_t* fail_list = reinterpret_cast<int32_t*>(area + align_up(t * L.cand_bytes) +
+                                                  align_up(t * L.cnt_bytes));
+  int32_t* fail_count = reinterpret_cast<int32_t*>(ws + L.off_failcnt);
+  float* scratch = reinterpret_cast<float*>(ws + L.off_scratch);
+  return for_each_chunk(d, chunk_tok, [&](const sgqa::Chunk& c) -> sgqa_status {
+    hipError_t e = sgqa::launch_index_filter(d, q_idx, k_blk, cand, cnt, fail_count, c, s);
+    if (e != hipSuccess) return hip_fail(e, "index filter launch");
+    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, s);
+    if (e != hipSuccess) return hip_fail(e, "candidate select launch");
+    e = sgqa::launch_select_fallback(d, q_idx, k_blk, fail_list, fail_count, scratch, sel, c, s);
+    if (e != hipSuccess) return hip_fail(e, "select fallback launch");
+    return SGQA_OK;
+  });
 }
 
 }  // namespace
@@ -215,6 +300,10 @@ sgqa_status sgqa_sizes(const sgqa_problem* prob, sgqa_sizes_t* out) {
   out->sel_bytes = dv.sel_bytes;
   out->attend_workspace_bytes = dv.packed_v_bytes;
   out->forward_workspace_bytes = forward_default_bytes(dv);
+  {
+    const ForwardLayout L = forward_layout(dv);
+    out->forward_workspace_min_bytes = L.fixed + chunk_bytes(L, 1);
+  }
   return ok();
 }
 
@@ -294,25 +383,46 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
   if (k_idx) SGQA_CHECK(check_ptr(k_idx, "k_idx"));
   if (sel_out) SGQA_CHECK(check_ptr(sel_out, "sel_out"));
   SGQA_CHECK(check_ptr(workspace, "workspace"));
-  const size_t fixed = forward_fixed_bytes(dv);
-  if (workspace_bytes < fixed + dv.score_row_bytes)
+  const ForwardLayout L = forward_layout(dv);
+  const int64_t chunk_tok = forward_chunk_tokens(dv, L, workspace_bytes);
+  if (chunk_tok < 1)
     return fail(SGQA_ERR_WORKSPACE, "forward workspace needs at least %zu bytes (got %zu)",
-                fixed + dv.score_row_bytes, workspace_bytes);
+                L.fixed + chunk_bytes(L, 1), workspace_bytes);
   char* ws = static_cast<char*>(workspace);
   void* packed_v = dv.packed_v_bytes ? ws : nullptr;
-  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + align_up(dv.packed_v_bytes));
-  float* scores = reinterpret_cast<float*>(ws + fixed);
-  int64_t chunk_tok = static_cast<int64_t>((workspace_bytes - fixed) / dv.score_row_bytes);
-  if (chunk_tok > d.Bt * d.Tq) chunk_tok = d.Bt * d.Tq;
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + L.off_sel);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  SGQA_CHECK(mark_stage(0, s));
   if (k_idx) {
     hipError_t e = sgqa::launch_compress(d, k_idx, k_blk, s);
     if (e != hipSuccess) return hip_fail(e, "compress launch");
   }
-  SGQA_CHECK(index_topk_chunked(d, q_idx, k_blk, scores, sel, chunk_tok, s));
-  hipError_t e = sgqa::launch_attend(d, q, k, v, gate, sel, out, packed_v, s);
+  SGQA_CHECK(mark_stage(1, s));
+  SGQA_CHECK(select_chunked(d, L, ws, chunk_tok, q_idx, k_blk, sel, s));
+  SGQA_CHECK(mark_stage(2, s));
+  hipError_t e = sgqa::launch_pack_v(d, v, packed_v, s);
+  if (e != hipSuccess) return hip_fail(e, "v packing launch");
+  SGQA_CHECK(mark_stage(3, s));
+  e = sgqa::launch_attend_packed(d, q, k, v, gate, sel, out, packed_v, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  SGQA_CHECK(mark_stage(4, s));
+  return ok();
+}
+
+sgqa_status sgqa_set_stage_events(void* const* events) {
+  if (!events) {
+    g_stage_armed = false;
+    return ok();
+  }
+  for (int i = 0; i < SGQA_STAGE_EVENTS; ++i) {
+    if (!events[i]) {
+      g_stage_armed = false;
+      return fail(SGQA_ERR_NULL, "stage event %d is NULL", i);
+    }
+  }
+  for (int i = 0; i < SGQA_STAGE_EVENTS; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_stage_armed = true;
   return ok();
 }
 

@@ -44,6 +44,26 @@ hipError_t launch_index(const Dims& d, const void* q_idx, const void* k_blk, flo
 hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const Chunk& c,
                        hipStream_t s);
 
+// ---- steps 2-3 fused (one-call forward) --------------------------------------------------------
+// Candidate capacity per row and whether the fused path serves the problem (bf16 index data,
+// budgets up to 513 blocks).
+int fused_select_capacity();
+bool fused_select_supported(const Dims& d);
+// Filter: per chunk row, the (key << 32 | block) candidates at or above a sampled threshold, in
+// ascending block order, into cand + rr * capacity (count in cnt[rr], possibly > capacity).  Also
+// zeroes *fail_count.
+hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
+                               int32_t* cnt, int32_t* fail_count, const Chunk& c, hipStream_t s);
+// Select from the candidates; rows it cannot settle are appended to fail_list.
+hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
+                                    int32_t* sel, int32_t* fail_list, int32_t* fail_count,
+                                    const Chunk& c, hipStream_t s);
+// Exact selection of the listed rows from recomputed full score rows.
+size_t select_fallback_scratch_bytes(const Dims& d);
+hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* k_blk,
+                                  const int32_t* fail_list, const int32_t* fail_count,
+                                  float* scratch, int32_t* sel, const Chunk& c, hipStream_t s);
+
 // ---- step 4: attention ------------------------------------------------------------------------
 // Bytes of the unit-packed V copy the matrix-core attention kernel reads (0 when the problem is
 // served by the plain kernel, which reads v directly).
@@ -52,6 +72,12 @@ size_t attend_packed_v_bytes(const Dims& d);
 bool attend_uses_mfma(const Dims& d);
 // Largest number of 8-token units one (query, group) selection can cover.
 int64_t units_per_query(const Dims& d);
+// V packing (matrix-core path only; no-op otherwise), then the attention kernel.
+hipError_t launch_pack_v(const Dims& d, const void* v, void* packed_v, hipStream_t s);
+hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* gate, const int32_t* sel, void* out,
+                                const void* packed_v, hipStream_t s);
+// Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
                          const void* gate, const int32_t* sel, void* out, void* packed_v,
                          hipStream_t s);

@@ -240,7 +240,66 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
   if (t == 0) out[need] = static_cast<int32_t>(o);   // the own block, last in ascending order
 }
 
+// Exact selection for rows the fused candidate filter could not settle (too few candidates passed
+// the sampled threshold, or more than the candidate capacity): the row's full score vector is
+// recomputed into a scratch row and selected as in topk_kernel.  Each workgroup walks the failure
+// list with a stride of gridDim.x; the list length is read from device memory.
+__global__ void __launch_bounds__(kThreads) select_fallback_kernel(
+    const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_blk,
+    const int32_t* __restrict__ fail_list, const int32_t* __restrict__ fail_count,
+    float* __restrict__ scratch, int32_t* __restrict__ sel, int64_t NB, int Di, int NS, int B, int G,
+    int64_t Tq, int64_t pos0, int64_t b0, int64_t i0, int64_t ntok) {
+  __shared__ TopkShared sh;
+  __shared__ float qs[128];
+  const int nfail = *fail_count;
+  float* srow = scratch + static_cast<int64_t>(blockIdx.x) * NB;
+  const int t = threadIdx.x;
+  for (int f = blockIdx.x; f < nfail; f += gridDim.x) {
+    const int64_t rr = fail_list[f];
+    const int64_t tok = rr / G;
+    const int g = static_cast<int>(rr - tok * G);
+    const int64_t b = b0 + tok / ntok;
+    const int64_t i = i0 + tok % ntok;
+    const int64_t o = (pos0 + i) / B;
+    int32_t* out = sel + ((b * Tq + i) * G + g) * NS;
+    const bf16_t* qrow = q_idx + ((b * Tq + i) * G + g) * Di;
+    if (t < Di) qs[t] = bf16_to_f32(qrow[t]);
+    __syncthreads();
+    const bf16_t* kb = k_blk + b * NB * Di;
+    for (int64_t j = t; j < o; j += kThreads) {
+      const bf16_t* kr = kb + j * Di;
+      float acc = 0.f;
+      for (int c = 0; c < Di; ++c) acc = fmaf(qs[c], bf16_to_f32(kr[c]), acc);
+      srow[j] = acc;
+    }
+    __syncthreads();
+    const int need = NS - 1;
+    int take_eq = 0;
+    const RowSource row{srow};
+    const uint32_t tau = radix_select(row, static_cast<int>(o), need, &take_eq, sh);
+    emit_selected(row, static_cast<int>(o), tau, take_eq, need, out, sh);
+    if (t == 0) out[need] = static_cast<int32_t>(o);
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+constexpr int kFallbackWorkgroups = 256;
+
+size_t select_fallback_scratch_bytes(const Dims& d) {
+  return static_cast<size_t>(kFallbackWorkgroups) * static_cast<size_t>(d.NB) * sizeof(float);
+}
+
+hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* k_blk,
+                                  const int32_t* fail_list, const int32_t* fail_count,
+                                  float* scratch, int32_t* sel, const Chunk& c, hipStream_t s) {
+  hipLaunchKernelGGL(select_fallback_kernel, dim3(kFallbackWorkgroups), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), fail_list,
+                     fail_count, scratch, sel, d.NB, d.Di, d.NS, d.B, d.G, d.Tq, d.pos0, c.b0, c.i0,
+                     c.ntok);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const Chunk& c,
                        hipStream_t s) {
