@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
-STAGES = ("compress", "index_topk", "pack_v", "attention")
+STAGES = ("compress", "index_topk", "pack_kv", "attn_lists", "attention", "attn_merge")
+N_MARKS = len(STAGES) + 1
 
 
 def parse():
@@ -67,7 +68,9 @@ def algorithmic_counts(w):
         "score_bytes": 4 * pairs,
         "sel_bytes": 4 * rows * w.n_sel,
         "attention_flops": 4 * w.head_dim * w.heads * att,
-        "pack_bytes": 2 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,
+        "pack_bytes": 4 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,   # read + write K and V
+        # range partials: fp32 O and (max, sum) per row and range, read once, plus gate and out
+        "merge_bytes": rows * w.heads * (4 * (4 * w.head_dim + 8) + 2 * 2 * w.head_dim),
         # compulsory attention traffic: q, gate, out once, plus each group's K/V once
         "attention_min_bytes": 3 * rows * w.heads * w.head_dim * dsz
                                + 2 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,
@@ -217,8 +220,8 @@ def main():
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    marks = [[ev.create() for _ in range(5)] for _ in range(args.steps)]
-    arr_t = ctypes.c_void_p * 5
+    marks = [[ev.create() for _ in range(N_MARKS)] for _ in range(args.steps)]
+    arr_t = ctypes.c_void_p * N_MARKS
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -233,7 +236,7 @@ def main():
     for m in marks:
         for j, s in enumerate(STAGES):
             stage_ms[s] += ev.elapsed_ms(m[j], m[j + 1]) / args.steps
-        gpu_ms += ev.elapsed_ms(m[0], m[4]) / args.steps
+        gpu_ms += ev.elapsed_ms(m[0], m[-1]) / args.steps
     ev.destroy()
 
     tokens = prob.batch * prob.t_q
@@ -242,13 +245,17 @@ def main():
     stages = {
         "compress": {"ms": stage_ms["compress"], "bound": "hbm",
                      "achieved_GBps": c["compress_bytes"] / (stage_ms["compress"] * 1e-3) / 1e9},
-        "index_topk": {"ms": stage_ms["index_topk"], "bound": "hbm",
-                       "achieved_GBps": 2 * c["score_bytes"] / (stage_ms["index_topk"] * 1e-3) / 1e9,
-                       "index_TFLOPs": c["index_flops"] / (stage_ms["index_topk"] * 1e-3) / 1e12},
-        "pack_v": {"ms": stage_ms["pack_v"], "bound": "hbm",
-                   "achieved_GBps": c["pack_bytes"] / max(stage_ms["pack_v"], 1e-9) / 1e6},
+        # scores never reach HBM on the fused path: the indexer product is the bound
+        "index_topk": {"ms": stage_ms["index_topk"], "bound": "mfma",
+                       "achieved_TFLOPs": c["index_flops"] / (stage_ms["index_topk"] * 1e-3) / 1e12},
+        "pack_kv": {"ms": stage_ms["pack_kv"], "bound": "hbm",
+                    "achieved_GBps": c["pack_bytes"] / max(stage_ms["pack_kv"], 1e-9) / 1e6},
+        "attn_lists": {"ms": stage_ms["attn_lists"], "bound": "hbm",
+                       "achieved_GBps": c["sel_bytes"] / max(stage_ms["attn_lists"], 1e-9) / 1e6},
         "attention": {"ms": stage_ms["attention"], "bound": "mfma",
                       "achieved_TFLOPs": c["attention_flops"] / (stage_ms["attention"] * 1e-3) / 1e12},
+        "attn_merge": {"ms": stage_ms["attn_merge"], "bound": "hbm",
+                       "achieved_GBps": c["merge_bytes"] / max(stage_ms["attn_merge"], 1e-9) / 1e6},
     }
     for s in stages.values():
         if "achieved_TFLOPs" in s:
@@ -257,19 +264,24 @@ def main():
             s["frac"] = s["achieved_GBps"] * 1e9 / PEAK_HBM_BYTES
     dominant = max(STAGES, key=lambda s: stage_ms[s])
     if dominant == "attention":
+        # the library takes the range-split kernels for bf16, 8 heads per group, B a multiple of 8
+        split = w.dtype == "bf16" and w.heads == 8 and w.block % 8 == 0
+        kname = f"attend_range_kernel<{w.head_dim}>" if split else f"attend_mfma_h8_kernel<{w.head_dim}>"
         ach = c["attention_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
-        roof = {"kernel": "attend_mfma_h8_kernel", "bound": "mfma", "achieved": ach,
+        roof = {"kernel": kname, "bound": "mfma", "achieved": ach,
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_BF16_FLOPS,
-                "traffic": load_traffic("attend", w.name),
+                "traffic": load_traffic("attend_range" if split else "attend_mfma", w.name),
+                "launch_ms": stage_ms["attention"],
                 "work_per_launch": f"{c['attention_flops']:.4e} FLOP = 4*d*h per attended "
                                    f"(query, group, token) x {c['attended']:.4e}"}
     else:
         ms = stage_ms[dominant]
-        byts = {"index_topk": 2 * c["score_bytes"], "compress": c["compress_bytes"],
-                "pack_v": c["pack_bytes"]}[dominant]
+        byts = {"index_topk": c["sel_bytes"], "compress": c["compress_bytes"],
+                "pack_kv": c["pack_bytes"], "attn_lists": c["sel_bytes"],
+                "attn_merge": c["merge_bytes"]}[dominant]
         ach = byts / (ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_BYTES / 1e9,
-                "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM_BYTES,
+                "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM_BYTES, "launch_ms": ms,
                 "traffic": load_traffic(dominant, w.name), "work_per_launch": f"{byts:.4e} B"}
 
     cpu, parity = (None, None)

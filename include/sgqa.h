@@ -171,12 +171,14 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
  *            to disarm.  The handles are copied; the array may be freed after the call.
  * While armed, every sgqa_forward call on the calling thread records, on its stream,
  *   events[0] before the first kernel, events[1] after block compression, events[2] after the
- *   indexer and top-k of every query chunk, events[3] after the V packing, events[4] after the
- *   attention kernel,
+ *   indexer and top-k of every query chunk, events[3] after the K/V packing, events[4] once the
+ *   attention work lists are built (the pair-union lists of the range-split path; right after
+ *   events[3] when there are none), events[5] after the main attention kernel and events[6]
+ *   after the merge of range partials (right after events[5] when there is none),
  * so that hipEventElapsedTime between consecutive markers is the duration of that stage.  Arming
  * costs nothing on the device; recording failures make sgqa_forward return SGQA_ERR_HIP.
  */
-#define SGQA_STAGE_EVENTS 5
+#define SGQA_STAGE_EVENTS 7
 sgqa_status sgqa_set_stage_events(void* const* events);
 
 #ifdef __cplusplus

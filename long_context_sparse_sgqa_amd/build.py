@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsgqa.so")
 
-SOURCES = ["sgqa_api.cpp", "compress.hip", "index.hip", "topk.hip", "select_fused.hip", "attend.hip"]
+SOURCES = ["sgqa_api.cpp", "compress.hip", "index.hip", "topk.hip", "select_fused.hip", "attend.hip", "attend_split.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -25,6 +25,7 @@
 // sequential online softmax over the attended tokens in fp32.
 #include "device_common.h"
 #include "sgqa_internal.h"
+#include "units.h"
 
 namespace sgqa {
 namespace {
@@ -66,116 +67,23 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const T* __restrict__ v, T*
   }
 }
 
-// ------------------------------------------------------------------------------------------------
-// Unit lists.  An entry is unit | (mask << 24): unit u covers tokens 8u .. 8u+7, mask bit e says
-// token 8u+e belongs to a selected block.
-// ------------------------------------------------------------------------------------------------
-__device__ __forceinline__ int lane_lt_count(uint64_t bal, int lane) {
-  return __popcll(bal & ((1ull << lane) - 1ull));
-}
-
-// Expands one token's selection (NS entries; entries outside [0, o] are ignored) into its sorted
-// unit list; returns the entry count.  B is a multiple of 8 or divides 8.
-__device__ int build_units(const int32_t* __restrict__ selrow, int NS, int B, int64_t o,
-                           uint32_t* list, int lane) {
-  int running = 0;
-  if (B >= 8) {
-    const int U = B >> 3;
-    for (int base = 0; base < NS; base += 64) {
-      const int e = base + lane;
-      const int blk = (e < NS) ? selrow[e] : -1;
-      const bool valid = blk >= 0 && blk <= o;
-      const uint64_t bal = __ballot(valid);
-      if (valid) {
-        const int pos = running + U * lane_lt_count(bal, lane);
-        for (int u = 0; u < U; ++u) list[pos + u] = static_cast<uint32_t>(blk * U + u) | (0xffu << 24);
-      }
-      running += U * __popcll(bal);
-    }
-  } else {
-    const uint32_t bmask = (1u << B) - 1u;
-    for (int base = 0; base < NS; base += 64) {
-      const int e = base + lane;
-      const int blk = (e < NS) ? selrow[e] : -1;
-      const bool valid = blk >= 0 && blk <= o;
-      const int unit = (blk * B) >> 3;
-      bool head = false;
-      uint32_t mask = 0u;
-      if (valid) {
-        const int prev = (e > 0) ? selrow[e - 1] : -1;
-        const bool prev_valid = prev >= 0 && prev <= o;
-        head = !(prev_valid && ((prev * B) >> 3) == unit);
-        if (head) {
-          mask = bmask << ((blk * B) & 7);
-          for (int k2 = 1; k2 < 8 && e + k2 < NS; ++k2) {
-            const int nb2 = selrow[e + k2];
-            if (!(nb2 >= 0 && nb2 <= o) || ((nb2 * B) >> 3) != unit) break;
-            mask |= bmask << ((nb2 * B) & 7);
-          }
-        }
-      }
-      const uint64_t bal = __ballot(head);
-      if (head) list[running + lane_lt_count(bal, lane)] = static_cast<uint32_t>(unit) | (mask << 24);
-      running += __popcll(bal);
-    }
+// K packing in MFMA operand order: kp[b, g, u, kc, h, lg, r, e] = k[b, g, 8u + 4h + r, 32kc + 8lg + e]
+// (zero past Tk).  A 16-lane group reading one unit's rows 4h..4h+3, d 32kc..32kc+31 then reads 256
+// contiguous bytes, and a wavefront 4 such runs: the coalesced pattern, unlike 16 rows x 64 bytes.
+__global__ void __launch_bounds__(256) pack_k_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ kp,
+                                                     int64_t Tk, int64_t NU, int D, int64_t total) {
+  // one thread per 16-byte piece: pieces per unit = D (8 rows x D bf16 / 8)
+  for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int q = static_cast<int>(id % D);            // piece within the unit, in packed order
+    const int64_t u = (id / D) % NU;
+    const int64_t bg = id / (static_cast<int64_t>(D) * NU);
+    const int r = q & 3, lg = (q >> 2) & 3, h = (q >> 4) & 1, kc = q >> 5;
+    const int64_t t = u * 8 + 4 * h + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t < Tk) v = *reinterpret_cast<const uint4*>(k + (bg * Tk + t) * D + 32 * kc + 8 * lg);
+    *reinterpret_cast<uint4*>(kp + (bg * NU + u) * D * 8 + static_cast<int64_t>(q) * 8) = v;
   }
-  return running;
-}
-
-// Number of entries of a sorted unit list whose unit is <= last_unit.
-__device__ int count_units_upto(const uint32_t* list, int n, int64_t last_unit, int lane) {
-  int cnt = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int e = base + lane;
-    const bool keep = e < n && static_cast<int64_t>(list[e] & 0xffffffu) <= last_unit;
-    cnt += __popcll(__ballot(keep));
-  }
-  return cnt;
-}
-
-__device__ __forceinline__ int lower_bound_units(const uint32_t* list, int n, uint32_t unit) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((list[mid] & 0xffffffu) < unit) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-// Union of the two sorted unit lists: uunit[] ascending, umask[] = maskA | maskB << 8.
-__device__ int merge_units(const uint32_t* la, int na, const uint32_t* lb, int nb, int32_t* uunit,
-                           uint32_t* umask, int lane) {
-  int dups = 0;
-  for (int base = 0; base < na; base += 64) {
-    const int i = base + lane;
-    const uint32_t ea = (i < na) ? la[i] : 0u;
-    const uint32_t ua = ea & 0xffffffu;
-    const int x = (i < na) ? lower_bound_units(lb, nb, ua) : 0;
-    const bool eq = (i < na) && x < nb && (lb[x] & 0xffffffu) == ua;
-    const uint64_t bal = __ballot(eq);
-    if (i < na) {
-      const int pos = i + x - (dups + lane_lt_count(bal, lane));
-      uunit[pos] = static_cast<int32_t>(ua);
-      umask[pos] = (ea >> 24) | (eq ? ((lb[x] >> 24) << 8) : 0u);
-    }
-    dups += __popcll(bal);
-  }
-  int dups_b = 0;
-  for (int base = 0; base < nb; base += 64) {
-    const int j = base + lane;
-    const uint32_t eb = (j < nb) ? lb[j] : 0u;
-    const uint32_t ub = eb & 0xffffffu;
-    const int x = (j < nb) ? lower_bound_units(la, na, ub) : 0;
-    const bool eq = (j < nb) && x < na && (la[x] & 0xffffffu) == ub;
-    const uint64_t bal = __ballot(eq);
-    if (j < nb && !eq) {
-      const int pos = j + x - (dups_b + lane_lt_count(bal, lane));
-      uunit[pos] = static_cast<int32_t>(ub);
-      umask[pos] = (eb >> 24) << 8;
-    }
-    dups_b += __popcll(bal);
-  }
-  return na + nb - dups;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -183,7 +91,7 @@ __device__ int merge_units(const uint32_t* la, int na, const uint32_t* lb, int n
 // ------------------------------------------------------------------------------------------------
 struct MfmaArgs {
   const bf16_t* q;
-  const bf16_t* k;
+  const bf16_t* kp;
   const bf16_t* vp;
   const bf16_t* gate;
   const int32_t* sel;
@@ -246,7 +154,7 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
     qf[kc] = rowvalid ? load_bf16x8(qrow + 32 * kc + 8 * lg) : zero_bf16x8();
 
   // buffer resources of this (sequence, group): 32-bit offsets, out-of-range reads return 0
-  const BufRsrc krs = make_rsrc(a.k + (b * a.G + g) * a.Tk * D, a.Tk * D * 2);
+  const BufRsrc krs = make_rsrc(a.kp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
 
   f32x4_t acc[D / 16];
@@ -256,18 +164,17 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
   const float ninf = -__builtin_inff();
 
   // K rows of a chunk for this lane: unit slot lr/4, tokens (lr%4) and (lr%4)+4 of that unit
-  auto k_offset = [&](int c0) -> int {
+  auto k_unit = [&](int c0) -> int {
     const int e = c0 + (lr >> 2);
-    const int u = (e < nu) ? uunit[e] : 0;
-    return ((u * 8 + (lr & 3)) * D + 8 * lg) * 2;
+    return (e < nu) ? uunit[e] : 0;
   };
   bf16x8_t k1[D / 32], k2[D / 32];
   if (nu > 0) {
-    const int ko = k_offset(0);
+    const int u = k_unit(0);
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
-      k1[kc] = buffer_load_bf16x8(krs, ko + kc * 64);
-      k2[kc] = buffer_load_bf16x8(krs, ko + 4 * D * 2 + kc * 64);
+      k1[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 0, lg, lr));
+      k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
     }
   }
 
@@ -293,11 +200,11 @@ __global__ void __launch_bounds__(256) attend_mfma_h8_kernel(MfmaArgs a) {
       s2 = mfma16x16x32(k2[kc], qf[kc], s2);
     }
     if (c0 + 4 < nu) {                             // prefetch the next chunk's K rows
-      const int ko = k_offset(c0 + 4);
+      const int u = k_unit(c0 + 4);
 #pragma unroll
       for (int kc = 0; kc < D / 32; ++kc) {
-        k1[kc] = buffer_load_bf16x8(krs, ko + kc * 64);
-        k2[kc] = buffer_load_bf16x8(krs, ko + 4 * D * 2 + kc * 64);
+        k1[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 0, lg, lr));
+        k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
       }
     }
 
@@ -436,30 +343,65 @@ int64_t units_per_query(const Dims& d) {
   return u < cap ? u : cap;
 }
 
-size_t attend_packed_v_bytes(const Dims& d) {
-  if (!attend_uses_mfma(d)) return 0;
-  return static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
+// Packed K then packed V, each [Bt, G, NU, 8 x D] bf16, on the matrix-core paths.
+size_t attend_packed_kv_bytes(const Dims& d) {
+  if (!attend_uses_mfma(d) && !attend_split_supported(d)) return 0;
+  const size_t one = static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
+  return 2 * ((one + 255) / 256 * 256);
 }
 
-hipError_t launch_pack_v(const Dims& d, const void* v, void* packed_v, hipStream_t s) {
-  if (!attend_uses_mfma(d)) return hipSuccess;
+size_t attend_workspace_bytes(const Dims& d) {
+  const size_t pkv = attend_packed_kv_bytes(d);
+  return pkv + (attend_split_supported(d) ? attend_split_bytes(d) : 0);
+}
+
+hipError_t launch_pack_kv(const Dims& d, const void* k, const void* v, void* packed, hipStream_t s) {
+  if (attend_packed_kv_bytes(d) == 0) return hipSuccess;
   const int64_t total = d.Bt * d.G * d.NU * d.D;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  bf16_t* kp = static_cast<bf16_t*>(packed);
+  bf16_t* vp = kp + attend_packed_kv_bytes(d) / 2 / sizeof(bf16_t);
+  hipLaunchKernelGGL(pack_k_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(k), kp, d.Tk, d.NU, d.D, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(v), static_cast<bf16_t*>(packed_v), d.Tk, d.NU, d.D,
-                     total);
+                     static_cast<const bf16_t*>(v), vp, d.Tk, d.NU, d.D, total);
   return hipGetLastError();
 }
 
+hipError_t launch_attend_single(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* gate, const int32_t* sel, void* out, const bf16_t* kp,
+                                const bf16_t* vp, hipStream_t s);
+
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
-                                const void* gate, const int32_t* sel, void* out,
-                                const void* packed_v, hipStream_t s) {
+                                const void* gate, const int32_t* sel, void* out, void* workspace,
+                                hipStream_t s, StageMark mark) {
+  const bf16_t* kp = static_cast<const bf16_t*>(workspace);
+  const bf16_t* vp = kp + attend_packed_kv_bytes(d) / 2 / sizeof(bf16_t);
+  if (attend_split_supported(d)) {
+    char* rest = static_cast<char*>(workspace) + attend_packed_kv_bytes(d);
+    return launch_attend_split(d, q, kp, gate, sel, out, vp, rest, s, mark);
+  }
+  if (mark) {
+    const hipError_t e = mark(4, s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch_attend_single(d, q, k, v, gate, sel, out, kp, vp, s);
+  if (e != hipSuccess || !mark) return e;
+  return mark(5, s);
+}
+
+// One attention kernel for the whole problem: matrix-core pair kernel or the plain kernel.
+hipError_t launch_attend_single(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* gate, const int32_t* sel, void* out, const bf16_t* kp,
+                                const bf16_t* vp, hipStream_t s) {
   if (attend_uses_mfma(d)) {
     MfmaArgs a;
     a.q = static_cast<const bf16_t*>(q);
-    a.k = static_cast<const bf16_t*>(k);
-    a.vp = static_cast<const bf16_t*>(packed_v);
+    a.kp = kp;
+    a.vp = vp;
     a.gate = static_cast<const bf16_t*>(gate);
     a.sel = sel;
     a.out = static_cast<bf16_t*>(out);
@@ -519,11 +461,11 @@ hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, con
 }
 
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* gate, const int32_t* sel, void* out, void* packed_v,
+                         const void* gate, const int32_t* sel, void* out, void* workspace,
                          hipStream_t s) {
-  hipError_t e = launch_pack_v(d, v, packed_v, s);
+  hipError_t e = launch_pack_kv(d, k, v, workspace, s);
   if (e != hipSuccess) return e;
-  return launch_attend_packed(d, q, k, v, gate, sel, out, packed_v, s);
+  return launch_attend_packed(d, q, k, v, gate, sel, out, workspace, s);
 }
 
 }  // namespace sgqa

@@ -52,7 +52,7 @@ constexpr size_t kForwardChunkBudget = size_t(2) << 30;   // 2 GiB
 
 struct Derived {
   sgqa::Dims d;
-  size_t k_blk_bytes, scores_bytes, sel_bytes, packed_v_bytes;
+  size_t k_blk_bytes, scores_bytes, sel_bytes, attend_ws_bytes;
   size_t score_row_bytes;   // per query token (all groups)
 };
 
@@ -117,7 +117,7 @@ sgqa_status derive(const sgqa_problem* p, Derived* out) {
   out->sel_bytes = static_cast<size_t>(x);
   if (!mul_ok(d.Bt * d.G, d.NU, &x) || !mul_ok(x, 8 * d.D, &x))
     return fail(SGQA_ERR_SHAPE, "k/v size overflows");
-  out->packed_v_bytes = sgqa::attend_packed_v_bytes(d);
+  out->attend_ws_bytes = sgqa::attend_workspace_bytes(d);
   out->score_row_bytes = static_cast<size_t>(d.G) * static_cast<size_t>(d.NB) * 4;
   return SGQA_OK;
 }
@@ -128,8 +128,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Forward workspace layout.
-//   fused path : [packed v][internal sel][fail count][fallback scratch][cand][cnt][fail list]
-//   split path : [packed v][internal sel][scores]
+//   fused path : [attention workspace][internal sel][fail count][fallback scratch][cand][cnt][fail list]
+//   split path : [attention workspace][internal sel][scores]
 // where the last group is sized per query token and repeats for `chunk_tok` tokens.
 struct ForwardLayout {
   bool fused;
@@ -143,7 +143,7 @@ ForwardLayout forward_layout(const Derived& dv) {
   ForwardLayout L{};
   const sgqa::Dims& d = dv.d;
   L.fused = sgqa::fused_select_supported(d);
-  size_t off = align_up(dv.packed_v_bytes);
+  size_t off = align_up(dv.attend_ws_bytes);
   L.off_sel = off;
   off += align_up(dv.sel_bytes);
   if (L.fused) {
@@ -201,6 +201,11 @@ sgqa_status mark_stage(int i, hipStream_t s) {
   hipError_t e = hipEventRecord(g_stage_events[i], s);
   if (e != hipSuccess) return hip_fail(e, "stage marker");
   return SGQA_OK;
+}
+
+// The same, in the form the attention launcher calls between its kernels.
+hipError_t mark_stage_hip(int i, hipStream_t s) {
+  return g_stage_armed ? hipEventRecord(g_stage_events[i], s) : hipSuccess;
 }
 
 #define SGQA_CHECK(expr)                \
@@ -298,7 +303,7 @@ sgqa_status sgqa_sizes(const sgqa_problem* prob, sgqa_sizes_t* out) {
   out->k_blk_bytes = dv.k_blk_bytes;
   out->scores_bytes = dv.scores_bytes;
   out->sel_bytes = dv.sel_bytes;
-  out->attend_workspace_bytes = dv.packed_v_bytes;
+  out->attend_workspace_bytes = dv.attend_ws_bytes;
   out->forward_workspace_bytes = forward_default_bytes(dv);
   {
     const ForwardLayout L = forward_layout(dv);
@@ -351,11 +356,11 @@ sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, 
   SGQA_CHECK(check_ptr(gate, "gate"));
   SGQA_CHECK(check_ptr(sel, "sel"));
   SGQA_CHECK(check_ptr(out, "out"));
-  if (dv.packed_v_bytes > 0) {
+  if (dv.attend_ws_bytes > 0) {
     SGQA_CHECK(check_ptr(workspace, "workspace"));
-    if (workspace_bytes < dv.packed_v_bytes)
+    if (workspace_bytes < dv.attend_ws_bytes)
       return fail(SGQA_ERR_WORKSPACE, "attend workspace needs %zu bytes (got %zu)",
-                  dv.packed_v_bytes, workspace_bytes);
+                  dv.attend_ws_bytes, workspace_bytes);
   }
   hipError_t e = sgqa::launch_attend(dv.d, q, k, v, gate, sel, out, workspace,
                                      static_cast<hipStream_t>(stream));
@@ -389,7 +394,7 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
     return fail(SGQA_ERR_WORKSPACE, "forward workspace needs at least %zu bytes (got %zu)",
                 L.fixed + chunk_bytes(L, 1), workspace_bytes);
   char* ws = static_cast<char*>(workspace);
-  void* packed_v = dv.packed_v_bytes ? ws : nullptr;
+  void* attend_ws = dv.attend_ws_bytes ? ws : nullptr;
   int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + L.off_sel);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -401,12 +406,13 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
   SGQA_CHECK(mark_stage(1, s));
   SGQA_CHECK(select_chunked(d, L, ws, chunk_tok, q_idx, k_blk, sel, s));
   SGQA_CHECK(mark_stage(2, s));
-  hipError_t e = sgqa::launch_pack_v(d, v, packed_v, s);
-  if (e != hipSuccess) return hip_fail(e, "v packing launch");
+  hipError_t e = sgqa::launch_pack_kv(d, k, v, attend_ws, s);
+  if (e != hipSuccess) return hip_fail(e, "k/v packing launch");
   SGQA_CHECK(mark_stage(3, s));
-  e = sgqa::launch_attend_packed(d, q, k, v, gate, sel, out, packed_v, s);
+  e = sgqa::launch_attend_packed(d, q, k, v, gate, sel, out, attend_ws, s,
+                                 g_stage_armed ? mark_stage_hip : nullptr);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  SGQA_CHECK(mark_stage(4, s));
+  SGQA_CHECK(mark_stage(6, s));
   return ok();
 }
 

@@ -65,21 +65,33 @@ hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* 
                                   float* scratch, int32_t* sel, const Chunk& c, hipStream_t s);
 
 // ---- step 4: attention ------------------------------------------------------------------------
-// Bytes of the unit-packed V copy the matrix-core attention kernel reads (0 when the problem is
-// served by the plain kernel, which reads v directly).
-size_t attend_packed_v_bytes(const Dims& d);
+// Bytes of the unit-packed K and V copies the matrix-core attention kernels read (0 when the
+// problem is served by the plain kernel, which reads k and v directly).
+size_t attend_packed_kv_bytes(const Dims& d);
 // True when the problem takes the matrix-core path.
 bool attend_uses_mfma(const Dims& d);
 // Largest number of 8-token units one (query, group) selection can cover.
 int64_t units_per_query(const Dims& d);
-// V packing (matrix-core path only; no-op otherwise), then the attention kernel.
-hipError_t launch_pack_v(const Dims& d, const void* v, void* packed_v, hipStream_t s);
+// Range-split attention (bf16, 8 heads, B a multiple of 8): pair-union lists and range partials.
+bool attend_split_supported(const Dims& d);
+size_t attend_split_bytes(const Dims& d);
+// Total attention workspace: packed K and V, then (range-split path) lists and partials.
+size_t attend_workspace_bytes(const Dims& d);
+// K and V packing (matrix-core paths only; no-op otherwise), then the attention kernel(s).
+hipError_t launch_pack_kv(const Dims& d, const void* k, const void* v, void* workspace,
+                          hipStream_t s);
+// Optional profiling marker: called with index 4 once the attention inputs are ready (pair-union
+// lists built on the range-split path) and 5 after the main attention kernel.
+using StageMark = hipError_t (*)(int index, hipStream_t s);
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
-                                const void* gate, const int32_t* sel, void* out,
-                                const void* packed_v, hipStream_t s);
+                                const void* gate, const int32_t* sel, void* out, void* workspace,
+                                hipStream_t s, StageMark mark = nullptr);
+hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
+                               const void* gate, const int32_t* sel, void* out,
+                               const void* packed_v, void* ws, hipStream_t s, StageMark mark);
 // Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
-                         const void* gate, const int32_t* sel, void* out, void* packed_v,
+                         const void* gate, const int32_t* sel, void* out, void* workspace,
                          hipStream_t s);
 
 }  // namespace sgqa

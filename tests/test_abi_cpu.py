@@ -53,7 +53,7 @@ def test_sizes_headline_workload():
     assert s["k_blk_bytes"] == 16384 * 128 * 2
     assert s["scores_bytes"] == 131072 * 8 * 16384 * 4
     assert s["sel_bytes"] == 131072 * 8 * 512 * 4
-    assert s["attend_workspace_bytes"] == 8 * 16384 * 8 * 128 * 2       # unit-packed V
+    assert s["attend_workspace_bytes"] >= 2 * 8 * 16384 * 8 * 128 * 2   # unit-packed K and V
     assert s["forward_workspace_bytes"] > s["forward_workspace_min_bytes"] > s["attend_workspace_bytes"]
     # the fused selection never stores full score rows: a 2 GiB chunk budget, not 68 GB
     assert s["forward_workspace_bytes"] < s["attend_workspace_bytes"] + s["sel_bytes"] + (3 << 30)
