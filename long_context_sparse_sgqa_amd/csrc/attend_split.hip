@@ -22,23 +22,36 @@
 #include "sgqa_internal.h"
 #include "units.h"
 
+#include <type_traits>
+
 namespace sgqa {
 namespace {
 
 constexpr int kRanges = 4;                      // unit ranges per query
 constexpr int kRangeWaves = 4;                  // pairs per workgroup (one per wave)
 constexpr uint32_t kUnitMask = 0x3fffffffu;
+// Entries of one pair's list: the union (at most 2 umax) with every range padded to a multiple of 4
+// entries, plus 20 entries the range kernel may read (and discard) past the end of the last chunk.
+__host__ __device__ constexpr int64_t list_stride(int umax) {
+  return (2 * static_cast<int64_t>(umax) + 4 * kRanges + 20 + 3) / 4 * 4;
+}
 
 // ------------------------------------------------------------------------------------------------
 // pair unions
 // ------------------------------------------------------------------------------------------------
 struct UnionArgs {
   const int32_t* sel;
-  uint32_t* ulist;         // [Bt * G * pairs][2 * umax]
-  int32_t* ucount;         // [Bt * G * pairs]
+  uint32_t* ulist;         // [Bt * G * pairs][list_stride(umax)]
+  int32_t* bounds;         // [Bt * G * pairs][kRanges + 1]: first entry of each range, then end
   int64_t Tq, pos0, pairs, total;
   int G, NS, B, umax;
 };
+
+// Unit ranges of a pair: range r covers units [r * u_end / R, (r + 1) * u_end / R) of the pair's
+// causal unit axis [0, u_end), u_end = last token's own unit + 1.
+__device__ __forceinline__ uint32_t range_start(int r, int64_t u_end) {
+  return static_cast<uint32_t>((r * u_end) / kRanges);
+}
 
 __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t lds[];
@@ -71,13 +84,52 @@ __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
   const int nu = merge_units(listA, na, listB, nb, uunit, umask, lane);
   __syncthreads();
   if (!active) return;
-  uint32_t* out = a.ulist + gp * 2 * a.umax;
+  // entries below each range's first unit; every lane ends with the totals
+  const int64_t tokA = 2 * pair;
+  const int64_t u_end = ((a.pos0 + tokA + (tokA + 1 < a.Tq ? 1 : 0)) >> 3) + 1;
+  int below[kRanges + 1];
+  below[0] = 0;
+  below[kRanges] = nu;
+#pragma unroll
+  for (int r = 1; r < kRanges; ++r) below[r] = 0;
   for (int e = lane; e < nu; e += 64) {
-    const uint32_t m = umask[e];
-    out[e] = static_cast<uint32_t>(uunit[e]) | ((m & 0xffu) ? (1u << 30) : 0u) |
-             ((m >> 8) ? (1u << 31) : 0u);
+    const uint32_t u = static_cast<uint32_t>(uunit[e]);
+#pragma unroll
+    for (int r = 1; r < kRanges; ++r) below[r] += u < range_start(r, u_end) ? 1 : 0;
   }
-  if (lane == 0) a.ucount[gp] = nu;
+#pragma unroll
+  for (int r = 1; r < kRanges; ++r) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) below[r] += __shfl_xor(below[r], m, 64);
+  }
+  // padded layout: range r starts at start[r], a multiple of 4, and is zero-filled to start[r + 1]
+  int start[kRanges + 1];
+  start[0] = 0;
+#pragma unroll
+  for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
+  uint32_t* out = a.ulist + gp * list_stride(a.umax);
+  for (int e = lane; e < nu; e += 64) {
+    int r = 0;
+#pragma unroll
+    for (int q = 1; q < kRanges; ++q) r += e >= below[q] ? 1 : 0;
+    int shift = 0;
+#pragma unroll
+    for (int q = 0; q < kRanges; ++q) shift = q == r ? start[q] - below[q] : shift;
+    const uint32_t m = umask[e];
+    out[e + shift] = static_cast<uint32_t>(uunit[e]) | ((m & 0xffu) ? (1u << 30) : 0u) |
+                     ((m >> 8) ? (1u << 31) : 0u);
+  }
+  if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by neither)
+    const int r = lane >> 2, j = start[r] + (below[r + 1] - below[r]) + (lane & 3);
+    if (j < start[r + 1]) out[j] = 0u;
+  }
+  int32_t* bnd = a.bounds + gp * (kRanges + 1);
+  if (lane <= kRanges) {
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q <= kRanges; ++q) v = q == lane ? start[q] : v;
+    bnd[lane] = v;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -88,7 +140,7 @@ struct RangeArgs {
   const bf16_t* kp;
   const bf16_t* vp;
   const uint32_t* ulist;
-  const int32_t* ucount;
+  const int32_t* bounds;
   float* part_o;           // [gp][R][16 rows][D]
   float2* part_ml;         // [gp][R][16 rows]  (running max in the exp2 domain, sum)
   int64_t Tq, Tk, NU, pos0, pairs, pair_groups;
@@ -96,20 +148,63 @@ struct RangeArgs {
   float scale_log2e;
 };
 
-// first index of the ascending list whose unit is >= unit (wave-uniform)
-__device__ __forceinline__ int list_lower_bound(const uint32_t* list, int n, uint32_t unit) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((list[mid] & kUnitMask) < unit) lo = mid + 1; else hi = mid;
+// s_waitcnt vmcnt(N): returns once at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// N consecutive 16-byte LDS reads at a 256-byte stride, waited for inside the same asm block.
+// Written as asm so the compiler, which cannot tell which LDS buffer a direct-to-LDS load writes,
+// does not make every LDS read wait for all such loads; the caller orders them with vmcnt instead.
+template <int N>
+__device__ __forceinline__ void lds_read_stride256(const unsigned char* p, bf16x8_t* out) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const uint32_t addr = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)(p)));
+  u32x4v r[8];
+  if constexpr (N == 8) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:256\n\t"
+        "ds_read_b128 %2, %8 offset:512\n\t"
+        "ds_read_b128 %3, %8 offset:768\n\t"
+        "ds_read_b128 %4, %8 offset:1024\n\t"
+        "ds_read_b128 %5, %8 offset:1280\n\t"
+        "ds_read_b128 %6, %8 offset:1536\n\t"
+        "ds_read_b128 %7, %8 offset:1792\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr)
+        : "memory");
+  } else {
+    static_assert(N == 4, "4 or 8 reads");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:256\n\t"
+        "ds_read_b128 %2, %4 offset:512\n\t"
+        "ds_read_b128 %3, %4 offset:768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(addr)
+        : "memory");
   }
-  return lo;
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = __builtin_bit_cast(bf16x8_t, r[i]);
 }
 
 template <int D>
 __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   constexpr int H = 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kUnitBytes = 8 * D * 2;                // one unit of packed V (8 tokens x D bf16)
+  constexpr int kVLoadsPerUnit = kUnitBytes / 1024;
+  constexpr int kVLoads = 4 * kVLoadsPerUnit;          // direct-to-LDS loads per chunk
+  constexpr int kVBuf = 4 * kUnitBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[kRangeWaves][2][kVBuf];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lr = lane & 15, lg = lane >> 4;
   const int X = lr >> 3, head = lr & 7;
   // workgroup id: range fastest, so the range decides the XCD
@@ -127,14 +222,10 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   const bool rowvalid = X ? validB : true;
   const int64_t pX = a.pos0 + tokA + X;
 
-  const uint32_t* list = a.ulist + gp * 2 * a.umax;
-  const int nu = a.ucount[gp];
-  // this range's share of the pair's causal unit axis [0, u_end)
-  const int64_t u_end = ((a.pos0 + tokA + (validB ? 1 : 0)) >> 3) + 1;
-  const uint32_t lo = static_cast<uint32_t>((r * u_end) / kRanges);
-  const uint32_t hi = static_cast<uint32_t>(((r + 1) * u_end) / kRanges);
-  const int e0 = list_lower_bound(list, nu, lo);
-  const int e1 = list_lower_bound(list, nu, hi);
+  const uint32_t* list = a.ulist + gp * list_stride(a.umax);
+  const int32_t* bnd = a.bounds + gp * (kRanges + 1);
+  const int e0 = __builtin_amdgcn_readfirstlane(bnd[r]);
+  const int e1 = __builtin_amdgcn_readfirstlane(bnd[r + 1]);
 
   bf16x8_t qf[D / 32];
   const bf16_t* qrow = a.q + (((b * a.Tq + (rowvalid ? tokA + X : tokA)) * a.G + g) * H + head) * D;
@@ -145,16 +236,44 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   const BufRsrc krs = make_rsrc(a.kp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
 
-  // K operands of the chunk at c: unit slot lr/4 of the chunk, rows lr%4 and lr%4 + 4
-  bf16x8_t k1[D / 32], k2[D / 32];
-  auto load_k = [&](int c) {
-    const int e = c + (lr >> 2);
-    const int u = (e < e1) ? static_cast<int>(list[e] & kUnitMask) : 0;
+  // List entries are read with scalar loads (constant address space, wave-uniform, 16-byte aligned
+  // because ranges start at multiples of 4): they count against lgkmcnt, so reading them never
+  // waits behind the K/V loads in flight.  Entries at or past e1 read as 0 (unit 0, not chosen).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
+  auto chunk_entries = [&](int c, uint32_t* ent4) {
+    const u32x4 v = *((ConstQuadPtr)(list + c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ent4[j] = c < e1 ? v[j] : 0u;
+  };
+  auto pick4 = [](const uint32_t* v, int i) -> uint32_t {
+    return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+  };
+
+  // K operands of a chunk (4 units) go to registers: unit slot lr/4, rows lr%4 and lr%4 + 4.
+  struct KRegs { bf16x8_t k1[D / 32], k2[D / 32]; };
+  auto load_k = [&](const uint32_t* ent4, KRegs& R) {
+    const int u = static_cast<int>(pick4(ent4, lr >> 2) & kUnitMask);
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
-      k1[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 0, lg, lr));
-      k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
+      R.k1[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 0, lg, lr));
+      R.k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
     }
+  };
+  // V of a chunk goes to this wave's LDS ring by direct-to-LDS loads: each load moves 1 KiB, a
+  // contiguous piece of one unit (unit-packed V keeps a unit's 8 x D values together).
+  unsigned char* const vring = &s_v[wave][0][0];
+  auto stage_v = [&](const uint32_t* ent4, int buf) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < kVLoads; ++j) {
+      const uint32_t u = ent4[j / kVLoadsPerUnit] & kUnitMask;
+      const int off = static_cast<int>(u) * kUnitBytes + (j % kVLoadsPerUnit) * 1024 + lane * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(vring + buf * kVBuf + j * 1024), 16, off,
+          0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
   };
 
   f32x4_t acc[D / 16];
@@ -163,27 +282,22 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   float m_run = -1e30f, l_run = 0.f;
   const float ninf = -__builtin_inff();
 
-  if (e0 < e1) load_k(e0);
-  for (int c = e0; c < e1; c += 4) {
-    const int eS = c + lg;
-    const uint32_t ent = (eS < e1) ? list[eS] : 0u;
+  // one chunk: S^T = K Q^T (tokens 0-3 of each unit slot in s1, 4-7 in s2), masks, online softmax,
+  // then O^T += V^T P^T once V of the chunk is in LDS (vmcnt at most `after` loads outstanding)
+  auto chunk = [&](const KRegs& K, const uint32_t* ent4, int buf, auto after_tag, auto issue_k) {
+    const uint32_t ent = pick4(ent4, lg);
     const int unitS = static_cast<int>(ent & kUnitMask);
-    // V^T operand rows of this chunk: coalesced 256-byte runs, in flight during S and softmax
-    bf16x8_t vf[D / 16];
-    const int vo = (unitS * D + lr) * 16;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) vf[t] = buffer_load_bf16x8(vrs, vo + t * 256);
-
-    // S^T = K Q^T: unit slot lr/4, tokens 0-3 (s1) and 4-7 (s2) of each unit
     f32x4_t s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t s2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
-      s1 = mfma16x16x32(k1[kc], qf[kc], s1);
-      s2 = mfma16x16x32(k2[kc], qf[kc], s2);
+      s1 = mfma16x16x32(K.k1[kc], qf[kc], s1);
+      s2 = mfma16x16x32(K.k2[kc], qf[kc], s2);
     }
-    if (c + 4 < e1) load_k(c + 4);                     // prefetch the next chunk's K operands
-    const bool chose = (eS < e1) && (X ? (ent >> 31) : ((ent >> 30) & 1u));
+    asm volatile("" ::: "memory");
+    issue_k();                                         // K two chunks ahead, into the freed set
+    asm volatile("" ::: "memory");
+    const bool chose = X ? (ent >> 31) : ((ent >> 30) & 1u);     // 0 past the range (ent = 0)
     const int64_t dlt = pX - static_cast<int64_t>(unitS) * 8;
     const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
     const uint32_t valid = chose ? causal : 0u;
@@ -212,8 +326,49 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
       l_run += pv[e];
     }
     const bf16x8_t pf = pack8_bf16(pv);
+    wait_vmem_le<decltype(after_tag)::value>();
+    bf16x8_t vf[D / 16];
+    lds_read_stride256<D / 16>(vring + buf * kVBuf + lg * kUnitBytes + lr * 16, vf);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) acc[t] = mfma16x16x32(vf[t], pf, acc[t]);
+  };
+
+  // Pipeline over chunks of 4 units (past the range's end the loads fetch unit 0, never used):
+  // V is staged one chunk ahead into a 2-slot LDS ring, K loaded two chunks ahead into 2 register
+  // sets.  Issue order per chunk c: V(c+4), then K(c+8) after S(c) frees its set.  Loads complete
+  // in order, so V(c) has landed once at most the loads issued after it -- K(c+4), V(c+4) and
+  // K(c+8) -- are outstanding.
+  if (e0 < e1) {
+    typedef std::integral_constant<int, kVLoads + D / 16 + D / 16> After;
+    uint32_t ent[4][4];                                // entries of chunks c, c+4, c+8, c+12
+    chunk_entries(e0, ent[0]);
+    chunk_entries(e0 + 4, ent[1]);
+    chunk_entries(e0 + 8, ent[2]);
+    KRegs kA, kB;
+    // same issue order as the steady state (K(c), V(c), K(c+4)), so the waits match it
+    load_k(ent[0], kA);
+    stage_v(ent[0], 0);
+    asm volatile("" ::: "memory");
+    load_k(ent[1], kB);
+    for (int c = e0; c < e1; c += 8) {
+      // chunk c: K in kA, V in slot 0
+      chunk_entries(c + 12, ent[3]);
+      stage_v(ent[1], 1);
+      chunk(kA, ent[0], 0, After{}, [&] { load_k(ent[2], kA); });
+      if (c + 4 >= e1) break;
+      // chunk c+4: K in kB, V in slot 1
+      chunk_entries(c + 16, ent[0]);
+      stage_v(ent[2], 0);
+      chunk(kB, ent[1], 1, After{}, [&] { load_k(ent[3], kB); });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t t0 = ent[0][j];
+        ent[0][j] = ent[2][j];
+        ent[1][j] = ent[3][j];
+        ent[2][j] = t0;
+      }
+    }
+    wait_vmem_le<0>();          // no direct-to-LDS load may still be writing when the wave ends
   }
 
   // partial of this range: unnormalised O, running max m and sum l per row
@@ -299,7 +454,8 @@ size_t attend_split_bytes(const Dims& d) {
   const int64_t pairs = (d.Tq + 1) / 2;
   const size_t n = static_cast<size_t>(d.Bt * d.G * pairs);
   const size_t umax = static_cast<size_t>(units_per_query(d));
-  return align256(n * 2 * umax * sizeof(uint32_t)) + align256(n * sizeof(int32_t)) +
+  return align256(n * list_stride(static_cast<int>(umax)) * sizeof(uint32_t)) +
+         align256(n * (kRanges + 1) * sizeof(int32_t)) +
          align256(n * kRanges * 16 * d.D * sizeof(float)) + align256(n * kRanges * 16 * sizeof(float2));
 }
 
@@ -311,9 +467,9 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   const int umax = static_cast<int>(units_per_query(d));
   char* p = static_cast<char*>(ws);
   uint32_t* ulist = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(total) * 2 * umax * sizeof(uint32_t));
-  int32_t* ucount = reinterpret_cast<int32_t*>(p);
-  p += align256(static_cast<size_t>(total) * sizeof(int32_t));
+  p += align256(static_cast<size_t>(total) * list_stride(umax) * sizeof(uint32_t));
+  int32_t* bounds = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<size_t>(total) * (kRanges + 1) * sizeof(int32_t));
   float* part_o = reinterpret_cast<float*>(p);
   p += align256(static_cast<size_t>(total) * kRanges * 16 * d.D * sizeof(float));
   float2* part_ml = reinterpret_cast<float2*>(p);
@@ -321,7 +477,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   UnionArgs ua;
   ua.sel = sel;
   ua.ulist = ulist;
-  ua.ucount = ucount;
+  ua.bounds = bounds;
   ua.Tq = d.Tq;
   ua.pos0 = d.pos0;
   ua.pairs = pairs;
@@ -342,7 +498,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   a.kp = static_cast<const bf16_t*>(packed_k);
   a.vp = static_cast<const bf16_t*>(packed_v);
   a.ulist = ulist;
-  a.ucount = ucount;
+  a.bounds = bounds;
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.Tq = d.Tq;
