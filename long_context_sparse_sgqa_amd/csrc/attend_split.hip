@@ -13,16 +13,17 @@
 //     selected 8-token units, entry = unit | token-A-chose << 30 | token-B-chose << 31 (B is a
 //     multiple of 8, so a unit is wholly selected by a token or not at all).
 //   attend_range_kernel  one wavefront per (pair, range), 16 rows = 2 tokens x 8 heads: the pair's
-//     entries inside the range in chunks of 4 units, exactly as attend.hip's inner loop
-//     (S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, masked online softmax in the
-//     exp2 domain), ending in an unnormalised partial (O, running max m, sum l) per row.
+//     entries inside the range in chunks of 4 units (S^T = K Q^T and O^T += V^T P^T on
+//     v_mfma_f32_16x16x32_bf16, masked online softmax in the exp2 domain), ending in an
+//     unnormalised partial (O, running max m, sum l) per row.  K and V come from the unit-packed
+//     copies, whose layout makes every 16-lane operand load one 256-byte run; K is loaded two chunks
+//     and V one chunk ahead of use, and list entries arrive by scalar loads, so each wave keeps
+//     about three chunks of operands in flight.
 //   merge_ranges_kernel  per row: rescale the R partials to their common max, sum, divide, apply
 //     sigmoid(gate), round to bf16.
 #include "device_common.h"
 #include "sgqa_internal.h"
 #include "units.h"
-
-#include <type_traits>
 
 namespace sgqa {
 namespace {
@@ -31,9 +32,9 @@ constexpr int kRanges = 4;                      // unit ranges per query
 constexpr int kRangeWaves = 4;                  // pairs per workgroup (one per wave)
 constexpr uint32_t kUnitMask = 0x3fffffffu;
 // Entries of one pair's list: the union (at most 2 umax) with every range padded to a multiple of 4
-// entries, plus 20 entries the range kernel may read (and discard) past the end of the last chunk.
+// entries, plus 16 entries the range kernel may read (and discard) past the end of the last chunk.
 __host__ __device__ constexpr int64_t list_stride(int umax) {
-  return (2 * static_cast<int64_t>(umax) + 4 * kRanges + 20 + 3) / 4 * 4;
+  return (2 * static_cast<int64_t>(umax) + 4 * kRanges + 16 + 3) / 4 * 4;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -148,61 +149,9 @@ struct RangeArgs {
   float scale_log2e;
 };
 
-// s_waitcnt vmcnt(N): returns once at most N vector-memory loads of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// N consecutive 16-byte LDS reads at a 256-byte stride, waited for inside the same asm block.
-// Written as asm so the compiler, which cannot tell which LDS buffer a direct-to-LDS load writes,
-// does not make every LDS read wait for all such loads; the caller orders them with vmcnt instead.
-template <int N>
-__device__ __forceinline__ void lds_read_stride256(const unsigned char* p, bf16x8_t* out) {
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  const uint32_t addr = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)(p)));
-  u32x4v r[8];
-  if constexpr (N == 8) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:256\n\t"
-        "ds_read_b128 %2, %8 offset:512\n\t"
-        "ds_read_b128 %3, %8 offset:768\n\t"
-        "ds_read_b128 %4, %8 offset:1024\n\t"
-        "ds_read_b128 %5, %8 offset:1280\n\t"
-        "ds_read_b128 %6, %8 offset:1536\n\t"
-        "ds_read_b128 %7, %8 offset:1792\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7])
-        : "v"(addr)
-        : "memory");
-  } else {
-    static_assert(N == 4, "4 or 8 reads");
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %4 offset:256\n\t"
-        "ds_read_b128 %2, %4 offset:512\n\t"
-        "ds_read_b128 %3, %4 offset:768\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(addr)
-        : "memory");
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) out[i] = __builtin_bit_cast(bf16x8_t, r[i]);
-}
-
 template <int D>
 __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   constexpr int H = 8;
-  constexpr int kUnitBytes = 8 * D * 2;                // one unit of packed V (8 tokens x D bf16)
-  constexpr int kVLoadsPerUnit = kUnitBytes / 1024;
-  constexpr int kVLoads = 4 * kVLoadsPerUnit;          // direct-to-LDS loads per chunk
-  constexpr int kVBuf = 4 * kUnitBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[kRangeWaves][2][kVBuf];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int lr = lane & 15, lg = lane >> 4;
@@ -260,20 +209,12 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
       R.k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
     }
   };
-  // V of a chunk goes to this wave's LDS ring by direct-to-LDS loads: each load moves 1 KiB, a
-  // contiguous piece of one unit (unit-packed V keeps a unit's 8 x D values together).
-  unsigned char* const vring = &s_v[wave][0][0];
-  auto stage_v = [&](const uint32_t* ent4, int buf) {
-    asm volatile("" ::: "memory");
+  // V^T operands of a chunk go to registers too: unit slot lg, coalesced 256-byte runs.
+  struct VRegs { bf16x8_t v[D / 16]; };
+  auto load_v = [&](const uint32_t* ent4, VRegs& R) {
+    const int vo = (static_cast<int>(pick4(ent4, lg) & kUnitMask) * D + lr) * 16;
 #pragma unroll
-    for (int j = 0; j < kVLoads; ++j) {
-      const uint32_t u = ent4[j / kVLoadsPerUnit] & kUnitMask;
-      const int off = static_cast<int>(u) * kUnitBytes + (j % kVLoadsPerUnit) * 1024 + lane * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (__attribute__((address_space(3))) void*)(vring + buf * kVBuf + j * 1024), 16, off,
-          0, 0, 0);
-    }
-    asm volatile("" ::: "memory");
+    for (int t = 0; t < D / 16; ++t) R.v[t] = buffer_load_bf16x8(vrs, vo + t * 256);
   };
 
   f32x4_t acc[D / 16];
@@ -283,8 +224,8 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   const float ninf = -__builtin_inff();
 
   // one chunk: S^T = K Q^T (tokens 0-3 of each unit slot in s1, 4-7 in s2), masks, online softmax,
-  // then O^T += V^T P^T once V of the chunk is in LDS (vmcnt at most `after` loads outstanding)
-  auto chunk = [&](const KRegs& K, const uint32_t* ent4, int buf, auto after_tag, auto issue_k) {
+  // O^T += V^T P^T.  `refill` runs once S has consumed K, to reuse its registers.
+  auto chunk = [&](const KRegs& K, const VRegs& V, const uint32_t* ent4, auto refill) {
     const uint32_t ent = pick4(ent4, lg);
     const int unitS = static_cast<int>(ent & kUnitMask);
     f32x4_t s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -294,9 +235,7 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
       s1 = mfma16x16x32(K.k1[kc], qf[kc], s1);
       s2 = mfma16x16x32(K.k2[kc], qf[kc], s2);
     }
-    asm volatile("" ::: "memory");
-    issue_k();                                         // K two chunks ahead, into the freed set
-    asm volatile("" ::: "memory");
+    refill();
     const bool chose = X ? (ent >> 31) : ((ent >> 30) & 1u);     // 0 past the range (ent = 0)
     const int64_t dlt = pX - static_cast<int64_t>(unitS) * 8;
     const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
@@ -326,49 +265,46 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
       l_run += pv[e];
     }
     const bf16x8_t pf = pack8_bf16(pv);
-    wait_vmem_le<decltype(after_tag)::value>();
-    bf16x8_t vf[D / 16];
-    lds_read_stride256<D / 16>(vring + buf * kVBuf + lg * kUnitBytes + lr * 16, vf);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) acc[t] = mfma16x16x32(vf[t], pf, acc[t]);
+    for (int t = 0; t < D / 16; ++t) acc[t] = mfma16x16x32(V.v[t], pf, acc[t]);
   };
 
-  // Pipeline over chunks of 4 units (past the range's end the loads fetch unit 0, never used):
-  // V is staged one chunk ahead into a 2-slot LDS ring, K loaded two chunks ahead into 2 register
-  // sets.  Issue order per chunk c: V(c+4), then K(c+8) after S(c) frees its set.  Loads complete
-  // in order, so V(c) has landed once at most the loads issued after it -- K(c+4), V(c+4) and
-  // K(c+8) -- are outstanding.
+  // Software pipeline over chunks of 4 units (past the range's end the loads fetch unit 0 and are
+  // masked out): K is loaded two chunks ahead and V one chunk ahead, two register sets each.  Per
+  // chunk x: V(x+4) is issued first, then K(x+8) once S(x) has freed its set; the compiler's vmcnt
+  // waits then leave up to three chunks' worth of K/V in flight.
   if (e0 < e1) {
-    typedef std::integral_constant<int, kVLoads + D / 16 + D / 16> After;
-    uint32_t ent[4][4];                                // entries of chunks c, c+4, c+8, c+12
-    chunk_entries(e0, ent[0]);
-    chunk_entries(e0 + 4, ent[1]);
-    chunk_entries(e0 + 8, ent[2]);
+    uint32_t ec[4], e1c[4], e2c[4], e3c[4];           // entries of chunks x, x+4, x+8, x+12
+    chunk_entries(e0, ec);
+    chunk_entries(e0 + 4, e1c);
+    chunk_entries(e0 + 8, e2c);
     KRegs kA, kB;
-    // same issue order as the steady state (K(c), V(c), K(c+4)), so the waits match it
-    load_k(ent[0], kA);
-    stage_v(ent[0], 0);
-    asm volatile("" ::: "memory");
-    load_k(ent[1], kB);
-    for (int c = e0; c < e1; c += 8) {
-      // chunk c: K in kA, V in slot 0
-      chunk_entries(c + 12, ent[3]);
-      stage_v(ent[1], 1);
-      chunk(kA, ent[0], 0, After{}, [&] { load_k(ent[2], kA); });
-      if (c + 4 >= e1) break;
-      // chunk c+4: K in kB, V in slot 1
-      chunk_entries(c + 16, ent[0]);
-      stage_v(ent[2], 0);
-      chunk(kB, ent[1], 1, After{}, [&] { load_k(ent[3], kB); });
+    VRegs v0, v1;
+    load_k(ec, kA);
+    load_k(e1c, kB);
+    load_v(ec, v0);
+    int nx = e0 + 12;                                  // next chunk whose entries are read
+    auto step = [&](KRegs& K, VRegs& Vcur, VRegs& Vnext) {
+      chunk_entries(nx, e3c);                          // entries a chunk ahead of their use
+      nx += 4;
+      load_v(e1c, Vnext);
+      chunk(K, Vcur, ec, [&] { load_k(e2c, K); });
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t t0 = ent[0][j];
-        ent[0][j] = ent[2][j];
-        ent[1][j] = ent[3][j];
-        ent[2][j] = t0;
+        ec[j] = e1c[j];
+        e1c[j] = e2c[j];
+        e2c[j] = e3c[j];
       }
+    };
+    // the loop body is one period of the register rotation, so every trip enters with the same
+    // loads in flight; the first chunk and the tail run outside it
+    step(kA, v0, v1);
+    int rem = (e1 - e0 - 4) >> 2;                      // chunks left
+    for (; rem >= 2; rem -= 2) {
+      step(kB, v1, v0);
+      step(kA, v0, v1);
     }
-    wait_vmem_le<0>();          // no direct-to-LDS load may still be writing when the wave ends
+    if (rem >= 1) step(kB, v1, v0);
   }
 
   // partial of this range: unnormalised O, running max m and sum l per row

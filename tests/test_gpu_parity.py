@@ -175,6 +175,12 @@ def test_decode_sampled_sequences():
     prob = sg.Problem.from_workload(w)
     out, sel = run_forward(prob, x)
     structural_check_sel(sel, prob)
+    # a small grid (2 token pairs per sequence) leaves many loads in flight per wave: repeated runs
+    # must agree bit for bit, or a pipelined kernel read an operand before it landed
+    for _ in range(2):
+        again, sel_again = run_forward(prob, x)
+        assert torch.equal(again, out) and torch.equal(sel_again, sel), "decode run-to-run"
+        del again, sel_again
     rows = [(b, i) for b in (0, 37) for i in range(w.t_q)]
     sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
     check_sel_rows(torch.stack([sel[b, i] for b, i in rows]), sel_ref)
