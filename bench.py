@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy a device buffer of this many MiB twice (a "
+                         "device-to-device blit of known size, for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -307,6 +310,15 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(rec), flush=True)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
 
 
 if __name__ == "__main__":

@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
     mx = wave_max_xor(mx, 16);
     mx = wave_max_xor(mx, 32);
     const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run)) {
+    if (__ballot(m_new > m_run + kLazyRescaleLog2)) {   // a row's max grew by > margin: rescale all
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll

@@ -79,6 +79,12 @@ __device__ __forceinline__ bf16x8_t buffer_load_bf16x8(BufRsrc r, int byte_offse
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Online softmax with a lazy running max: the accumulators are rescaled only when some row's
+// maximum (log2 domain) exceeds the max they are referenced to by more than this margin.  Until
+// then probabilities exp2(s - m) may reach 2^margin (256), far inside fp32 and bf16 range, and the
+// result is the same softmax: O, l and m stay mutually consistent whatever reference m is used.
+constexpr float kLazyRescaleLog2 = 8.0f;
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -35,6 +35,13 @@ __device__ __forceinline__ uint32_t order_key_f(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The smallest float whose order key is >= thr (thr has its low 16 bits clear): scores pass the
+// threshold exactly when score >= that float.  Keys at or below the key of -inf admit everything.
+__device__ __forceinline__ float key_threshold_to_float(uint32_t thr) {
+  if (thr <= 0x007fffffu) return -__builtin_inff();
+  return (thr & 0x80000000u) ? __uint_as_float(thr & 0x7fffffffu) : __uint_as_float(~thr);
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -156,13 +163,26 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     if (threadIdx.x < kRows) s_thr[threadIdx.x] = 0u;
   }
   __syncthreads();
-  uint32_t c_thr[4];
+  // per C row e of this lane: float threshold (NaN for rows past the tile: never passes), causal
+  // limit o as 32 bits, and the row's candidate list
+  float c_thr[4];
+  int32_t c_o32[4];
+  uint64_t* c_list[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) c_thr[e] = s_thr[wave * 16 + lg * 4 + e];
+  for (int e = 0; e < 4; ++e) {
+    c_thr[e] = c_valid[e] ? key_threshold_to_float(s_thr[wave * 16 + lg * 4 + e]) : __builtin_nanf("");
+    c_o32[e] = static_cast<int32_t>(c_o[e]);
+    c_list[e] = a.cand + c_rr[e] * a.cap;
+  }
 
   // ---------------- phase 2: every causal score, filtered, ordered appends ----------------
+  // A candidate is (float bits of the score << 32 | block); each row's list stays in ascending block
+  // order because a row's 16 columns of a step sit in one 16-lane group, ranked by lane.
   int count[4] = {0, 0, 0, 0};
   const int64_t ntiles = (o_max + kCols - 1) / kCols;
+  // tiles below every row's causal limit need no per-column check
+  const int64_t o_min = row_o(0, nullptr);
+  const int64_t full_tiles = o_min / kCols;
   // staging: 128 blocks x DI bf16 = 128 x (DI/8) 16-byte pieces over 256 threads; the next tile
   // is fetched into registers before the current one is multiplied and written to LDS after it
   constexpr int kPer = kCols * (DI / 8) / 256;
@@ -191,31 +211,44 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     store_tile(0);
   }
   __syncthreads();
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const uint64_t lane_bit = 1ull << lane;
+  const uint64_t grp_all = 0xffffull << (lg * 16);          // this lane's 16-lane group
+  const uint64_t grp_lt = grp_all & (lane_bit - 1ull);      // lanes of the group below this one
+  auto scores16 = [&](const unsigned char* src, int n) -> f32x4_t {
+    f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < DI / 32; ++kc) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src + (n * 16 + lr) * kRowBytes + kc * 64 + lg * 16);
+      c = mfma16x16x32(qa[kc], bf16x8_from_u4(u), c);
+    }
+    return c;
+  };
+  auto append = [&](const f32x4_t& c, int32_t col, bool check_causal) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool pass = c[e] >= c_thr[e];
+      if (check_causal) pass = pass && col < c_o32[e];
+      const uint64_t bal = __ballot(pass);
+      const int pos = count[e] + __popcll(bal & grp_lt);
+      if (pass && pos < a.cap)
+        c_list[e][pos] = (static_cast<uint64_t>(__float_as_uint(c[e])) << 32) | static_cast<uint32_t>(col);
+      count[e] += __popcll(bal & grp_all);
+    }
+  };
   for (int64_t t = 0; t < ntiles; ++t) {
     const int buf = static_cast<int>(t & 1);
-    if (t + 1 < ntiles) load_tile(t + 1);
     const unsigned char* src = lds + buf * kTileBytes;
-#pragma unroll 2
+    const int32_t col0 = static_cast<int32_t>(t * kCols) + lr;
+    const bool check = t >= full_tiles;
+    // the products of step n+1 are issued before the appends of step n, hiding their latency
+    f32x4_t cur = scores16(src, 0);
+    if (t + 1 < ntiles) load_tile(t + 1);
+#pragma unroll
     for (int n = 0; n < kCols / 16; ++n) {
-      const int64_t col = t * kCols + n * 16 + lr;
-      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < DI / 32; ++kc) {
-        const uint4 u = *reinterpret_cast<const uint4*>(src + (n * 16 + lr) * kRowBytes + kc * 64 + lg * 16);
-        c = mfma16x16x32(qa[kc], bf16x8_from_u4(u), c);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = order_key_f(c[e]);
-        const bool pass = c_valid[e] && col < c_o[e] && key >= c_thr[e];
-        const uint64_t bal = __ballot(pass);
-        const uint32_t grp = static_cast<uint32_t>(bal >> (lg * 16)) & 0xffffu;
-        const int pos = count[e] + __popc(static_cast<uint32_t>((bal & lt_mask) >> (lg * 16)));
-        if (pass && pos < a.cap)
-          a.cand[c_rr[e] * a.cap + pos] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(col);
-        count[e] += __popc(grp);
-      }
+      f32x4_t nxt = cur;
+      if (n + 1 < kCols / 16) nxt = scores16(src, n + 1);
+      if (check) append(cur, col0 + n * 16, true); else append(cur, col0 + n * 16, false);
+      cur = nxt;
     }
     if (t + 1 < ntiles) store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier below in t-1
     __syncthreads();
@@ -242,6 +275,21 @@ struct SelectArgs {
 
 constexpr int kSelPer = 32;        // candidates per lane held in registers (cap <= 64 * kSelPer)
 
+// The need-th largest of the wave's keys (slots >= NE are zero), searched bit by bit below `top`
+// from the common prefix tau0.
+template <int NE>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t tau0, int top, int need) {
+  uint32_t tau = tau0;
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) c += key[e] >= cand ? 1 : 0;
+    if (wave_sum(c) >= need) tau = cand;
+  }
+  return tau;
+}
+
 __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -264,20 +312,30 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   }
   const uint64_t* cr = a.cand + rr * a.cap;
   uint32_t key[kSelPer];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) {
     const int x = e * 64 + lane;
-    key[e] = x < m ? static_cast<uint32_t>(cr[x] >> 32) : 0u;
+    key[e] = 0u;
+    if (x < m) {
+      key[e] = order_key_f(__uint_as_float(static_cast<uint32_t>(cr[x] >> 32)));
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
   }
-  // tau = the need-th largest key: the largest v with #(key >= v) >= need
-  uint32_t tau = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int c = 0;
 #pragma unroll
-    for (int e = 0; e < kSelPer; ++e) c += key[e] >= cand ? 1 : 0;
-    if (wave_sum(c) >= need) tau = cand;
+  for (int o2 = 32; o2 > 0; o2 >>= 1) {
+    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o2, 64)));
+    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o2, 64)));
   }
+  // tau = the need-th largest key: the largest v with #(key >= v) >= need.  kmin <= tau <= kmax,
+  // so the bits above the highest bit where kmin and kmax differ are those of kmin.  Lists of at
+  // most 1024 candidates (the usual size) search over the first 16 register slots only.
+  const uint32_t diff = kmin ^ kmax;
+  const int top = diff ? 31 - __clz(diff) : -1;
+  const uint32_t tau0 = top >= 0 ? (kmin & ~((2u << top) - 1u)) : kmin;
+  const uint32_t tau = m <= 16 * 64 ? kth_largest<16>(key, tau0, top, need)
+                                    : kth_largest<kSelPer>(key, tau0, top, need);
   int gt = 0;
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) gt += key[e] > tau ? 1 : 0;

@@ -266,10 +266,19 @@ __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
     if (t < Di) qs[t] = bf16_to_f32(qrow[t]);
     __syncthreads();
     const bf16_t* kb = k_blk + b * NB * Di;
+    // one block row per thread, 16 bytes (8 index dims) per load
     for (int64_t j = t; j < o; j += kThreads) {
-      const bf16_t* kr = kb + j * Di;
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + j * Di);
       float acc = 0.f;
-      for (int c = 0; c < Di; ++c) acc = fmaf(qs[c], bf16_to_f32(kr[c]), acc);
+      for (int c8 = 0; c8 < Di / 8; ++c8) {
+        const uint4 u = kr[c8];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc = fmaf(qs[c8 * 8 + 2 * h], __uint_as_float(w[h] << 16), acc);
+          acc = fmaf(qs[c8 * 8 + 2 * h + 1], __uint_as_float(w[h] & 0xffff0000u), acc);
+        }
+      }
       srow[j] = acc;
     }
     __syncthreads();
