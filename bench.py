@@ -72,8 +72,8 @@ def algorithmic_counts(w):
         "sel_bytes": 4 * rows * w.n_sel,
         "attention_flops": 4 * w.head_dim * w.heads * att,
         "pack_bytes": 4 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,   # read + write K and V
-        # range partials: fp32 O and (max, sum) per row and range, read once, plus gate and out
-        "merge_bytes": rows * w.heads * (4 * (4 * w.head_dim + 8) + 2 * 2 * w.head_dim),
+        # 4 range partials per row (bf16 O, fp32 max and sum) read once, plus gate and out
+        "merge_bytes": rows * w.heads * (4 * (2 * w.head_dim + 8) + 2 * 2 * w.head_dim),
         # compulsory attention traffic: q, gate, out once, plus each group's K/V once
         "attention_min_bytes": 3 * rows * w.heads * w.head_dim * dsz
                                + 2 * w.batch * w.groups * w.t_kv * w.head_dim * dsz,

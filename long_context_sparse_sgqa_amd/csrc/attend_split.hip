@@ -11,16 +11,17 @@
 // Three kernels:
 //   pair_union_kernel  per (sequence, group, token pair): the sorted union of the two tokens'
 //     selected 8-token units, entry = unit | token-A-chose << 30 | token-B-chose << 31 (B is a
-//     multiple of 8, so a unit is wholly selected by a token or not at all).
+//     multiple of 8, so a unit is wholly selected by a token or not at all), built through LDS
+//     bitmaps; every range is padded to a multiple of 4 entries and its first entry recorded.
 //   attend_range_kernel  one wavefront per (pair, range), 16 rows = 2 tokens x 8 heads: the pair's
 //     entries inside the range in chunks of 4 units (S^T = K Q^T and O^T += V^T P^T on
-//     v_mfma_f32_16x16x32_bf16, masked online softmax in the exp2 domain), ending in an
-//     unnormalised partial (O, running max m, sum l) per row.  K and V come from the unit-packed
+//     v_mfma_f32_16x16x32_bf16, masked online softmax in the exp2 domain), ending in a partial
+//     per row: O / l rounded to bf16, and the running max m and sum l in fp32.  K and V come from the unit-packed
 //     copies, whose layout makes every 16-lane operand load one 256-byte run; K is loaded two chunks
 //     and V one chunk ahead of use, and list entries arrive by scalar loads, so each wave keeps
 //     about three chunks of operands in flight.
-//   merge_ranges_kernel  per row: rescale the R partials to their common max, sum, divide, apply
-//     sigmoid(gate), round to bf16.
+//   merge_ranges_kernel  per row: weight each partial by its sum rescaled to the common max,
+//     combine, apply sigmoid(gate), round to bf16.
 #include "device_common.h"
 #include "sgqa_internal.h"
 #include "units.h"
@@ -45,7 +46,7 @@ struct UnionArgs {
   uint32_t* ulist;         // [Bt * G * pairs][list_stride(umax)]
   int32_t* bounds;         // [Bt * G * pairs][kRanges + 1]: first entry of each range, then end
   int64_t Tq, pos0, pairs, total;
-  int G, NS, B, umax;
+  int G, NS, B, umax, words;   // words: bitmap words per token (ceil(NU / 32))
 };
 
 // Unit ranges of a pair: range r covers units [r * u_end / R, (r + 1) * u_end / R) of the pair's
@@ -54,71 +55,105 @@ __device__ __forceinline__ uint32_t range_start(int r, int64_t u_end) {
   return static_cast<uint32_t>((r * u_end) / kRanges);
 }
 
+// Union through two LDS bitmaps (one bit per unit for each token of the pair): each selected block
+// sets its units' bits (units past the token's own unit are left out: t <= p), then one scan over
+// the words emits the union in ascending unit order with both tokens' chosen bits, each range
+// padded to a multiple of 4 entries.
 __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gp = static_cast<int64_t>(blockIdx.x) * 4 + wave;   // (b * G + g) * pairs + pair
-  uint32_t* listA = lds + static_cast<size_t>(wave) * 6 * a.umax;
-  uint32_t* listB = listA + a.umax;
-  int32_t* uunit = reinterpret_cast<int32_t*>(listB + a.umax);
-  uint32_t* umask = reinterpret_cast<uint32_t*>(uunit + 2 * a.umax);
-  int na = 0, nb = 0;
-  int64_t pair = 0, bg = 0;
-  const bool active = gp < a.total;
-  if (active) {
-    pair = gp % a.pairs;
-    bg = gp / a.pairs;
-    const int64_t g = bg % a.G, b = bg / a.G;
-    const int64_t tokA = 2 * pair;
-    const int64_t pA = a.pos0 + tokA;
-    na = build_units(a.sel + ((b * a.Tq + tokA) * a.G + g) * a.NS, a.NS, a.B, pA / a.B, listA, lane);
-    if (tokA + 1 < a.Tq)
-      nb = build_units(a.sel + ((b * a.Tq + tokA + 1) * a.G + g) * a.NS, a.NS, a.B, (pA + 1) / a.B,
-                       listB, lane);
-  }
-  __syncthreads();
-  if (active) {
-    const int64_t pA = a.pos0 + 2 * pair;
-    na = count_units_upto(listA, na, pA >> 3, lane);
-    nb = count_units_upto(listB, nb, (pA + 1) >> 3, lane);
-  }
-  const int nu = merge_units(listA, na, listB, nb, uunit, umask, lane);
-  __syncthreads();
-  if (!active) return;
-  // entries below each range's first unit; every lane ends with the totals
+  if (gp >= a.total) return;                          // whole wave; no workgroup barriers below
+  uint32_t* bmA = lds + static_cast<size_t>(wave) * 2 * a.words;
+  uint32_t* bmB = bmA + a.words;
+  const int64_t pair = gp % a.pairs;
+  const int64_t bg = gp / a.pairs;
+  const int64_t g = bg % a.G, b = bg / a.G;
   const int64_t tokA = 2 * pair;
-  const int64_t u_end = ((a.pos0 + tokA + (tokA + 1 < a.Tq ? 1 : 0)) >> 3) + 1;
-  int below[kRanges + 1];
-  below[0] = 0;
-  below[kRanges] = nu;
-#pragma unroll
-  for (int r = 1; r < kRanges; ++r) below[r] = 0;
-  for (int e = lane; e < nu; e += 64) {
-    const uint32_t u = static_cast<uint32_t>(uunit[e]);
-#pragma unroll
-    for (int r = 1; r < kRanges; ++r) below[r] += u < range_start(r, u_end) ? 1 : 0;
+  const bool hasB = tokA + 1 < a.Tq;
+  const int64_t pA = a.pos0 + tokA;
+  const int64_t u_end = ((pA + (hasB ? 1 : 0)) >> 3) + 1;        // units 0 .. u_end-1 can occur
+  const int nw = static_cast<int>((u_end + 31) >> 5);
+  for (int w = lane; w < nw; w += 64) {
+    bmA[w] = 0u;
+    bmB[w] = 0u;
   }
+  const int U = a.B >> 3;                               // units per block
+  auto mark = [&](const int32_t* selrow, int64_t p, uint32_t* bm) {
+    const int64_t o = p / a.B, last_unit = p >> 3;
+    for (int e = lane; e < a.NS; e += 64) {
+      const int blk = selrow[e];
+      if (blk < 0 || blk > o) continue;
+      for (int k = 0; k < U; ++k) {
+        const int64_t u = static_cast<int64_t>(blk) * U + k;
+        if (u <= last_unit) atomicOr(&bm[u >> 5], 1u << (u & 31));
+      }
+    }
+  };
+  mark(a.sel + ((b * a.Tq + tokA) * a.G + g) * a.NS, pA, bmA);
+  if (hasB) mark(a.sel + ((b * a.Tq + tokA + 1) * a.G + g) * a.NS, pA + 1, bmB);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // each lane owns a contiguous run of words; counts below each range start and in total
+  const int per = (nw + 63) >> 6;
+  const int w0 = lane * per, w1 = min(w0 + per, nw);
+  uint32_t lo[kRanges + 1];
+#pragma unroll
+  for (int r = 0; r <= kRanges; ++r) lo[r] = r < kRanges ? range_start(r, u_end) : static_cast<uint32_t>(u_end);
+  int mine = 0;
+  int below[kRanges + 1];
+#pragma unroll
+  for (int r = 0; r <= kRanges; ++r) below[r] = 0;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = bmA[w] | bmB[w];
+    mine += __popc(x);
+#pragma unroll
+    for (int r = 1; r < kRanges; ++r) {
+      const int64_t rel = static_cast<int64_t>(lo[r]) - 32 * w;   // bits of this word below lo[r]
+      const uint32_t m = rel >= 32 ? 0xffffffffu : (rel <= 0 ? 0u : ((1u << rel) - 1u));
+      below[r] += __popc(x & m);
+    }
+  }
+  // exclusive prefix of `mine` over the lanes, and the totals
+  int incl = mine;
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    const int v = __shfl_up(incl, o2, 64);
+    if (lane >= o2) incl += v;
+  }
+  const int nu = __shfl(incl, 63, 64);
+  int excl = incl - mine;
 #pragma unroll
   for (int r = 1; r < kRanges; ++r) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) below[r] += __shfl_xor(below[r], m, 64);
   }
-  // padded layout: range r starts at start[r], a multiple of 4, and is zero-filled to start[r + 1]
+  below[0] = 0;
+  below[kRanges] = nu;
   int start[kRanges + 1];
   start[0] = 0;
 #pragma unroll
   for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
+
   uint32_t* out = a.ulist + gp * list_stride(a.umax);
-  for (int e = lane; e < nu; e += 64) {
-    int r = 0;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t xa = bmA[w], xb = bmB[w];
+    uint32_t x = xa | xb;
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      x &= x - 1u;
+      const uint32_t u = static_cast<uint32_t>(32 * w + bit);
+      int r = 0;
 #pragma unroll
-    for (int q = 1; q < kRanges; ++q) r += e >= below[q] ? 1 : 0;
-    int shift = 0;
+      for (int q = 1; q < kRanges; ++q) r += u >= lo[q] ? 1 : 0;
+      int shift = 0;
 #pragma unroll
-    for (int q = 0; q < kRanges; ++q) shift = q == r ? start[q] - below[q] : shift;
-    const uint32_t m = umask[e];
-    out[e + shift] = static_cast<uint32_t>(uunit[e]) | ((m & 0xffu) ? (1u << 30) : 0u) |
-                     ((m >> 8) ? (1u << 31) : 0u);
+      for (int q = 0; q < kRanges; ++q) shift = q == r ? start[q] - below[q] : shift;
+      out[excl + shift] = u | (((xa >> bit) & 1u) << 30) | (((xb >> bit) & 1u) << 31);
+      ++excl;
+    }
   }
   if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by neither)
     const int r = lane >> 2, j = start[r] + (below[r + 1] - below[r]) + (lane & 3);
@@ -142,7 +177,7 @@ struct RangeArgs {
   const bf16_t* vp;
   const uint32_t* ulist;
   const int32_t* bounds;
-  float* part_o;           // [gp][R][16 rows][D]
+  bf16_t* part_o;          // [gp][R][16 rows][D], normalised by the partial's own sum
   float2* part_ml;         // [gp][R][16 rows]  (running max in the exp2 domain, sum)
   int64_t Tq, Tk, NU, pos0, pairs, pair_groups;
   int G, umax;
@@ -307,15 +342,21 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
     if (rem >= 1) step(kB, v1, v0);
   }
 
-  // partial of this range: unnormalised O, running max m and sum l per row
+  // partial of this range: O / l in bf16 (0 for a row with nothing in the range), and the running
+  // max m and sum l per row in fp32
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t pbase = (gp * kRanges + r) * 16 + lr;
-  float* po = a.part_o + pbase * D;
+  bf16_t* po = a.part_o + pbase * D;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    *reinterpret_cast<float4*>(po + 16 * t + 4 * lg) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  for (int t = 0; t < D / 16; ++t) {
+    uint2 w;
+    w.x = pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv);
+    w.y = pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv);
+    *reinterpret_cast<uint2*>(po + 16 * t + 4 * lg) = w;
+  }
   if (lg == 0) a.part_ml[pbase] = make_float2(m_run, l_tot);
 }
 
@@ -323,7 +364,7 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
 // merge of the range partials, gate, bf16 output
 // ------------------------------------------------------------------------------------------------
 struct MergeArgs {
-  const float* part_o;
+  const bf16_t* part_o;
   const float2* part_ml;
   const bf16_t* gate;
   bf16_t* out;
@@ -354,13 +395,13 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
     for (int r = 0; r < kRanges; ++r) {
       const int64_t pb = (gp * kRanges + r) * 16 + row;
       const float2 ml = a.part_ml[pb];
-      const float w = __builtin_amdgcn_exp2f(ml.x - mx);
-      L += ml.y * w;
-      const float4 po = *reinterpret_cast<const float4*>(a.part_o + pb * a.D + d0);
-      o.x += po.x * w;
-      o.y += po.y * w;
-      o.z += po.z * w;
-      o.w += po.w * w;
+      const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mx);     // partial sum at the common max
+      L += w;
+      const uint2 pw = *reinterpret_cast<const uint2*>(a.part_o + pb * a.D + d0);
+      o.x += bf16_to_f32(static_cast<bf16_t>(pw.x & 0xffffu)) * w;
+      o.y += bf16_to_f32(static_cast<bf16_t>(pw.x >> 16)) * w;
+      o.z += bf16_to_f32(static_cast<bf16_t>(pw.y & 0xffffu)) * w;
+      o.w += bf16_to_f32(static_cast<bf16_t>(pw.y >> 16)) * w;
     }
     const float inv = 1.f / L;
     const int64_t obase = (((b * a.Tq + tok) * a.G + g) * 8 + (row & 7)) * a.D + d0;
@@ -381,9 +422,10 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 bool attend_split_supported(const Dims& d) {
+  // the pair-union bitmaps of 4 waves (2 x ceil(NU/32) words each) must fit in 160 KiB of LDS
   return d.bf16 && d.H == 8 && (d.D == 64 || d.D == 128) && d.B % 8 == 0 &&
          d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31) &&
-         units_per_query(d) <= 1024;
+         units_per_query(d) <= 1024 && (d.NU + 31) / 32 <= 5120;
 }
 
 size_t attend_split_bytes(const Dims& d) {
@@ -392,7 +434,7 @@ size_t attend_split_bytes(const Dims& d) {
   const size_t umax = static_cast<size_t>(units_per_query(d));
   return align256(n * list_stride(static_cast<int>(umax)) * sizeof(uint32_t)) +
          align256(n * (kRanges + 1) * sizeof(int32_t)) +
-         align256(n * kRanges * 16 * d.D * sizeof(float)) + align256(n * kRanges * 16 * sizeof(float2));
+         align256(n * kRanges * 16 * d.D * sizeof(bf16_t)) + align256(n * kRanges * 16 * sizeof(float2));
 }
 
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
@@ -406,8 +448,8 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   p += align256(static_cast<size_t>(total) * list_stride(umax) * sizeof(uint32_t));
   int32_t* bounds = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<size_t>(total) * (kRanges + 1) * sizeof(int32_t));
-  float* part_o = reinterpret_cast<float*>(p);
-  p += align256(static_cast<size_t>(total) * kRanges * 16 * d.D * sizeof(float));
+  bf16_t* part_o = reinterpret_cast<bf16_t*>(p);
+  p += align256(static_cast<size_t>(total) * kRanges * 16 * d.D * sizeof(bf16_t));
   float2* part_ml = reinterpret_cast<float2*>(p);
 
   UnionArgs ua;
@@ -422,7 +464,8 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.NS = d.NS;
   ua.B = d.B;
   ua.umax = umax;
-  const size_t lds = static_cast<size_t>(4) * 6 * umax * sizeof(uint32_t);
+  ua.words = static_cast<int>((d.NU + 31) / 32);
+  const size_t lds = static_cast<size_t>(4) * 2 * ua.words * sizeof(uint32_t);
   hipLaunchKernelGGL(pair_union_kernel, dim3(static_cast<unsigned>((total + 3) / 4)), dim3(256), lds,
                      s, ua);
   hipError_t e = hipGetLastError();
