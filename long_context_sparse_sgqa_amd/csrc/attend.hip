@@ -67,21 +67,34 @@ __global__ void __launch_bounds__(256) pack_v_kernel(const T* __restrict__ v, T*
   }
 }
 
-// K packing in MFMA operand order: kp[b, g, u, kc, h, lg, r, e] = k[b, g, 8u + 4h + r, 32kc + 8lg + e]
-// (zero past Tk).  A 16-lane group reading one unit's rows 4h..4h+3, d 32kc..32kc+31 then reads 256
-// contiguous bytes, and a wavefront 4 such runs: the coalesced pattern, unlike 16 rows x 64 bytes.
+// K packing in MFMA operand order (zero past Tk), one of two layouts:
+//   pairs  (v_mfma_f32_16x16x32_bf16 kernel, kp_offset): kp[b, g, u, kc, h, lg, r, e] =
+//          k[b, g, 8u + 4h + r, 32kc + 8lg + e]: the 16 lanes reading one unit's rows 4h..4h+3 of
+//          d 32kc..32kc+31 read 256 contiguous bytes;
+//   groups of 4 tokens (v_mfma_f32_32x32x16_bf16 kernel, kq_offset): kp[b, g, u, kc, t, hh, e] =
+//          k[b, g, 8u + t, 16kc + 8hh + e]: the 16 lanes reading one unit's 8 tokens of d
+//          16kc..16kc+15 read 256 contiguous bytes.
+// Either way a wavefront load is 4 such runs: the coalesced pattern, unlike 16 rows x 64 bytes.
 __global__ void __launch_bounds__(256) pack_k_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ kp,
-                                                     int64_t Tk, int64_t NU, int D, int64_t total) {
+                                                     int64_t Tk, int64_t NU, int D, int64_t total,
+                                                     int quad_layout) {
   // one thread per 16-byte piece: pieces per unit = D (8 rows x D bf16 / 8)
   for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
        id += (int64_t)gridDim.x * blockDim.x) {
     const int q = static_cast<int>(id % D);            // piece within the unit, in packed order
     const int64_t u = (id / D) % NU;
     const int64_t bg = id / (static_cast<int64_t>(D) * NU);
-    const int r = q & 3, lg = (q >> 2) & 3, h = (q >> 4) & 1, kc = q >> 5;
-    const int64_t t = u * 8 + 4 * h + r;
+    int row, col;
+    if (quad_layout) {
+      row = (q >> 1) & 7;
+      col = 16 * (q >> 4) + 8 * (q & 1);
+    } else {
+      row = 4 * ((q >> 4) & 1) + (q & 3);
+      col = 32 * (q >> 5) + 8 * ((q >> 2) & 3);
+    }
+    const int64_t t = u * 8 + row;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (t < Tk) v = *reinterpret_cast<const uint4*>(k + (bg * Tk + t) * D + 32 * kc + 8 * lg);
+    if (t < Tk) v = *reinterpret_cast<const uint4*>(k + (bg * Tk + t) * D + col);
     *reinterpret_cast<uint4*>(kp + (bg * NU + u) * D * 8 + static_cast<int64_t>(q) * 8) = v;
   }
 }
@@ -363,7 +376,8 @@ hipError_t launch_pack_kv(const Dims& d, const void* k, const void* v, void* pac
   bf16_t* kp = static_cast<bf16_t*>(packed);
   bf16_t* vp = kp + attend_packed_kv_bytes(d) / 2 / sizeof(bf16_t);
   hipLaunchKernelGGL(pack_k_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(k), kp, d.Tk, d.NU, d.D, total);
+                     static_cast<const bf16_t*>(k), kp, d.Tk, d.NU, d.D, total,
+                     attend_split_supported(d) ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,

@@ -1,25 +1,30 @@
-// Step 4, range-split variant: gated GQA over the selected tokens, with each query's selected units
-// split into R contiguous unit ranges that run on different XCDs and are merged afterwards.
+// Step 4, range-split variant: gated GQA over the selected tokens for groups of 4 adjacent query
+// tokens, with each group's selected units split into R contiguous unit ranges that run on
+// different XCDs and are merged afterwards.
 //
 // Same method as attend.hip (Step 5 Preview pages, mo.ai.kr summary, section
 // "모델 구조와 학습 안정성": Sparse GQA on Gated GQA attends only over each KV group's selected
-// blocks).  Gathering the selected K/V units is what bounds this step; most of those gathers are L2
-// misses when every XCD serves random units of a whole group.  Here range r of every query goes to
-// the workgroups numbered r mod R, which the dispatcher deals to XCDs r, r+R, ..., so each XCD's L2
-// caches only 1/R of a group's K/V: the popular part of that range fits, and the hit rate rises.
+// blocks, and batching adjacent tokens, whose selections overlap, raises GPU utilisation).
+// Gathering the selected K/V units is what bounds this step.  Two things cut that traffic here:
+//   * a wavefront serves 4 adjacent tokens x 8 heads = 32 rows (the M of v_mfma_f32_32x32x16_bf16)
+//     and walks the union of their selections, so a unit chosen by several of the 4 tokens is
+//     loaded once (the union of 4 tokens is ~0.84x the units that 2 pairs would load);
+//   * range r of every group goes to the workgroups numbered r mod R, which the dispatcher deals to
+//     XCDs r, r+R, ..., so each XCD's L2 caches only 1/R of a KV group's keys and values.
 //
 // Three kernels:
-//   pair_union_kernel  per (sequence, group, token pair): the sorted union of the two tokens'
-//     selected 8-token units, entry = unit | token-A-chose << 30 | token-B-chose << 31 (B is a
-//     multiple of 8, so a unit is wholly selected by a token or not at all), built through LDS
-//     bitmaps; every range is padded to a multiple of 4 entries and its first entry recorded.
-//   attend_range_kernel  one wavefront per (pair, range), 16 rows = 2 tokens x 8 heads: the pair's
-//     entries inside the range in chunks of 4 units (S^T = K Q^T and O^T += V^T P^T on
-//     v_mfma_f32_16x16x32_bf16, masked online softmax in the exp2 domain), ending in a partial
-//     per row: O / l rounded to bf16, and the running max m and sum l in fp32.  K and V come from the unit-packed
-//     copies, whose layout makes every 16-lane operand load one 256-byte run; K is loaded two chunks
-//     and V one chunk ahead of use, and list entries arrive by scalar loads, so each wave keeps
-//     about three chunks of operands in flight.
+//   quad_union_kernel  per (sequence, group, 4 tokens): the sorted union of the tokens' selected
+//     8-token units, entry = unit | chosen-by-token-t << (27 + t) (B is a multiple of 8, so a unit
+//     is wholly selected by a token or not at all), built through LDS bitmaps; every range is
+//     padded to a multiple of 4 entries and its first entry recorded.
+//   attend_range_kernel  one wavefront per (group of 4 tokens, range): the entries inside the
+//     range in chunks of 4 units (32 tokens).  S^T = K Q^T on D/16 MFMAs with the K rows permuted
+//     so that every lane holds the 16 scores of one row for two units; masks, online softmax in
+//     the exp2 domain, O^T += V^T P^T on D/16 MFMAs whose P operand is a lane's own probabilities.
+//     K comes from the unit-packed copy laid out for this kernel and V from the unit-packed V,
+//     so every 16-lane operand load is one 256-byte run; K is loaded two chunks and V one chunk
+//     ahead, list entries arrive by scalar loads, and Q is read from LDS.  The result per row:
+//     O / l rounded to bf16, and the running max m and sum l in fp32.
 //   merge_ranges_kernel  per row: weight each partial by its sum rescaled to the common max,
 //     combine, apply sigmoid(gate), round to bf16.
 #include "device_common.h"
@@ -29,85 +34,93 @@
 namespace sgqa {
 namespace {
 
-constexpr int kRanges = 4;                      // unit ranges per query
-constexpr int kRangeWaves = 4;                  // pairs per workgroup (one per wave)
-constexpr uint32_t kUnitMask = 0x3fffffffu;
-// Entries of one pair's list: the union (at most 2 umax) with every range padded to a multiple of 4
-// entries, plus 16 entries the range kernel may read (and discard) past the end of the last chunk.
+constexpr int kRanges = 4;                      // unit ranges per group of tokens
+constexpr int kRangeWaves = 4;                  // token groups per workgroup (one per wave)
+constexpr int kTok = 4;                         // query tokens per group
+constexpr uint32_t kUnitMask = 0x07ffffffu;     // entry bits 0..26: unit; 27..30: chosen bits
+constexpr int kChoseShift = 27;
+// Entries of one group's list: the union (at most kTok umax) with every range padded to a multiple
+// of 4 entries, plus 16 entries the range kernel may read (and discard) past the end of the last
+// chunk.
 __host__ __device__ constexpr int64_t list_stride(int umax) {
-  return (2 * static_cast<int64_t>(umax) + 4 * kRanges + 16 + 3) / 4 * 4;
+  return (kTok * static_cast<int64_t>(umax) + 4 * kRanges + 16 + 3) / 4 * 4;
 }
 
-// ------------------------------------------------------------------------------------------------
-// pair unions
-// ------------------------------------------------------------------------------------------------
-struct UnionArgs {
-  const int32_t* sel;
-  uint32_t* ulist;         // [Bt * G * pairs][list_stride(umax)]
-  int32_t* bounds;         // [Bt * G * pairs][kRanges + 1]: first entry of each range, then end
-  int64_t Tq, pos0, pairs, total;
-  int G, NS, B, umax, words;   // words: bitmap words per token (ceil(NU / 32))
-};
-
-// Unit ranges of a pair: range r covers units [r * u_end / R, (r + 1) * u_end / R) of the pair's
-// causal unit axis [0, u_end), u_end = last token's own unit + 1.
+// Unit ranges of a group: range r covers units [r * u_end / R, (r + 1) * u_end / R) of the
+// group's causal unit axis [0, u_end), u_end = the last token's own unit + 1.
 __device__ __forceinline__ uint32_t range_start(int r, int64_t u_end) {
   return static_cast<uint32_t>((r * u_end) / kRanges);
 }
 
-// Union through two LDS bitmaps (one bit per unit for each token of the pair): each selected block
-// sets its units' bits (units past the token's own unit are left out: t <= p), then one scan over
-// the words emits the union in ascending unit order with both tokens' chosen bits, each range
-// padded to a multiple of 4 entries.
-__global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
+__device__ __forceinline__ int64_t group_u_end(int64_t pos0, int64_t tok0, int64_t Tq) {
+  const int64_t last = (tok0 + kTok - 1 < Tq ? tok0 + kTok - 1 : Tq - 1);
+  return ((pos0 + last) >> 3) + 1;
+}
+
+// ------------------------------------------------------------------------------------------------
+// unions of 4 tokens' selections
+// ------------------------------------------------------------------------------------------------
+struct UnionArgs {
+  const int32_t* sel;
+  uint32_t* ulist;         // [Bt * G * ngroups][list_stride(umax)]
+  int32_t* bounds;         // [Bt * G * ngroups][kRanges + 1]: first entry of each range, then end
+  int64_t Tq, pos0, ngroups, total;
+  int G, NS, B, umax, words, waves;   // words: bitmap words per token (ceil(NU / 32))
+};
+
+// Each selected block sets its units' bits in the token's LDS bitmap (units past the token's own
+// unit are left out: t <= p); one scan over the words then emits the union in ascending unit order
+// with every token's chosen bit.
+__global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gp = static_cast<int64_t>(blockIdx.x) * 4 + wave;   // (b * G + g) * pairs + pair
-  if (gp >= a.total) return;                          // whole wave; no workgroup barriers below
-  uint32_t* bmA = lds + static_cast<size_t>(wave) * 2 * a.words;
-  uint32_t* bmB = bmA + a.words;
-  const int64_t pair = gp % a.pairs;
-  const int64_t bg = gp / a.pairs;
+  const int64_t gq = static_cast<int64_t>(blockIdx.x) * a.waves + wave;  // (b*G + g)*ngroups + q
+  if (gq >= a.total) return;                          // whole wave; no workgroup barriers below
+  uint32_t* bm = lds + static_cast<size_t>(wave) * kTok * a.words;
+  const int64_t qi = gq % a.ngroups;
+  const int64_t bg = gq / a.ngroups;
   const int64_t g = bg % a.G, b = bg / a.G;
-  const int64_t tokA = 2 * pair;
-  const bool hasB = tokA + 1 < a.Tq;
-  const int64_t pA = a.pos0 + tokA;
-  const int64_t u_end = ((pA + (hasB ? 1 : 0)) >> 3) + 1;        // units 0 .. u_end-1 can occur
+  const int64_t tok0 = kTok * qi;
+  const int64_t u_end = group_u_end(a.pos0, tok0, a.Tq);
   const int nw = static_cast<int>((u_end + 31) >> 5);
   for (int w = lane; w < nw; w += 64) {
-    bmA[w] = 0u;
-    bmB[w] = 0u;
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) bm[t * a.words + w] = 0u;
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int U = a.B >> 3;                               // units per block
-  auto mark = [&](const int32_t* selrow, int64_t p, uint32_t* bm) {
+  for (int t = 0; t < kTok; ++t) {
+    if (tok0 + t >= a.Tq) break;
+    const int64_t p = a.pos0 + tok0 + t;
     const int64_t o = p / a.B, last_unit = p >> 3;
+    const int32_t* selrow = a.sel + ((b * a.Tq + tok0 + t) * a.G + g) * a.NS;
+    uint32_t* bmt = bm + t * a.words;
     for (int e = lane; e < a.NS; e += 64) {
       const int blk = selrow[e];
       if (blk < 0 || blk > o) continue;
       for (int k = 0; k < U; ++k) {
         const int64_t u = static_cast<int64_t>(blk) * U + k;
-        if (u <= last_unit) atomicOr(&bm[u >> 5], 1u << (u & 31));
+        if (u <= last_unit) atomicOr(&bmt[u >> 5], 1u << (u & 31));
       }
     }
-  };
-  mark(a.sel + ((b * a.Tq + tokA) * a.G + g) * a.NS, pA, bmA);
-  if (hasB) mark(a.sel + ((b * a.Tq + tokA + 1) * a.G + g) * a.NS, pA + 1, bmB);
-  __builtin_amdgcn_wave_barrier();
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // each lane owns a contiguous run of words; counts below each range start and in total
   const int per = (nw + 63) >> 6;
   const int w0 = lane * per, w1 = min(w0 + per, nw);
-  uint32_t lo[kRanges + 1];
+  uint32_t lo[kRanges];
 #pragma unroll
-  for (int r = 0; r <= kRanges; ++r) lo[r] = r < kRanges ? range_start(r, u_end) : static_cast<uint32_t>(u_end);
+  for (int r = 0; r < kRanges; ++r) lo[r] = range_start(r, u_end);
   int mine = 0;
   int below[kRanges + 1];
 #pragma unroll
   for (int r = 0; r <= kRanges; ++r) below[r] = 0;
   for (int w = w0; w < w1; ++w) {
-    const uint32_t x = bmA[w] | bmB[w];
+    uint32_t x = 0u;
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) x |= bm[t * a.words + w];
     mine += __popc(x);
 #pragma unroll
     for (int r = 1; r < kRanges; ++r) {
@@ -124,7 +137,7 @@ __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
     if (lane >= o2) incl += v;
   }
   const int nu = __shfl(incl, 63, 64);
-  int excl = incl - mine;
+  int pos = incl - mine;
 #pragma unroll
   for (int r = 1; r < kRanges; ++r) {
 #pragma unroll
@@ -137,10 +150,14 @@ __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
 #pragma unroll
   for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
 
-  uint32_t* out = a.ulist + gp * list_stride(a.umax);
+  uint32_t* out = a.ulist + gq * list_stride(a.umax);
   for (int w = w0; w < w1; ++w) {
-    const uint32_t xa = bmA[w], xb = bmB[w];
-    uint32_t x = xa | xb;
+    uint32_t xt[kTok], x = 0u;
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      xt[t] = bm[t * a.words + w];
+      x |= xt[t];
+    }
     while (x) {
       const int bit = __builtin_ctz(x);
       x &= x - 1u;
@@ -151,15 +168,18 @@ __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
       int shift = 0;
 #pragma unroll
       for (int q = 0; q < kRanges; ++q) shift = q == r ? start[q] - below[q] : shift;
-      out[excl + shift] = u | (((xa >> bit) & 1u) << 30) | (((xb >> bit) & 1u) << 31);
-      ++excl;
+      uint32_t ent = u;
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) ent |= ((xt[t] >> bit) & 1u) << (kChoseShift + t);
+      out[pos + shift] = ent;
+      ++pos;
     }
   }
-  if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by neither)
+  if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by none)
     const int r = lane >> 2, j = start[r] + (below[r + 1] - below[r]) + (lane & 3);
     if (j < start[r + 1]) out[j] = 0u;
   }
-  int32_t* bnd = a.bounds + gp * (kRanges + 1);
+  int32_t* bnd = a.bounds + gq * (kRanges + 1);
   if (lane <= kRanges) {
     int v = 0;
 #pragma unroll
@@ -169,53 +189,74 @@ __global__ void __launch_bounds__(256) pair_union_kernel(UnionArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// one unit range of one pair
+// one unit range of one group of 4 tokens
 // ------------------------------------------------------------------------------------------------
 struct RangeArgs {
   const bf16_t* q;
-  const bf16_t* kp;
-  const bf16_t* vp;
+  const bf16_t* kp;        // unit-packed K, 4-token layout (kq_offset)
+  const bf16_t* vp;        // unit-packed V [.., unit, d, 8 tokens]
   const uint32_t* ulist;
   const int32_t* bounds;
-  bf16_t* part_o;          // [gp][R][16 rows][D], normalised by the partial's own sum
-  float2* part_ml;         // [gp][R][16 rows]  (running max in the exp2 domain, sum)
-  int64_t Tq, Tk, NU, pos0, pairs, pair_groups;
+  bf16_t* part_o;          // [gq][R][32 rows][D], normalised by the partial's own sum
+  float2* part_ml;         // [gq][R][32 rows]  (running max in the exp2 domain, sum)
+  int64_t Tq, Tk, NU, pos0, ngroups, wg_groups;
   int G, umax;
   float scale_log2e;
 };
 
+// K rows of the S^T product, permuted: output r' (0..15) of a lane in half h is C row
+// 8 (r'/4) + 4h + r'%4, and should hold token r' % 8 of unit slot (r' < 8 ? h : 2 + h).  So K
+// row i (an A operand row, i = lane % 32) is token kq_tok(i) of unit slot kq_slot(i).
+__device__ __forceinline__ int kq_slot(int i) {
+  const int h = (i >> 2) & 1, j = (i >> 3) * 4 + (i & 3);
+  return j < 8 ? h : 2 + h;
+}
+__device__ __forceinline__ int kq_tok(int i) { return ((i >> 3) * 4 + (i & 3)) & 7; }
+
 template <int D>
-__global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_range_kernel(RangeArgs a) {
   constexpr int H = 8;
+  constexpr int kQRow = D * 2 + 16;                      // padded LDS row of Q (bytes)
+  __shared__ __attribute__((aligned(16))) unsigned char s_q[kRangeWaves][32 * kQRow];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-  const int lr = lane & 15, lg = lane >> 4;
-  const int X = lr >> 3, head = lr & 7;
+  const int c = lane & 31, h = lane >> 5;                // Q row (token c/8, head c%8), lane half
+  const int trow = c >> 3, head = c & 7;
   // workgroup id: range fastest, so the range decides the XCD
   const int r = static_cast<int>(blockIdx.x % kRanges);
   const int64_t rest = blockIdx.x / kRanges;
-  const int64_t pg = rest % a.pair_groups;
-  const int64_t bg = rest / a.pair_groups;
+  const int64_t wgq = rest % a.wg_groups;
+  const int64_t bg = rest / a.wg_groups;
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
-  const int64_t pair = pg * kRangeWaves + wave;
-  if (pair >= a.pairs) return;                         // whole wave; no workgroup barriers follow
-  const int64_t gp = bg * a.pairs + pair;
-  const int64_t tokA = 2 * pair;
-  const bool validB = tokA + 1 < a.Tq;
-  const bool rowvalid = X ? validB : true;
-  const int64_t pX = a.pos0 + tokA + X;
+  const int64_t qi = wgq * kRangeWaves + wave;
+  if (qi >= a.ngroups) return;                           // whole wave; no workgroup barriers follow
+  const int64_t gq = bg * a.ngroups + qi;
+  const int64_t tok0 = kTok * qi;
+  const bool rowvalid = tok0 + trow < a.Tq;
+  const int64_t pX = a.pos0 + tok0 + trow;
 
-  const uint32_t* list = a.ulist + gp * list_stride(a.umax);
-  const int32_t* bnd = a.bounds + gp * (kRanges + 1);
+  const uint32_t* list = a.ulist + gq * list_stride(a.umax);
+  const int32_t* bnd = a.bounds + gq * (kRanges + 1);
   const int e0 = __builtin_amdgcn_readfirstlane(bnd[r]);
   const int e1 = __builtin_amdgcn_readfirstlane(bnd[r + 1]);
 
-  bf16x8_t qf[D / 32];
-  const bf16_t* qrow = a.q + (((b * a.Tq + (rowvalid ? tokA + X : tokA)) * a.G + g) * H + head) * D;
+  // Q rows of the group into this wave's LDS slice: lane (c, h) copies d in [D/2 h, D/2 (h+1))
+  unsigned char* sq = &s_q[wave][0];
+  {
+    const bf16_t* qrow = a.q + (((b * a.Tq + (rowvalid ? tok0 + trow : tok0)) * a.G + g) * H + head) * D;
 #pragma unroll
-  for (int kc = 0; kc < D / 32; ++kc)
-    qf[kc] = rowvalid ? load_bf16x8(qrow + 32 * kc + 8 * lg) : zero_bf16x8();
+    for (int k = 0; k < D / 16; ++k) {
+      const int d = (D / 2) * h + 8 * k;
+      const uint4 v = rowvalid ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(sq + c * kQRow + d * 2) = v;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // Q^T operand of d-slice kc: B[8h + e][c] = q[c][16 kc + 8h + e]
+  auto q_operand = [&](int kc) -> bf16x8_t {
+    return bf16x8_from_u4(*reinterpret_cast<const uint4*>(sq + c * kQRow + (16 * kc + 8 * h) * 2));
+  };
 
   const BufRsrc krs = make_rsrc(a.kp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
@@ -225,83 +266,98 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
   // waits behind the K/V loads in flight.  Entries at or past e1 read as 0 (unit 0, not chosen).
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
-  auto chunk_entries = [&](int c, uint32_t* ent4) {
-    const u32x4 v = *((ConstQuadPtr)(list + c));
+  auto chunk_entries = [&](int cpos, uint32_t* ent4) {
+    const u32x4 v = *((ConstQuadPtr)(list + cpos));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ent4[j] = c < e1 ? v[j] : 0u;
+    for (int j = 0; j < 4; ++j) ent4[j] = cpos < e1 ? v[j] : 0u;
   };
   auto pick4 = [](const uint32_t* v, int i) -> uint32_t {
     return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
   };
 
-  // K operands of a chunk (4 units) go to registers: unit slot lr/4, rows lr%4 and lr%4 + 4.
-  struct KRegs { bf16x8_t k1[D / 32], k2[D / 32]; };
+  // K operands of a chunk: A row c = token kq_tok(c) of unit slot kq_slot(c), d-half h.
+  const int kslot = kq_slot(c), ktok = kq_tok(c);
+  struct KRegs { bf16x8_t k[D / 16]; };
   auto load_k = [&](const uint32_t* ent4, KRegs& R) {
-    const int u = static_cast<int>(pick4(ent4, lr >> 2) & kUnitMask);
+    const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
 #pragma unroll
-    for (int kc = 0; kc < D / 32; ++kc) {
-      R.k1[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 0, lg, lr));
-      R.k2[kc] = buffer_load_bf16x8(krs, kp_offset(u, D, kc, 1, lg, lr));
-    }
+    for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
   };
-  // V^T operands of a chunk go to registers too: unit slot lg, coalesced 256-byte runs.
+  // V^T operands of d-tile dt for the units of slot h (first product) and slot 2 + h (second).
   struct VRegs { bf16x8_t v[D / 16]; };
   auto load_v = [&](const uint32_t* ent4, VRegs& R) {
-    const int vo = (static_cast<int>(pick4(ent4, lg) & kUnitMask) * D + lr) * 16;
+    const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
+    const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) R.v[t] = buffer_load_bf16x8(vrs, vo + t * 256);
+    for (int dt = 0; dt < D / 32; ++dt) {
+      R.v[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
+      R.v[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
+    }
   };
 
-  f32x4_t acc[D / 16];
+  f32x16_t acc[D / 32];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
   const float ninf = -__builtin_inff();
 
-  // one chunk: S^T = K Q^T (tokens 0-3 of each unit slot in s1, 4-7 in s2), masks, online softmax,
-  // O^T += V^T P^T.  `refill` runs once S has consumed K, to reuse its registers.
-  auto chunk = [&](const KRegs& K, const VRegs& V, const uint32_t* ent4, auto refill) {
-    const uint32_t ent = pick4(ent4, lg);
-    const int unitS = static_cast<int>(ent & kUnitMask);
-    f32x4_t s1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t s2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < D / 32; ++kc) {
-      s1 = mfma16x16x32(K.k1[kc], qf[kc], s1);
-      s2 = mfma16x16x32(K.k2[kc], qf[kc], s2);
-    }
-    refill();
-    const bool chose = X ? (ent >> 31) : ((ent >> 30) & 1u);     // 0 past the range (ent = 0)
-    const int64_t dlt = pX - static_cast<int64_t>(unitS) * 8;
+  // valid-token mask (8 bits) of this lane's row for a unit entry
+  auto row_mask = [&](uint32_t ent) -> uint32_t {
+    const bool chose = (ent >> (kChoseShift + trow)) & 1u;      // 0 past the range (ent = 0)
+    const int dlt = static_cast<int>(pX) - static_cast<int>(ent & kUnitMask) * 8;
     const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
-    const uint32_t valid = chose ? causal : 0u;
-    float sv[8];
+    return chose ? causal : 0u;
+  };
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  // one chunk: S^T = K Q^T, masks, online softmax, O^T += V^T P^T.  `refill` runs once S has
+  // consumed K, to reuse its registers.  Masked scores become -inf by adding a bias built from the
+  // mask bit; the scale enters through one fma in the exp2 argument; the row sum adds the bf16
+  // probabilities the product uses, two at a time.
+  auto chunk = [&](const KRegs& K, const VRegs& V, const uint32_t* ent4, auto refill) {
+    f32x16_t s = {};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = ((valid >> e) & 1u) ? s1[e] * a.scale_log2e : ninf;
-      sv[e + 4] = ((valid >> (e + 4)) & 1u) ? s2[e] * a.scale_log2e : ninf;
+    for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(K.k[kc], q_operand(kc), s);
+    refill();
+    const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int bit = static_cast<int>(msk << (31 - i)) >> 31;      // -1 valid, 0 masked
+      t[i] = s[i] + __int_as_float(~bit & static_cast<int>(0xff800000u));
     }
-    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = wave_max_xor(mx, 16);
+    float mx = fmaxf(fmaxf(t[0], t[1]), t[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, t[i]), t[i + 1]);
+    mx = fmaxf(mx, t[15]);
     mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * a.scale_log2e);
     if (__ballot(m_new > m_run + kLazyRescaleLog2)) {   // a row's max grew by > margin: rescale all
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) acc[t] *= alpha;
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
       m_run = m_new;
     }
-    float pv[8];
+    float pv[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(sv[e] - m_run);
-      l_run += pv[e];
+    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(t[i], a.scale_log2e, -m_run));
+    const bf16x8_t pa = pack8_bf16(pv), pb = pack8_bf16(pv + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t x = {pa[2 * i], pa[2 * i + 1]};
+      const bf16x2_t y = {pb[2 * i], pb[2 * i + 1]};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(x, ones2, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(y, ones2, l_run, false);
     }
-    const bf16x8_t pf = pack8_bf16(pv);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) acc[t] = mfma16x16x32(V.v[t], pf, acc[t]);
+    for (int dt = 0; dt < D / 32; ++dt) {
+      acc[dt] = mfma32x32x16(V.v[2 * dt], pa, acc[dt]);
+      acc[dt] = mfma32x32x16(V.v[2 * dt + 1], pb, acc[dt]);
+    }
   };
 
   // Software pipeline over chunks of 4 units (past the range's end the loads fetch unit 0 and are
@@ -314,16 +370,15 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
     chunk_entries(e0 + 4, e1c);
     chunk_entries(e0 + 8, e2c);
     KRegs kA, kB;
-    VRegs v0, v1;
+    VRegs v0;
     load_k(ec, kA);
     load_k(e1c, kB);
-    load_v(ec, v0);
     int nx = e0 + 12;                                  // next chunk whose entries are read
-    auto step = [&](KRegs& K, VRegs& Vcur, VRegs& Vnext) {
+    auto step = [&](KRegs& K) {
       chunk_entries(nx, e3c);                          // entries a chunk ahead of their use
       nx += 4;
-      load_v(e1c, Vnext);
-      chunk(K, Vcur, ec, [&] { load_k(e2c, K); });
+      load_v(ec, v0);
+      chunk(K, v0, ec, [&] { load_k(e2c, K); });
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ec[j] = e1c[j];
@@ -333,31 +388,33 @@ __global__ void __launch_bounds__(256) attend_range_kernel(RangeArgs a) {
     };
     // the loop body is one period of the register rotation, so every trip enters with the same
     // loads in flight; the first chunk and the tail run outside it
-    step(kA, v0, v1);
+    step(kA);
     int rem = (e1 - e0 - 4) >> 2;                      // chunks left
     for (; rem >= 2; rem -= 2) {
-      step(kB, v1, v0);
-      step(kA, v0, v1);
+      step(kB);
+      step(kA);
     }
-    if (rem >= 1) step(kB, v1, v0);
+    if (rem >= 1) step(kB);
   }
 
   // partial of this range: O / l in bf16 (0 for a row with nothing in the range), and the running
-  // max m and sum l per row in fp32
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  // max m and sum l per row in fp32.  Lane (c, h) holds d = 32 dt + 8 (i/4) + 4h + i%4 of row c.
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t pbase = (gp * kRanges + r) * 16 + lr;
+  const int64_t pbase = (gq * kRanges + r) * 32 + c;
   bf16_t* po = a.part_o + pbase * D;
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    uint2 w;
-    w.x = pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv);
-    w.y = pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv);
-    *reinterpret_cast<uint2*>(po + 16 * t + 4 * lg) = w;
-  }
-  if (lg == 0) a.part_ml[pbase] = make_float2(m_run, l_tot);
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4v v = {acc[dt][4 * i4] * inv, acc[dt][4 * i4 + 1] * inv, acc[dt][4 * i4 + 2] * inv,
+                        acc[dt][4 * i4 + 3] * inv};
+      *reinterpret_cast<uint2*>(po + 32 * dt + 8 * i4 + 4 * h) =
+          __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4v));
+    }
+  if (h == 0) a.part_ml[pbase] = make_float2(m_run, l_tot);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -368,32 +425,32 @@ struct MergeArgs {
   const float2* part_ml;
   const bf16_t* gate;
   bf16_t* out;
-  int64_t Tq, pairs, total_pairs;
+  int64_t Tq, ngroups, total_groups;
   int G, D;
 };
 
 __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
   const int per_row = a.D / 4;
-  const int64_t total = a.total_pairs * 16 * per_row;
+  const int64_t total = a.total_groups * 32 * per_row;
   for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
        id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int d0 = static_cast<int>(id % per_row) * 4;
-    const int64_t gr = id / per_row;                 // gp * 16 + row
-    const int row = static_cast<int>(gr % 16);
-    const int64_t gp = gr / 16;
-    const int64_t pair = gp % a.pairs;
-    const int64_t bg = gp / a.pairs;
-    const int64_t tok = 2 * pair + (row >> 3);
+    const int64_t gr = id / per_row;                 // gq * 32 + row
+    const int row = static_cast<int>(gr % 32);
+    const int64_t gq = gr / 32;
+    const int64_t qi = gq % a.ngroups;
+    const int64_t bg = gq / a.ngroups;
+    const int64_t tok = kTok * qi + (row >> 3);
     if (tok >= a.Tq) continue;
     const int64_t g = bg % a.G, b = bg / a.G;
     float mx = -1e30f;
 #pragma unroll
-    for (int r = 0; r < kRanges; ++r) mx = fmaxf(mx, a.part_ml[(gp * kRanges + r) * 16 + row].x);
+    for (int r = 0; r < kRanges; ++r) mx = fmaxf(mx, a.part_ml[(gq * kRanges + r) * 32 + row].x);
     float L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int r = 0; r < kRanges; ++r) {
-      const int64_t pb = (gp * kRanges + r) * 16 + row;
+      const int64_t pb = (gq * kRanges + r) * 32 + row;
       const float2 ml = a.part_ml[pb];
       const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mx);     // partial sum at the common max
       L += w;
@@ -419,29 +476,37 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Token groups whose union bitmaps (kTok x words each) share one workgroup's LDS (0: none fits).
+int union_waves(const Dims& d) {
+  const int64_t words = (d.NU + 31) / 32;
+  const int64_t per_wave = kTok * words * static_cast<int64_t>(sizeof(uint32_t));
+  const int64_t fit = (160 * 1024) / per_wave;
+  return static_cast<int>(fit >= 4 ? 4 : fit);
+}
+
 }  // namespace
 
 bool attend_split_supported(const Dims& d) {
-  // the pair-union bitmaps of 4 waves (2 x ceil(NU/32) words each) must fit in 160 KiB of LDS
+  // one token group's union bitmaps must fit in 160 KiB of LDS
   return d.bf16 && d.H == 8 && (d.D == 64 || d.D == 128) && d.B % 8 == 0 &&
          d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31) &&
-         units_per_query(d) <= 1024 && (d.NU + 31) / 32 <= 5120;
+         units_per_query(d) <= 1024 && union_waves(d) >= 1;
 }
 
 size_t attend_split_bytes(const Dims& d) {
-  const int64_t pairs = (d.Tq + 1) / 2;
-  const size_t n = static_cast<size_t>(d.Bt * d.G * pairs);
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const size_t n = static_cast<size_t>(d.Bt * d.G * ng);
   const size_t umax = static_cast<size_t>(units_per_query(d));
   return align256(n * list_stride(static_cast<int>(umax)) * sizeof(uint32_t)) +
          align256(n * (kRanges + 1) * sizeof(int32_t)) +
-         align256(n * kRanges * 16 * d.D * sizeof(bf16_t)) + align256(n * kRanges * 16 * sizeof(float2));
+         align256(n * kRanges * 32 * d.D * sizeof(bf16_t)) + align256(n * kRanges * 32 * sizeof(float2));
 }
 
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark) {
-  const int64_t pairs = (d.Tq + 1) / 2;
-  const int64_t total = d.Bt * d.G * pairs;
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
   char* p = static_cast<char*>(ws);
   uint32_t* ulist = reinterpret_cast<uint32_t*>(p);
@@ -449,7 +514,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   int32_t* bounds = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<size_t>(total) * (kRanges + 1) * sizeof(int32_t));
   bf16_t* part_o = reinterpret_cast<bf16_t*>(p);
-  p += align256(static_cast<size_t>(total) * kRanges * 16 * d.D * sizeof(bf16_t));
+  p += align256(static_cast<size_t>(total) * kRanges * 32 * d.D * sizeof(bf16_t));
   float2* part_ml = reinterpret_cast<float2*>(p);
 
   UnionArgs ua;
@@ -458,16 +523,17 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.bounds = bounds;
   ua.Tq = d.Tq;
   ua.pos0 = d.pos0;
-  ua.pairs = pairs;
+  ua.ngroups = ng;
   ua.total = total;
   ua.G = d.G;
   ua.NS = d.NS;
   ua.B = d.B;
   ua.umax = umax;
   ua.words = static_cast<int>((d.NU + 31) / 32);
-  const size_t lds = static_cast<size_t>(4) * 2 * ua.words * sizeof(uint32_t);
-  hipLaunchKernelGGL(pair_union_kernel, dim3(static_cast<unsigned>((total + 3) / 4)), dim3(256), lds,
-                     s, ua);
+  ua.waves = union_waves(d);
+  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
+  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
+                     dim3(64 * ua.waves), lds, s, ua);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(4, s);
   if (e != hipSuccess) return e;
@@ -484,12 +550,12 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   a.Tk = d.Tk;
   a.NU = d.NU;
   a.pos0 = d.pos0;
-  a.pairs = pairs;
-  a.pair_groups = (pairs + kRangeWaves - 1) / kRangeWaves;
+  a.ngroups = ng;
+  a.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
   a.G = d.G;
   a.umax = umax;
   a.scale_log2e = d.scale * 1.4426950408889634f;
-  const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.pair_groups * kRanges));
+  const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
   if (d.D == 128)
     hipLaunchKernelGGL(attend_range_kernel<128>, grid, dim3(256), 0, s, a);
   else
@@ -504,11 +570,11 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   m.gate = static_cast<const bf16_t*>(gate);
   m.out = static_cast<bf16_t*>(out);
   m.Tq = d.Tq;
-  m.pairs = pairs;
-  m.total_pairs = total;
+  m.ngroups = ng;
+  m.total_groups = total;
   m.G = d.G;
   m.D = d.D;
-  const int64_t items = total * 16 * (d.D / 4);
+  const int64_t items = total * 32 * (d.D / 4);
   int64_t blocks = (items + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(merge_ranges_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, m);

@@ -57,6 +57,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate (v_mfma_f32_32x32x16_bf16).
+// Lane l supplies A[l % 32][8*(l/32) .. +8] and B[8*(l/32) .. +8][l % 32]; it receives
+// C[8*(r/4) + 4*(l/32) + r%4][l % 32] for r = 0..15.
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Hardware round-to-nearest-even packing of 8 fp32 into the bf16x8 MFMA operand.
 __device__ __forceinline__ bf16x8_t pack8_bf16(const float* v) {
   typedef float f32x8_t __attribute__((ext_vector_type(8)));

@@ -66,6 +66,7 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   constexpr int kLds = (kSampBytes > 2 * kTileBytes) ? kSampBytes : 2 * kTileBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   __shared__ uint32_t s_thr[kRows];
+  __shared__ int s_cnt[kRows];                            // candidates appended per row
 
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
 
@@ -175,10 +176,10 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     c_list[e] = a.cand + c_rr[e] * a.cap;
   }
 
-  // ---------------- phase 2: every causal score, filtered, ordered appends ----------------
-  // A candidate is (float bits of the score << 32 | block); each row's list stays in ascending block
-  // order because a row's 16 columns of a step sit in one 16-lane group, ranked by lane.
-  int count[4] = {0, 0, 0, 0};
+  // ---------------- phase 2: every causal score, filtered, appended ----------------
+  // A candidate is (float bits of the score << 32 | block).  Appends take their slot from a per-row
+  // LDS counter, so a row's list is in no particular order (the select kernel orders its output).
+  if (threadIdx.x < kRows) s_cnt[threadIdx.x] = 0;
   const int64_t ntiles = (o_max + kCols - 1) / kCols;
   // tiles below every row's causal limit need no per-column check
   const int64_t o_min = row_o(0, nullptr);
@@ -211,9 +212,6 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     store_tile(0);
   }
   __syncthreads();
-  const uint64_t lane_bit = 1ull << lane;
-  const uint64_t grp_all = 0xffffull << (lg * 16);          // this lane's 16-lane group
-  const uint64_t grp_lt = grp_all & (lane_bit - 1ull);      // lanes of the group below this one
   auto scores16 = [&](const unsigned char* src, int n) -> f32x4_t {
     f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -223,17 +221,19 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     }
     return c;
   };
+  int* row_cnt = &s_cnt[wave * 16 + lg * 4];
   auto append = [&](const f32x4_t& c, int32_t col, bool check_causal) {
+    int pos[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       bool pass = c[e] >= c_thr[e];
       if (check_causal) pass = pass && col < c_o32[e];
-      const uint64_t bal = __ballot(pass);
-      const int pos = count[e] + __popcll(bal & grp_lt);
-      if (pass && pos < a.cap)
-        c_list[e][pos] = (static_cast<uint64_t>(__float_as_uint(c[e])) << 32) | static_cast<uint32_t>(col);
-      count[e] += __popcll(bal & grp_all);
+      pos[e] = pass ? atomicAdd(&row_cnt[e], 1) : a.cap;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (pos[e] < a.cap)
+        c_list[e][pos[e]] = (static_cast<uint64_t>(__float_as_uint(c[e])) << 32) | static_cast<uint32_t>(col);
   };
   for (int64_t t = 0; t < ntiles; ++t) {
     const int buf = static_cast<int>(t & 1);
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   if (lr == 0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (c_valid[e]) a.cnt[c_rr[e]] = count[e];
+      if (c_valid[e]) a.cnt[c_rr[e]] = row_cnt[e];
   }
 }
 
@@ -270,7 +270,7 @@ struct SelectArgs {
   int32_t* fail_list;
   int32_t* fail_count;
   int64_t b0, i0, ntok, Tq, pos0, rows;
-  int G, B, NS, cap;
+  int G, B, NS, cap, words, waves;     // words: bitmap words per row (ceil(NB / 32))
 };
 
 constexpr int kSelPer = 32;        // candidates per lane held in registers (cap <= 64 * kSelPer)
@@ -290,10 +290,15 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t ta
   return tau;
 }
 
+// Each wave owns one row and two LDS bitmaps over the row's candidate blocks: blocks whose key is
+// above tau, and blocks whose key equals tau.  Scanning them in block order emits the selection
+// ascending, with the lowest-indexed ties taken first.
 __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
+  extern __shared__ uint32_t bm_all[];
   const int lane = threadIdx.x & 63;
-  const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (rr >= a.rows) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rr = static_cast<int64_t>(blockIdx.x) * a.waves + wave;
+  if (rr >= a.rows) return;                           // whole wave; no workgroup barriers below
   const int64_t tok = rr / a.G;
   const int g = static_cast<int>(rr - tok * a.G);
   const int64_t bseq = a.b0 + tok / a.ntok;
@@ -311,14 +316,17 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
     return;
   }
   const uint64_t* cr = a.cand + rr * a.cap;
-  uint32_t key[kSelPer];
+  uint32_t key[kSelPer], col[kSelPer];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) {
     const int x = e * 64 + lane;
     key[e] = 0u;
+    col[e] = 0u;
     if (x < m) {
-      key[e] = order_key_f(__uint_as_float(static_cast<uint32_t>(cr[x] >> 32)));
+      const uint64_t v = cr[x];
+      key[e] = order_key_f(__uint_as_float(static_cast<uint32_t>(v >> 32)));
+      col[e] = static_cast<uint32_t>(v);
       kmin = min(kmin, key[e]);
       kmax = max(kmax, key[e]);
     }
@@ -336,29 +344,78 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   const uint32_t tau0 = top >= 0 ? (kmin & ~((2u << top) - 1u)) : kmin;
   const uint32_t tau = m <= 16 * 64 ? kth_largest<16>(key, tau0, top, need)
                                     : kth_largest<kSelPer>(key, tau0, top, need);
+
+  // bitmaps over blocks 0 .. o-1: above tau, equal to tau
+  const int nw = static_cast<int>((o + 31) >> 5);
+  uint32_t* bgt = bm_all + static_cast<size_t>(wave) * 2 * a.words;
+  uint32_t* beq = bgt + a.words;
+  for (int w = lane; w < nw; w += 64) {
+    bgt[w] = 0u;
+    beq[w] = 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   int gt = 0;
 #pragma unroll
-  for (int e = 0; e < kSelPer; ++e) gt += key[e] > tau ? 1 : 0;
-  const int take_eq = need - wave_sum(gt);
-  // ordered emit (candidates are in ascending block order)
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  int written = 0, eq_seen = 0;
-#pragma unroll
   for (int e = 0; e < kSelPer; ++e) {
-    if (e * 64 >= m) break;
-    const int x = e * 64 + lane;
-    const bool valid = x < m;
-    const bool is_gt = valid && key[e] > tau;
-    const bool is_eq = valid && key[e] == tau;
-    const uint64_t beq = __ballot(is_eq);
-    const int eq_rank = eq_seen + __popcll(beq & lt_mask);
-    const bool take = is_gt || (is_eq && eq_rank < take_eq);
-    const uint64_t btk = __ballot(take);
-    if (take) out[written + __popcll(btk & lt_mask)] = static_cast<int32_t>(cr[x] & 0xffffffffu);
-    written += __popcll(btk);
-    eq_seen += __popcll(beq);
+    if (key[e] > tau) {
+      atomicOr(&bgt[col[e] >> 5], 1u << (col[e] & 31));
+      ++gt;
+    } else if (key[e] == tau) {
+      atomicOr(&beq[col[e] >> 5], 1u << (col[e] & 31));
+    }
+  }
+  int take_eq = need - wave_sum(gt);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // each lane scans a contiguous run of words; ties are taken in block order up to take_eq
+  const int per = (nw + 63) >> 6;
+  const int w0 = lane * per, w1 = min(w0 + per, nw);
+  int n_eq = 0;
+  for (int w = w0; w < w1; ++w) n_eq += __popc(beq[w]);
+  int eq_before = n_eq;                                 // inclusive prefix over lanes
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    const int v = __shfl_up(eq_before, o2, 64);
+    if (lane >= o2) eq_before += v;
+  }
+  eq_before -= n_eq;
+  int n_sel = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t e = beq[w];
+    uint32_t keep = 0u;
+    while (e && eq_before < take_eq) {
+      const uint32_t bit = e & (0u - e);
+      keep |= bit;
+      e ^= bit;
+      ++eq_before;
+    }
+    const uint32_t x = bgt[w] | keep;
+    bgt[w] = x;
+    n_sel += __popc(x);
+  }
+  int pos = n_sel;                                      // exclusive prefix over lanes
+#pragma unroll
+  for (int o2 = 1; o2 < 64; o2 <<= 1) {
+    const int v = __shfl_up(pos, o2, 64);
+    if (lane >= o2) pos += v;
+  }
+  pos -= n_sel;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t x = bgt[w];
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      x &= x - 1u;
+      out[pos++] = 32 * w + bit;
+    }
   }
   if (lane == 0) out[need] = static_cast<int32_t>(o);
+}
+
+// Rows per select workgroup: each needs two bitmaps of ceil(NB / 32) words in LDS (0: none fits).
+int select_waves(const Dims& d) {
+  const int64_t per_wave = 2 * ((d.NB + 31) / 32) * static_cast<int64_t>(sizeof(uint32_t));
+  const int64_t fit = (160 * 1024) / per_wave;
+  return static_cast<int>(fit >= 4 ? 4 : fit);
 }
 
 }  // namespace
@@ -367,7 +424,8 @@ int fused_select_capacity() { return 64 * kSelPer; }
 
 bool fused_select_supported(const Dims& d) {
   // the candidate list holds about twice the budget: budgets up to 512 blocks
-  return d.idx_bf16 && d.NS <= 513 && (d.Di == 32 || d.Di == 64 || d.Di == 128);
+  return d.idx_bf16 && d.NS <= 513 && (d.Di == 32 || d.Di == 64 || d.Di == 128) &&
+         select_waves(d) >= 1;
 }
 
 hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
@@ -419,8 +477,11 @@ hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const i
   a.B = d.B;
   a.NS = d.NS;
   a.cap = fused_select_capacity();
-  const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
-  hipLaunchKernelGGL(select_candidates_kernel, grid, dim3(256), 0, s, a);
+  a.words = static_cast<int>((d.NB + 31) / 32);
+  a.waves = select_waves(d);
+  const dim3 grid(static_cast<unsigned>((a.rows + a.waves - 1) / a.waves));
+  const size_t lds = static_cast<size_t>(a.waves) * 2 * a.words * sizeof(uint32_t);
+  hipLaunchKernelGGL(select_candidates_kernel, grid, dim3(64 * a.waves), lds, s, a);
   return hipGetLastError();
 }
 

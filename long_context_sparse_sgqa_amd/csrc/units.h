@@ -128,4 +128,11 @@ __device__ __forceinline__ int kp_offset(int u, int D, int kc, int h, int lg, in
   return u * D * 16 + (((kc * 2 + h) * 4 + lg) * 4 + (lr & 3)) * 16;
 }
 
+// Unit-packed K for the 4-token kernels: k[8u + t][16kc + 8h + e] is stored at element
+// ((u * D/16 + kc) * 8 + t) * 16 + h * 8 + e, so the 16 lanes that feed one unit's 8 tokens x 2
+// halves of a 16-wide d-slice to v_mfma_f32_32x32x16_bf16 read one contiguous 256-byte block.
+__device__ __forceinline__ int kq_offset(int u, int D, int kc, int t, int h) {
+  return u * D * 16 + ((kc * 8 + t) * 2 + h) * 16;
+}
+
 }  // namespace sgqa
