@@ -54,28 +54,32 @@ def test_tiny_every_step_every_row():
 # small bf16 cases through the matrix-core path: ragged shapes, several block sizes, every row
 # ----------------------------------------------------------------------------------------------
 SMALL_CASES = [
-    # t_q, t_kv, block, topk, groups, index_dim, sharp
-    (300, 1001, 8, 256, 2, 128, False),
-    (517, 517, 8, 128, 3, 64, False),
-    (517, 517, 8, 128, 2, 128, True),
-    (257, 700, 16, 256, 2, 32, False),
-    (401, 601, 4, 128, 2, 128, False),
-    (333, 333, 2, 64, 1, 128, True),
-    (1, 333, 8, 64, 2, 128, False),
-    (2, 2, 8, 64, 2, 128, False),
-    (64, 64, 8, 4096, 2, 128, False),        # budget covers the whole context: dense
+    # t_q, t_kv, block, topk, groups, index_dim, sharp, head_dim, batch
+    (300, 1001, 8, 256, 2, 128, False, 128, 1),
+    (517, 517, 8, 128, 3, 64, False, 128, 1),
+    (517, 517, 8, 128, 2, 128, True, 128, 1),
+    (257, 700, 16, 256, 2, 32, False, 128, 1),
+    (401, 601, 4, 128, 2, 128, False, 128, 1),
+    (333, 333, 2, 64, 1, 128, True, 128, 1),
+    (1, 333, 8, 64, 2, 128, False, 128, 1),
+    (2, 2, 8, 64, 2, 128, False, 128, 1),
+    (64, 64, 8, 4096, 2, 128, False, 128, 1),      # budget covers the whole context: dense
+    (301, 999, 8, 256, 2, 128, True, 64, 1),       # head dim 64
+    (203, 650, 16, 128, 2, 64, False, 64, 1),
+    (150, 700, 8, 128, 2, 128, True, 128, 3),      # several sequences
+    (7, 1300, 8, 256, 2, 128, False, 128, 2),      # a short query chunk at the end of the keys
 ]
 
 
-@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d-di%d%s" % (
-    c[0], c[1], c[2], c[3], c[4], c[5], "-sharp" if c[6] else ""))
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d-di%d%s-d%d-b%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "-sharp" if c[6] else "", c[7], c[8]))
 def test_small_bf16_every_row(case):
-    t_q, t_kv, B, k, G, di, sharp = case
+    t_q, t_kv, B, k, G, di, sharp, d, bt = case
     say("case:", case)
-    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=128, index_dim=di,
-                          block=B, topk=k, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
-                          needles=1 if (t_kv // B) >= 2 * G else 0, seed=11, device="cuda",
-                          sharp=sharp)
+    w, x = generate_small(batch=bt, t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=d,
+                          index_dim=di, block=B, topk=k, dtype="bf16", index_dtype="bf16",
+                          scaled_qkv=True, needles=1 if (t_kv // B) >= 2 * G else 0, seed=11,
+                          device="cuda", sharp=sharp)
     prob = sg.Problem.from_workload(w)
     k_blk, scores, sel, out = run_split(prob, x)
     sel_ref, out_ref, kblk_ref = oracle.forward(x, B, k, w.softmax_scale)
