@@ -25,6 +25,8 @@
 namespace sgqa {
 namespace {
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kRows = 64;          // rows per workgroup
 constexpr int kSamp = 512;         // sampled blocks per row
 constexpr int kCols = 128;         // K_blk columns per staged tile
@@ -168,12 +170,10 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   // limit o as 32 bits, and the row's candidate list
   float c_thr[4];
   int32_t c_o32[4];
-  uint64_t* c_list[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     c_thr[e] = c_valid[e] ? key_threshold_to_float(s_thr[wave * 16 + lg * 4 + e]) : __builtin_nanf("");
     c_o32[e] = static_cast<int32_t>(c_o[e]);
-    c_list[e] = a.cand + c_rr[e] * a.cap;
   }
 
   // ---------------- phase 2: every causal score, filtered, appended ----------------
@@ -222,6 +222,15 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     return c;
   };
   int* row_cnt = &s_cnt[wave * 16 + lg * 4];
+  // Candidate stores go through a buffer descriptor over this workgroup's rows and are issued for
+  // every lane: lanes without a candidate use an out-of-range offset, which the hardware drops.
+  // With no branches around them, the number of stores per tile is fixed and the wait for the next
+  // tile's loads need not wait for them.
+  const BufRsrc crs = make_rsrc(a.cand + (seq * a.seq_rows + row0) * a.cap,
+                                static_cast<int64_t>(kRows) * a.cap * 8);
+  int c_off[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c_off[e] = (wave * 16 + lg * 4 + e) * a.cap * 8;
   auto append = [&](const f32x4_t& c, int32_t col, bool check_causal) {
     int pos[4];
 #pragma unroll
@@ -231,24 +240,43 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
       pos[e] = pass ? atomicAdd(&row_cnt[e], 1) : a.cap;
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (pos[e] < a.cap)
-        c_list[e][pos[e]] = (static_cast<uint64_t>(__float_as_uint(c[e])) << 32) | static_cast<uint32_t>(col);
+    for (int e = 0; e < 4; ++e) {
+      const u32x2_t v = {static_cast<uint32_t>(col), __float_as_uint(c[e])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, crs, pos[e] < a.cap ? c_off[e] + pos[e] * 8 : 0x7fffffff,
+                                            0, 0);
+    }
   };
+  // Per tile: all products first (LDS reads and MFMAs only), then the next tile's global loads,
+  // then the appends (compares, LDS counters, candidate stores), then the staging of the next tile.
   for (int64_t t = 0; t < ntiles; ++t) {
     const int buf = static_cast<int>(t & 1);
     const unsigned char* src = lds + buf * kTileBytes;
     const int32_t col0 = static_cast<int32_t>(t * kCols) + lr;
-    const bool check = t >= full_tiles;
-    // the products of step n+1 are issued before the appends of step n, hiding their latency
-    f32x4_t cur = scores16(src, 0);
-    if (t + 1 < ntiles) load_tile(t + 1);
+    // B operands of step n+1 are read from LDS before the products of step n are issued
+    f32x4_t sc[kCols / 16];
+    uint4 opb[2][DI / 32];
+    auto read_ops = [&](int n, uint4* op) {
+#pragma unroll
+      for (int kc = 0; kc < DI / 32; ++kc)
+        op[kc] = *reinterpret_cast<const uint4*>(src + (n * 16 + lr) * kRowBytes + kc * 64 + lg * 16);
+    };
+    read_ops(0, opb[0]);
 #pragma unroll
     for (int n = 0; n < kCols / 16; ++n) {
-      f32x4_t nxt = cur;
-      if (n + 1 < kCols / 16) nxt = scores16(src, n + 1);
-      if (check) append(cur, col0 + n * 16, true); else append(cur, col0 + n * 16, false);
-      cur = nxt;
+      if (n + 1 < kCols / 16) read_ops(n + 1, opb[(n + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);               // keep the reads ahead of the products
+      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < DI / 32; ++kc) c = mfma16x16x32(qa[kc], bf16x8_from_u4(opb[n & 1][kc]), c);
+      sc[n] = c;
+    }
+    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t >= full_tiles) {
+#pragma unroll
+      for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, true);
+    } else {
+#pragma unroll
+      for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, false);
     }
     if (t + 1 < ntiles) store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier below in t-1
     __syncthreads();
