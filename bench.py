@@ -3,7 +3,11 @@
 
 One step = one sgqa_forward call (block compression + indexer + top-k + gated attention) over the
 whole 128K prefill (1 sequence x 131072 query tokens, 8 KV groups x 8 heads, d = 128, d_idx = 128,
-B = 8, k = 4096, bf16), with every input already resident in HBM.  W untimed warm-up steps, then K
+B = 8, k = 4096, bf16), with every input already resident in HBM.
+
+`--workload decode` measures the decode path instead: 64 sequences of 262 144 cached tokens in a
+paged cache; one step appends 4 new tokens to every sequence (K, V, index keys, block keys) and
+decodes them (indexer, top-k, gated attention over the pages).  W untimed warm-up steps, then K
 timed steps bracketed by device synchronisation; HIP events recorded by the library between its
 stages give the per-stage (per-kernel) durations on the stream the kernels run on.
 
@@ -190,12 +194,202 @@ def cpu_baseline(w, x, out_gpu, sel_gpu, target_s, seed):
     return base, parity
 
 
+# ------------------------------------------------------------------------------------------------
+# decode over the paged cache
+# ------------------------------------------------------------------------------------------------
+DECODE_STAGES = ("index", "topk", "attn_lists", "attention", "attn_merge")
+
+
+def decode_union_tokens(sel, pos_last, block):
+    """Tokens whose K and V the decode step must read: per (sequence, group), the union of its new
+    tokens' selected blocks (tokens <= the last query's position)."""
+    import torch
+    bt, tq, g, ns = sel.shape
+    s = sel.permute(0, 2, 1, 3).reshape(bt * g, tq * ns).to(torch.int64)
+    s, _ = torch.sort(s, dim=1)
+    distinct = ((s[:, 1:] != s[:, :-1]) & (s[:, 1:] >= 0)).sum(dim=1) + (s[:, 0] >= 0).to(torch.int64)
+    tail = block - 1 - (pos_last % block)          # tokens of the own block past the last query
+    return int(distinct.sum().item()) * block - bt * g * tail
+
+
+def cpu_baseline_decode(w, x_cpu, lens, out_gpu, sel_gpu, target_s):
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        pass
+    torch.set_num_threads(1)
+    t_begin = time.perf_counter()
+    rows, sels, outs = [], [], []
+    for j in range(x_cpu["q"].shape[0]):
+        for i in range(w.t_q):
+            s, o, _ = oracle.sequence_rows(x_cpu, lens, w.block, w.topk, w.softmax_scale, [(j, i)])
+            rows.append((j, i))
+            sels.append(s[0])
+            outs.append(o[0])
+        if time.perf_counter() - t_begin >= target_s:
+            break
+    elapsed = time.perf_counter() - t_begin
+    sg_ = np.stack([sel_gpu[j, i].cpu().numpy() for j, i in rows]).astype(np.int64)
+    og = np.stack([out_gpu[j, i].to("cpu", torch.float64).numpy() for j, i in rows])
+    parity = {"rows": len(rows) * w.groups,
+              "sel_mismatch_rows": int((sg_ != np.stack(sels)).any(axis=-1).sum()),
+              "max_abs_err": float(np.abs(og - np.stack(outs)).max()), "tolerance": 1e-2}
+    base = {"value": len(rows) / elapsed, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} decoded query tokens ({len(rows) // w.t_q} sequences x {w.t_q}), "
+                      f"all {w.groups} KV groups, each sequence's block compression included; "
+                      f"fp64 numpy oracle, 1 thread, {elapsed:.1f} s"}
+    return base, parity
+
+
+def main_decode(args):
+    import torch
+    import long_context_sparse_sgqa_amd as sg
+    from sgqa_inputs import generate, get_workload
+
+    w = get_workload("decode")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = sg.load_library()
+    x = generate(w, device=dev, seed=args.seed)
+    P = 64
+    n_steps = args.warmup + args.steps
+    cap = w.t_kv + w.t_q * n_steps                    # the longest any sequence gets
+    max_pages = -(-cap // P)
+    num_pages = w.batch * max_pages
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(1)).to(torch.int32)
+    table = perm.view(w.batch, max_pages).to(dev)
+    cache = sg.Cache(num_pages, P, max_pages)
+    prob = sg.Problem.from_workload(w, t_kv=cap)
+    pools = sg.alloc_cache(prob, cache, dev)
+    stream = torch.cuda.current_stream()
+    # prefill: the first t_kv - t_q tokens of every sequence, in chunks
+    prefix = w.t_kv - w.t_q
+    done = 0
+    while done < prefix:
+        n = min(32768, prefix - done)
+        seq = torch.full((w.batch,), done + n, dtype=torch.int32, device=dev)
+        sg.cache_append(prob, cache, seq, table, x["k"][:, :, done:done + n].contiguous(),
+                        x["v"][:, :, done:done + n].contiguous(),
+                        x["k_idx"][:, done:done + n].contiguous(), pools, stream=stream)
+        done += n
+    torch.cuda.synchronize()
+    # every step appends the workload's last t_q tokens at the next positions and decodes them
+    k_new = x["k"][:, :, prefix:].contiguous()
+    v_new = x["v"][:, :, prefix:].contiguous()
+    ki_new = x["k_idx"][:, prefix:].contiguous()
+    lens = [torch.full((w.batch,), prefix + w.t_q * (k + 1), dtype=torch.int32, device=dev)
+            for k in range(n_steps)]
+    out = torch.empty(w.batch, w.t_q, w.groups, w.heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    sel = torch.empty(w.batch, w.t_q, w.groups, w.n_sel, dtype=torch.int32, device=dev)
+    ws = torch.empty(sg.decode_workspace_size(prob, cache), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        sg.cache_append(prob, cache, lens[k], table, k_new, v_new, ki_new, pools, stream=stream)
+        sg.decode(prob, cache, lens[k], table, x["q"], x["gate"], x["q_idx"], pools, out=out,
+                  sel=sel, workspace=ws, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    marks = [[ev.create() for _ in range(N_MARKS)] for _ in range(args.steps)]
+    app = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    arr_t = ctypes.c_void_p * N_MARKS
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        k = args.warmup + j
+        lib.sgqa_set_stage_events(arr_t(*[m.value for m in marks[j]]))
+        app[j][0].record(stream)
+        sg.cache_append(prob, cache, lens[k], table, k_new, v_new, ki_new, pools, stream=stream)
+        app[j][1].record(stream)
+        sg.decode(prob, cache, lens[k], table, x["q"], x["gate"], x["q_idx"], pools, out=out,
+                  sel=sel, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.sgqa_set_stage_events(None)
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    names = ("index", "topk", "-", "attn_lists", "attention", "attn_merge")
+    st = {s: 0.0 for s in DECODE_STAGES}
+    for m in marks:
+        for j, s in enumerate(names):
+            if s != "-":
+                st[s] += ev.elapsed_ms(m[j], m[j + 1]) / args.steps
+    ev.destroy()
+    st["append"] = sum(a.elapsed_time(b) for a, b in app) / args.steps
+
+    # algorithmic bytes of the last step (sequences of L tokens, queries at L - t_q .. L - 1)
+    L = prefix + w.t_q * n_steps
+    nb = (L - w.t_q) // w.block                       # scored blocks of the first query (approx. all)
+    rows = w.batch * w.t_q * w.groups
+    kv_tokens = decode_union_tokens(sel, L - 1, w.block)
+    bytes_ = {
+        "append": w.batch * w.t_q * (2 * w.groups * w.head_dim + w.index_dim) * 2 * 2
+                  + w.batch * 2 * w.block * w.index_dim * 2,
+        "index": w.batch * nb * w.index_dim * 2 + rows * nb * 4,       # K_blk scan, score rows
+        "topk": rows * nb * 4 + rows * w.n_sel * 4,
+        "attn_lists": rows * w.n_sel * 4,
+        "attention": kv_tokens * w.head_dim * 2 * 2 + 2 * rows * w.heads * w.head_dim * 2,
+        "attn_merge": rows * w.heads * (4 * (2 * w.head_dim + 8) + 2 * 2 * w.head_dim),
+    }
+    stages = {s: {"ms": st[s], "bound": "hbm", "bytes": bytes_[s],
+                  "achieved_GBps": bytes_[s] / max(st[s], 1e-9) / 1e6} for s in bytes_}
+    for s in stages.values():
+        s["frac"] = s["achieved_GBps"] * 1e9 / PEAK_HBM_BYTES
+    dominant = max(stages, key=lambda s: stages[s]["ms"])
+    ach = stages[dominant]["achieved_GBps"]
+    kname = {"attention": "attend_range_kernel<128, paged>", "index": "index_bf16_kernel",
+             "topk": "topk_kernel"}.get(dominant, dominant)
+    roof = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_BYTES / 1e9,
+            "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM_BYTES, "launch_ms": stages[dominant]["ms"],
+            "traffic": load_traffic("attend_range_paged" if dominant == "attention" else dominant,
+                                    "decode"),
+            "work_per_launch": f"{bytes_[dominant]:.4e} B"}
+
+    cpu, parity = (None, None)
+    if args.cpu_seconds > 0:
+        pick = [0, 37]
+        xs = {}
+        for n in ("q", "gate", "q_idx"):
+            xs[n] = x[n][pick].cpu()
+        # the cache now holds the workload's prefix followed by the last t_q tokens n_steps times
+        idx = torch.cat([torch.arange(prefix), torch.arange(prefix, prefix + w.t_q).repeat(n_steps)])
+        for n in ("k", "v"):
+            xs[n] = x[n][pick][:, :, idx.to(dev)].cpu()
+        xs["k_idx"] = x["k_idx"][pick][:, idx.to(dev)].cpu()
+        cpu, parity = cpu_baseline_decode(w, xs, [L] * 2, out[pick], sel[pick], args.cpu_seconds)
+
+    tokens = w.batch * w.t_q
+    rec = {
+        "metric": "Sparse-GQA decode query-tokens/s (64 sequences x 262K cached tokens, 4 new "
+                  "tokens each; append + index + topk + attn)",
+        "value": tokens / (wall_ms / 1e3), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; the decode workload's tokens in a paged cache with shuffled "
+                "pages; every step appends the workload's last 4 tokens again)",
+        "config": {"workload": "decode (paged cache, 64 tokens per page)", "batch": w.batch,
+                   "t_q": w.t_q, "t_kv_last": L, "kv_groups": w.groups, "heads_per_group": w.heads,
+                   "head_dim": w.head_dim, "index_dim": w.index_dim, "block": w.block,
+                   "topk_tokens": w.topk, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "stages": stages, "parity": parity,
+        "kv_union_tokens": kv_tokens, "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload == "decode":
+        return main_decode(args)
     import torch
     import long_context_sparse_sgqa_amd as sg
     from sgqa_inputs import generate, get_workload

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SGQA_ABI_VERSION 1
+#define SGQA_ABI_VERSION 2
 
 typedef enum {
   SGQA_OK = 0,
@@ -177,9 +177,82 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
  *   after the merge of range partials (right after events[5] when there is none),
  * so that hipEventElapsedTime between consecutive markers is the duration of that stage.  Arming
  * costs nothing on the device; recording failures make sgqa_forward return SGQA_ERR_HIP.
+ * sgqa_decode records the same markers with events[1] after the indexer, events[2] after the
+ * top-k and events[3] right after events[2] (the paged cache needs no packing).
  */
 #define SGQA_STAGE_EVENTS 7
 sgqa_status sgqa_set_stage_events(void* const* events);
+
+/* ---------------------------------------------------------------------------------------------
+ * Decode over a paged cache.
+ *
+ * The pages run Sparse GQA at contexts up to 1M tokens (Step 5 Preview summary on mo.ai.kr,
+ * section "모델 구조와 학습 안정성") and serve the model with MTP-3 heads and a KV cache (same
+ * page, section "장기 강화학습과 실행 비용"): new tokens arrive a few at a time.  The method is the forward's: for every new query token,
+ * steps 2-4 over the sequence's cached keys, with the block keys of step 1 kept per sequence and
+ * recomputed only for the blocks that new tokens fall into.  Sequences may hold different numbers
+ * of tokens; every call appends / queries the same number of new tokens per sequence.
+ *
+ * Cache (all device memory, owned by the caller; P = page_tokens):
+ *   k_cache    : [num_pages, G, P/8, 8*D]   bf16.  Token t (0..7) of 8-token unit u of a page holds
+ *                k[.., d] at element ((d/16)*8 + t)*16 + d%16 of the unit (the operand order the
+ *                attention kernel reads).
+ *   v_cache    : [num_pages, G, P/8, D, 8]  bf16.  v[.., d] of token t at element d*8 + t.
+ *   kidx_cache : [num_pages, P, Di]         index_dtype (bf16).  Index key of each token.
+ *   k_blk      : [Bt, max_pages*P/B, Di]    index_dtype.  Block keys of each sequence.
+ *   block_table: [Bt, max_pages] int32: logical page j (tokens j*P .. j*P+P-1) of sequence b is
+ *                physical page block_table[b*max_pages + j].  Distinct sequences must not share a
+ *                page that either of them appends to.
+ *   seq_lens   : [Bt] int32: tokens held by each sequence, including the new ones.
+ *   (seq_lens and block_table need 4-byte alignment only; every other pointer 16 bytes.)
+ * Only sgqa_cache_append writes the cache; it keeps tokens past a sequence's length inside the
+ * sequence's last 8-token unit at zero.  Host-side validation covers every size; device-side
+ * values (seq_lens, block_table) are clamped into range by the kernels, so a bad entry gives
+ * wrong results for that sequence but never an out-of-bounds access.  Required:
+ * prob->t_q <= seq_lens[b] <= prob->t_kv <= max_pages * P for sgqa_decode (n_new instead of t_q
+ * for sgqa_cache_append), block_table entries in [0, num_pages).
+ * --------------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t num_pages;        /* pages in each pool                                         */
+  int32_t page_tokens;      /* P: a power of two, a multiple of 8 and of the block size   */
+  int32_t max_pages;        /* entries per block_table row; max_pages * P >= prob->t_kv    */
+} sgqa_cache;
+
+/*
+ * Append n_new tokens to every sequence: positions seq_lens[b] - n_new .. seq_lens[b] - 1 of
+ * sequence b receive k_new, v_new ([Bt, G, n_new, D], dtype bf16) and kidx_new ([Bt, n_new, Di],
+ * index_dtype bf16); then every block those positions fall into is recomputed in k_blk as the sum
+ * of the cached index keys of its tokens below seq_lens[b] (fp32, token order, rounded once: the
+ * same value step 1 gives for the whole sequence).  prob->t_kv bounds seq_lens; prob->t_q is
+ * ignored.  A bulk append (n_new = the whole prompt) fills an empty sequence.
+ */
+sgqa_status sgqa_cache_append(const sgqa_problem* prob, const sgqa_cache* cache,
+                              const int32_t* seq_lens, const int32_t* block_table, int64_t n_new,
+                              const void* k_new, const void* v_new, const void* kidx_new,
+                              void* k_cache, void* v_cache, void* kidx_cache, void* k_blk,
+                              void* stream);
+
+/* Workspace bytes sgqa_decode needs for `prob` (Bt sequences, t_q new tokens each, at most t_kv
+ * tokens per sequence).  Host only. */
+sgqa_status sgqa_decode_workspace_size(const sgqa_problem* prob, const sgqa_cache* cache,
+                                       size_t* bytes);
+
+/*
+ * Steps 2-4 for the t_q newest tokens of every sequence, over the paged cache.
+ *   q, gate : [Bt, t_q, G, H, D] bf16;  q_idx : [Bt, t_q, G, Di] bf16.
+ *   Query i of sequence b sits at position p = seq_lens[b] - t_q + i; its selection and output are
+ *   those sgqa_forward gives for a sequence of seq_lens[b] tokens (scores of the strictly past
+ *   blocks against k_blk, top NS-1 + own block, gated attention over the selected tokens <= p).
+ *   sel_out : [Bt, t_q, G, NS] int32 or NULL.   out : [Bt, t_q, G, H, D] bf16.
+ *   Supported: dtype and index_dtype bf16, H == 8, D in {64, 128}, B a multiple of 8.
+ * The selection runs on stored score rows ([Bt * t_q * G, ceil(t_kv / B)] fp32 in the workspace):
+ * with few query rows and long rows that is the layout that spreads over the whole GPU.
+ */
+sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
+                        const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                        const void* gate, const void* q_idx, const void* k_cache,
+                        const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -9,6 +9,9 @@ Layouts and semantics are those of include/sgqa.h:
   q, gate, out : [Bt, Tq, G, H, D]       k, v : [Bt, G, Tk, D]
   q_idx        : [Bt, Tq, G, Di]         k_idx: [Bt, Tk, Di]        k_blk: [Bt, NB, Di]
   scores       : [Bt, Tq, G, NB] fp32    sel  : [Bt, Tq, G, NS] int32
+Decode over a paged cache (Cache: num_pages, page_tokens P, max_pages):
+  k_cache [pages, G, P/8, 8 D]   v_cache [pages, G, P/8, D, 8]   kidx_cache [pages, P, Di]
+  k_blk   [Bt, max_pages P / B, Di]   block_table [Bt, max_pages] int32   seq_lens [Bt] int32
 """
 from __future__ import annotations
 
@@ -19,8 +22,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["Problem", "load_library", "library_path", "abi_version", "sizes", "index", "topk",
-           "attend", "forward", "SgqaError", "EXPORTED_SYMBOLS"]
+__all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
+           "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
+           "decode", "SgqaError", "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsgqa.so"
@@ -30,7 +34,8 @@ _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
                     "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
-                    "sgqa_set_stage_events")
+                    "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
+                    "sgqa_decode")
 
 
 class SgqaError(RuntimeError):
@@ -54,6 +59,21 @@ class _Sizes(ctypes.Structure):
                 ("sel_bytes", ctypes.c_size_t), ("attend_workspace_bytes", ctypes.c_size_t),
                 ("forward_workspace_bytes", ctypes.c_size_t),
                 ("forward_workspace_min_bytes", ctypes.c_size_t)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("num_pages", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
+
+
+class Cache:
+    """Paged cache descriptor (sgqa_cache)."""
+
+    def __init__(self, num_pages, page_tokens, max_pages):
+        self.num_pages, self.page_tokens, self.max_pages = int(num_pages), int(page_tokens), int(max_pages)
+
+    def _c(self) -> _Cache:
+        return _Cache(self.num_pages, self.page_tokens, self.max_pages)
 
 
 class Problem:
@@ -121,8 +141,13 @@ def load_library():
     lib.sgqa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sgqa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sgqa_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    C = ctypes.POINTER(_Cache)
+    lib.sgqa_cache_append.argtypes = [P, C, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sgqa_decode_workspace_size.argtypes = [P, C, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sgqa_decode.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
-                 "sgqa_set_stage_events"):
+                 "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
+                 "sgqa_decode"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -240,4 +265,78 @@ def forward(prob: Problem, q, k, v, gate, q_idx, k_idx, k_blk=None, out=None, se
                             _ptr(sel, "sel", sh["sel"], torch.int32),
                             _ptr(out, "out", sh["q"], prob.dtype), workspace.data_ptr(),
                             workspace.numel(), _stream(stream)))
+    return (out, sel) if return_sel else out
+
+
+# ----------------------------------------------------------------------------------------------
+# decode over a paged cache
+# ----------------------------------------------------------------------------------------------
+def _cache_shapes(p: Problem, c: Cache):
+    P = c.page_tokens
+    return dict(k_cache=(c.num_pages, p.kv_groups, P // 8, 8 * p.head_dim),
+                v_cache=(c.num_pages, p.kv_groups, P // 8, p.head_dim, 8),
+                kidx_cache=(c.num_pages, P, p.index_dim),
+                k_blk=(p.batch, c.max_pages * P // p.block, p.index_dim),
+                block_table=(p.batch, c.max_pages), seq_lens=(p.batch,))
+
+
+def alloc_cache(prob: Problem, cache: Cache, device) -> dict:
+    """Zero-filled cache pools and block keys for `cache` (device memory from torch)."""
+    sh = _cache_shapes(prob, cache)
+    return {name: torch.zeros(sh[name], dtype=torch.bfloat16, device=device)
+            for name in ("k_cache", "v_cache", "kidx_cache", "k_blk")}
+
+
+def cache_append(prob: Problem, cache: Cache, seq_lens, block_table, k_new, v_new, kidx_new,
+                 pools: dict, stream=None):
+    """Append k_new, v_new [Bt, G, n, D] and kidx_new [Bt, n, Di] at positions seq_lens - n ..
+    seq_lens - 1 and recompute the touched block keys.  `pools` as from alloc_cache."""
+    lib = load_library()
+    sh = _cache_shapes(prob, cache)
+    n = int(k_new.shape[2])
+    Bt, G, D, Di = prob.batch, prob.kv_groups, prob.head_dim, prob.index_dim
+    _check(lib.sgqa_cache_append(
+        ctypes.byref(prob._c()), ctypes.byref(cache._c()),
+        _ptr(seq_lens, "seq_lens", sh["seq_lens"], torch.int32),
+        _ptr(block_table, "block_table", sh["block_table"], torch.int32), n,
+        _ptr(k_new, "k_new", (Bt, G, n, D), torch.bfloat16),
+        _ptr(v_new, "v_new", (Bt, G, n, D), torch.bfloat16),
+        _ptr(kidx_new, "kidx_new", (Bt, n, Di), torch.bfloat16),
+        _ptr(pools["k_cache"], "k_cache", sh["k_cache"], torch.bfloat16),
+        _ptr(pools["v_cache"], "v_cache", sh["v_cache"], torch.bfloat16),
+        _ptr(pools["kidx_cache"], "kidx_cache", sh["kidx_cache"], torch.bfloat16),
+        _ptr(pools["k_blk"], "k_blk", sh["k_blk"], torch.bfloat16), _stream(stream)))
+
+
+def decode_workspace_size(prob: Problem, cache: Cache) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().sgqa_decode_workspace_size(ctypes.byref(prob._c()),
+                                                     ctypes.byref(cache._c()), ctypes.byref(n)))
+    return n.value
+
+
+def decode(prob: Problem, cache: Cache, seq_lens, block_table, q, gate, q_idx, pools: dict,
+           out=None, sel=None, return_sel=False, workspace=None, stream=None):
+    """Steps 2-4 for the prob.t_q newest tokens of every sequence over the paged cache."""
+    lib = load_library()
+    sh = _shapes(prob)
+    csh = _cache_shapes(prob, cache)
+    dev = q.device
+    if out is None:
+        out = torch.empty(sh["q"], dtype=torch.bfloat16, device=dev)
+    if sel is None and return_sel:
+        sel = torch.empty(sh["sel"], dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_size(prob, cache), dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_decode(
+        ctypes.byref(prob._c()), ctypes.byref(cache._c()),
+        _ptr(seq_lens, "seq_lens", csh["seq_lens"], torch.int32),
+        _ptr(block_table, "block_table", csh["block_table"], torch.int32),
+        _ptr(q, "q", sh["q"], torch.bfloat16), _ptr(gate, "gate", sh["q"], torch.bfloat16),
+        _ptr(q_idx, "q_idx", sh["q_idx"], torch.bfloat16),
+        _ptr(pools["k_cache"], "k_cache", csh["k_cache"], torch.bfloat16),
+        _ptr(pools["v_cache"], "v_cache", csh["v_cache"], torch.bfloat16),
+        _ptr(pools["k_blk"], "k_blk", csh["k_blk"], torch.bfloat16),
+        _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], torch.bfloat16),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return (out, sel) if return_sel else out

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsgqa.so")
 
-SOURCES = ["sgqa_api.cpp", "compress.hip", "index.hip", "topk.hip", "select_fused.hip", "attend.hip", "attend_split.hip"]
+SOURCES = ["sgqa_api.cpp", "compress.hip", "index.hip", "topk.hip", "select_fused.hip", "attend.hip",
+           "attend_split.hip", "paged.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

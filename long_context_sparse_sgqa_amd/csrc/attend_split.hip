@@ -65,6 +65,7 @@ struct UnionArgs {
   uint32_t* ulist;         // [Bt * G * ngroups][list_stride(umax)]
   int32_t* bounds;         // [Bt * G * ngroups][kRanges + 1]: first entry of each range, then end
   int64_t Tq, pos0, ngroups, total;
+  const int32_t* seq_len;  // per-sequence key counts, or null
   int G, NS, B, umax, words, waves;   // words: bitmap words per token (ceil(NU / 32))
 };
 
@@ -82,7 +83,8 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int64_t bg = gq / a.ngroups;
   const int64_t g = bg % a.G, b = bg / a.G;
   const int64_t tok0 = kTok * qi;
-  const int64_t u_end = group_u_end(a.pos0, tok0, a.Tq);
+  const int64_t pos0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq);
+  const int64_t u_end = group_u_end(pos0, tok0, a.Tq);
   const int nw = static_cast<int>((u_end + 31) >> 5);
   for (int w = lane; w < nw; w += 64) {
 #pragma unroll
@@ -92,7 +94,7 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int U = a.B >> 3;                               // units per block
   for (int t = 0; t < kTok; ++t) {
     if (tok0 + t >= a.Tq) break;
-    const int64_t p = a.pos0 + tok0 + t;
+    const int64_t p = pos0 + tok0 + t;
     const int64_t o = p / a.B, last_unit = p >> 3;
     const int32_t* selrow = a.sel + ((b * a.Tq + tok0 + t) * a.G + g) * a.NS;
     uint32_t* bmt = bm + t * a.words;
@@ -202,6 +204,12 @@ struct RangeArgs {
   int64_t Tq, Tk, NU, pos0, ngroups, wg_groups;
   int G, umax;
   float scale_log2e;
+  const int32_t* seq_len;      // per-sequence key counts, or null
+  // paged cache (kPaged): kp / vp are the page pools, unit u of sequence b lives in page
+  // block_table[b * max_pages + (u >> ul2)] at unit u & (2^ul2 - 1)
+  const int32_t* block_table;
+  int64_t max_pages, num_pages;
+  int ul2;
 };
 
 // K rows of the S^T product, permuted: output r' (0..15) of a lane in half h is C row
@@ -213,7 +221,7 @@ __device__ __forceinline__ int kq_slot(int i) {
 }
 __device__ __forceinline__ int kq_tok(int i) { return ((i >> 3) * 4 + (i & 3)) & 7; }
 
-template <int D>
+template <int D, bool kPaged>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_range_kernel(RangeArgs a) {
   constexpr int H = 8;
   constexpr int kQRow = D * 2 + 16;                      // padded LDS row of Q (bytes)
@@ -234,7 +242,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t gq = bg * a.ngroups + qi;
   const int64_t tok0 = kTok * qi;
   const bool rowvalid = tok0 + trow < a.Tq;
-  const int64_t pX = a.pos0 + tok0 + trow;
+  const int64_t pX = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + tok0 + trow;
 
   const uint32_t* list = a.ulist + gq * list_stride(a.umax);
   const int32_t* bnd = a.bounds + gq * (kRanges + 1);
@@ -264,12 +272,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // List entries are read with scalar loads (constant address space, wave-uniform, 16-byte aligned
   // because ranges start at multiples of 4): they count against lgkmcnt, so reading them never
   // waits behind the K/V loads in flight.  Entries at or past e1 read as 0 (unit 0, not chosen).
+  // On a paged cache the page of each entry's unit is looked up the same way, giving the unit's
+  // index in the pools (pu4).
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
-  auto chunk_entries = [&](int cpos, uint32_t* ent4) {
+  typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
+  const int32_t* btrow = kPaged ? a.block_table + b * a.max_pages : nullptr;
+  const uint32_t umask_pg = (1u << a.ul2) - 1u;
+  auto chunk_entries = [&](int cpos, uint32_t* ent4, uint32_t* pu4) {
     const u32x4 v = *((ConstQuadPtr)(list + cpos));
 #pragma unroll
     for (int j = 0; j < 4; ++j) ent4[j] = cpos < e1 ? v[j] : 0u;
+    if constexpr (kPaged) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u = ent4[j] & kUnitMask;
+        int64_t page = *((ConstIntPtr)(btrow + (u >> a.ul2)));
+        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+        pu4[j] = static_cast<uint32_t>(((page * a.G + g) << a.ul2) | (u & umask_pg));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pu4[j] = 0u;
+    }
   };
   auto pick4 = [](const uint32_t* v, int i) -> uint32_t {
     return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
@@ -278,20 +303,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // K operands of a chunk: A row c = token kq_tok(c) of unit slot kq_slot(c), d-half h.
   const int kslot = kq_slot(c), ktok = kq_tok(c);
   struct KRegs { bf16x8_t k[D / 16]; };
-  auto load_k = [&](const uint32_t* ent4, KRegs& R) {
-    const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
+  auto load_k = [&](const uint32_t* ent4, const uint32_t* pu4, KRegs& R) {
+    if constexpr (kPaged) {
+      const bf16_t* base = a.kp + static_cast<uint64_t>(pick4(pu4, kslot)) * (D * 8) + (ktok * 2 + h) * 8;
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
+      for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = load_bf16x8(base + kc * 128);
+    } else {
+      const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
+    }
   };
   // V^T operands of d-tile dt for the units of slot h (first product) and slot 2 + h (second).
   struct VRegs { bf16x8_t v[D / 16]; };
-  auto load_v = [&](const uint32_t* ent4, VRegs& R) {
-    const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
-    const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
+  auto load_v = [&](const uint32_t* ent4, const uint32_t* pu4, VRegs& R) {
+    if constexpr (kPaged) {
+      const bf16_t* va = a.vp + static_cast<uint64_t>(pick4(pu4, h)) * (D * 8) + c * 8;
+      const bf16_t* vb = a.vp + static_cast<uint64_t>(pick4(pu4, 2 + h)) * (D * 8) + c * 8;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      R.v[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
-      R.v[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        R.v[2 * dt] = load_bf16x8(va + 256 * dt);
+        R.v[2 * dt + 1] = load_bf16x8(vb + 256 * dt);
+      }
+    } else {
+      const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
+      const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        R.v[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
+        R.v[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
+      }
     }
   };
 
@@ -366,24 +407,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // waits then leave up to three chunks' worth of K/V in flight.
   if (e0 < e1) {
     uint32_t ec[4], e1c[4], e2c[4], e3c[4];           // entries of chunks x, x+4, x+8, x+12
-    chunk_entries(e0, ec);
-    chunk_entries(e0 + 4, e1c);
-    chunk_entries(e0 + 8, e2c);
+    uint32_t pc[4], p1c[4], p2c[4], p3c[4];           // their pool units (paged cache)
+    chunk_entries(e0, ec, pc);
+    chunk_entries(e0 + 4, e1c, p1c);
+    chunk_entries(e0 + 8, e2c, p2c);
     KRegs kA, kB;
     VRegs v0;
-    load_k(ec, kA);
-    load_k(e1c, kB);
+    load_k(ec, pc, kA);
+    load_k(e1c, p1c, kB);
     int nx = e0 + 12;                                  // next chunk whose entries are read
     auto step = [&](KRegs& K) {
-      chunk_entries(nx, e3c);                          // entries a chunk ahead of their use
+      chunk_entries(nx, e3c, p3c);                     // entries a chunk ahead of their use
       nx += 4;
-      load_v(ec, v0);
-      chunk(K, v0, ec, [&] { load_k(e2c, K); });
+      load_v(ec, pc, v0);
+      chunk(K, v0, ec, [&] { load_k(e2c, p2c, K); });
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ec[j] = e1c[j];
         e1c[j] = e2c[j];
         e2c[j] = e3c[j];
+        pc[j] = p1c[j];
+        p1c[j] = p2c[j];
+        p2c[j] = p3c[j];
       }
     };
     // the loop body is one period of the register rotation, so every trip enters with the same
@@ -504,7 +549,8 @@ size_t attend_split_bytes(const Dims& d) {
 
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
-                               const void* packed_v, void* ws, hipStream_t s, StageMark mark) {
+                               const void* packed_v, void* ws, hipStream_t s, StageMark mark,
+                               const PagedKV* paged) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
@@ -523,6 +569,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.bounds = bounds;
   ua.Tq = d.Tq;
   ua.pos0 = d.pos0;
+  ua.seq_len = d.seq_len;
   ua.ngroups = ng;
   ua.total = total;
   ua.G = d.G;
@@ -555,11 +602,30 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   a.G = d.G;
   a.umax = umax;
   a.scale_log2e = d.scale * 1.4426950408889634f;
+  a.seq_len = d.seq_len;
+  a.block_table = nullptr;
+  a.max_pages = a.num_pages = 0;
+  a.ul2 = 0;
+  if (paged) {
+    a.kp = static_cast<const bf16_t*>(paged->k);
+    a.vp = static_cast<const bf16_t*>(paged->v);
+    a.block_table = paged->block_table;
+    a.max_pages = paged->max_pages;
+    a.num_pages = paged->num_pages;
+    a.ul2 = paged->page_units_log2;
+  }
   const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
-  if (d.D == 128)
-    hipLaunchKernelGGL(attend_range_kernel<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(attend_range_kernel<64>, grid, dim3(256), 0, s, a);
+  if (paged) {
+    if (d.D == 128)
+      hipLaunchKernelGGL((attend_range_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_range_kernel<64, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (d.D == 128)
+      hipLaunchKernelGGL((attend_range_kernel<128, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_range_kernel<64, false>), grid, dim3(256), 0, s, a);
+  }
   e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(5, s);
   if (e != hipSuccess) return e;

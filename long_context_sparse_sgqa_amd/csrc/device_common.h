@@ -94,6 +94,17 @@ __device__ __forceinline__ bf16x8_t buffer_load_bf16x8(BufRsrc r, int byte_offse
 // result is the same softmax: O, l and m stay mutually consistent whatever reference m is used.
 constexpr float kLazyRescaleLog2 = 8.0f;
 
+// Position of query 0 of sequence b.  Equal-length sequences: pos0 = Tk - Tq.  With per-sequence
+// key counts (decode over a paged cache) the queries are the last Tq of seq_len[b] tokens; the
+// count is clamped to [Tq, Tk] so that a bad entry can never index outside the buffers.
+__device__ __forceinline__ int64_t seq_pos0(const int32_t* seq_len, int64_t b, int64_t pos0,
+                                            int64_t Tq) {
+  if (!seq_len) return pos0;
+  int64_t L = seq_len[b];
+  L = L < Tq ? Tq : (L > pos0 + Tq ? pos0 + Tq : L);
+  return L - Tq;
+}
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -24,6 +24,11 @@ constexpr int kColTile = 128;
 struct RowMap {
   int64_t b0, i0, ntok, Tq, pos0;
   int G, B;
+  const int32_t* seq_len;   // per-sequence key counts, or null (every sequence holds Tk keys)
+  // causal limit o = p / B of row (b, i)
+  __device__ __forceinline__ int64_t own_block(int64_t b, int64_t i) const {
+    return (seq_pos0(seq_len, b, pos0, Tq) + i) / B;
+  }
   // token coordinates of chunk row rr
   __device__ __forceinline__ void at(int64_t rr, int64_t& b, int64_t& i, int& g) const {
     const int64_t tok = rr / G;
@@ -36,8 +41,8 @@ struct RowMap {
 __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restrict__ q_idx,
                                                          const bf16_t* __restrict__ k_blk,
                                                          float* __restrict__ scores, RowMap map,
-                                                         int64_t NB, int Di, int64_t seq_rows,
-                                                         int64_t tiles_per_seq) {
+                                                         int64_t NB, int64_t kblk_stride, int Di,
+                                                         int64_t seq_rows, int64_t tiles_per_seq) {
   const int64_t seq = blockIdx.x / tiles_per_seq;
   const int64_t tile = blockIdx.x - seq * tiles_per_seq;
   const int64_t row0 = tile * kRowTile;                        // first row within the sequence
@@ -49,7 +54,7 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
     int64_t b, i;
     int g;
     map.at(seq * seq_rows + row0 + rows_here - 1, b, i, g);
-    const int64_t o_max = (map.pos0 + i) / map.B;
+    const int64_t o_max = map.own_block(b, i);
     if (col0 >= o_max) return;
   }
 
@@ -59,7 +64,7 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
   const int lr = lane & 15, lk = lane >> 4;
 
   const int64_t b_seq = map.b0 + seq;
-  const bf16_t* kb = k_blk + b_seq * NB * Di;
+  const bf16_t* kb = k_blk + b_seq * kblk_stride * Di;
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -84,7 +89,7 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int64_t j = col0 + wc * 64 + n * 16 + lr;
-    bvalid[n] = j < NB;
+    bvalid[n] = j < NB;                 // NB <= kblk_stride
     brow[n] = kb + (bvalid[n] ? j : 0) * Di;
   }
 
@@ -111,7 +116,7 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
       int g;
       const int64_t rr = seq * seq_rows + rl;
       map.at(rr, b, i, g);
-      const int64_t o = (map.pos0 + i) / map.B;
+      const int64_t o = map.own_block(b, i);
       float* dst = scores + rr * NB;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -125,15 +130,16 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
 __global__ void __launch_bounds__(256) index_f32_kernel(const float* __restrict__ q_idx,
                                                         const float* __restrict__ k_blk,
                                                         float* __restrict__ scores, RowMap map,
-                                                        int64_t NB, int Di, int64_t rows) {
+                                                        int64_t NB, int64_t kblk_stride, int Di,
+                                                        int64_t rows) {
   const int64_t rr = blockIdx.x;
   if (rr >= rows) return;
   int64_t b, i;
   int g;
   map.at(rr, b, i, g);
-  const int64_t o = (map.pos0 + i) / map.B;
+  const int64_t o = map.own_block(b, i);
   const float* q = q_idx + ((b * map.Tq + i) * map.G + g) * Di;
-  const float* kb = k_blk + b * NB * Di;
+  const float* kb = k_blk + b * kblk_stride * Di;
   for (int64_t j = blockIdx.y * (int64_t)blockDim.x + threadIdx.x; j < o;
        j += (int64_t)gridDim.y * blockDim.x) {
     const float* kr = kb + j * Di;
@@ -147,7 +153,8 @@ __global__ void __launch_bounds__(256) index_f32_kernel(const float* __restrict_
 
 hipError_t launch_index(const Dims& d, const void* q_idx, const void* k_blk, float* scores,
                         const Chunk& c, hipStream_t s) {
-  RowMap map{c.b0, c.i0, c.ntok, d.Tq, d.pos0, d.G, d.B};
+  RowMap map{c.b0, c.i0, c.ntok, d.Tq, d.pos0, d.G, d.B, d.seq_len};
+  const int64_t kstride = d.kblk_stride > 0 ? d.kblk_stride : d.NB;
   const int64_t rows = c.rows(d.G);
   if (rows == 0) return hipSuccess;
   if (d.idx_bf16) {
@@ -157,14 +164,14 @@ hipError_t launch_index(const Dims& d, const void* q_idx, const void* k_blk, flo
     dim3 grid(static_cast<unsigned>(tps * c.nseq), static_cast<unsigned>(col_tiles));
     hipLaunchKernelGGL(index_bf16_kernel, grid, dim3(256), 0, s,
                        static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), scores,
-                       map, d.NB, d.Di, seq_rows, tps);
+                       map, d.NB, kstride, d.Di, seq_rows, tps);
   } else {
     const int64_t max_o = (d.Tk - 1) / d.B;
     int64_t gy = (max_o + 255) / 256;
     gy = gy < 1 ? 1 : (gy > 1024 ? 1024 : gy);
     dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>(gy));
     hipLaunchKernelGGL(index_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(q_idx),
-                       static_cast<const float*>(k_blk), scores, map, d.NB, d.Di, rows);
+                       static_cast<const float*>(k_blk), scores, map, d.NB, kstride, d.Di, rows);
   }
   return hipGetLastError();
 }

@@ -136,7 +136,7 @@ struct ForwardLayout {
   size_t off_sel, off_failcnt, off_scratch, off_chunk;
   size_t fixed;           // bytes before the per-chunk area
   size_t per_token;       // per-chunk bytes per query token (all groups)
-  size_t cand_bytes, cnt_bytes;   // per token, fused path
+  size_t cand_bytes, cnt_bytes, fail_bytes;   // per token, fused path
 };
 
 ForwardLayout forward_layout(const Derived& dv) {
@@ -153,7 +153,8 @@ ForwardLayout forward_layout(const Derived& dv) {
     off += align_up(sgqa::select_fallback_scratch_bytes(d));
     L.cand_bytes = static_cast<size_t>(d.G) * sgqa::fused_select_capacity() * sizeof(uint64_t);
     L.cnt_bytes = static_cast<size_t>(d.G) * sizeof(int32_t);
-    L.per_token = L.cand_bytes + 2 * L.cnt_bytes;     // cand + cnt + fail list
+    L.fail_bytes = static_cast<size_t>(d.G) * sizeof(int32_t);
+    L.per_token = L.cand_bytes + L.cnt_bytes + L.fail_bytes;
   } else {
     L.per_token = dv.score_row_bytes;
   }
@@ -165,7 +166,7 @@ ForwardLayout forward_layout(const Derived& dv) {
 // Bytes of the per-chunk area for `tok` tokens (each sub-array aligned).
 size_t chunk_bytes(const ForwardLayout& L, int64_t tok) {
   const size_t t = static_cast<size_t>(tok);
-  if (L.fused) return align_up(t * L.cand_bytes) + 2 * align_up(t * L.cnt_bytes);
+  if (L.fused) return align_up(t * L.cand_bytes) + align_up(t * L.cnt_bytes) + align_up(t * L.fail_bytes);
   return align_up(t * L.per_token);
 }
 
@@ -188,10 +189,10 @@ int64_t forward_chunk_tokens(const Derived& dv, const ForwardLayout& L, size_t w
   return chunk;
 }
 
-sgqa_status check_ptr(const void* p, const char* name) {
+sgqa_status check_ptr(const void* p, const char* name, unsigned align = 16) {
   if (!p) return fail(SGQA_ERR_NULL, "%s is NULL", name);
-  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-    return fail(SGQA_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(SGQA_ERR_ALIGN, "%s is not %u-byte aligned", name, align);
   return SGQA_OK;
 }
 
@@ -271,6 +272,60 @@ sgqa_status select_chunked(const sgqa::Dims& d, const ForwardLayout& L, char* ws
     if (e != hipSuccess) return hip_fail(e, "select fallback launch");
     return SGQA_OK;
   });
+}
+
+// ---- decode over a paged cache ------------------------------------------------------------------
+struct DecodeDerived {
+  Derived dv;
+  sgqa::PagedKV pk;
+  size_t scores_bytes, sel_bytes, attend_bytes;
+};
+
+sgqa_status derive_cache(const sgqa_problem* prob, const sgqa_cache* cache, DecodeDerived* out) {
+  SGQA_CHECK(derive(prob, &out->dv));
+  sgqa::Dims& d = out->dv.d;
+  if (!cache) return fail(SGQA_ERR_NULL, "cache descriptor is NULL");
+  const int64_t P = cache->page_tokens;
+  if (P < 8 || (P & (P - 1)) != 0 || P % d.B != 0)
+    return fail(SGQA_ERR_SHAPE, "page_tokens must be a power of two, >= 8 and a multiple of block "
+                "(got %lld, block %d)", (long long)P, d.B);
+  if (cache->num_pages < 1 || cache->max_pages < 1)
+    return fail(SGQA_ERR_SHAPE, "num_pages and max_pages must be >= 1");
+  int64_t x;
+  if (!mul_ok(cache->max_pages, P, &x) || x < d.Tk)
+    return fail(SGQA_ERR_SHAPE, "max_pages * page_tokens (%lld) must cover t_kv (%lld)",
+                (long long)x, (long long)d.Tk);
+  if (!mul_ok(cache->num_pages, d.G, &x) || !mul_ok(x, P / 8, &x) || x >= (int64_t(1) << 32))
+    return fail(SGQA_ERR_UNSUPPORTED, "num_pages * kv_groups * page_tokens / 8 must be < 2^32");
+  if (!(d.bf16 && d.idx_bf16))
+    return fail(SGQA_ERR_UNSUPPORTED, "the paged cache holds bf16 data (dtype and index_dtype)");
+  if (d.B % 8 != 0)
+    return fail(SGQA_ERR_UNSUPPORTED, "the paged cache needs block to be a multiple of 8 (got %d)", d.B);
+  int l2 = 0;
+  while ((int64_t(8) << l2) < P) ++l2;
+  out->pk.k = out->pk.v = nullptr;
+  out->pk.block_table = nullptr;
+  out->pk.num_pages = cache->num_pages;
+  out->pk.max_pages = cache->max_pages;
+  out->pk.page_units_log2 = l2;
+  d.kblk_stride = cache->max_pages * P / d.B;
+  return SGQA_OK;
+}
+
+sgqa_status derive_decode(const sgqa_problem* prob, const sgqa_cache* cache, DecodeDerived* out) {
+  SGQA_CHECK(derive_cache(prob, cache, out));
+  const sgqa::Dims& d = out->dv.d;
+  if (!sgqa::attend_split_supported(d))
+    return fail(SGQA_ERR_UNSUPPORTED, "decode needs heads_per_group == 8, head_dim 64 or 128 and "
+                "topk_tokens / block small enough for the grouped attention kernel");
+  out->scores_bytes = out->dv.scores_bytes;
+  out->sel_bytes = out->dv.sel_bytes;
+  out->attend_bytes = sgqa::attend_split_bytes(d);
+  return SGQA_OK;
+}
+
+size_t decode_workspace(const DecodeDerived& dd) {
+  return align_up(dd.scores_bytes) + align_up(dd.sel_bytes) + align_up(dd.attend_bytes);
 }
 
 }  // namespace
@@ -411,6 +466,94 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
   SGQA_CHECK(mark_stage(3, s));
   e = sgqa::launch_attend_packed(d, q, k, v, gate, sel, out, attend_ws, s,
                                  g_stage_armed ? mark_stage_hip : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  SGQA_CHECK(mark_stage(6, s));
+  return ok();
+}
+
+sgqa_status sgqa_cache_append(const sgqa_problem* prob, const sgqa_cache* cache,
+                              const int32_t* seq_lens, const int32_t* block_table, int64_t n_new,
+                              const void* k_new, const void* v_new, const void* kidx_new,
+                              void* k_cache, void* v_cache, void* kidx_cache, void* k_blk,
+                              void* stream) {
+  DecodeDerived dd;
+  SGQA_CHECK(derive_cache(prob, cache, &dd));
+  sgqa::Dims d = dd.dv.d;
+  if (n_new < 1 || n_new > d.Tk)
+    return fail(SGQA_ERR_SHAPE, "n_new must be in [1, t_kv] (got %lld)", (long long)n_new);
+  SGQA_CHECK(check_ptr(seq_lens, "seq_lens", 4));
+  SGQA_CHECK(check_ptr(block_table, "block_table", 4));
+  SGQA_CHECK(check_ptr(k_new, "k_new"));
+  SGQA_CHECK(check_ptr(v_new, "v_new"));
+  SGQA_CHECK(check_ptr(kidx_new, "kidx_new"));
+  SGQA_CHECK(check_ptr(k_cache, "k_cache"));
+  SGQA_CHECK(check_ptr(v_cache, "v_cache"));
+  SGQA_CHECK(check_ptr(kidx_cache, "kidx_cache"));
+  SGQA_CHECK(check_ptr(k_blk, "k_blk"));
+  d.seq_len = seq_lens;
+  sgqa::PagedKV pk = dd.pk;
+  pk.k = k_cache;
+  pk.v = v_cache;
+  pk.block_table = block_table;
+  hipError_t e = sgqa::launch_cache_append(d, pk, n_new, k_new, v_new, kidx_new, kidx_cache, k_blk,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  return ok();
+}
+
+sgqa_status sgqa_decode_workspace_size(const sgqa_problem* prob, const sgqa_cache* cache,
+                                       size_t* bytes) {
+  DecodeDerived dd;
+  SGQA_CHECK(derive_decode(prob, cache, &dd));
+  if (!bytes) return fail(SGQA_ERR_NULL, "bytes is NULL");
+  *bytes = decode_workspace(dd);
+  return ok();
+}
+
+sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
+                        const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                        const void* gate, const void* q_idx, const void* k_cache,
+                        const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeDerived dd;
+  SGQA_CHECK(derive_decode(prob, cache, &dd));
+  SGQA_CHECK(check_ptr(seq_lens, "seq_lens", 4));
+  SGQA_CHECK(check_ptr(block_table, "block_table", 4));
+  SGQA_CHECK(check_ptr(q, "q"));
+  SGQA_CHECK(check_ptr(gate, "gate"));
+  SGQA_CHECK(check_ptr(q_idx, "q_idx"));
+  SGQA_CHECK(check_ptr(k_cache, "k_cache"));
+  SGQA_CHECK(check_ptr(v_cache, "v_cache"));
+  SGQA_CHECK(check_ptr(k_blk, "k_blk"));
+  SGQA_CHECK(check_ptr(out, "out"));
+  if (sel_out) SGQA_CHECK(check_ptr(sel_out, "sel_out"));
+  SGQA_CHECK(check_ptr(workspace, "workspace"));
+  const size_t need = decode_workspace(dd);
+  if (workspace_bytes < need)
+    return fail(SGQA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  sgqa::Dims d = dd.dv.d;
+  d.seq_len = seq_lens;
+  sgqa::PagedKV pk = dd.pk;
+  pk.k = k_cache;
+  pk.v = v_cache;
+  pk.block_table = block_table;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + align_up(dd.scores_bytes));
+  void* attend_ws = ws + align_up(dd.scores_bytes) + align_up(dd.sel_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const sgqa::Chunk c{0, d.Bt, 0, d.Tq};
+  SGQA_CHECK(mark_stage(0, s));
+  hipError_t e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  SGQA_CHECK(mark_stage(1, s));
+  e = sgqa::launch_topk(d, scores, sel, c, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  SGQA_CHECK(mark_stage(2, s));
+  SGQA_CHECK(mark_stage(3, s));
+  e = sgqa::launch_attend_split(d, q, nullptr, gate, sel, out, nullptr, attend_ws, s,
+                                g_stage_armed ? mark_stage_hip : nullptr, &pk);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   SGQA_CHECK(mark_stage(6, s));
   return ok();

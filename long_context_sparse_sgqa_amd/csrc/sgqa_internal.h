@@ -19,7 +19,30 @@ struct Dims {
   float scale;           // softmax scale
   bool bf16;             // q/k/v/gate/out are bf16 (else fp32)
   bool idx_bf16;         // q_idx/k_idx/k_blk are bf16 (else fp32)
+  // Decode over a paged cache: per-sequence key counts (device, nullable: all sequences hold Tk
+  // keys) and the k_blk row stride in blocks (NB for the contiguous layout).
+  const int32_t* seq_len = nullptr;
+  int64_t kblk_stride = 0;
 };
+
+// Paged K/V cache (decode).  Page p of the pools holds page_tokens consecutive tokens of one
+// sequence for every KV group: K as [G][page_tokens / 8] units in the 4-token operand layout
+// (kq_offset), V as [G][page_tokens / 8][D][8].  Logical page j of sequence b is
+// block_table[b * max_pages + j].
+struct PagedKV {
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  int64_t num_pages, max_pages;
+  int page_units_log2;   // log2(page_tokens / 8)
+};
+
+// ---- decode: appending to the paged cache ----------------------------------------------------
+// Writes n_new tokens per sequence (ending at d.seq_len[b]) into the K/V pools of `pk` and the
+// index-key pool, then recomputes the touched block keys in k_blk (row stride d.kblk_stride).
+hipError_t launch_cache_append(const Dims& d, const PagedKV& pk, int64_t n_new, const void* k_new,
+                               const void* v_new, const void* kidx_new, void* kidx_pool,
+                               void* k_blk, hipStream_t s);
 
 // ---- step 1: block compression -------------------------------------------------------------
 hipError_t launch_compress(const Dims& d, const void* k_idx, void* k_blk, hipStream_t s);
@@ -49,9 +72,9 @@ hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const C
 // budgets up to 513 blocks).
 int fused_select_capacity();
 bool fused_select_supported(const Dims& d);
-// Filter: per chunk row, the (key << 32 | block) candidates at or above a sampled threshold, in
-// ascending block order, into cand + rr * capacity (count in cnt[rr], possibly > capacity).  Also
-// zeroes *fail_count.
+// Filter: per chunk row, the (score bits << 32 | block) candidates at or above a sampled
+// threshold, in no particular order, into cand + rr * capacity (count in cnt[rr], possibly
+// > capacity).  Also zeroes *fail_count.
 hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
                                int32_t* cnt, int32_t* fail_count, const Chunk& c, hipStream_t s);
 // Select from the candidates; rows it cannot settle are appended to fail_list.
@@ -86,9 +109,12 @@ using StageMark = hipError_t (*)(int index, hipStream_t s);
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
                                 const void* gate, const int32_t* sel, void* out, void* workspace,
                                 hipStream_t s, StageMark mark = nullptr);
+// With `paged`, K and V come from the paged cache (packed_k / packed_v are ignored) and query
+// positions follow d.seq_len.
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
-                               const void* packed_v, void* ws, hipStream_t s, StageMark mark);
+                               const void* packed_v, void* ws, hipStream_t s, StageMark mark,
+                               const PagedKV* paged = nullptr);
 // Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
                          const void* gate, const int32_t* sel, void* out, void* workspace,

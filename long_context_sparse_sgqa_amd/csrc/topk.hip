@@ -159,15 +159,15 @@ __device__ int emit_selected(const Src& src, int n, uint32_t tau, int take_eq, i
 __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ scores,
                                                         int32_t* __restrict__ sel, int64_t NB,
                                                         int NS, int B, int G, int64_t Tq,
-                                                        int64_t pos0, int64_t b0, int64_t i0,
-                                                        int64_t ntok) {
+                                                        int64_t pos0, const int32_t* seq_len,
+                                                        int64_t b0, int64_t i0, int64_t ntok) {
   __shared__ TopkShared sh;
   const int64_t rr = blockIdx.x;
   const int64_t tok = rr / G;
   const int g = static_cast<int>(rr - tok * G);
   const int64_t b = b0 + tok / ntok;
   const int64_t i = i0 + tok % ntok;
-  const int64_t p = pos0 + i;
+  const int64_t p = seq_pos0(seq_len, b, pos0, Tq) + i;
   const int64_t o = p / B;
   int32_t* out = sel + ((b * Tq + i) * G + g) * NS;
   const int t = threadIdx.x;
@@ -315,7 +315,7 @@ hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const C
   const int64_t rows = c.rows(d.G);
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, s, scores,
-                     sel, d.NB, d.NS, d.B, d.G, d.Tq, d.pos0, c.b0, c.i0, c.ntok);
+                     sel, d.NB, d.NS, d.B, d.G, d.Tq, d.pos0, d.seq_len, c.b0, c.i0, c.ntok);
   return hipGetLastError();
 }
 

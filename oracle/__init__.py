@@ -17,4 +17,5 @@ from .sgqa_oracle import (  # noqa: F401
     forward,
     scored_candidates,
     inclusion_rate,
+    sequence_rows,
 )

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "num_blocks", "n_selected_blocks", "query_positions", "compress", "block_scores",
     "select_blocks", "attended_tokens", "gated_attention", "forward_rows", "forward",
-    "scored_candidates", "inclusion_rate",
+    "scored_candidates", "inclusion_rate", "sequence_rows",
 ]
 
 
@@ -220,6 +220,34 @@ def forward(inputs, block: int, topk_tokens: int, scale: float):
     h, d = out.shape[2], out.shape[3]
     k_blk = np.stack([kblk[b] for b in range(bt)])
     return sel.reshape(bt, t_q, G, n_sel), out.reshape(bt, t_q, G, h, d), k_blk
+
+
+def sequence_rows(inputs, seq_lens, block: int, topk_tokens: int, scale: float, rows):
+    """Rows of sequences that hold different numbers of tokens (decode over a cache).
+
+    Sequence b holds seq_lens[b] tokens: its keys, values and index keys are the first seq_lens[b]
+    of inputs' k, v, k_idx (anything past them is not part of the sequence), and its t_q queries
+    are the last t_q positions of those tokens (reading 10 applied per sequence).  Each sequence is
+    therefore the forward path on its own prefix; the rows (b, i) are computed that way.
+    Returns (sel [n, G, n_sel], out [n, G, h, d], {b: K_blk[b]}) like forward_rows.
+    """
+    rows = list(rows)
+    G, n_sel = inputs["q_idx"].shape[2], n_selected_blocks(topk_tokens, block)
+    h, d = inputs["q"].shape[3], inputs["q"].shape[4]
+    sel_out = np.full((len(rows), G, n_sel), -1, dtype=np.int64)
+    out = np.zeros((len(rows), G, h, d), dtype=np.float64)
+    kblk = {}
+    for b in sorted({b for b, _ in rows}):
+        L = int(seq_lens[b])
+        seq = {"q": inputs["q"][b:b + 1], "gate": inputs["gate"][b:b + 1],
+               "q_idx": inputs["q_idx"][b:b + 1], "k": inputs["k"][b:b + 1, :, :L],
+               "v": inputs["v"][b:b + 1, :, :L], "k_idx": inputs["k_idx"][b:b + 1, :L]}
+        mine = [r for r, (bb, _) in enumerate(rows) if bb == b]
+        s_b, o_b, kb = forward_rows(seq, block, topk_tokens, scale, [(0, rows[r][1]) for r in mine])
+        sel_out[mine] = s_b
+        out[mine] = o_b
+        kblk[b] = kb[0]
+    return sel_out, out, kblk
 
 
 # ----------------------------------------------------------------------------------------------

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert sg.abi_version() == 1
+    assert sg.abi_version() == 2
     assert lib.sgqa_status_string(0) == b"ok"
     assert lib.sgqa_status_string(ERR_WORKSPACE) == b"workspace too small"
 
@@ -101,3 +101,63 @@ def test_null_misaligned_and_workspace_errors(lib):
     P = sg.Problem(1, 64, 64, 2, 8, 128, 128, 3, 24)._c()   # B=3: selection fine, attention not
     assert lib.sgqa_attend(ctypes.byref(P), *([good] * 7), 1 << 20, None) == ERR_UNSUPPORTED
     assert lib.sgqa_topk(None, good, good, None) == ERR_NULL
+
+
+# ----------------------------------------------------------------------------------------------
+# decode over a paged cache: host-side validation and sizes
+# ----------------------------------------------------------------------------------------------
+def _dprob(**kw):
+    base = dict(batch=64, t_q=4, t_kv=262148, kv_groups=8, heads_per_group=8, head_dim=128,
+                index_dim=128, block=8, topk_tokens=4096)
+    base.update(kw)
+    return sg.Problem(**base)
+
+
+def test_decode_workspace_size_decode_workload(lib):
+    cache = sg.Cache(64 * 4097, 64, 4097)
+    n = sg.decode_workspace_size(_dprob(), cache)
+    rows = 64 * 4 * 8
+    scores = rows * 32769 * 4
+    assert scores + rows * 512 * 4 < n < scores + (64 << 20)   # scores, sel, lists and partials
+
+
+@pytest.mark.parametrize("cache,kw,status", [
+    ((40, 48, 6000), {}, ERR_SHAPE),                  # page not a power of two
+    ((40, 4, 70000), {}, ERR_SHAPE),                  # page smaller than 8 tokens
+    ((40, 64, 100), {}, ERR_SHAPE),                   # max_pages * page < t_kv
+    ((0, 64, 4097), {}, ERR_SHAPE),
+    ((64 * 4097, 64, 4097), dict(dtype=torch.float32), ERR_UNSUPPORTED),
+    ((64 * 4097, 64, 4097), dict(heads_per_group=4), ERR_UNSUPPORTED),
+    ((64 * 4097, 64, 4097), dict(block=4, topk_tokens=2048), ERR_UNSUPPORTED),
+    ((1 << 30, 64, 4097), {}, ERR_UNSUPPORTED),       # pool units past 2^32
+])
+def test_decode_rejects(lib, cache, kw, status):
+    with pytest.raises(sg.SgqaError) as e:
+        sg.decode_workspace_size(_dprob(**kw), sg.Cache(*cache))
+    assert e.value.status == status
+    assert lib.sgqa_last_error()
+
+
+def test_decode_and_append_null_and_workspace_errors(lib):
+    """Bogus (never dereferenced) addresses: validation fails before any device access."""
+    P = _dprob()._c()
+    C = sg.Cache(64 * 4097, 64, 4097)._c()
+    good = 0x10000
+    # seq_lens block_table q gate q_idx k_cache v_cache k_blk sel out workspace
+    ptrs = [good] * 11
+    assert lib.sgqa_decode(ctypes.byref(P), ctypes.byref(C), *ptrs, 16, None) == ERR_WORKSPACE
+    ptrs[0] = None
+    assert lib.sgqa_decode(ctypes.byref(P), ctypes.byref(C), *ptrs, 1 << 40, None) == ERR_NULL
+    ptrs[0] = good + 2
+    assert lib.sgqa_decode(ctypes.byref(P), ctypes.byref(C), *ptrs, 1 << 40, None) == ERR_ALIGN
+    ptrs[0] = good
+    ptrs[2] = good + 4                                  # q needs 16 bytes
+    assert lib.sgqa_decode(ctypes.byref(P), ctypes.byref(C), *ptrs, 1 << 40, None) == ERR_ALIGN
+    assert lib.sgqa_decode(ctypes.byref(P), None, *([good] * 11), 1 << 40, None) == ERR_NULL
+    # seq_lens block_table n_new k_new v_new kidx_new k_cache v_cache kidx_cache k_blk
+    app = [good, good, 4] + [good] * 7
+    app[2] = 0
+    assert lib.sgqa_cache_append(ctypes.byref(P), ctypes.byref(C), *app, None) == ERR_SHAPE
+    app[2] = 4
+    app[3] = None
+    assert lib.sgqa_cache_append(ctypes.byref(P), ctypes.byref(C), *app, None) == ERR_NULL

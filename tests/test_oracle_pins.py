@@ -347,3 +347,53 @@ def test_inclusion_rate_edge_cases():
     assert np.all(dense == 1.0)          # a dense selection includes everything
     r = oracle.inclusion_rate(inp["q_idx"], inp["k_idx"], rows, 64, (8, 16), (1, 16))
     assert np.all((r >= 0) & (r <= 1)) and r.min() < 1.0
+
+
+# ----------------------------------------------------------------------------------------------
+# sequences of different lengths (decode over a cache)
+# ----------------------------------------------------------------------------------------------
+def test_sequence_rows_equal_lengths_is_forward():
+    """With every sequence holding all t_kv tokens, the per-sequence reading is the forward's."""
+    w, inp = generate_small(t_q=5, t_kv=90, groups=2, heads=2, head_dim=8, index_dim=4, block=8,
+                            topk=32, seed=21, batch=3)
+    rows = [(b, i) for b in range(3) for i in range(5)]
+    s_ref, o_ref, _ = oracle.forward_rows(inp, w.block, w.topk, w.softmax_scale, rows)
+    s, o, _ = oracle.sequence_rows(inp, [90, 90, 90], w.block, w.topk, w.softmax_scale, rows)
+    assert np.array_equal(s, s_ref)
+    np.testing.assert_array_equal(o, o_ref)
+
+
+def test_sequence_rows_dense_equals_sdpa_on_prefix():
+    """Budget covering the context: each sequence's queries are the last t_q of its own L tokens,
+    so the result is dense SDPA over k[:, :L] with a bottom-right causal mask (torch, fp64)."""
+    t_q, t_kv = 4, 70
+    w, inp = generate_small(t_q=t_q, t_kv=t_kv, groups=2, heads=3, head_dim=8, index_dim=4,
+                            block=8, topk=128, seed=5, batch=3)
+    lens = [70, 41, 9]
+    rows = [(b, i) for b in range(3) for i in range(t_q)]
+    _, out, _ = oracle.sequence_rows(inp, lens, w.block, w.topk, w.softmax_scale, rows)
+    for b, L in enumerate(lens):
+        sub = {"q": inp["q"][b:b + 1], "gate": inp["gate"][b:b + 1],
+               "k": inp["k"][b:b + 1, :, :L], "v": inp["v"][b:b + 1, :, :L]}
+        pos = torch.arange(L - t_q, L)
+        mask = torch.arange(L)[None, :] <= pos[:, None]
+        ref = _sdpa_reference(sub, mask, w.softmax_scale)[0]
+        np.testing.assert_allclose(out[b * t_q:(b + 1) * t_q], ref, rtol=0, atol=1e-12)
+
+
+def test_sequence_rows_ignore_tokens_past_length():
+    """Keys, values and index keys past a sequence's length do not change its rows."""
+    w, inp = generate_small(t_q=3, t_kv=120, groups=2, heads=2, head_dim=8, index_dim=4, block=8,
+                            topk=32, seed=8, batch=2)
+    lens = [120, 77]
+    rows = [(b, i) for b in range(2) for i in range(3)]
+    s1, o1, k1 = oracle.sequence_rows(inp, lens, w.block, w.topk, w.softmax_scale, rows)
+    other = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    other["k"][1, :, 77:] = 100.0
+    other["v"][1, :, 77:] = -100.0
+    other["k_idx"][1, 77:] = 4.0
+    s2, o2, k2 = oracle.sequence_rows(other, lens, w.block, w.topk, w.softmax_scale, rows)
+    assert np.array_equal(s1, s2)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(k1[1], k2[1])
+    assert k1[1].shape[0] == -(-77 // 8)
