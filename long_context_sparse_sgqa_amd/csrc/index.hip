@@ -127,6 +127,65 @@ __global__ void __launch_bounds__(256) index_bf16_kernel(const bf16_t* __restric
   }
 }
 
+// Few rows per sequence (decode: 4 new tokens x 8 groups): all of a sequence's rows (<= 32) form
+// the M = 32 side of v_mfma_f32_32x32x16_bf16 and a workgroup sweeps a slab of blocks, 32 columns
+// per wave per step, so every block key is read once.  Lane (c, h) feeds query row c and block
+// col0 + c (index dims 16 kc + 8 h ..), and receives rows 8 (r/4) + 4h + r%4 of column c.
+template <int DI>
+__global__ void __launch_bounds__(256) index_rows32_kernel(const bf16_t* __restrict__ q_idx,
+                                                           const bf16_t* __restrict__ k_blk,
+                                                           float* __restrict__ scores, RowMap map,
+                                                           int64_t NB, int64_t kblk_stride,
+                                                           int64_t seq_rows, int64_t slab_cols) {
+  const int64_t seq = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  int64_t b, i;
+  int g;
+  map.at(seq * seq_rows + seq_rows - 1, b, i, g);
+  const int64_t o_max = map.own_block(b, i);
+  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * slab_cols;
+  const int64_t c_end = min(c_begin + slab_cols, o_max);
+  if (c_begin >= c_end) return;
+
+  bf16x8_t qa[DI / 16];
+  {
+    const bool ok = c < seq_rows;
+    map.at(seq * seq_rows + (ok ? c : 0), b, i, g);
+    const bf16_t* qrow = q_idx + ((b * map.Tq + i) * map.G + g) * DI;
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc) qa[kc] = ok ? load_bf16x8(qrow + 16 * kc + 8 * h) : zero_bf16x8();
+  }
+  // causal limit and score row of each output row of this lane (o = 0 past the sequence's rows)
+  int32_t o_r[16];
+  float* dst_r[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+    const bool ok = row < seq_rows;
+    const int64_t rr = seq * seq_rows + (ok ? row : 0);
+    map.at(rr, b, i, g);
+    o_r[r] = ok ? static_cast<int32_t>(map.own_block(b, i)) : 0;
+    dst_r[r] = scores + rr * NB;
+  }
+  map.at(seq * seq_rows, b, i, g);
+  const bf16_t* kb = k_blk + b * kblk_stride * DI;
+  for (int64_t col0 = c_begin + 32 * wave; col0 < c_end; col0 += 128) {
+    const int64_t col = col0 + c;
+    const bool ok = col < NB;
+    bf16x8_t kk[DI / 16];
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc)
+      kk[kc] = ok ? load_bf16x8(kb + col * DI + 16 * kc + 8 * h) : zero_bf16x8();
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], kk[kc], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (col < o_r[r]) dst_r[r][col] = acc[r];
+  }
+}
+
 __global__ void __launch_bounds__(256) index_f32_kernel(const float* __restrict__ q_idx,
                                                         const float* __restrict__ k_blk,
                                                         float* __restrict__ scores, RowMap map,
@@ -157,7 +216,26 @@ hipError_t launch_index(const Dims& d, const void* q_idx, const void* k_blk, flo
   const int64_t kstride = d.kblk_stride > 0 ? d.kblk_stride : d.NB;
   const int64_t rows = c.rows(d.G);
   if (rows == 0) return hipSuccess;
-  if (d.idx_bf16) {
+  if (d.idx_bf16 && c.ntok * d.G <= 32) {
+    const int64_t seq_rows = c.ntok * d.G;
+    const int64_t slab = 1024;
+    const int64_t max_o = (d.Tk - 1) / d.B;                  // no query has a past block: no scores
+    const dim3 grid(static_cast<unsigned>((max_o + slab - 1) / slab), static_cast<unsigned>(c.nseq));
+    if (max_o == 0)
+      return hipSuccess;
+    else if (d.Di == 128)
+      hipLaunchKernelGGL(index_rows32_kernel<128>, grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), scores,
+                         map, d.NB, kstride, seq_rows, slab);
+    else if (d.Di == 64)
+      hipLaunchKernelGGL(index_rows32_kernel<64>, grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), scores,
+                         map, d.NB, kstride, seq_rows, slab);
+    else
+      hipLaunchKernelGGL(index_rows32_kernel<32>, grid, dim3(256), 0, s,
+                         static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), scores,
+                         map, d.NB, kstride, seq_rows, slab);
+  } else if (d.idx_bf16) {
     const int64_t seq_rows = c.ntok * d.G;
     const int64_t tps = (seq_rows + kRowTile - 1) / kRowTile;
     const int64_t col_tiles = (d.NB + kColTile - 1) / kColTile;

@@ -200,17 +200,27 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
     const int lo = wave * per_wave;
     const int hi = min(n, lo + per_wave);
     int cnt = 0;
-    for (int x0 = lo; x0 < hi; x0 += 64) {
-      const int x = x0 + lane;
-      const uint32_t k = (x < hi) ? row.key(x) : 0u;
-      const bool keep = (x < hi) && k >= guess;
-      const uint64_t bal = __ballot(keep);
-      const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-      if (keep && pos < kSegCap) {
-        sh.key[wave * kSegCap + pos] = k;
-        sh.idx[wave * kSegCap + pos] = x;
+    // kUnroll loads in flight per lane, then the survivors of each 64-wide step in index order
+    constexpr int kUnroll = 8;
+    for (int x0 = lo; x0 < hi; x0 += 64 * kUnroll) {
+      uint32_t k[kUnroll];
+#pragma unroll
+      for (int e = 0; e < kUnroll; ++e) {
+        const int x = x0 + 64 * e + lane;
+        k[e] = (x < hi) ? row.key(x) : 0u;
       }
-      cnt += __popcll(bal);
+#pragma unroll
+      for (int e = 0; e < kUnroll; ++e) {
+        const int x = x0 + 64 * e + lane;
+        const bool keep = (x < hi) && k[e] >= guess;
+        const uint64_t bal = __ballot(keep);
+        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+        if (keep && pos < kSegCap) {
+          sh.key[wave * kSegCap + pos] = k[e];
+          sh.idx[wave * kSegCap + pos] = x;
+        }
+        cnt += __popcll(bal);
+      }
     }
     if (lane == 0) sh.seg_cnt[wave] = cnt;
     __syncthreads();
