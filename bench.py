@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="128k")
+    ap.add_argument("--layer", default="sparse", choices=("sparse", "swa"),
+                    help="swa: the gated sliding-window layer on the workload's q/k/v/gate")
+    ap.add_argument("--window", type=int, default=4096, help="sliding window (tokens) for --layer swa")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
@@ -382,6 +385,76 @@ def main_decode(args):
     print(json.dumps(rec), flush=True)
 
 
+# ------------------------------------------------------------------------------------------------
+# gated sliding-window layer
+# ------------------------------------------------------------------------------------------------
+def main_swa(args):
+    import torch
+    import long_context_sparse_sgqa_amd as sg
+    from sgqa_inputs import generate, get_workload
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x = generate(w, device=dev, seed=args.seed)
+    prob = sg.Problem.from_workload(w)
+    W = args.window
+    out = torch.empty(w.batch, w.t_q, w.groups, w.heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(sg.swa_workspace_size(prob, W), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sg.swa(prob, W, x["q"], x["k"], x["v"], x["gate"], out=out, workspace=ws, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        ev[j][0].record(stream)
+        sg.swa(prob, W, x["q"], x["k"], x["v"], x["gate"], out=out, workspace=ws, stream=stream)
+        ev[j][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv, dtype=np.int64)
+    att = int(np.minimum(pos + 1, W).sum()) * w.groups * w.batch
+    flops = 4 * w.head_dim * w.heads * att
+    ach = flops / (gpu_ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        torch.set_num_threads(1)
+        xc = {n: x[n].cpu() for n in ("q", "k", "v", "gate")}
+        rng = np.random.default_rng(args.seed)
+        t_begin, n_done, errs = time.perf_counter(), 0, []
+        for i in rng.permutation(w.t_q):
+            ref = oracle.window_rows(xc, W, w.softmax_scale, [(0, int(i))])
+            errs.append(float(np.abs(out[0, int(i)].to("cpu", torch.float64).numpy() - ref[0]).max()))
+            n_done += 1
+            if time.perf_counter() - t_begin >= args.cpu_seconds and n_done >= 4:
+                break
+        el = time.perf_counter() - t_begin
+        cpu = {"value": n_done / el, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_done} random query tokens of the {w.name} workload, all {w.groups} KV "
+                         f"groups, window {W}; fp64 numpy oracle, 1 thread, {el:.1f} s; max-abs "
+                         f"error of those rows {max(errs):.2e}"}
+    rec = {
+        "metric": f"Gated SWA (window {W}) query-tokens/s on the {w.name} workload",
+        "value": w.batch * w.t_q / (wall_ms / 1e3), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,k,v ~ N(0,1)/sqrt(d); gate ~ N(0,1))",
+        "config": {"workload": f"{w.name} gated sliding window", "window": W, "batch": w.batch,
+                   "t_q": w.t_q, "t_kv": w.t_kv, "kv_groups": w.groups, "heads_per_group": w.heads,
+                   "head_dim": w.head_dim, "parallelism": "single GPU"},
+        "roofline": {"kernel": "sgqa_swa (pack + lists + attend_range_kernel + merge)", "bound": "mfma",
+                     "achieved": ach, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": ach * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
+                     "work_per_launch": f"{flops:.4e} FLOP = 4*d*h per attended (query, group, token)"},
+        "cpu_baseline": cpu, "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -390,6 +463,8 @@ def main():
         sys.exit(2)
     if args.workload == "decode":
         return main_decode(args)
+    if args.layer == "swa":
+        return main_swa(args)
     import torch
     import long_context_sparse_sgqa_amd as sg
     from sgqa_inputs import generate, get_workload

@@ -254,6 +254,21 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
                         const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Gated sliding-window attention: the efficient layers placed three to one with the sparse layer
+ * (Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성"; ai.info article, section
+ * "Perché StepFun ha scelto 92 blocchi transformer").  The pages name the layer (Gated SWA) but no
+ * window size, so the window is an argument.  For query i at p = Tk - Tq + i, head j of group g:
+ *   out = sigmoid(gate) * sum_t softmax_t(scale * q . k_t) v_t over t in [max(0, p - window + 1), p]
+ * with the same layouts, dtypes and rounding as sgqa_attend (k_idx, q_idx and the selection play
+ * no part; prob's block / topk fields must still be valid).  Supported: bf16, H == 8, D in
+ * {64, 128}.  The workspace holds block-packed K and V and the per-group work lists.
+ * --------------------------------------------------------------------------------------------- */
+sgqa_status sgqa_swa_workspace_size(const sgqa_problem* prob, int64_t window, size_t* bytes);
+sgqa_status sgqa_swa(const sgqa_problem* prob, int64_t window, const void* q, const void* k,
+                     const void* v, const void* gate, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

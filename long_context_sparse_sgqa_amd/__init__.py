@@ -24,7 +24,7 @@ import torch
 
 __all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
            "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
-           "decode", "SgqaError", "EXPORTED_SYMBOLS"]
+           "decode", "swa_workspace_size", "swa", "SgqaError", "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsgqa.so"
@@ -35,7 +35,7 @@ _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
                     "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                     "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                    "sgqa_decode")
+                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa")
 
 
 class SgqaError(RuntimeError):
@@ -145,9 +145,11 @@ def load_library():
     lib.sgqa_cache_append.argtypes = [P, C, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sgqa_decode_workspace_size.argtypes = [P, C, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgqa_decode.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sgqa_swa_workspace_size.argtypes = [P, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sgqa_swa.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                  "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                 "sgqa_decode"):
+                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -340,3 +342,28 @@ def decode(prob: Problem, cache: Cache, seq_lens, block_table, q, gate, q_idx, p
         _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], torch.bfloat16),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return (out, sel) if return_sel else out
+
+
+# ----------------------------------------------------------------------------------------------
+# gated sliding-window attention
+# ----------------------------------------------------------------------------------------------
+def swa_workspace_size(prob: Problem, window: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().sgqa_swa_workspace_size(ctypes.byref(prob._c()), int(window),
+                                                   ctypes.byref(n)))
+    return n.value
+
+
+def swa(prob: Problem, window: int, q, k, v, gate, out=None, workspace=None, stream=None):
+    """Gated attention of every query over the last `window` tokens up to its position."""
+    lib = load_library()
+    sh = _shapes(prob)
+    if out is None:
+        out = torch.empty(sh["q"], dtype=prob.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(swa_workspace_size(prob, window), dtype=torch.uint8, device=q.device)
+    _check(lib.sgqa_swa(ctypes.byref(prob._c()), int(window), _ptr(q, "q", sh["q"], prob.dtype),
+                        _ptr(k, "k", sh["k"], prob.dtype), _ptr(v, "v", sh["k"], prob.dtype),
+                        _ptr(gate, "gate", sh["q"], prob.dtype), _ptr(out, "out", sh["q"], prob.dtype),
+                        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out

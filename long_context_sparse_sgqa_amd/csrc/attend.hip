@@ -389,6 +389,27 @@ hipError_t launch_attend_single(const Dims& d, const void* q, const void* k, con
                                 const void* gate, const int32_t* sel, void* out, const bf16_t* kp,
                                 const bf16_t* vp, hipStream_t s);
 
+size_t packed_kv_quad_bytes(const Dims& d) {
+  const size_t one = static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
+  return 2 * ((one + 255) / 256 * 256);
+}
+
+hipError_t launch_pack_kv_quad(const Dims& d, const void* k, const void* v, void* packed,
+                               hipStream_t s) {
+  const int64_t total = d.Bt * d.G * d.NU * d.D;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  bf16_t* kp = static_cast<bf16_t*>(packed);
+  bf16_t* vp = kp + packed_kv_quad_bytes(d) / 2 / sizeof(bf16_t);
+  hipLaunchKernelGGL(pack_k_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(k), kp, d.Tk, d.NU, d.D, total, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_v_kernel<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(v), vp, d.Tk, d.NU, d.D, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
                                 const void* gate, const int32_t* sel, void* out, void* workspace,
                                 hipStream_t s, StageMark mark) {

@@ -191,6 +191,46 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// sliding-window lists: every token of a group attends to the contiguous units of its window
+// ------------------------------------------------------------------------------------------------
+struct WindowArgs {
+  uint32_t* ulist;
+  int32_t* bounds;
+  int64_t Tq, pos0, ngroups, total;
+  int win_m1, umax;
+};
+
+// One wave per group of 4 tokens: units from the first token's window start to the last token's
+// own unit, all marked as chosen by every token present (the range kernel masks each token's
+// window and causal limit per token), split into kRanges equal unit ranges padded to 4 entries.
+__global__ void __launch_bounds__(256) window_lists_kernel(WindowArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gq = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gq >= a.total) return;
+  const int64_t qi = gq % a.ngroups;
+  const int64_t tok0 = kTok * qi;
+  const int64_t p0 = a.pos0 + tok0;
+  const int64_t u_lo = (p0 - a.win_m1 > 0 ? p0 - a.win_m1 : 0) >> 3;
+  const int64_t u_end = group_u_end(a.pos0, tok0, a.Tq);
+  const int64_t n = u_end - u_lo;
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) bits |= (tok0 + t < a.Tq ? 1u : 0u) << (kChoseShift + t);
+  uint32_t* out = a.ulist + gq * list_stride(a.umax);
+  int start = 0;
+#pragma unroll
+  for (int r = 0; r < kRanges; ++r) {
+    const int64_t lo = u_lo + (r * n) / kRanges, hi = u_lo + ((r + 1) * n) / kRanges;
+    const int cnt = static_cast<int>(hi - lo), padded = (cnt + 3) & ~3;
+    for (int j = lane; j < padded; j += 64)
+      out[start + j] = j < cnt ? (static_cast<uint32_t>(lo + j) | bits) : 0u;
+    if (lane == 0) a.bounds[gq * (kRanges + 1) + r] = start;
+    start += padded;
+  }
+  if (lane == 0) a.bounds[gq * (kRanges + 1) + kRanges] = start;
+}
+
+// ------------------------------------------------------------------------------------------------
 // one unit range of one group of 4 tokens
 // ------------------------------------------------------------------------------------------------
 struct RangeArgs {
@@ -210,6 +250,7 @@ struct RangeArgs {
   const int32_t* block_table;
   int64_t max_pages, num_pages;
   int ul2;
+  int win_m1;                  // sliding window: tokens t >= p - win_m1 only (huge: no window)
 };
 
 // K rows of the S^T product, permuted: output r' (0..15) of a lane in half h is C row
@@ -349,7 +390,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool chose = (ent >> (kChoseShift + trow)) & 1u;      // 0 past the range (ent = 0)
     const int dlt = static_cast<int>(pX) - static_cast<int>(ent & kUnitMask) * 8;
     const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
-    return chose ? causal : 0u;
+    const int lo = dlt - a.win_m1;                               // first token inside the window
+    const uint32_t window = lo <= 0 ? 0xffu : (lo >= 8 ? 0u : ((0xffu << lo) & 0xffu));
+    return chose ? (causal & window) : 0u;
   };
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -529,70 +572,58 @@ int union_waves(const Dims& d) {
   return static_cast<int>(fit >= 4 ? 4 : fit);
 }
 
-}  // namespace
-
-bool attend_split_supported(const Dims& d) {
-  // one token group's union bitmaps must fit in 160 KiB of LDS
-  return d.bf16 && d.H == 8 && (d.D == 64 || d.D == 128) && d.B % 8 == 0 &&
-         d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31) &&
-         units_per_query(d) <= 1024 && union_waves(d) >= 1;
-}
-
-size_t attend_split_bytes(const Dims& d) {
+size_t split_bytes_for(const Dims& d, int umax) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const size_t n = static_cast<size_t>(d.Bt * d.G * ng);
-  const size_t umax = static_cast<size_t>(units_per_query(d));
-  return align256(n * list_stride(static_cast<int>(umax)) * sizeof(uint32_t)) +
+  return align256(n * list_stride(umax) * sizeof(uint32_t)) +
          align256(n * (kRanges + 1) * sizeof(int32_t)) +
          align256(n * kRanges * 32 * d.D * sizeof(bf16_t)) + align256(n * kRanges * 32 * sizeof(float2));
 }
 
-hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
-                               const void* gate, const int32_t* sel, void* out,
-                               const void* packed_v, void* ws, hipStream_t s, StageMark mark,
-                               const PagedKV* paged) {
+// Units a sliding window of `window` tokens covers for a group of 4 tokens, as list entries per
+// token (the list stride holds kTok times this).
+int window_umax(int64_t window) {
+  const int64_t n = (window + kTok - 1 + 7) / 8 + 1;
+  return static_cast<int>((n + kTok - 1) / kTok);
+}
+
+struct SplitBuffers {
+  uint32_t* ulist;
+  int32_t* bounds;
+  bf16_t* part_o;
+  float2* part_ml;
+};
+
+SplitBuffers split_buffers(const Dims& d, int umax, void* ws) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
-  const int umax = static_cast<int>(units_per_query(d));
+  SplitBuffers sb;
   char* p = static_cast<char*>(ws);
-  uint32_t* ulist = reinterpret_cast<uint32_t*>(p);
+  sb.ulist = reinterpret_cast<uint32_t*>(p);
   p += align256(static_cast<size_t>(total) * list_stride(umax) * sizeof(uint32_t));
-  int32_t* bounds = reinterpret_cast<int32_t*>(p);
+  sb.bounds = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<size_t>(total) * (kRanges + 1) * sizeof(int32_t));
-  bf16_t* part_o = reinterpret_cast<bf16_t*>(p);
+  sb.part_o = reinterpret_cast<bf16_t*>(p);
   p += align256(static_cast<size_t>(total) * kRanges * 32 * d.D * sizeof(bf16_t));
-  float2* part_ml = reinterpret_cast<float2*>(p);
+  sb.part_ml = reinterpret_cast<float2*>(p);
+  return sb;
+}
 
-  UnionArgs ua;
-  ua.sel = sel;
-  ua.ulist = ulist;
-  ua.bounds = bounds;
-  ua.Tq = d.Tq;
-  ua.pos0 = d.pos0;
-  ua.seq_len = d.seq_len;
-  ua.ngroups = ng;
-  ua.total = total;
-  ua.G = d.G;
-  ua.NS = d.NS;
-  ua.B = d.B;
-  ua.umax = umax;
-  ua.words = static_cast<int>((d.NU + 31) / 32);
-  ua.waves = union_waves(d);
-  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
-  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
-                     dim3(64 * ua.waves), lds, s, ua);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && mark) e = mark(4, s);
-  if (e != hipSuccess) return e;
-
+// The range kernel over prepared lists, then the merge.
+hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* packed_k,
+                                   const void* gate, void* out, const void* packed_v,
+                                   const SplitBuffers& sb, int umax, int win_m1, hipStream_t s,
+                                   StageMark mark, const PagedKV* paged) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
   RangeArgs a;
   a.q = static_cast<const bf16_t*>(q);
   a.kp = static_cast<const bf16_t*>(packed_k);
   a.vp = static_cast<const bf16_t*>(packed_v);
-  a.ulist = ulist;
-  a.bounds = bounds;
-  a.part_o = part_o;
-  a.part_ml = part_ml;
+  a.ulist = sb.ulist;
+  a.bounds = sb.bounds;
+  a.part_o = sb.part_o;
+  a.part_ml = sb.part_ml;
   a.Tq = d.Tq;
   a.Tk = d.Tk;
   a.NU = d.NU;
@@ -606,6 +637,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   a.block_table = nullptr;
   a.max_pages = a.num_pages = 0;
   a.ul2 = 0;
+  a.win_m1 = win_m1;
   if (paged) {
     a.kp = static_cast<const bf16_t*>(paged->k);
     a.vp = static_cast<const bf16_t*>(paged->v);
@@ -626,13 +658,13 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
     else
       hipLaunchKernelGGL((attend_range_kernel<64, false>), grid, dim3(256), 0, s, a);
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(5, s);
   if (e != hipSuccess) return e;
 
   MergeArgs m;
-  m.part_o = part_o;
-  m.part_ml = part_ml;
+  m.part_o = sb.part_o;
+  m.part_ml = sb.part_ml;
   m.gate = static_cast<const bf16_t*>(gate);
   m.out = static_cast<bf16_t*>(out);
   m.Tq = d.Tq;
@@ -645,6 +677,86 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(merge_ranges_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, m);
   return hipGetLastError();
+}
+
+}  // namespace
+
+bool attend_split_supported(const Dims& d) {
+  // one token group's union bitmaps must fit in 160 KiB of LDS
+  return d.bf16 && d.H == 8 && (d.D == 64 || d.D == 128) && d.B % 8 == 0 &&
+         d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31) &&
+         units_per_query(d) <= 1024 && union_waves(d) >= 1;
+}
+
+size_t attend_split_bytes(const Dims& d) {
+  return split_bytes_for(d, static_cast<int>(units_per_query(d)));
+}
+
+hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
+                               const void* gate, const int32_t* sel, void* out,
+                               const void* packed_v, void* ws, hipStream_t s, StageMark mark,
+                               const PagedKV* paged) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
+  const int umax = static_cast<int>(units_per_query(d));
+  const SplitBuffers sb = split_buffers(d, umax, ws);
+
+  UnionArgs ua;
+  ua.sel = sel;
+  ua.ulist = sb.ulist;
+  ua.bounds = sb.bounds;
+  ua.Tq = d.Tq;
+  ua.pos0 = d.pos0;
+  ua.seq_len = d.seq_len;
+  ua.ngroups = ng;
+  ua.total = total;
+  ua.G = d.G;
+  ua.NS = d.NS;
+  ua.B = d.B;
+  ua.umax = umax;
+  ua.words = static_cast<int>((d.NU + 31) / 32);
+  ua.waves = union_waves(d);
+  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
+  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
+                     dim3(64 * ua.waves), lds, s, ua);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && mark) e = mark(4, s);
+  if (e != hipSuccess) return e;
+  return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, 1 << 30, s, mark,
+                                 paged);
+}
+
+bool attend_window_supported(const Dims& d) {
+  return d.bf16 && d.H == 8 && (d.D == 64 || d.D == 128) &&
+         d.NU * 8 * static_cast<int64_t>(d.D) * 2 < (int64_t(1) << 31);
+}
+
+size_t attend_window_bytes(const Dims& d, int64_t window) {
+  return split_bytes_for(d, window_umax(window));
+}
+
+hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, const void* packed_k,
+                                const void* gate, void* out, const void* packed_v, void* ws,
+                                hipStream_t s) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
+  const int umax = window_umax(window);
+  const SplitBuffers sb = split_buffers(d, umax, ws);
+  WindowArgs wa;
+  wa.ulist = sb.ulist;
+  wa.bounds = sb.bounds;
+  wa.Tq = d.Tq;
+  wa.pos0 = d.pos0;
+  wa.ngroups = ng;
+  wa.total = total;
+  wa.win_m1 = static_cast<int>(window - 1);
+  wa.umax = umax;
+  hipLaunchKernelGGL(window_lists_kernel, dim3(static_cast<unsigned>((total + 3) / 4)), dim3(256), 0,
+                     s, wa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, wa.win_m1, s,
+                                 nullptr, nullptr);
 }
 
 }  // namespace sgqa

@@ -559,6 +559,54 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
   return ok();
 }
 
+sgqa_status derive_swa(const sgqa_problem* prob, int64_t window, Derived* dv, int64_t* w_eff,
+                       size_t* bytes) {
+  SGQA_CHECK(derive(prob, dv));
+  if (window < 1) return fail(SGQA_ERR_SHAPE, "window must be >= 1 (got %lld)", (long long)window);
+  if (!sgqa::attend_window_supported(dv->d))
+    return fail(SGQA_ERR_UNSUPPORTED, "sliding-window attention needs bf16, heads_per_group == 8 "
+                "and head_dim 64 or 128");
+  *w_eff = window < dv->d.Tk ? window : dv->d.Tk;      // a window past the context is the context
+  *bytes = align_up(sgqa::packed_kv_quad_bytes(dv->d)) + sgqa::attend_window_bytes(dv->d, *w_eff);
+  return SGQA_OK;
+}
+
+sgqa_status sgqa_swa_workspace_size(const sgqa_problem* prob, int64_t window, size_t* bytes) {
+  Derived dv;
+  int64_t w;
+  size_t need;
+  SGQA_CHECK(derive_swa(prob, window, &dv, &w, &need));
+  if (!bytes) return fail(SGQA_ERR_NULL, "bytes is NULL");
+  *bytes = need;
+  return ok();
+}
+
+sgqa_status sgqa_swa(const sgqa_problem* prob, int64_t window, const void* q, const void* k,
+                     const void* v, const void* gate, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  Derived dv;
+  int64_t w;
+  size_t need;
+  SGQA_CHECK(derive_swa(prob, window, &dv, &w, &need));
+  SGQA_CHECK(check_ptr(q, "q"));
+  SGQA_CHECK(check_ptr(k, "k"));
+  SGQA_CHECK(check_ptr(v, "v"));
+  SGQA_CHECK(check_ptr(gate, "gate"));
+  SGQA_CHECK(check_ptr(out, "out"));
+  SGQA_CHECK(check_ptr(workspace, "workspace"));
+  if (workspace_bytes < need)
+    return fail(SGQA_ERR_WORKSPACE, "sliding-window workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t pkv = sgqa::packed_kv_quad_bytes(dv.d);
+  hipError_t e = sgqa::launch_pack_kv_quad(dv.d, k, v, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "k/v packing launch");
+  e = sgqa::launch_attend_window(dv.d, w, q, ws, gate, out, ws + pkv / 2, ws + align_up(pkv), s);
+  if (e != hipSuccess) return hip_fail(e, "sliding-window attention launch");
+  return ok();
+}
+
 sgqa_status sgqa_set_stage_events(void* const* events) {
   if (!events) {
     g_stage_armed = false;

@@ -115,6 +115,18 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark,
                                const PagedKV* paged = nullptr);
+// Gated sliding-window attention (the efficient layers): every query attends to the tokens
+// t in [p - window + 1, p], with the range kernel over contiguous unit lists; K and V packed as
+// for launch_attend_split (launch_pack_kv with quad layout).
+bool attend_window_supported(const Dims& d);
+size_t attend_window_bytes(const Dims& d, int64_t window);
+hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, const void* packed_k,
+                                const void* gate, void* out, const void* packed_v, void* ws,
+                                hipStream_t s);
+// Packed K and V in the 4-token layout the range kernel reads: bytes, and the packing.
+size_t packed_kv_quad_bytes(const Dims& d);
+hipError_t launch_pack_kv_quad(const Dims& d, const void* k, const void* v, void* packed,
+                               hipStream_t s);
 // Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
                          const void* gate, const int32_t* sel, void* out, void* workspace,

@@ -18,4 +18,5 @@ from .sgqa_oracle import (  # noqa: F401
     scored_candidates,
     inclusion_rate,
     sequence_rows,
+    window_rows,
 )

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "num_blocks", "n_selected_blocks", "query_positions", "compress", "block_scores",
     "select_blocks", "attended_tokens", "gated_attention", "forward_rows", "forward",
-    "scored_candidates", "inclusion_rate", "sequence_rows",
+    "scored_candidates", "inclusion_rate", "sequence_rows", "window_rows",
 ]
 
 
@@ -248,6 +248,28 @@ def sequence_rows(inputs, seq_lens, block: int, topk_tokens: int, scale: float, 
         out[mine] = o_b
         kblk[b] = kb[0]
     return sel_out, out, kblk
+
+
+def window_rows(inputs, window: int, scale: float, rows):
+    """Gated sliding-window attention (the efficient layers the pages interleave three to one with
+    Sparse GQA; Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성").  The pages
+    give no window size, so it is an argument: a query at position p attends to the tokens
+    t in [max(0, p - window + 1), p], with the same gate, scale and GQA reading as the sparse layer.
+    Returns out [n, G, h, d] float64 for the listed (b, i)."""
+    q, k, v, gate = (inputs[n] for n in ("q", "k", "v", "gate"))
+    t_q, G = q.shape[1], q.shape[2]
+    t_kv = k.shape[2]
+    pos = query_positions(t_q, t_kv)
+    rows = list(rows)
+    out = np.zeros((len(rows), G, q.shape[3], q.shape[4]), dtype=np.float64)
+    for r, (b, i) in enumerate(rows):
+        p = int(pos[i])
+        toks = np.arange(max(0, p - window + 1), p + 1)
+        qb, gb = _np64(q[b, i]), _np64(gate[b, i])
+        for g in range(G):
+            out[r, g] = gated_attention(qb[g], _rows64(k, b, g, toks), _rows64(v, b, g, toks),
+                                        gb[g], np.arange(toks.size), scale)
+    return out
 
 
 # ----------------------------------------------------------------------------------------------

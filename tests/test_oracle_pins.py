@@ -397,3 +397,36 @@ def test_sequence_rows_ignore_tokens_past_length():
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(k1[1], k2[1])
     assert k1[1].shape[0] == -(-77 // 8)
+
+
+# ----------------------------------------------------------------------------------------------
+# gated sliding-window attention
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("window", [1, 5, 16, 37])
+def test_window_equals_band_masked_sdpa(window):
+    """torch SDPA (fp64) with an explicit band mask t in [p - window + 1, p], times sigmoid(gate)."""
+    t_q, t_kv = 30, 70
+    w, inp = generate_small(t_q=t_q, t_kv=t_kv, groups=2, heads=3, head_dim=8, index_dim=4,
+                            block=8, topk=64, seed=17)
+    rows = [(0, i) for i in range(t_q)]
+    out = oracle.window_rows(inp, window, w.softmax_scale, rows)
+    pos = torch.arange(t_kv - t_q, t_kv)
+    t = torch.arange(t_kv)[None, :]
+    mask = (t <= pos[:, None]) & (t > pos[:, None] - window)
+    ref = _sdpa_reference(inp, mask, w.softmax_scale)[0]
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_window_one_is_own_value_and_wide_window_is_dense():
+    w, inp = generate_small(t_q=12, t_kv=40, groups=2, heads=2, head_dim=8, index_dim=4, block=8,
+                            topk=64, seed=2)
+    rows = [(0, i) for i in range(12)]
+    one = oracle.window_rows(inp, 1, w.softmax_scale, rows)
+    v = inp["v"].to(torch.float64).numpy()[0]               # [G, Tkv, d]
+    gate = torch.sigmoid(inp["gate"].to(torch.float64)).numpy()[0]   # [Tq, G, h, d]
+    for i in range(12):
+        p = 40 - 12 + i
+        np.testing.assert_allclose(one[i], gate[i] * v[:, p][:, None, :], rtol=0, atol=1e-15)
+    wide = oracle.window_rows(inp, 1000, w.softmax_scale, rows)
+    _, dense, _ = oracle.forward(inp, w.block, 4096, w.softmax_scale)
+    np.testing.assert_allclose(wide, dense[0], rtol=0, atol=1e-12)
