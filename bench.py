@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--layer", default="sparse", choices=("sparse", "swa"),
                     help="swa: the gated sliding-window layer on the workload's q/k/v/gate")
     ap.add_argument("--window", type=int, default=4096, help="sliding window (tokens) for --layer swa")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
+                    help="fp8: K and V stored as e4m3 codes with per-tensor scales (sgqa_forward_fp8kv)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
@@ -483,9 +485,18 @@ def main():
     ws = torch.empty(sz["forward_workspace_bytes"], dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"], k_blk=k_blk,
-                   out=out, sel=sel, workspace=ws, stream=stream)
+    if args.kv == "fp8":
+        from sgqa_inputs import quantize_e4m3
+        k8, ks = quantize_e4m3(x["k"])
+        v8, vs = quantize_e4m3(x["v"])
+
+        def step():
+            sg.forward_fp8kv(prob, x["q"], k8, v8, ks, vs, x["gate"], x["q_idx"], x["k_idx"],
+                             k_blk=k_blk, out=out, sel=sel, workspace=ws, stream=stream)
+    else:
+        def step():
+            sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"], k_blk=k_blk,
+                       out=out, sel=sel, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -557,11 +568,12 @@ def main():
                 "traffic": load_traffic(dominant, w.name), "work_per_launch": f"{byts:.4e} B"}
 
     cpu, parity = (None, None)
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.kv == "bf16":
         cpu, parity = cpu_baseline(w, x, out, sel, args.cpu_seconds, args.seed)
 
     rec = {
-        "metric": "Sparse-GQA prefill query-tokens/s at 128K ctx (index+topk+attn); % roofline",
+        "metric": "Sparse-GQA prefill query-tokens/s at 128K ctx (index+topk+attn); % roofline"
+                  + (" [fp8 e4m3 K/V variant]" if args.kv == "fp8" else ""),
         "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

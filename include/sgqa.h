@@ -255,6 +255,20 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Steps 1-4 with K and V stored as fp8.  The pages run the KV cache in FP8 (trained for it: FP8
+ * KV QAT; Step 5 Preview summary on mo.ai.kr, section "장기 강화학습과 실행 비용").  Here k8 and v8
+ * hold OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f /
+ * 0xff are NaN) in the layout of k and v ([Bt, G, Tk, D], one byte each), and the values attended
+ * to are code * k_scale and code * v_scale (per-tensor scales, finite and > 0).  Everything else
+ * is sgqa_forward: same selection, same gate, bf16 q / gate / out, same workspace size
+ * (sizes.forward_workspace_*).  Supported: dtype bf16, H == 8, D in {64, 128}, B a multiple of 8.
+ * --------------------------------------------------------------------------------------------- */
+sgqa_status sgqa_forward_fp8kv(const sgqa_problem* prob, const void* q, const void* k8,
+                               const void* v8, float k_scale, float v_scale, const void* gate,
+                               const void* q_idx, const void* k_idx, void* k_blk, int32_t* sel_out,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Gated sliding-window attention: the efficient layers placed three to one with the sparse layer
  * (Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성"; ai.info article, section
  * "Perché StepFun ha scelto 92 blocchi transformer").  The pages name the layer (Gated SWA) but no

@@ -24,7 +24,8 @@ import torch
 
 __all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
            "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
-           "decode", "swa_workspace_size", "swa", "SgqaError", "EXPORTED_SYMBOLS"]
+           "decode", "swa_workspace_size", "swa", "forward_fp8kv", "SgqaError",
+           "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsgqa.so"
@@ -35,7 +36,7 @@ _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
                     "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                     "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa")
+                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv")
 
 
 class SgqaError(RuntimeError):
@@ -147,9 +148,12 @@ def load_library():
     lib.sgqa_decode.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sgqa_swa_workspace_size.argtypes = [P, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgqa_swa.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    f32 = ctypes.c_float
+    lib.sgqa_forward_fp8kv.argtypes = [P, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                  "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa"):
+                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -341,6 +345,37 @@ def decode(prob: Problem, cache: Cache, seq_lens, block_table, q, gate, q_idx, p
         _ptr(pools["k_blk"], "k_blk", csh["k_blk"], torch.bfloat16),
         _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], torch.bfloat16),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return (out, sel) if return_sel else out
+
+
+# ----------------------------------------------------------------------------------------------
+# fp8 K/V
+# ----------------------------------------------------------------------------------------------
+def forward_fp8kv(prob: Problem, q, k8, v8, k_scale: float, v_scale: float, gate, q_idx, k_idx,
+                  k_blk=None, out=None, sel=None, return_sel=False, workspace=None, stream=None):
+    """Steps 1-4 with K and V given as e4m3 codes (torch.float8_e4m3fn or uint8 tensors of k's
+    shape) dequantised by per-tensor scales."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q.device
+    k8 = k8.view(torch.uint8) if k8.dtype != torch.uint8 else k8
+    v8 = v8.view(torch.uint8) if v8.dtype != torch.uint8 else v8
+    if k_blk is None:
+        k_blk = torch.empty(sh["k_blk"], dtype=prob.index_dtype, device=dev)
+    if out is None:
+        out = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    if sel is None and return_sel:
+        sel = torch.empty(sh["sel"], dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(sizes(prob)["forward_workspace_bytes"], dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_forward_fp8kv(
+        ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype), _ptr(k8, "k8", sh["k"], torch.uint8),
+        _ptr(v8, "v8", sh["k"], torch.uint8), float(k_scale), float(v_scale),
+        _ptr(gate, "gate", sh["q"], prob.dtype), _ptr(q_idx, "q_idx", sh["q_idx"], prob.index_dtype),
+        _ptr(k_idx, "k_idx", sh["k_idx"], prob.index_dtype),
+        _ptr(k_blk, "k_blk", sh["k_blk"], prob.index_dtype), _ptr(sel, "sel", sh["sel"], torch.int32),
+        _ptr(out, "out", sh["q"], prob.dtype), workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
     return (out, sel) if return_sel else out
 
 

@@ -389,6 +389,78 @@ hipError_t launch_attend_single(const Dims& d, const void* q, const void* k, con
                                 const void* gate, const int32_t* sel, void* out, const bf16_t* kp,
                                 const bf16_t* vp, hipStream_t s);
 
+// fp8 e4m3 packing for the range kernel (zero past Tk).  K: unit byte ((m*8 + t)*2 + h)*16 + kk*8
+// + e holds k[8u + t][32m + 16kk + 8h + e], so one 16-byte load gives a lane its operands of two
+// consecutive 16-wide d-slices.  V: unit byte (n*32 + c)*16 + kk*8 + t holds v[8u + t][64n +
+// 32kk + c], so one 16-byte load gives a lane its 8 tokens for two consecutive 32-wide d-tiles.
+// One thread per 16-byte piece (D/2 pieces per unit).
+__global__ void __launch_bounds__(256) pack_k_fp8_kernel(const uint8_t* __restrict__ k8,
+                                                         uint8_t* __restrict__ kp, int64_t Tk,
+                                                         int64_t NU, int D, int64_t total) {
+  const int per = D / 2;
+  for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int q = static_cast<int>(id % per);
+    const int64_t u = (id / per) % NU;
+    const int64_t bg = id / (static_cast<int64_t>(per) * NU);
+    const int h = q & 1, t = (q >> 1) & 7, m = q >> 4;
+    const int64_t tok = u * 8 + t;
+    uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+    if (tok < Tk) {
+      const uint8_t* row = k8 + (bg * Tk + tok) * D + 32 * m + 8 * h;
+      lo = *reinterpret_cast<const uint2*>(row);
+      hi = *reinterpret_cast<const uint2*>(row + 16);
+    }
+    *reinterpret_cast<uint4*>(kp + (bg * NU + u) * D * 8 + static_cast<int64_t>(q) * 16) =
+        make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+__global__ void __launch_bounds__(256) pack_v_fp8_kernel(const uint8_t* __restrict__ v8,
+                                                         uint8_t* __restrict__ vp, int64_t Tk,
+                                                         int64_t NU, int D, int64_t total) {
+  const int per = D / 2;
+  for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int q = static_cast<int>(id % per);
+    const int64_t u = (id / per) % NU;
+    const int64_t bg = id / (static_cast<int64_t>(per) * NU);
+    const int c = q & 31, n = q >> 5;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int64_t tok = u * 8 + t;
+        const uint32_t byte = tok < Tk ? v8[(bg * Tk + tok) * D + 64 * n + 32 * kk + c] : 0u;
+        w[(kk * 8 + t) >> 2] |= byte << (8 * (t & 3));
+      }
+    *reinterpret_cast<uint4*>(vp + (bg * NU + u) * D * 8 + static_cast<int64_t>(q) * 16) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+size_t packed_kv_fp8_bytes(const Dims& d) {
+  const size_t one = static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D;
+  return 2 * ((one + 255) / 256 * 256);
+}
+
+hipError_t launch_pack_kv_fp8(const Dims& d, const void* k8, const void* v8, void* packed,
+                              hipStream_t s) {
+  const int64_t total = d.Bt * d.G * d.NU * (d.D / 2);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  uint8_t* kp = static_cast<uint8_t*>(packed);
+  uint8_t* vp = kp + packed_kv_fp8_bytes(d) / 2;
+  hipLaunchKernelGGL(pack_k_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(k8), kp, d.Tk, d.NU, d.D, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_v_fp8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(v8), vp, d.Tk, d.NU, d.D, total);
+  return hipGetLastError();
+}
+
 size_t packed_kv_quad_bytes(const Dims& d) {
   const size_t one = static_cast<size_t>(d.Bt) * d.G * d.NU * 8 * d.D * 2;
   return 2 * ((one + 255) / 256 * 256);

@@ -251,7 +251,19 @@ struct RangeArgs {
   int64_t max_pages, num_pages;
   int ul2;
   int win_m1;                  // sliding window: tokens t >= p - win_m1 only (huge: no window)
+  float v_scale;               // fp8 K/V: dequantisation scale of V (k_scale is in scale_log2e)
 };
+
+// 8 fp8 e4m3 values (two dwords, bytes in element order) as 8 bf16 operand values.  Every e4m3
+// value is exactly representable in bf16, so the conversion is exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v w = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
 
 // K rows of the S^T product, permuted: output r' (0..15) of a lane in half h is C row
 // 8 (r'/4) + 4h + r'%4, and should hold token r' % 8 of unit slot (r' < 8 ? h : 2 + h).  So K
@@ -262,7 +274,7 @@ __device__ __forceinline__ int kq_slot(int i) {
 }
 __device__ __forceinline__ int kq_tok(int i) { return ((i >> 3) * 4 + (i & 3)) & 7; }
 
-template <int D, bool kPaged>
+template <int D, bool kPaged, bool kFp8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_range_kernel(RangeArgs a) {
   constexpr int H = 8;
   constexpr int kQRow = D * 2 + 16;                      // padded LDS row of Q (bytes)
@@ -307,8 +319,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     return bf16x8_from_u4(*reinterpret_cast<const uint4*>(sq + c * kQRow + (16 * kc + 8 * h) * 2));
   };
 
-  const BufRsrc krs = make_rsrc(a.kp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
-  const BufRsrc vrs = make_rsrc(a.vp + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
+  constexpr int64_t kElem = kFp8 ? 1 : 2;                 // bytes per packed K/V element
+  const BufRsrc krs = make_rsrc(reinterpret_cast<const char*>(a.kp) + (b * a.G + g) * a.NU * D * 8 * kElem,
+                                a.NU * D * 8 * kElem);
+  const BufRsrc vrs = make_rsrc(reinterpret_cast<const char*>(a.vp) + (b * a.G + g) * a.NU * D * 8 * kElem,
+                                a.NU * D * 8 * kElem);
 
   // List entries are read with scalar loads (constant address space, wave-uniform, 16-byte aligned
   // because ranges start at multiples of 4): they count against lgkmcnt, so reading them never
@@ -341,11 +356,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
   };
 
-  // K operands of a chunk: A row c = token kq_tok(c) of unit slot kq_slot(c), d-half h.
+  // K operands of a chunk: A row c = token kq_tok(c) of unit slot kq_slot(c), d-half h.  With fp8
+  // K and V the registers hold the raw bytes (one 16-byte load covers two operands) and are
+  // converted to bf16 right before the products.
   const int kslot = kq_slot(c), ktok = kq_tok(c);
-  struct KRegs { bf16x8_t k[D / 16]; };
+  struct KRegs {
+    bf16x8_t k[kFp8 ? 1 : D / 16];
+    uint4 r[kFp8 ? D / 32 : 1];
+  };
   auto load_k = [&](const uint32_t* ent4, const uint32_t* pu4, KRegs& R) {
-    if constexpr (kPaged) {
+    if constexpr (kFp8) {
+      // fp8 unit layout: bytes ((m * 8 + t) * 2 + h) * 16 hold d 32m + 8h + [0, 8) then
+      // 32m + 16 + 8h + [0, 8) of token t
+      const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        R.r[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     krs, u * D * 8 + ((m * 8 + ktok) * 2 + h) * 16, 0, 0));
+    } else if constexpr (kPaged) {
       const bf16_t* base = a.kp + static_cast<uint64_t>(pick4(pu4, kslot)) * (D * 8) + (ktok * 2 + h) * 8;
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = load_bf16x8(base + kc * 128);
@@ -355,10 +383,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
     }
   };
+  auto k_op = [&](const KRegs& K, int kc) -> bf16x8_t {
+    if constexpr (kFp8) {
+      const uint4 w = K.r[kc >> 1];
+      return (kc & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+    } else {
+      return K.k[kc];
+    }
+  };
   // V^T operands of d-tile dt for the units of slot h (first product) and slot 2 + h (second).
-  struct VRegs { bf16x8_t v[D / 16]; };
+  struct VRegs {
+    bf16x8_t v[kFp8 ? 1 : D / 16];
+    uint4 r[kFp8 ? D / 32 : 1];
+  };
   auto load_v = [&](const uint32_t* ent4, const uint32_t* pu4, VRegs& R) {
-    if constexpr (kPaged) {
+    if constexpr (kFp8) {
+      // fp8 unit layout: bytes (n * 32 + c) * 16 hold tokens 0..7 of d 64n + c, then of 64n + 32 + c
+      const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
+      const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
+#pragma unroll
+      for (int n = 0; n < D / 64; ++n) {
+        R.r[2 * n] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                         vrs, ua * D * 8 + (n * 32 + c) * 16, 0, 0));
+        R.r[2 * n + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                             vrs, ub * D * 8 + (n * 32 + c) * 16, 0, 0));
+      }
+    } else if constexpr (kPaged) {
       const bf16_t* va = a.vp + static_cast<uint64_t>(pick4(pu4, h)) * (D * 8) + c * 8;
       const bf16_t* vb = a.vp + static_cast<uint64_t>(pick4(pu4, 2 + h)) * (D * 8) + c * 8;
 #pragma unroll
@@ -374,6 +424,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         R.v[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
         R.v[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
       }
+    }
+  };
+  // operand of d-tile dt, unit slot h (sb = 0) or 2 + h (sb = 1)
+  auto v_op = [&](const VRegs& V, int dt, int sb) -> bf16x8_t {
+    if constexpr (kFp8) {
+      const uint4 w = V.r[(dt >> 1) * 2 + sb];
+      return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+    } else {
+      return V.v[2 * dt + sb];
     }
   };
 
@@ -404,7 +463,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   auto chunk = [&](const KRegs& K, const VRegs& V, const uint32_t* ent4, auto refill) {
     f32x16_t s = {};
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(K.k[kc], q_operand(kc), s);
+    for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(k_op(K, kc), q_operand(kc), s);
     refill();
     const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
     float t[16];
@@ -417,7 +476,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, t[i]), t[i + 1]);
     mx = fmaxf(mx, t[15]);
-    mx = wave_max_xor(mx, 32);
+    mx = max_with_other_half(mx);
     const float m_new = fmaxf(m_run, mx * a.scale_log2e);
     if (__ballot(m_new > m_run + kLazyRescaleLog2)) {   // a row's max grew by > margin: rescale all
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -439,8 +498,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      acc[dt] = mfma32x32x16(V.v[2 * dt], pa, acc[dt]);
-      acc[dt] = mfma32x32x16(V.v[2 * dt + 1], pb, acc[dt]);
+      acc[dt] = mfma32x32x16(v_op(V, dt, 0), pa, acc[dt]);
+      acc[dt] = mfma32x32x16(v_op(V, dt, 1), pb, acc[dt]);
     }
   };
 
@@ -488,7 +547,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // partial of this range: O / l in bf16 (0 for a row with nothing in the range), and the running
   // max m and sum l per row in fp32.  Lane (c, h) holds d = 32 dt + 8 (i/4) + 4h + i%4 of row c.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
   const int64_t pbase = (gq * kRanges + r) * 32 + c;
   bf16_t* po = a.part_o + pbase * D;
   typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -613,7 +672,7 @@ SplitBuffers split_buffers(const Dims& d, int umax, void* ws) {
 hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* packed_k,
                                    const void* gate, void* out, const void* packed_v,
                                    const SplitBuffers& sb, int umax, int win_m1, hipStream_t s,
-                                   StageMark mark, const PagedKV* paged) {
+                                   StageMark mark, const PagedKV* paged, const Fp8Scales* fp8) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   RangeArgs a;
@@ -632,7 +691,8 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
   a.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
   a.G = d.G;
   a.umax = umax;
-  a.scale_log2e = d.scale * 1.4426950408889634f;
+  a.scale_log2e = d.scale * (fp8 ? fp8->k_scale : 1.0f) * 1.4426950408889634f;
+  a.v_scale = fp8 ? fp8->v_scale : 1.0f;
   a.seq_len = d.seq_len;
   a.block_table = nullptr;
   a.max_pages = a.num_pages = 0;
@@ -649,14 +709,19 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
   const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
   if (paged) {
     if (d.D == 128)
-      hipLaunchKernelGGL((attend_range_kernel<128, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_range_kernel<128, true, false>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((attend_range_kernel<64, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_range_kernel<64, true, false>), grid, dim3(256), 0, s, a);
+  } else if (fp8) {
+    if (d.D == 128)
+      hipLaunchKernelGGL((attend_range_kernel<128, false, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_range_kernel<64, false, true>), grid, dim3(256), 0, s, a);
   } else {
     if (d.D == 128)
-      hipLaunchKernelGGL((attend_range_kernel<128, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_range_kernel<128, false, false>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((attend_range_kernel<64, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_range_kernel<64, false, false>), grid, dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(5, s);
@@ -695,7 +760,7 @@ size_t attend_split_bytes(const Dims& d) {
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark,
-                               const PagedKV* paged) {
+                               const PagedKV* paged, const Fp8Scales* fp8) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
@@ -723,7 +788,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   if (e == hipSuccess && mark) e = mark(4, s);
   if (e != hipSuccess) return e;
   return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, 1 << 30, s, mark,
-                                 paged);
+                                 paged, fp8);
 }
 
 bool attend_window_supported(const Dims& d) {
@@ -756,7 +821,7 @@ hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, co
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, wa.win_m1, s,
-                                 nullptr, nullptr);
+                                 nullptr, nullptr, nullptr);
 }
 
 }  // namespace sgqa

@@ -109,4 +109,13 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// max(v, v of lane ^ 32) without LDS: v_permlane32_swap exchanges the two 32-lane halves of its
+// operands, so with both operands = v one result holds v of the other half in lanes 0..31 and the
+// other in lanes 32..63.  (A ds_bpermute would count against lgkmcnt, and a wait for it would also
+// wait for any scalar load in flight.)
+__device__ __forceinline__ float max_with_other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 }  // namespace sgqa

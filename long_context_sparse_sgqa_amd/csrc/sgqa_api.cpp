@@ -607,6 +607,57 @@ sgqa_status sgqa_swa(const sgqa_problem* prob, int64_t window, const void* q, co
   return ok();
 }
 
+sgqa_status sgqa_forward_fp8kv(const sgqa_problem* prob, const void* q, const void* k8,
+                               const void* v8, float k_scale, float v_scale, const void* gate,
+                               const void* q_idx, const void* k_idx, void* k_blk, int32_t* sel_out,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Derived dv;
+  SGQA_CHECK(derive(prob, &dv));
+  const sgqa::Dims& d = dv.d;
+  if (!sgqa::attend_split_supported(d))
+    return fail(SGQA_ERR_UNSUPPORTED, "fp8 K/V needs bf16 q/gate/out, heads_per_group == 8, head_dim "
+                "64 or 128, block a multiple of 8 and topk_tokens / block within the grouped kernel");
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(SGQA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  SGQA_CHECK(check_ptr(q, "q"));
+  SGQA_CHECK(check_ptr(k8, "k"));
+  SGQA_CHECK(check_ptr(v8, "v"));
+  SGQA_CHECK(check_ptr(gate, "gate"));
+  SGQA_CHECK(check_ptr(q_idx, "q_idx"));
+  SGQA_CHECK(check_ptr(k_blk, "k_blk"));
+  SGQA_CHECK(check_ptr(out, "out"));
+  if (k_idx) SGQA_CHECK(check_ptr(k_idx, "k_idx"));
+  if (sel_out) SGQA_CHECK(check_ptr(sel_out, "sel_out"));
+  SGQA_CHECK(check_ptr(workspace, "workspace"));
+  const ForwardLayout L = forward_layout(dv);
+  const int64_t chunk_tok = forward_chunk_tokens(dv, L, workspace_bytes);
+  if (chunk_tok < 1)
+    return fail(SGQA_ERR_WORKSPACE, "forward workspace needs at least %zu bytes (got %zu)",
+                L.fixed + chunk_bytes(L, 1), workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + L.off_sel);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SGQA_CHECK(mark_stage(0, s));
+  if (k_idx) {
+    hipError_t e = sgqa::launch_compress(d, k_idx, k_blk, s);
+    if (e != hipSuccess) return hip_fail(e, "compress launch");
+  }
+  SGQA_CHECK(mark_stage(1, s));
+  SGQA_CHECK(select_chunked(d, L, ws, chunk_tok, q_idx, k_blk, sel, s));
+  SGQA_CHECK(mark_stage(2, s));
+  // the fp8 copies fit in the space of the bf16 ones; the range lists follow that space
+  hipError_t e = sgqa::launch_pack_kv_fp8(d, k8, v8, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "fp8 k/v packing launch");
+  SGQA_CHECK(mark_stage(3, s));
+  const sgqa::Fp8Scales sc{k_scale, v_scale};
+  e = sgqa::launch_attend_split(d, q, ws, gate, sel, out, ws + sgqa::packed_kv_fp8_bytes(d) / 2,
+                                ws + sgqa::attend_packed_kv_bytes(d), s,
+                                g_stage_armed ? mark_stage_hip : nullptr, nullptr, &sc);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  SGQA_CHECK(mark_stage(6, s));
+  return ok();
+}
+
 sgqa_status sgqa_set_stage_events(void* const* events) {
   if (!events) {
     g_stage_armed = false;

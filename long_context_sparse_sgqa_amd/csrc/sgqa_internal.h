@@ -37,6 +37,11 @@ struct PagedKV {
   int page_units_log2;   // log2(page_tokens / 8)
 };
 
+// fp8 (e4m3) K and V: k = code * k_scale, v = code * v_scale.
+struct Fp8Scales {
+  float k_scale, v_scale;
+};
+
 // ---- decode: appending to the paged cache ----------------------------------------------------
 // Writes n_new tokens per sequence (ending at d.seq_len[b]) into the K/V pools of `pk` and the
 // index-key pool, then recomputes the touched block keys in k_blk (row stride d.kblk_stride).
@@ -110,11 +115,17 @@ hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, con
                                 const void* gate, const int32_t* sel, void* out, void* workspace,
                                 hipStream_t s, StageMark mark = nullptr);
 // With `paged`, K and V come from the paged cache (packed_k / packed_v are ignored) and query
-// positions follow d.seq_len.
+// positions follow d.seq_len.  With `fp8`, packed_k / packed_v hold fp8 copies
+// (launch_pack_kv_fp8).
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark,
-                               const PagedKV* paged = nullptr);
+                               const PagedKV* paged = nullptr, const Fp8Scales* fp8 = nullptr);
+// fp8 e4m3 K and V ([Bt, G, Tk, D] bytes) packed per 8-token unit for the range kernel: bytes of
+// one copy, and the packing of both into `packed` (K copy, then V copy at packed_kv_fp8_bytes / 2).
+size_t packed_kv_fp8_bytes(const Dims& d);
+hipError_t launch_pack_kv_fp8(const Dims& d, const void* k8, const void* v8, void* packed,
+                              hipStream_t s);
 // Gated sliding-window attention (the efficient layers): every query attends to the tokens
 // t in [p - window + 1, p], with the range kernel over contiguous unit lists; K and V packed as
 // for launch_attend_split (launch_pack_kv with quad layout).

@@ -19,4 +19,5 @@ from .sgqa_oracle import (  # noqa: F401
     inclusion_rate,
     sequence_rows,
     window_rows,
+    e4m3_decode,
 )

@@ -41,7 +41,7 @@ import numpy as np
 __all__ = [
     "num_blocks", "n_selected_blocks", "query_positions", "compress", "block_scores",
     "select_blocks", "attended_tokens", "gated_attention", "forward_rows", "forward",
-    "scored_candidates", "inclusion_rate", "sequence_rows", "window_rows",
+    "scored_candidates", "inclusion_rate", "sequence_rows", "window_rows", "e4m3_decode",
 ]
 
 
@@ -248,6 +248,19 @@ def sequence_rows(inputs, seq_lens, block: int, topk_tokens: int, scale: float, 
         out[mine] = o_b
         kblk[b] = kb[0]
     return sel_out, out, kblk
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP fp8 e4m3 codes (the FP8 KV cache the pages train for: Step 5 Preview summary
+    on mo.ai.kr, section "장기 강화학습과 실행 비용").  Bit 7 is the sign, bits 3-6 the exponent
+    (bias 7), bits 0-2 the mantissa; exponent 0 is subnormal (m * 2^-9); there are no infinities
+    and S.1111.111 is NaN.  Exact in float64."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, sign * mag)
 
 
 def window_rows(inputs, window: int, scale: float, rows):

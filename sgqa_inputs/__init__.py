@@ -193,3 +193,13 @@ def generate_small(batch=1, t_q=64, t_kv=64, groups=2, heads=4, head_dim=64, ind
     w = Workload("custom", batch, t_q, t_kv, groups, heads, head_dim, index_dim, block, topk,
                  dtype, index_dtype, needles, scaled_qkv)
     return w, generate(w, device=device, seed=seed, sharp=sharp)
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Synthetic fp8 K / V for the fp8-KV variant: per-tensor amax scaling (scale = max|x| / 448)
+    and torch's round-to-nearest-even conversion to OCP e4m3.  Returns (codes as uint8 of x's
+    shape, scale as a Python float)."""
+    amax = float(x.abs().max().item())
+    scale = amax / 448.0 if amax > 0 else 1.0
+    codes = (x.to(torch.float32) / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8), scale

@@ -27,7 +27,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "sgqa.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sgqa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sgqa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):

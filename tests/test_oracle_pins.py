@@ -430,3 +430,17 @@ def test_window_one_is_own_value_and_wide_window_is_dense():
     wide = oracle.window_rows(inp, 1000, w.softmax_scale, rows)
     _, dense, _ = oracle.forward(inp, w.block, 4096, w.softmax_scale)
     np.testing.assert_allclose(wide, dense[0], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# fp8 e4m3 codes (the fp8-KV variant)
+# ----------------------------------------------------------------------------------------------
+def test_e4m3_decode_matches_torch_and_fixed_points():
+    codes = np.arange(256)
+    got = oracle.e4m3_decode(codes)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # hand-worked codes: 1.0, the largest finite value, the smallest subnormal, -2.0
+    assert oracle.e4m3_decode([0x38, 0x7E, 0x01, 0xC0]).tolist() == [1.0, 448.0, 2.0 ** -9, -2.0]
