@@ -20,4 +20,5 @@ from .sgqa_oracle import (  # noqa: F401
     sequence_rows,
     window_rows,
     e4m3_decode,
+    attention_backward,
 )

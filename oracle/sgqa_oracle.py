@@ -42,6 +42,7 @@ __all__ = [
     "num_blocks", "n_selected_blocks", "query_positions", "compress", "block_scores",
     "select_blocks", "attended_tokens", "gated_attention", "forward_rows", "forward",
     "scored_candidates", "inclusion_rate", "sequence_rows", "window_rows", "e4m3_decode",
+    "attention_backward",
 ]
 
 
@@ -261,6 +262,46 @@ def e4m3_decode(codes) -> np.ndarray:
     m = (c & 0x7).astype(np.float64)
     mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
     return np.where((e == 15) & ((c & 7) == 7), np.nan, sign * mag)
+
+
+def attention_backward(inputs, sel, dout, block: int, scale: float):
+    """Gradients of the gated attention step for a fixed selection (training at long context is
+    the pages' setting: Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성").
+    The selection comes from the indexer and is not differentiated.  Per query row (b, i, g, head)
+    with attended tokens A, s_t = scale q.k_t, P = softmax(s), O = sum_t P_t v_t and
+    out = sigmoid(gate) * O, the chain rule gives
+        dO = dout * sigmoid(gate),   dgate = dout * O * sigmoid(gate) * (1 - sigmoid(gate)),
+        dP_t = dO . v_t,   D = sum_t P_t dP_t (= dO . O),   dS_t = P_t (dP_t - D),
+        dq = scale sum_t dS_t k_t,   dk_t += scale dS_t q,   dv_t += P_t dO.
+    inputs: q, k, v, gate as for forward_rows; sel [Bt, Tq, G, n_sel]; dout like q.
+    Returns float64 (dq, dk, dv, dgate) shaped like q, k, v, gate.  Small inputs only."""
+    q, k, v, gate = (_np64(inputs[n]) for n in ("q", "k", "v", "gate"))
+    sel = np.asarray(sel)
+    dout = _np64(dout)
+    bt, t_q, G, h, d = q.shape
+    t_kv = k.shape[2]
+    pos = query_positions(t_q, t_kv)
+    dq, dk, dv, dgate = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(gate))
+    for b in range(bt):
+        for i in range(t_q):
+            p = int(pos[i])
+            for g in range(G):
+                toks = attended_tokens(sel[b, i, g], block, p, t_kv)
+                kk, vv = k[b, g, toks], v[b, g, toks]                  # [n, d]
+                for j in range(h):
+                    s = scale * (kk @ q[b, i, g, j])
+                    w = np.exp(s - s.max())
+                    P = w / w.sum()
+                    O = P @ vv
+                    sg = 1.0 / (1.0 + np.exp(-gate[b, i, g, j]))
+                    dO = dout[b, i, g, j] * sg
+                    dgate[b, i, g, j] = dout[b, i, g, j] * O * sg * (1.0 - sg)
+                    dP = vv @ dO
+                    dS = P * (dP - P @ dP)
+                    dq[b, i, g, j] = scale * (dS @ kk)
+                    dk[b, g, toks] += scale * np.outer(dS, q[b, i, g, j])
+                    dv[b, g, toks] += np.outer(P, dO)
+    return dq, dk, dv, dgate
 
 
 def window_rows(inputs, window: int, scale: float, rows):

@@ -444,3 +444,52 @@ def test_e4m3_decode_matches_torch_and_fixed_points():
     assert np.array_equal(got[ok], ref[ok])
     # hand-worked codes: 1.0, the largest finite value, the smallest subnormal, -2.0
     assert oracle.e4m3_decode([0x38, 0x7E, 0x01, 0xC0]).tolist() == [1.0, 448.0, 2.0 ** -9, -2.0]
+
+
+# ----------------------------------------------------------------------------------------------
+# backward of the gated attention step
+# ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("topk", [16, 256])
+def test_attention_backward_equals_autograd(topk):
+    """torch autograd (fp64) through dense SDPA under the selection's token mask, times
+    sigmoid(gate): the library routine's gradients equal the oracle's explicit chain rule."""
+    w, inp = generate_small(t_q=24, t_kv=60, groups=2, heads=3, head_dim=8, index_dim=4, block=4,
+                            topk=topk, seed=31)
+    sel, _, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    g = torch.Generator().manual_seed(5)
+    dout = torch.randn(inp["q"].shape, generator=g, dtype=torch.float64)
+    dq, dk, dv, dgate = oracle.attention_backward(inp, sel, dout, w.block, w.softmax_scale)
+
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv)
+    leaves = {n: inp[n].to(torch.float64).clone().requires_grad_(True) for n in ("q", "k", "v", "gate")}
+    outs = []
+    for gg in range(w.groups):
+        mask = torch.zeros(w.t_q, w.t_kv, dtype=torch.bool)
+        for i in range(w.t_q):
+            toks = oracle.attended_tokens(sel[0, i, gg], w.block, int(pos[i]), w.t_kv)
+            mask[i, torch.from_numpy(toks)] = True
+        qg = leaves["q"][0, :, gg].transpose(0, 1)                            # [h, Tq, d]
+        kg = leaves["k"][0, gg].unsqueeze(0).expand(qg.shape[0], -1, -1)
+        vg = leaves["v"][0, gg].unsqueeze(0).expand(qg.shape[0], -1, -1)
+        o = torch.nn.functional.scaled_dot_product_attention(qg, kg, vg, attn_mask=mask,
+                                                             scale=w.softmax_scale)
+        outs.append(o.transpose(0, 1) * torch.sigmoid(leaves["gate"][0, :, gg]))
+    out = torch.stack(outs, dim=1).unsqueeze(0)
+    out.backward(dout)
+    for name, mine in (("q", dq), ("k", dk), ("v", dv), ("gate", dgate)):
+        np.testing.assert_allclose(mine, leaves[name].grad.numpy(), rtol=0, atol=1e-12, err_msg=name)
+
+
+def test_attention_backward_single_token_closed_form():
+    """One attended token (p = 0): out = sigmoid(g) v_0, so dq = 0, dk_0 = 0, dv_0 = sum over
+    query heads of dout * sigmoid(g), dgate = dout * v_0 * sigmoid'(g)."""
+    w, inp = generate_small(t_q=1, t_kv=1, groups=1, heads=2, head_dim=4, index_dim=4, block=4,
+                            topk=8, seed=4)
+    sel, _, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    dout = torch.ones(inp["q"].shape, dtype=torch.float64) * 0.5
+    dq, dk, dv, dgate = oracle.attention_backward(inp, sel, dout, w.block, w.softmax_scale)
+    sg = torch.sigmoid(inp["gate"].to(torch.float64)).numpy()[0, 0, 0]        # [h, d]
+    v0 = inp["v"].to(torch.float64).numpy()[0, 0, 0]
+    assert np.abs(dq).max() == 0.0 and np.abs(dk).max() == 0.0
+    np.testing.assert_allclose(dv[0, 0, 0], (0.5 * sg).sum(axis=0), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dgate[0, 0, 0], 0.5 * v0[None, :] * sg * (1 - sg), rtol=0, atol=1e-15)
