@@ -45,8 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="128k")
-    ap.add_argument("--layer", default="sparse", choices=("sparse", "swa"),
-                    help="swa: the gated sliding-window layer on the workload's q/k/v/gate")
+    ap.add_argument("--layer", default="sparse", choices=("sparse", "swa", "backward"),
+                    help="swa: the gated sliding-window layer on the workload's q/k/v/gate; "
+                         "backward: sgqa_attend_backward for the forward's selection")
     ap.add_argument("--window", type=int, default=4096, help="sliding window (tokens) for --layer swa")
     ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: K and V stored as e4m3 codes with per-tensor scales (sgqa_forward_fp8kv)")
@@ -457,6 +458,64 @@ def main_swa(args):
     print(json.dumps(rec), flush=True)
 
 
+# ------------------------------------------------------------------------------------------------
+# backward of the attention step
+# ------------------------------------------------------------------------------------------------
+def main_backward(args):
+    import torch
+    import long_context_sparse_sgqa_amd as sg
+    from sgqa_inputs import generate, get_workload
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = sg.load_library()
+    x = generate(w, device=dev, seed=args.seed)
+    prob = sg.Problem.from_workload(w)
+    _, sel = sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"],
+                        return_sel=True)
+    g = torch.Generator(device=dev).manual_seed(args.seed + 1)
+    dout = torch.randn(x["q"].shape, generator=g, device=dev).to(torch.bfloat16)
+    n = ctypes.c_size_t()
+    lib.sgqa_attend_backward_workspace_size(ctypes.byref(prob._c()), ctypes.byref(n))
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout, workspace=ws, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        ev[j][0].record(stream)
+        sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout, workspace=ws, stream=stream)
+        ev[j][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    c = algorithmic_counts(w)
+    # five products of 2 d FLOP per (query head, attended token): S, dP, dQ, dK, dV
+    flops = 10 * w.head_dim * w.heads * c["attended"]
+    ach = flops / (gpu_ms * 1e-3) / 1e12
+    rec = {
+        "metric": f"Sparse-GQA attention backward query-tokens/s on the {w.name} workload",
+        "value": w.batch * w.t_q / (wall_ms / 1e3), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_ms, "gpu_ms_per_step": gpu_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded workload; dout ~ N(0,1); the forward's selection)",
+        "config": {"workload": f"{w.name} attention backward", "batch": w.batch, "t_q": w.t_q,
+                   "t_kv": w.t_kv, "kv_groups": w.groups, "heads_per_group": w.heads,
+                   "head_dim": w.head_dim, "block": w.block, "topk_tokens": w.topk,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "sgqa_attend_backward (recompute + attend_bwd_kernel)", "bound": "mfma",
+                     "achieved": ach, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": ach * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
+                     "work_per_launch": f"{flops:.4e} FLOP = 10*d*h per attended (query, group, token)"},
+        "cpu_baseline": None, "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -467,6 +526,8 @@ def main():
         return main_decode(args)
     if args.layer == "swa":
         return main_swa(args)
+    if args.layer == "backward":
+        return main_backward(args)
     import torch
     import long_context_sparse_sgqa_amd as sg
     from sgqa_inputs import generate, get_workload

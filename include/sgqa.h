@@ -255,6 +255,25 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Backward of step 4 (training at long context; Step 5 Preview summary on mo.ai.kr, section
+ * "모델 구조와 학습 안정성").  For a fixed selection `sel` (the indexer is not differentiated) and
+ * the output gradient dout ([Bt, Tq, G, H, D], dtype), with s_t = scale q.k_t, P = softmax(s) over
+ * the selected tokens t <= p, O = sum_t P_t v_t, out = sigmoid(gate) * O:
+ *   dO = dout * sigmoid(gate);  dgate = dout * O * sigmoid(gate) (1 - sigmoid(gate));
+ *   dS_t = P_t (dO.v_t - dO.O);  dq = scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dO
+ *   dq, dgate : [Bt, Tq, G, H, D] dtype (rounded to nearest even)
+ *   dk, dv    : [Bt, G, Tk, D] float32, overwritten (contributions of every query head summed)
+ * The forward softmax statistics are recomputed.  dk / dv are accumulated with fp32 atomics, so
+ * their low bits vary from run to run.  Supported: bf16, H == 8, D in {64, 128}, B a multiple of 8,
+ * topk_tokens / block within the grouped kernel (as for the range-split forward).
+ * --------------------------------------------------------------------------------------------- */
+sgqa_status sgqa_attend_backward_workspace_size(const sgqa_problem* prob, size_t* bytes);
+sgqa_status sgqa_attend_backward(const sgqa_problem* prob, const void* q, const void* k,
+                                 const void* v, const void* gate, const int32_t* sel,
+                                 const void* dout, void* dq, float* dk, float* dv, void* dgate,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Steps 1-4 with K and V stored as fp8.  The pages run the KV cache in FP8 (trained for it: FP8
  * KV QAT; Step 5 Preview summary on mo.ai.kr, section "장기 강화학습과 실행 비용").  Here k8 and v8
  * hold OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f /

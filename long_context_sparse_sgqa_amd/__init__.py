@@ -24,7 +24,7 @@ import torch
 
 __all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
            "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
-           "decode", "swa_workspace_size", "swa", "forward_fp8kv", "SgqaError",
+           "decode", "swa_workspace_size", "swa", "forward_fp8kv", "attend_backward", "SgqaError",
            "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,8 @@ _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
                     "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                     "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv")
+                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv",
+                    "sgqa_attend_backward_workspace_size", "sgqa_attend_backward")
 
 
 class SgqaError(RuntimeError):
@@ -151,9 +152,12 @@ def load_library():
     f32 = ctypes.c_float
     lib.sgqa_forward_fp8kv.argtypes = [P, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, vp, vp,
                                        ctypes.c_size_t, vp]
+    lib.sgqa_attend_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sgqa_attend_backward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                  "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv"):
+                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv",
+                 "sgqa_attend_backward_workspace_size", "sgqa_attend_backward"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -402,3 +406,29 @@ def swa(prob: Problem, window: int, q, k, v, gate, out=None, workspace=None, str
                         _ptr(gate, "gate", sh["q"], prob.dtype), _ptr(out, "out", sh["q"], prob.dtype),
                         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
+
+
+# ----------------------------------------------------------------------------------------------
+# backward of the attention step
+# ----------------------------------------------------------------------------------------------
+def attend_backward(prob: Problem, q, k, v, gate, sel, dout, workspace=None, stream=None):
+    """Gradients of out = sigmoid(gate) * attention for a fixed selection.
+    Returns dq, dk, dv, dgate (dq, dgate in q's dtype; dk, dv float32 [Bt, G, Tk, D])."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q.device
+    dq = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    dgate = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    dk = torch.empty(sh["k"], dtype=torch.float32, device=dev)
+    dv = torch.empty(sh["k"], dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = ctypes.c_size_t()
+        _check(lib.sgqa_attend_backward_workspace_size(ctypes.byref(prob._c()), ctypes.byref(n)))
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_attend_backward(
+        ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype), _ptr(k, "k", sh["k"], prob.dtype),
+        _ptr(v, "v", sh["k"], prob.dtype), _ptr(gate, "gate", sh["q"], prob.dtype),
+        _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(dout, "dout", sh["q"], prob.dtype),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dgate.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(stream)))
+    return dq, dk, dv, dgate

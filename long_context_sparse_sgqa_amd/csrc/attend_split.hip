@@ -621,6 +621,305 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// backward of the gated attention step (fixed selection)
+// ------------------------------------------------------------------------------------------------
+// Forward statistics for the backward, from the range partials: per row the log-sum-exp in the
+// kernel's exp2 domain, lse2 = m + log2(l), the pre-gate output O, and from dout:
+// dO = dout * sigmoid(gate) (bf16, the backward's operand), dgate = dout * O * sigmoid'(gate) and
+// Dr = dO . O (fp32).  One thread per (row, 4 d); a row's threads are consecutive lanes.
+struct StatsArgs {
+  const bf16_t* part_o;
+  const float2* part_ml;
+  const bf16_t* gate;
+  const bf16_t* dout;
+  bf16_t* d_o;
+  bf16_t* dgate;
+  float* lse2;
+  float* Dr;
+  int64_t Tq, ngroups, total_groups;
+  int G, D;
+};
+
+__global__ void __launch_bounds__(256) merge_stats_kernel(StatsArgs a) {
+  const int per_row = a.D / 4;                       // 16 or 32 lanes per row, aligned in a wave
+  const int64_t total = a.total_groups * 32 * per_row;
+  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
+       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int d0 = static_cast<int>(id % per_row) * 4;
+    const int64_t gr = id / per_row;
+    const int row = static_cast<int>(gr % 32);
+    const int64_t gq = gr / 32;
+    const int64_t qi = gq % a.ngroups;
+    const int64_t bg = gq / a.ngroups;
+    const int64_t tok = kTok * qi + (row >> 3);
+    if (tok >= a.Tq) continue;                        // whole rows: the lanes of a row agree
+    const int64_t g = bg % a.G, b = bg / a.G;
+    float mx = -1e30f;
+#pragma unroll
+    for (int r = 0; r < kRanges; ++r) mx = fmaxf(mx, a.part_ml[(gq * kRanges + r) * 32 + row].x);
+    float L = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kRanges; ++r) {
+      const int64_t pb = (gq * kRanges + r) * 32 + row;
+      const float2 ml = a.part_ml[pb];
+      const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mx);
+      L += w;
+      const uint2 pw = *reinterpret_cast<const uint2*>(a.part_o + pb * a.D + d0);
+      o[0] += bf16_to_f32(static_cast<bf16_t>(pw.x & 0xffffu)) * w;
+      o[1] += bf16_to_f32(static_cast<bf16_t>(pw.x >> 16)) * w;
+      o[2] += bf16_to_f32(static_cast<bf16_t>(pw.y & 0xffffu)) * w;
+      o[3] += bf16_to_f32(static_cast<bf16_t>(pw.y >> 16)) * w;
+    }
+    const float inv = 1.f / L;
+    const int64_t rr = ((b * a.Tq + tok) * a.G + g) * 8 + (row & 7);
+    const int64_t base = rr * a.D + d0;
+    const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + base);
+    const uint2 dw = *reinterpret_cast<const uint2*>(a.dout + base);
+    const float gv[4] = {bf16_to_f32(static_cast<bf16_t>(gw.x & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(gw.x >> 16)),
+                         bf16_to_f32(static_cast<bf16_t>(gw.y & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(gw.y >> 16))};
+    const float dv[4] = {bf16_to_f32(static_cast<bf16_t>(dw.x & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(dw.x >> 16)),
+                         bf16_to_f32(static_cast<bf16_t>(dw.y & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(dw.y >> 16))};
+    float dO[4], dg[4], part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ov = o[e] * inv;
+      const float sg = 1.f / (1.f + __expf(-gv[e]));
+      dO[e] = dv[e] * sg;
+      dg[e] = dv[e] * ov * sg * (1.f - sg);
+      part += dO[e] * ov;
+    }
+    for (int m = per_row / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+    *reinterpret_cast<uint2*>(a.d_o + base) = make_uint2(pack_bf16x2(dO[0], dO[1]), pack_bf16x2(dO[2], dO[3]));
+    *reinterpret_cast<uint2*>(a.dgate + base) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+    if (d0 == 0) {
+      a.lse2[rr] = mx + __builtin_amdgcn_logf(L);    // v_log_f32 is log2
+      a.Dr[rr] = part;
+    }
+  }
+}
+
+struct BwdArgs {
+  const bf16_t* q;
+  const bf16_t* d_o;       // dout * sigmoid(gate), bf16, q's layout
+  const float* lse2;
+  const float* Dr;
+  const bf16_t* kq;        // K, 4-token operand layout (kq_offset)
+  const bf16_t* vq;        // V, same layout
+  const bf16_t* kv;        // K, transposed unit layout [unit][d][8 tokens]
+  const uint32_t* ulist;
+  const int32_t* bounds;
+  bf16_t* dq;
+  float* dk;               // [Bt, G, Tk, D], accumulated with atomics
+  float* dv;
+  int64_t Tq, Tk, NU, pos0, ngroups, total;
+  int G, umax;
+  float scale_log2e, scale;
+};
+
+// One wave per group of 4 tokens over its whole union (all ranges), chunks of 4 units as in the
+// forward: S^T = K Q^T and dP^T = V dO^T on the same K-row permutation, P = exp2(S scale log2e -
+// lse2) under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in registers (the forward's
+// P V product with K in the transposed unit layout); dV = P^T dO and dK = scale dS^T Q through an
+// LDS transpose of P and dS, added to dv / dk with fp32 atomics.
+template <int D>
+__global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
+  constexpr int H = 8;
+  constexpr int kRowB = D * 2 + 16;                      // LDS row of Q / dO (bytes)
+  constexpr int kTRow = 32 * 2 + 16;                     // LDS row of Q^T / dO^T / P^T / dS^T
+  __shared__ __attribute__((aligned(16))) unsigned char s_q[32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_do[32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_qt[D * kTRow];
+  __shared__ __attribute__((aligned(16))) unsigned char s_dot[D * kTRow];
+  __shared__ __attribute__((aligned(16))) unsigned char s_p[32 * kTRow];
+  __shared__ __attribute__((aligned(16))) unsigned char s_ds[32 * kTRow];
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const int trow = c >> 3, head = c & 7;
+  const int64_t gq = blockIdx.x;
+  if (gq >= a.total) return;
+  const int64_t qi = gq % a.ngroups;
+  const int64_t bg = gq / a.ngroups;
+  const int g = static_cast<int>(bg % a.G);
+  const int64_t b = bg / a.G;
+  const int64_t tok0 = kTok * qi;
+  const bool rowvalid = tok0 + trow < a.Tq;
+  const int64_t pX = a.pos0 + tok0 + trow;
+  const uint32_t* list = a.ulist + gq * list_stride(a.umax);
+  const int e0 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1)]);
+  const int e1 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1) + kRanges]);
+
+  // Q and dO rows (row-major) and their transposes into LDS; lane (c, h) copies d in
+  // [D/2 h, D/2 (h+1)) of row c
+  const int64_t rr = ((b * a.Tq + (rowvalid ? tok0 + trow : tok0)) * a.G + g) * H + head;
+  {
+    const bf16_t* qrow = a.q + rr * D;
+    const bf16_t* orow = a.d_o + rr * D;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) {
+      const int d = (D / 2) * h + 8 * k;
+      const uint4 vq = rowvalid ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 vo = rowvalid ? *reinterpret_cast<const uint4*>(orow + d) : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(s_q + c * kRowB + d * 2) = vq;
+      *reinterpret_cast<uint4*>(s_do + c * kRowB + d * 2) = vo;
+      const uint32_t wq[4] = {vq.x, vq.y, vq.z, vq.w}, wo[4] = {vo.x, vo.y, vo.z, vo.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        *reinterpret_cast<uint16_t*>(s_qt + (d + e) * kTRow + c * 2) = static_cast<uint16_t>(wq[e >> 1] >> (16 * (e & 1)));
+        *reinterpret_cast<uint16_t*>(s_dot + (d + e) * kTRow + c * 2) = static_cast<uint16_t>(wo[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+  const float lse_c = rowvalid ? a.lse2[rr] : 0.f;
+  const float D_c = rowvalid ? a.Dr[rr] : 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  auto ld16 = [](const unsigned char* p) -> bf16x8_t { return bf16x8_from_u4(*reinterpret_cast<const uint4*>(p)); };
+
+  const BufRsrc krs = make_rsrc(a.kq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
+  const BufRsrc vrs = make_rsrc(a.vq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
+  const BufRsrc ktrs = make_rsrc(a.kv + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
+  float* dkg = a.dk + (b * a.G + g) * a.Tk * D;
+  float* dvg = a.dv + (b * a.G + g) * a.Tk * D;
+
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
+  auto pick4 = [](const uint32_t* v, int i) -> uint32_t {
+    return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+  };
+  const int kslot = kq_slot(c), ktok = kq_tok(c);
+  struct Ops {
+    bf16x8_t k[D / 16], v[D / 16], kt[D / 16];
+  };
+  auto load_ops = [&](int cpos, uint32_t* ent4, Ops& R) {
+    const u32x4 w = *((ConstQuadPtr)(list + cpos));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ent4[j] = cpos < e1 ? w[j] : 0u;
+    const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
+    const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
+    const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
+      R.v[kc] = buffer_load_bf16x8(vrs, kq_offset(u, D, kc, ktok, h));
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      R.kt[2 * dt] = buffer_load_bf16x8(ktrs, (ua * D + 32 * dt + c) * 16);
+      R.kt[2 * dt + 1] = buffer_load_bf16x8(ktrs, (ub * D + 32 * dt + c) * 16);
+    }
+  };
+  auto row_mask = [&](uint32_t ent) -> uint32_t {
+    const bool chose = (ent >> (kChoseShift + trow)) & 1u;
+    const int dlt = static_cast<int>(pX) - static_cast<int>(ent & kUnitMask) * 8;
+    const uint32_t causal = dlt >= 7 ? 0xffu : (dlt < 0 ? 0u : ((2u << dlt) - 1u));
+    return chose ? causal : 0u;
+  };
+
+  f32x16_t accq[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accq[dt][i] = 0.f;
+
+  auto chunk = [&](const Ops& R, const uint32_t* ent4) {
+    f32x16_t s = {}, dp = {};
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      s = mfma32x32x16(R.k[kc], ld16(s_q + c * kRowB + (16 * kc + 8 * h) * 2), s);
+      dp = mfma32x32x16(R.v[kc], ld16(s_do + c * kRowB + (16 * kc + 8 * h) * 2), dp);
+    }
+    const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool on = (msk >> i) & 1u;
+      const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2e, -lse_c)) : 0.f;
+      pv[i] = p;
+      dsv[i] = p * (dp[i] - D_c);
+    }
+    const bf16x8_t da = pack8_bf16(dsv), db = pack8_bf16(dsv + 8);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      accq[dt] = mfma32x32x16(R.kt[2 * dt], da, accq[dt]);
+      accq[dt] = mfma32x32x16(R.kt[2 * dt + 1], db, accq[dt]);
+    }
+    // P^T and dS^T tiles [token m = 8 slot + t][row], bf16
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i < 8 ? h : 2 + h) + (i & 7);
+      *reinterpret_cast<bf16_t*>(s_p + m * kTRow + c * 2) = f32_to_bf16(pv[i]);
+      *reinterpret_cast<bf16_t*>(s_ds + m * kTRow + c * 2) = f32_to_bf16(dsv[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // dV and dK tiles: C[m][d] = sum over rows; lane (c, h) holds m = 8 (r/4) + 4h + r%4, d = 32 dt + c
+    const bf16x8_t pa0 = ld16(s_p + c * kTRow + (8 * h) * 2), pa1 = ld16(s_p + c * kTRow + (16 + 8 * h) * 2);
+    const bf16x8_t sa0 = ld16(s_ds + c * kTRow + (8 * h) * 2), sa1 = ld16(s_ds + c * kTRow + (16 + 8 * h) * 2);
+    bool live[4];
+    int32_t tokb[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const uint32_t e = pick4(ent4, sl);
+      live[sl] = (e >> kChoseShift) != 0u;             // some token of the group chose the unit
+      tokb[sl] = static_cast<int32_t>(e & kUnitMask) * 8;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      f32x16_t cv = {}, ck = {};
+      cv = mfma32x32x16(pa0, ld16(s_dot + (32 * dt + c) * kTRow + (8 * h) * 2), cv);
+      cv = mfma32x32x16(pa1, ld16(s_dot + (32 * dt + c) * kTRow + (16 + 8 * h) * 2), cv);
+      ck = mfma32x32x16(sa0, ld16(s_qt + (32 * dt + c) * kTRow + (8 * h) * 2), ck);
+      ck = mfma32x32x16(sa1, ld16(s_qt + (32 * dt + c) * kTRow + (16 + 8 * h) * 2), ck);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        if (!live[sl]) continue;                        // wave-uniform
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * sl + j;
+          const int64_t tok = tokb[sl] + 4 * h + j;
+          if (tok < a.Tk) {
+            atomicAdd(dvg + tok * D + 32 * dt + c, cv[r]);
+            atomicAdd(dkg + tok * D + 32 * dt + c, ck[r] * a.scale);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  if (e0 < e1) {
+    uint32_t entA[4], entB[4];
+    Ops A, B;
+    load_ops(e0, entA, A);
+    for (int cpos = e0; cpos < e1; cpos += 8) {
+      if (cpos + 4 < e1) load_ops(cpos + 4, entB, B);
+      chunk(A, entA);
+      if (cpos + 4 >= e1) break;
+      if (cpos + 8 < e1) load_ops(cpos + 8, entA, A);
+      chunk(B, entB);
+    }
+  }
+
+  // dq = scale * acc: lane (c, h) holds d = 32 dt + 8 (i/4) + 4h + i%4 of row c
+  if (rowvalid) {
+    bf16_t* dqr = a.dq + rr * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float x0 = accq[dt][4 * i4] * a.scale, x1 = accq[dt][4 * i4 + 1] * a.scale;
+        const float x2 = accq[dt][4 * i4 + 2] * a.scale, x3 = accq[dt][4 * i4 + 3] * a.scale;
+        *reinterpret_cast<uint2*>(dqr + 32 * dt + 8 * i4 + 4 * h) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+      }
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float4* p, int64_t n4) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Token groups whose union bitmaps (kTok x words each) share one workgroup's LDS (0: none fits).
@@ -822,6 +1121,148 @@ hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, co
   if (e != hipSuccess) return e;
   return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, wa.win_m1, s,
                                  nullptr, nullptr, nullptr);
+}
+
+size_t attend_backward_bytes(const Dims& d) {
+  const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * 8;
+  return 2 * packed_kv_quad_bytes(d) + attend_split_bytes(d) + 2 * align256(rows * sizeof(float)) +
+         align256(rows * d.D * sizeof(bf16_t));
+}
+
+hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
+                                  const void* gate, const int32_t* sel, const void* dout, void* dq,
+                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
+  const int umax = static_cast<int>(units_per_query(d));
+  const size_t pkv = packed_kv_quad_bytes(d);
+  char* p = static_cast<char*>(ws);
+  char* fwd_kv = p;                  // K in the operand layout, V transposed (the forward's copies)
+  char* bwd_kv = p + pkv;            // V in the operand layout, K transposed
+  char* split = bwd_kv + pkv;
+  const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * 8;
+  float* lse2 = reinterpret_cast<float*>(split + attend_split_bytes(d));
+  float* Dr = reinterpret_cast<float*>(reinterpret_cast<char*>(lse2) + align256(rows * sizeof(float)));
+  bf16_t* d_o = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(Dr) + align256(rows * sizeof(float)));
+
+  hipError_t e = launch_pack_kv_quad(d, k, v, fwd_kv, s);
+  if (e != hipSuccess) return e;
+  e = launch_pack_kv_quad(d, v, k, bwd_kv, s);
+  if (e != hipSuccess) return e;
+  // forward recompute up to the range partials
+  const SplitBuffers sb = split_buffers(d, umax, split);
+  UnionArgs ua;
+  ua.sel = sel;
+  ua.ulist = sb.ulist;
+  ua.bounds = sb.bounds;
+  ua.Tq = d.Tq;
+  ua.pos0 = d.pos0;
+  ua.seq_len = nullptr;
+  ua.ngroups = ng;
+  ua.total = total;
+  ua.G = d.G;
+  ua.NS = d.NS;
+  ua.B = d.B;
+  ua.umax = umax;
+  ua.words = static_cast<int>((d.NU + 31) / 32);
+  ua.waves = union_waves(d);
+  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
+  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
+                     dim3(64 * ua.waves), lds, s, ua);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RangeArgs a;
+  a.q = static_cast<const bf16_t*>(q);
+  a.kp = reinterpret_cast<const bf16_t*>(fwd_kv);
+  a.vp = reinterpret_cast<const bf16_t*>(fwd_kv + pkv / 2);
+  a.ulist = sb.ulist;
+  a.bounds = sb.bounds;
+  a.part_o = sb.part_o;
+  a.part_ml = sb.part_ml;
+  a.Tq = d.Tq;
+  a.Tk = d.Tk;
+  a.NU = d.NU;
+  a.pos0 = d.pos0;
+  a.ngroups = ng;
+  a.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
+  a.G = d.G;
+  a.umax = umax;
+  a.scale_log2e = d.scale * 1.4426950408889634f;
+  a.v_scale = 1.0f;
+  a.seq_len = nullptr;
+  a.block_table = nullptr;
+  a.max_pages = a.num_pages = 0;
+  a.ul2 = 0;
+  a.win_m1 = 1 << 30;
+  const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
+  if (d.D == 128)
+    hipLaunchKernelGGL((attend_range_kernel<128, false, false>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_range_kernel<64, false, false>), grid, dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  StatsArgs st;
+  st.part_o = sb.part_o;
+  st.part_ml = sb.part_ml;
+  st.gate = static_cast<const bf16_t*>(gate);
+  st.dout = static_cast<const bf16_t*>(dout);
+  st.d_o = d_o;
+  st.dgate = static_cast<bf16_t*>(dgate);
+  st.lse2 = lse2;
+  st.Dr = Dr;
+  st.Tq = d.Tq;
+  st.ngroups = ng;
+  st.total_groups = total;
+  st.G = d.G;
+  st.D = d.D;
+  {
+    const int64_t items = total * 32 * (d.D / 4);
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(merge_stats_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, st);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dk, dv accumulate from zero
+  {
+    const int64_t n4 = d.Bt * d.G * d.Tk * d.D / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(dk), n4);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       reinterpret_cast<float4*>(dv), n4);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdArgs ba;
+  ba.q = static_cast<const bf16_t*>(q);
+  ba.d_o = d_o;
+  ba.lse2 = lse2;
+  ba.Dr = Dr;
+  ba.kq = reinterpret_cast<const bf16_t*>(fwd_kv);
+  ba.vq = reinterpret_cast<const bf16_t*>(bwd_kv);
+  ba.kv = reinterpret_cast<const bf16_t*>(bwd_kv + pkv / 2);
+  ba.ulist = sb.ulist;
+  ba.bounds = sb.bounds;
+  ba.dq = static_cast<bf16_t*>(dq);
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.Tq = d.Tq;
+  ba.Tk = d.Tk;
+  ba.NU = d.NU;
+  ba.pos0 = d.pos0;
+  ba.ngroups = ng;
+  ba.total = total;
+  ba.G = d.G;
+  ba.umax = umax;
+  ba.scale_log2e = d.scale * 1.4426950408889634f;
+  ba.scale = d.scale;
+  if (d.D == 128)
+    hipLaunchKernelGGL(attend_bwd_kernel<128>, dim3(static_cast<unsigned>(total)), dim3(64), 0, s, ba);
+  else
+    hipLaunchKernelGGL(attend_bwd_kernel<64>, dim3(static_cast<unsigned>(total)), dim3(64), 0, s, ba);
+  return hipGetLastError();
 }
 
 }  // namespace sgqa

@@ -658,6 +658,51 @@ sgqa_status sgqa_forward_fp8kv(const sgqa_problem* prob, const void* q, const vo
   return ok();
 }
 
+sgqa_status derive_backward(const sgqa_problem* prob, Derived* dv, size_t* bytes) {
+  SGQA_CHECK(derive(prob, dv));
+  if (!sgqa::attend_split_supported(dv->d))
+    return fail(SGQA_ERR_UNSUPPORTED, "the backward needs bf16, heads_per_group == 8, head_dim 64 or "
+                "128, block a multiple of 8 and topk_tokens / block within the grouped kernel");
+  *bytes = sgqa::attend_backward_bytes(dv->d);
+  return SGQA_OK;
+}
+
+sgqa_status sgqa_attend_backward_workspace_size(const sgqa_problem* prob, size_t* bytes) {
+  Derived dv;
+  size_t need;
+  SGQA_CHECK(derive_backward(prob, &dv, &need));
+  if (!bytes) return fail(SGQA_ERR_NULL, "bytes is NULL");
+  *bytes = need;
+  return ok();
+}
+
+sgqa_status sgqa_attend_backward(const sgqa_problem* prob, const void* q, const void* k,
+                                 const void* v, const void* gate, const int32_t* sel,
+                                 const void* dout, void* dq, float* dk, float* dv, void* dgate,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  Derived d;
+  size_t need;
+  SGQA_CHECK(derive_backward(prob, &d, &need));
+  SGQA_CHECK(check_ptr(q, "q"));
+  SGQA_CHECK(check_ptr(k, "k"));
+  SGQA_CHECK(check_ptr(v, "v"));
+  SGQA_CHECK(check_ptr(gate, "gate"));
+  SGQA_CHECK(check_ptr(sel, "sel"));
+  SGQA_CHECK(check_ptr(dout, "dout"));
+  SGQA_CHECK(check_ptr(dq, "dq"));
+  SGQA_CHECK(check_ptr(dk, "dk"));
+  SGQA_CHECK(check_ptr(dv, "dv"));
+  SGQA_CHECK(check_ptr(dgate, "dgate"));
+  SGQA_CHECK(check_ptr(workspace, "workspace"));
+  if (workspace_bytes < need)
+    return fail(SGQA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  hipError_t e = sgqa::launch_attend_backward(d.d, q, k, v, gate, sel, dout, dq, dk, dv, dgate,
+                                              workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
+}
+
 sgqa_status sgqa_set_stage_events(void* const* events) {
   if (!events) {
     g_stage_armed = false;

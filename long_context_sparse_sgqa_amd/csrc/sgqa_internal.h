@@ -138,6 +138,12 @@ hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, co
 size_t packed_kv_quad_bytes(const Dims& d);
 hipError_t launch_pack_kv_quad(const Dims& d, const void* k, const void* v, void* packed,
                                hipStream_t s);
+// Backward of the gated attention step for a fixed selection (range-split constraints): dq and
+// dgate in q's layout and dtype, dk / dv as fp32 [Bt, G, Tk, D] (zeroed, then accumulated).
+size_t attend_backward_bytes(const Dims& d);
+hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
+                                  const void* gate, const int32_t* sel, const void* dout, void* dq,
+                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s);
 // Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
                          const void* gate, const int32_t* sel, void* out, void* workspace,

@@ -1,0 +1,101 @@
+"""Backward of the gated attention step (sgqa_attend_backward) through the C ABI against the
+oracle's explicit chain rule (oracle.attention_backward, pinned against torch autograd), on every
+element for small shapes, and on sampled rows plus exact sums at the 32K workload."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_sgqa_amd as sg
+import oracle
+from gpu_helpers import say
+from sgqa_inputs import generate, generate_small, get_workload
+
+pytestmark = pytest.mark.gpu
+
+# The matrix cores take P, dS, dO, q, k, v as bf16 (relative rounding 2^-9 each), so a gradient
+# element's error grows with the size of the sums behind it: dv_t and dk_t add one term per query
+# row that attends to t.  Bar: max-abs error <= 1e-2 * max(1, max |ref|) -- the forward's 1e-2 for
+# gradients of size <= 1, 1 % of the largest magnitude above -- and <= 5 % of max |ref| + 1e-4.
+# The floor covers gradients that vanish exactly (a query attending one token has dq = 0): there
+# dS = P (dO.v - dO.O) keeps the ~2^-9 difference between the bf16 product and the fp32 dot.
+ATOL, REL_OF_MAX, FLOOR = 1e-2, 5e-2, 1e-4
+
+
+def check(name, got, ref):
+    got = got.detach().to("cpu", torch.float64).numpy()
+    err = float(np.abs(got - ref).max())
+    top = float(np.abs(ref).max())
+    say(f"  {name}: max-abs err {err:.3e}, max |ref| {top:.3e}")
+    assert err <= ATOL * max(1.0, top) and err <= REL_OF_MAX * top + FLOOR, (name, err, top)
+
+
+BWD_CASES = [
+    # t_q, t_kv, block, topk, groups, index_dim, sharp, head_dim, batch
+    (128, 400, 8, 128, 2, 64, False, 128, 1),
+    (64, 64, 8, 4096, 2, 32, True, 64, 1),          # dense: budget covers the context
+    (100, 333, 16, 128, 2, 64, True, 128, 2),
+    (7, 1300, 8, 256, 2, 128, False, 128, 1),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d%s-d%d-b%d" % (
+    c[0], c[1], c[2], c[3], c[4], "-sharp" if c[6] else "", c[7], c[8]))
+def test_backward_small_every_element(case):
+    t_q, t_kv, B, k, G, di, sharp, d, bt = case
+    say("case: backward", case)
+    w, x = generate_small(batch=bt, t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=d,
+                          index_dim=di, block=B, topk=k, dtype="bf16", index_dtype="bf16",
+                          scaled_qkv=True, seed=23, device="cuda", sharp=sharp)
+    prob = sg.Problem.from_workload(w)
+    xc = {n: (v.cpu() if torch.is_tensor(v) else v) for n, v in x.items()}
+    sel_ref, _, _ = oracle.forward(xc, B, k, w.softmax_scale)
+    sel = torch.from_numpy(sel_ref.astype(np.int32)).to("cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv, dgate = sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout)
+    torch.cuda.synchronize()
+    r_dq, r_dk, r_dv, r_dg = oracle.attention_backward(xc, sel_ref, dout.cpu(), B, w.softmax_scale)
+    check("dq", dq, r_dq)
+    check("dk", dk, r_dk)
+    check("dv", dv, r_dv)
+    check("dgate", dgate, r_dg)
+
+
+def test_backward_32k_sampled_rows_and_sums():
+    """32K workload: dq and dgate of sampled query rows against the oracle (they depend on that
+    row alone); dk and dv through exact sums over the tokens: sum_t dv_t = sum over every query
+    row of dO (softmax rows sum to 1) and sum_t dk_t = 0 (dS rows sum to 0)."""
+    w = get_workload("32k")
+    say("case: backward 32K")
+    x = generate(w, device="cuda", seed=0)
+    prob = sg.Problem.from_workload(w)
+    out, sel = sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"],
+                          return_sel=True)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq, dk, dv, dgate = sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout)
+    torch.cuda.synchronize()
+    toks = [0, 5, 4095, 4096, 20000, 32767]
+    xc = {n: x[n][:, toks].cpu() if n in ("q", "gate", "q_idx") else x[n].cpu()
+          for n in ("q", "gate", "q_idx", "k", "v", "k_idx")}
+    # the oracle's backward on the sampled rows alone: positions come from t_kv - t_q + i, so the
+    # sampled rows keep their positions through a one-row problem per token
+    for j, i in enumerate(toks):
+        one = {n: (xc[n][:, j:j + 1] if n in ("q", "gate", "q_idx") else xc[n][:, :, :i + 1]
+                   if n in ("k", "v") else xc[n][:, :i + 1]) for n in xc}
+        r_dq, _, _, r_dg = oracle.attention_backward(one, sel[:, i:i + 1].cpu().numpy(),
+                                                      dout[:, i:i + 1].cpu(), w.block,
+                                                      w.softmax_scale)
+        check(f"dq row {i}", dq[:, i:i + 1], r_dq)
+        check(f"dgate row {i}", dgate[:, i:i + 1], r_dg)
+    sig = torch.sigmoid(x["gate"].float())
+    dO = (dout.float() * sig)                                       # [Bt, Tq, G, H, D]
+    want_v = dO.sum(dim=(1, 3)).double()                            # [Bt, G, D]
+    got_v = dv.double().sum(dim=2)
+    err_v = float((got_v - want_v).abs().max())
+    err_k = float(dk.double().sum(dim=2).abs().max())
+    say(f"  sum dv err {err_v:.3e} (max {float(want_v.abs().max()):.3e}); sum dk {err_k:.3e}")
+    assert err_v <= 2e-2 * float(want_v.abs().max())
+    assert err_k <= 2e-2 * float(dk.double().abs().sum(dim=2).max())
+    del x, out, sel, dq, dk, dv, dgate
+    torch.cuda.empty_cache()
