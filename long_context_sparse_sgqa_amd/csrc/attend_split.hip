@@ -442,7 +442,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
-  const float ninf = -__builtin_inff();
 
   // valid-token mask (8 bits) of this lane's row for a unit entry
   auto row_mask = [&](uint32_t ent) -> uint32_t {
@@ -466,11 +465,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(k_op(K, kc), q_operand(kc), s);
     refill();
     const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
+    // masked scores become -inf: a sign-extended bit field (all ones when the bit is set) selects
+    // between the score and -inf in one bitwise op (two VALU ops per score)
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int bit = static_cast<int>(msk << (31 - i)) >> 31;      // -1 valid, 0 masked
-      t[i] = s[i] + __int_as_float(~bit & static_cast<int>(0xff800000u));
+      const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(msk), i, 1));
+      t[i] = __uint_as_float((__float_as_uint(s[i]) & m) | (~m & 0xff800000u));
     }
     float mx = fmaxf(fmaxf(t[0], t[1]), t[2]);
 #pragma unroll

@@ -212,15 +212,6 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     store_tile(0);
   }
   __syncthreads();
-  auto scores16 = [&](const unsigned char* src, int n) -> f32x4_t {
-    f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < DI / 32; ++kc) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src + (n * 16 + lr) * kRowBytes + kc * 64 + lg * 16);
-      c = mfma16x16x32(qa[kc], bf16x8_from_u4(u), c);
-    }
-    return c;
-  };
   int* row_cnt = &s_cnt[wave * 16 + lg * 4];
   // Candidate stores go through a buffer descriptor over this workgroup's rows and are issued for
   // every lane: lanes without a candidate use an out-of-range offset, which the hardware drops.
