@@ -132,19 +132,11 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
     }
   }
   // exclusive prefix of `mine` over the lanes, and the totals
-  int incl = mine;
-#pragma unroll
-  for (int o2 = 1; o2 < 64; o2 <<= 1) {
-    const int v = __shfl_up(incl, o2, 64);
-    if (lane >= o2) incl += v;
-  }
-  const int nu = __shfl(incl, 63, 64);
+  const int incl = wave_inclusive_scan(mine);
+  const int nu = __builtin_amdgcn_readlane(incl, 63);
   int pos = incl - mine;
 #pragma unroll
-  for (int r = 1; r < kRanges; ++r) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) below[r] += __shfl_xor(below[r], m, 64);
-  }
+  for (int r = 1; r < kRanges; ++r) below[r] = wave_total(below[r]);
   below[0] = 0;
   below[kRanges] = nu;
   int start[kRanges + 1];

@@ -118,4 +118,42 @@ __device__ __forceinline__ float max_with_other_half(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Wave-wide reductions and scans on DPP (data-parallel primitives on rows of 16 lanes) instead of
+// ds_bpermute: no LDS round trip and no lgkmcnt wait per step.  All 64 lanes must be active.
+// DPP controls: quad_perm [1,0,3,2] = 0xb1, [2,3,0,1] = 0x4e, row_half_mirror = 0x141,
+// row_mirror = 0x140, row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+//
+// Reduction: after the quad exchanges and the two mirrors every lane holds its row's result;
+// the four row results are read into scalars and combined.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xb1, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4e, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xf, 0xf, false)));
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t r2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t r3 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ int wave_total(int v) {
+  return static_cast<int>(wave_reduce_u32(static_cast<uint32_t>(v),
+                                          [](uint32_t x, uint32_t y) { return x + y; }));
+}
+
+// Inclusive prefix sum over lanes 0..63: a shift-and-add scan inside each row of 16 lanes (lanes
+// shifted in from outside the row read 0), then the last lane of row 0 is added to row 1 and of
+// row 2 to row 3, then lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 }  // namespace sgqa

@@ -12,8 +12,8 @@
 //      the row's threshold (kept as the top 16 bits of the order-preserving key: any threshold is
 //      correct, it only sizes the candidate list);
 //   2. filter: every causal score, column tiles of K_blk staged in LDS (double-buffered) and
-//      shared by the 4 waves; a wave owns 16 whole rows, so its ballot-ordered appends keep each
-//      row's (key, block) candidates in ascending block order.
+//      shared by the 4 waves; a passing score takes the next slot of its row from a per-row LDS
+//      counter, so a row's list is unordered.
 // select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
 //   candidates held in registers, then an ordered ballot emit of keys > tau and the lowest-indexed
 //   keys == tau.  Exact whenever at least NS-1 candidates passed (every member of the top set is
@@ -44,11 +44,6 @@ __device__ __forceinline__ float key_threshold_to_float(uint32_t thr) {
   return (thr & 0x80000000u) ? __uint_as_float(thr & 0x7fffffffu) : __uint_as_float(~thr);
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 struct FilterArgs {
   const bf16_t* q_idx;
@@ -133,6 +128,7 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     }
     __syncthreads();
     // per row: the r-th largest sampled key (top 16 bits), one row at a time per wave
+#pragma unroll 1
     for (int rloc = 0; rloc < 16; ++rloc) {
       const int local = wave * 16 + rloc;
       uint32_t thr = 0u;
@@ -150,12 +146,13 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
             kv[e] = s < nvalid ? samp[local * kSamp + s] : 0u;
           }
           uint32_t prefix = 0u;
+#pragma unroll 1
           for (int bit = 15; bit >= 0; --bit) {
             const uint32_t cand = prefix | (1u << bit);
             int c = 0;
 #pragma unroll
-            for (int e = 0; e < kSamp / 64; ++e) c += kv[e] >= cand ? 1 : 0;
-            if (wave_sum(c) >= r) prefix = cand;
+            for (int e = 0; e < kSamp / 64; ++e) c += __popcll(__ballot(kv[e] >= cand));
+            if (c >= r) prefix = cand;
           }
           thr = prefix << 16;
         }
@@ -301,10 +298,10 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t ta
   uint32_t tau = tau0;
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
-    int c = 0;
+    int c = 0;                                       // ballots counted on the scalar unit
 #pragma unroll
-    for (int e = 0; e < NE; ++e) c += key[e] >= cand ? 1 : 0;
-    if (wave_sum(c) >= need) tau = cand;
+    for (int e = 0; e < NE; ++e) c += __popcll(__ballot(key[e] >= cand));
+    if (c >= need) tau = cand;
   }
   return tau;
 }
@@ -350,11 +347,8 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
       kmax = max(kmax, key[e]);
     }
   }
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) {
-    kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o2, 64)));
-    kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o2, 64)));
-  }
+  kmin = wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+  kmax = wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   // tau = the need-th largest key: the largest v with #(key >= v) >= need.  kmin <= tau <= kmax,
   // so the bits above the highest bit where kmin and kmax differ are those of kmin.  Lists of at
   // most 1024 candidates (the usual size) search over the first 16 register slots only.
@@ -383,7 +377,7 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
       atomicOr(&beq[col[e] >> 5], 1u << (col[e] & 31));
     }
   }
-  int take_eq = need - wave_sum(gt);
+  int take_eq = need - wave_total(gt);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // each lane scans a contiguous run of words; ties are taken in block order up to take_eq
@@ -391,13 +385,7 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   const int w0 = lane * per, w1 = min(w0 + per, nw);
   int n_eq = 0;
   for (int w = w0; w < w1; ++w) n_eq += __popc(beq[w]);
-  int eq_before = n_eq;                                 // inclusive prefix over lanes
-#pragma unroll
-  for (int o2 = 1; o2 < 64; o2 <<= 1) {
-    const int v = __shfl_up(eq_before, o2, 64);
-    if (lane >= o2) eq_before += v;
-  }
-  eq_before -= n_eq;
+  int eq_before = wave_inclusive_scan(n_eq) - n_eq;     // exclusive prefix over lanes
   int n_sel = 0;
   for (int w = w0; w < w1; ++w) {
     uint32_t e = beq[w];
@@ -412,13 +400,7 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
     bgt[w] = x;
     n_sel += __popc(x);
   }
-  int pos = n_sel;                                      // exclusive prefix over lanes
-#pragma unroll
-  for (int o2 = 1; o2 < 64; o2 <<= 1) {
-    const int v = __shfl_up(pos, o2, 64);
-    if (lane >= o2) pos += v;
-  }
-  pos -= n_sel;
+  int pos = wave_inclusive_scan(n_sel) - n_sel;         // exclusive prefix over lanes
   for (int w = w0; w < w1; ++w) {
     uint32_t x = bgt[w];
     while (x) {

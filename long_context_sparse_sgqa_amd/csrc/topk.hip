@@ -110,12 +110,7 @@ __device__ uint32_t radix_select(const Src& src, int n, int need, int* take_eq, 
     __syncthreads();
     // inclusive scan over digits from the top: thread t holds digit 255 - t
     const int h = static_cast<int>(sh.hist[255 - t]);
-    int incl = h;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane_id() >= o) incl += y;
-    }
+    int incl = wave_inclusive_scan(h);
     if (lane_id() == 63) sh.wave_cnt[t >> 6] = incl;
     __syncthreads();
     for (int w = 0; w < (t >> 6); ++w) incl += sh.wave_cnt[w];
