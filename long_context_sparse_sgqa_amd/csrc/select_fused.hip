@@ -296,6 +296,7 @@ constexpr int kSelPer = 32;        // candidates per lane held in registers (cap
 template <int NE>
 __device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t tau0, int top, int need) {
   uint32_t tau = tau0;
+#pragma unroll 1
   for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int c = 0;                                       // ballots counted on the scalar unit
@@ -350,13 +351,16 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   kmin = wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
   kmax = wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
   // tau = the need-th largest key: the largest v with #(key >= v) >= need.  kmin <= tau <= kmax,
-  // so the bits above the highest bit where kmin and kmax differ are those of kmin.  Lists of at
-  // most 1024 candidates (the usual size) search over the first 16 register slots only.
+  // so the bits above the highest bit where kmin and kmax differ are those of kmin.  The search
+  // counts over the register slots in use only (16, 20, 24 or all 32 per lane).
   const uint32_t diff = kmin ^ kmax;
   const int top = diff ? 31 - __clz(diff) : -1;
   const uint32_t tau0 = top >= 0 ? (kmin & ~((2u << top) - 1u)) : kmin;
-  const uint32_t tau = m <= 16 * 64 ? kth_largest<16>(key, tau0, top, need)
-                                    : kth_largest<kSelPer>(key, tau0, top, need);
+  const int ne = (m + 63) >> 6;                          // register slots in use per lane
+  const uint32_t tau = ne <= 16   ? kth_largest<16>(key, tau0, top, need)
+                       : ne <= 20 ? kth_largest<20>(key, tau0, top, need)
+                       : ne <= 24 ? kth_largest<24>(key, tau0, top, need)
+                                  : kth_largest<kSelPer>(key, tau0, top, need);
 
   // bitmaps over blocks 0 .. o-1: above tau, equal to tau
   const int nw = static_cast<int>((o + 31) >> 5);
