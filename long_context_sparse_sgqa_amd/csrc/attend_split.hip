@@ -569,49 +569,53 @@ struct MergeArgs {
   int G, D;
 };
 
+// One thread per (row, 8 d): 16-byte loads of each partial and of the gate, one 16-byte store.
 __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
-  const int per_row = a.D / 4;
-  const int64_t total = a.total_groups * 32 * per_row;
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int d0 = static_cast<int>(id % per_row) * 4;
-    const int64_t gr = id / per_row;                 // gq * 32 + row
-    const int row = static_cast<int>(gr % 32);
-    const int64_t gq = gr / 32;
-    const int64_t qi = gq % a.ngroups;
-    const int64_t bg = gq / a.ngroups;
-    const int64_t tok = kTok * qi + (row >> 3);
-    if (tok >= a.Tq) continue;
-    const int64_t g = bg % a.G, b = bg / a.G;
-    float mx = -1e30f;
+  const int per_row = a.D / 8;                         // 16 (D = 128) or 8 (D = 64) threads per row
+  const int64_t gr = static_cast<int64_t>(blockIdx.x) * (256 / per_row) + threadIdx.x / per_row;
+  if (gr >= a.total_groups * 32) return;
+  const int d0 = static_cast<int>(threadIdx.x % per_row) * 8;
+  const int row = static_cast<int>(gr & 31);
+  const int64_t gq = gr >> 5;
+  const int64_t qi = gq % a.ngroups;
+  const int64_t bg = gq / a.ngroups;
+  const int64_t tok = kTok * qi + (row >> 3);
+  if (tok >= a.Tq) return;
+  const int64_t g = bg % a.G, b = bg / a.G;
+  float2 ml[kRanges];
+  float mx = -1e30f;
 #pragma unroll
-    for (int r = 0; r < kRanges; ++r) mx = fmaxf(mx, a.part_ml[(gq * kRanges + r) * 32 + row].x);
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int r = 0; r < kRanges; ++r) {
-      const int64_t pb = (gq * kRanges + r) * 32 + row;
-      const float2 ml = a.part_ml[pb];
-      const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mx);     // partial sum at the common max
-      L += w;
-      const uint2 pw = *reinterpret_cast<const uint2*>(a.part_o + pb * a.D + d0);
-      o.x += bf16_to_f32(static_cast<bf16_t>(pw.x & 0xffffu)) * w;
-      o.y += bf16_to_f32(static_cast<bf16_t>(pw.x >> 16)) * w;
-      o.z += bf16_to_f32(static_cast<bf16_t>(pw.y & 0xffffu)) * w;
-      o.w += bf16_to_f32(static_cast<bf16_t>(pw.y >> 16)) * w;
-    }
-    const float inv = 1.f / L;
-    const int64_t obase = (((b * a.Tq + tok) * a.G + g) * 8 + (row & 7)) * a.D + d0;
-    const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + obase);
-    const float g0 = bf16_to_f32(static_cast<bf16_t>(gw.x & 0xffffu));
-    const float g1 = bf16_to_f32(static_cast<bf16_t>(gw.x >> 16));
-    const float g2 = bf16_to_f32(static_cast<bf16_t>(gw.y & 0xffffu));
-    const float g3 = bf16_to_f32(static_cast<bf16_t>(gw.y >> 16));
-    uint2 ow;
-    ow.x = pack_bf16x2(o.x * inv / (1.f + __expf(-g0)), o.y * inv / (1.f + __expf(-g1)));
-    ow.y = pack_bf16x2(o.z * inv / (1.f + __expf(-g2)), o.w * inv / (1.f + __expf(-g3)));
-    *reinterpret_cast<uint2*>(a.out + obase) = ow;
+  for (int r = 0; r < kRanges; ++r) {
+    ml[r] = a.part_ml[(gq * kRanges + r) * 32 + row];
+    mx = fmaxf(mx, ml[r].x);
   }
+  float L = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kRanges; ++r) {
+    const int64_t pb = (gq * kRanges + r) * 32 + row;
+    const float w = ml[r].y * __builtin_amdgcn_exp2f(ml[r].x - mx);   // partial sum at the common max
+    L += w;
+    const uint4 pw = *reinterpret_cast<const uint4*>(a.part_o + pb * a.D + d0);
+    const uint32_t pv[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] += bf16_to_f32(static_cast<bf16_t>(pv[j] & 0xffffu)) * w;
+      o[2 * j + 1] += bf16_to_f32(static_cast<bf16_t>(pv[j] >> 16)) * w;
+    }
+  }
+  const float inv = 1.f / L;
+  const int64_t obase = (((b * a.Tq + tok) * a.G + g) * 8 + (row & 7)) * a.D + d0;
+  const uint4 gw = *reinterpret_cast<const uint4*>(a.gate + obase);
+  const uint32_t gv[4] = {gw.x, gw.y, gw.z, gw.w};
+  uint32_t ov[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float g0 = bf16_to_f32(static_cast<bf16_t>(gv[j] & 0xffffu));
+    const float g1 = bf16_to_f32(static_cast<bf16_t>(gv[j] >> 16));
+    ov[j] = pack_bf16x2(o[2 * j] * inv / (1.f + __expf(-g0)), o[2 * j + 1] * inv / (1.f + __expf(-g1)));
+  }
+  *reinterpret_cast<uint4*>(a.out + obase) = make_uint4(ov[0], ov[1], ov[2], ov[3]);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1029,9 +1033,8 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
   m.total_groups = total;
   m.G = d.G;
   m.D = d.D;
-  const int64_t items = total * 32 * (d.D / 4);
-  int64_t blocks = (items + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t rows_per_block = 256 / (d.D / 8);
+  const int64_t blocks = (total * 32 + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(merge_ranges_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, m);
   return hipGetLastError();
 }
