@@ -86,25 +86,48 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int64_t pos0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq);
   const int64_t u_end = group_u_end(pos0, tok0, a.Tq);
   const int nw = static_cast<int>((u_end + 31) >> 5);
+  const int U = a.B >> 3;                               // units per block
+  // The selections of budgets up to 512 blocks are loaded at once (8 entries per lane and token),
+  // so the four tokens cost one memory round trip, and the bitmaps are cleared meanwhile.
+  constexpr int kPer = 8;
+  int blk[kTok][kPer];
+  const bool in_regs = a.NS <= 64 * kPer;
+  if (in_regs) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      const int64_t tt = tok0 + t < a.Tq ? tok0 + t : tok0;
+      const int32_t* selrow = a.sel + ((b * a.Tq + tt) * a.G + g) * a.NS;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int e = lane + 64 * k;
+        blk[t][k] = (e < a.NS && tok0 + t < a.Tq) ? selrow[e] : -1;
+      }
+    }
+  }
   for (int w = lane; w < nw; w += 64) {
 #pragma unroll
     for (int t = 0; t < kTok; ++t) bm[t * a.words + w] = 0u;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int U = a.B >> 3;                               // units per block
-  for (int t = 0; t < kTok; ++t) {
-    if (tok0 + t >= a.Tq) break;
+  auto mark = [&](int t, int bk) {
     const int64_t p = pos0 + tok0 + t;
     const int64_t o = p / a.B, last_unit = p >> 3;
-    const int32_t* selrow = a.sel + ((b * a.Tq + tok0 + t) * a.G + g) * a.NS;
-    uint32_t* bmt = bm + t * a.words;
-    for (int e = lane; e < a.NS; e += 64) {
-      const int blk = selrow[e];
-      if (blk < 0 || blk > o) continue;
-      for (int k = 0; k < U; ++k) {
-        const int64_t u = static_cast<int64_t>(blk) * U + k;
-        if (u <= last_unit) atomicOr(&bmt[u >> 5], 1u << (u & 31));
-      }
+    if (bk < 0 || bk > o) return;
+    for (int k = 0; k < U; ++k) {
+      const int64_t u = static_cast<int64_t>(bk) * U + k;
+      if (u <= last_unit) atomicOr(&bm[t * a.words + (u >> 5)], 1u << (u & 31));
+    }
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) mark(t, blk[t][k]);
+  } else {
+    for (int t = 0; t < kTok; ++t) {
+      if (tok0 + t >= a.Tq) break;
+      const int32_t* selrow = a.sel + ((b * a.Tq + tok0 + t) * a.G + g) * a.NS;
+      for (int e = lane; e < a.NS; e += 64) mark(t, selrow[e]);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
