@@ -327,12 +327,18 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
     return;
   }
   const int need = a.NS - 1;
-  const int m = a.cnt[rr];
-  if (m < need || m > a.cap) {
-    if (lane == 0) a.fail_list[atomicAdd(a.fail_count, 1)] = static_cast<int32_t>(rr);
-    return;
-  }
+  // The first 16 slots per lane (the usual list size) are loaded together with the count: they lie
+  // inside the row's capacity region whatever the count, and slots past it are discarded below.
+  // A row whose count is outside [NS - 1, cap] leaves for the exact fallback only after the keys
+  // are reduced, so that no branch stands between these loads and the count.
   const uint64_t* cr = a.cand + rr * a.cap;
+  constexpr int kSpec = 16;
+  uint64_t spec[kSpec];
+#pragma unroll
+  for (int e = 0; e < kSpec; ++e) spec[e] = cr[e * 64 + lane];
+  const int m_raw = a.cnt[rr];
+  const bool fail = m_raw < need || m_raw > a.cap;
+  const int m = fail ? 0 : m_raw;
   uint32_t key[kSelPer], col[kSelPer];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -340,7 +346,14 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
     const int x = e * 64 + lane;
     key[e] = 0u;
     col[e] = 0u;
-    if (x < m) {
+    if (e < kSpec) {                                  // branch-free use of the loaded slots
+      const bool ok = x < m;
+      const uint32_t k = order_key_f(__uint_as_float(static_cast<uint32_t>(spec[e] >> 32)));
+      key[e] = ok ? k : 0u;
+      col[e] = ok ? static_cast<uint32_t>(spec[e]) : 0u;
+      kmin = ok ? min(kmin, k) : kmin;
+      kmax = ok ? max(kmax, k) : kmax;
+    } else if (x < m) {
       const uint64_t v = cr[x];
       key[e] = order_key_f(__uint_as_float(static_cast<uint32_t>(v >> 32)));
       col[e] = static_cast<uint32_t>(v);
@@ -350,6 +363,10 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   }
   kmin = wave_reduce_u32(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
   kmax = wave_reduce_u32(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (fail) {
+    if (lane == 0) a.fail_list[atomicAdd(a.fail_count, 1)] = static_cast<int32_t>(rr);
+    return;
+  }
   // tau = the need-th largest key: the largest v with #(key >= v) >= need.  kmin <= tau <= kmax,
   // so the bits above the highest bit where kmin and kmax differ are those of kmin.  The search
   // counts over the register slots in use only (16, 20, 24 or all 32 per lane).
