@@ -107,24 +107,68 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     if (!c_valid[e]) c_rr[e] = 0;
   }
 
+  const int64_t ntiles = (o_max + kCols - 1) / kCols;
+  // staging: 128 blocks x DI bf16 = 128 x (DI/8) 16-byte pieces over 256 threads; the next tile
+  // is fetched into registers before the current one is multiplied and written to LDS after it
+  constexpr int kPer = kCols * (DI / 8) / 256;
+  uint4 pre[kPer];
+  auto load_tile = [&](int64_t t) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int pc = threadIdx.x + k * 256;
+      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
+      const int64_t col = t * kCols + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(kb + (col < a.NB ? col : a.NB - 1) * DI + part * 8);
+      pre[k] = col < a.NB ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* dst = lds + buf * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int pc = threadIdx.x + k * 256;
+      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
+      *reinterpret_cast<uint4*>(dst + row * kRowBytes + part * 16) = pre[k];
+    }
+  };
+  // the first tile's loads are issued now: their latency passes under the sampling phase (the LDS
+  // they go to is the sample area until the thresholds are taken)
+  if (ntiles > 0) load_tile(0);
+
   // ---------------- phase 1: sampled scores -> per-row threshold ----------------
   const bool sampling = o_max > a.cap;
   if (sampling) {
     const int64_t stride = (o_max + kSamp - 1) / kSamp;
     uint16_t* samp = reinterpret_cast<uint16_t*>(lds);
-    for (int n = 0; n < kSamp / 16; ++n) {
-      const int64_t col = (static_cast<int64_t>(n) * 16 + lr) * stride;
-      const bool ok = col < a.NB;
-      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // four column steps per batch: their 16 operand loads are issued before the products (columns
+    // past NB load the last block and are zeroed, so no branch splits the batch)
+    constexpr int kBatch = 4;
+#pragma unroll 1
+    for (int n0 = 0; n0 < kSamp / 16; n0 += kBatch) {
+      uint4 bb[kBatch][DI / 32];
+      bool ok[kBatch];
 #pragma unroll
-      for (int kc = 0; kc < DI / 32; ++kc) {
-        const bf16x8_t bb = ok ? load_bf16x8(kb + col * DI + kc * 32 + lg * 8) : zero_bf16x8();
-        c = mfma16x16x32(qa[kc], bb, c);
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t col = (static_cast<int64_t>(n0 + j) * 16 + lr) * stride;
+        ok[j] = col < a.NB;
+        const int64_t cc = ok[j] ? col : a.NB - 1;
+#pragma unroll
+        for (int kc = 0; kc < DI / 32; ++kc)
+          bb[j][kc] = *reinterpret_cast<const uint4*>(kb + cc * DI + kc * 32 + lg * 8);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        samp[(wave * 16 + lg * 4 + e) * kSamp + n * 16 + lr] =
-            static_cast<uint16_t>(order_key_f(c[e]) >> 16);
+      for (int j = 0; j < kBatch; ++j) {
+        f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < DI / 32; ++kc) {
+          const uint4 u = ok[j] ? bb[j][kc] : make_uint4(0u, 0u, 0u, 0u);
+          c = mfma16x16x32(qa[kc], bf16x8_from_u4(u), c);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          samp[(wave * 16 + lg * 4 + e) * kSamp + (n0 + j) * 16 + lr] =
+              static_cast<uint16_t>(order_key_f(c[e]) >> 16);
+      }
     }
     __syncthreads();
     // per row: the r-th largest sampled key (top 16 bits), one row at a time per wave
@@ -177,37 +221,10 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   // A candidate is (float bits of the score << 32 | block).  Appends take their slot from a per-row
   // LDS counter, so a row's list is in no particular order (the select kernel orders its output).
   if (threadIdx.x < kRows) s_cnt[threadIdx.x] = 0;
-  const int64_t ntiles = (o_max + kCols - 1) / kCols;
   // tiles below every row's causal limit need no per-column check
   const int64_t o_min = row_o(0, nullptr);
   const int64_t full_tiles = o_min / kCols;
-  // staging: 128 blocks x DI bf16 = 128 x (DI/8) 16-byte pieces over 256 threads; the next tile
-  // is fetched into registers before the current one is multiplied and written to LDS after it
-  constexpr int kPer = kCols * (DI / 8) / 256;
-  uint4 pre[kPer];
-  auto load_tile = [&](int64_t t) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int pc = threadIdx.x + k * 256;
-      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
-      const int64_t col = t * kCols + row;
-      pre[k] = col < a.NB ? *reinterpret_cast<const uint4*>(kb + col * DI + part * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* dst = lds + buf * kTileBytes;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int pc = threadIdx.x + k * 256;
-      const int row = pc / (DI / 8), part = pc - row * (DI / 8);
-      *reinterpret_cast<uint4*>(dst + row * kRowBytes + part * 16) = pre[k];
-    }
-  };
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) store_tile(0);
   __syncthreads();
   int* row_cnt = &s_cnt[wave * 16 + lg * 4];
   // Candidate stores go through a buffer descriptor over this workgroup's rows and are issued for
