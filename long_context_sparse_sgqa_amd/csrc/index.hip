@@ -140,10 +140,11 @@ __global__ void __launch_bounds__(256) index_rows32_kernel(const bf16_t* __restr
   const int64_t seq = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 31, h = lane >> 5;
-  int64_t b, i;
-  int g;
-  map.at(seq * seq_rows + seq_rows - 1, b, i, g);
-  const int64_t o_max = map.own_block(b, i);
+  // All rows of the workgroup belong to sequence b0 + seq: row r is token i0 + r / G, group r % G,
+  // so one load of the sequence's length gives every row's position.
+  const int64_t b = map.b0 + seq;
+  const int64_t p0 = seq_pos0(map.seq_len, b, map.pos0, map.Tq) + map.i0;   // position of row 0's token
+  const int64_t o_max = (p0 + (seq_rows - 1) / map.G) / map.B;
   const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * slab_cols;
   const int64_t c_end = min(c_begin + slab_cols, o_max);
   if (c_begin >= c_end) return;
@@ -151,38 +152,58 @@ __global__ void __launch_bounds__(256) index_rows32_kernel(const bf16_t* __restr
   bf16x8_t qa[DI / 16];
   {
     const bool ok = c < seq_rows;
-    map.at(seq * seq_rows + (ok ? c : 0), b, i, g);
-    const bf16_t* qrow = q_idx + ((b * map.Tq + i) * map.G + g) * DI;
+    const int row = ok ? c : 0;
+    const bf16_t* qrow = q_idx + ((b * map.Tq + map.i0 + row / map.G) * map.G + row % map.G) * DI;
 #pragma unroll
     for (int kc = 0; kc < DI / 16; ++kc) qa[kc] = ok ? load_bf16x8(qrow + 16 * kc + 8 * h) : zero_bf16x8();
   }
-  // causal limit and score row of each output row of this lane (o = 0 past the sequence's rows)
+  // causal limit and score-row offset of each output row of this lane (o = 0 past the sequence's
+  // rows).  Scores are written through a buffer descriptor over the sequence's rows with no branch:
+  // masked entries take an out-of-range offset, which the hardware drops, so the compiler can count
+  // the stores and the next step's loads stay in flight across them.
   int32_t o_r[16];
-  float* dst_r[16];
+  int32_t off_r[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = 8 * (r >> 2) + 4 * h + (r & 3);
     const bool ok = row < seq_rows;
-    const int64_t rr = seq * seq_rows + (ok ? row : 0);
-    map.at(rr, b, i, g);
-    o_r[r] = ok ? static_cast<int32_t>(map.own_block(b, i)) : 0;
-    dst_r[r] = scores + rr * NB;
+    o_r[r] = ok ? static_cast<int32_t>((p0 + row / map.G) / map.B) : 0;
+    off_r[r] = static_cast<int32_t>((ok ? row : 0) * NB * 4);
   }
-  map.at(seq * seq_rows, b, i, g);
+  const BufRsrc srs = make_rsrc(scores + seq * seq_rows * NB, seq_rows * NB * 4);
   const bf16_t* kb = k_blk + b * kblk_stride * DI;
-  for (int64_t col0 = c_begin + 32 * wave; col0 < c_end; col0 += 128) {
+  // The next step's block keys are loaded before this step's products, unconditionally (columns
+  // past NB load the last block; their scores are never stored, since every row's causal limit is
+  // below NB), so no branch hides the loads from the compiler's wait counting and each step's loads
+  // overlap the previous step's products and stores.  Two register sets are used in turn (a copy
+  // between them would wait for the loads).
+  auto load_keys = [&](int64_t col0, uint4* kk) {
     const int64_t col = col0 + c;
-    const bool ok = col < NB;
-    bf16x8_t kk[DI / 16];
+    const int64_t cc = col < NB ? col : NB - 1;
 #pragma unroll
     for (int kc = 0; kc < DI / 16; ++kc)
-      kk[kc] = ok ? load_bf16x8(kb + col * DI + 16 * kc + 8 * h) : zero_bf16x8();
+      kk[kc] = *reinterpret_cast<const uint4*>(kb + cc * DI + 16 * kc + 8 * h);
+  };
+  int64_t col0 = c_begin + 32 * wave;
+  uint4 kA[DI / 16], kB[DI / 16];
+  load_keys(col0, kA);
+  auto step = [&](const uint4* kcur, uint4* knext) {
+    load_keys(col0 + 128, knext);
+    const int64_t col = col0 + c;
     f32x16_t acc = {};
 #pragma unroll
-    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], kk[kc], acc);
+    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], bf16x8_from_u4(kcur[kc]), acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (col < o_r[r]) dst_r[r][col] = acc[r];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), srs,
+                                            col < o_r[r] ? off_r[r] + static_cast<int32_t>(col) * 4 : 0x7fffffff,
+                                            0, 0);
+    col0 += 128;
+  };
+  while (col0 < c_end) {
+    step(kA, kB);
+    if (col0 >= c_end) break;
+    step(kB, kA);
   }
 }
 
