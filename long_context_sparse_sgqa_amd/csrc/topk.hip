@@ -191,30 +191,65 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
 
     // stream the row once; each wave keeps its contiguous quarter's survivors in order
     const int wave = t >> 6, lane = lane_id();
-    const int per_wave = (n + kWaves - 1) / kWaves;
+    const int per_wave = ((n + kWaves - 1) / kWaves + 3) & ~3;   // multiple of 4: aligned quads
     const int lo = wave * per_wave;
     const int hi = min(n, lo + per_wave);
     int cnt = 0;
-    // kUnroll loads in flight per lane, then the survivors of each 64-wide step in index order
-    constexpr int kUnroll = 8;
-    for (int x0 = lo; x0 < hi; x0 += 64 * kUnroll) {
-      uint32_t k[kUnroll];
+    // survivors of one 64-lane step in index order (lane l holds the keys x .. x + nq - 1)
+    const uint64_t below = (1ull << lane) - 1ull;
+    auto keep_step = [&](const uint32_t* kq, int x, int nq) {
+      bool keep[4];
+      uint64_t bal[4];
+      int before = 0;
 #pragma unroll
-      for (int e = 0; e < kUnroll; ++e) {
-        const int x = x0 + 64 * e + lane;
-        k[e] = (x < hi) ? row.key(x) : 0u;
+      for (int q = 0; q < 4; ++q) {
+        keep[q] = q < nq && (x + q < hi) && kq[q] >= guess;
+        bal[q] = __ballot(keep[q]);
+        before += __popcll(bal[q] & below);
+      }
+      int mine = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pos = cnt + before + mine;
+        if (keep[q] && pos < kSegCap) {
+          sh.key[wave * kSegCap + pos] = kq[q];
+          sh.idx[wave * kSegCap + pos] = x + q;
+        }
+        mine += keep[q] ? 1 : 0;
       }
 #pragma unroll
-      for (int e = 0; e < kUnroll; ++e) {
-        const int x = x0 + 64 * e + lane;
-        const bool keep = (x < hi) && k[e] >= guess;
-        const uint64_t bal = __ballot(keep);
-        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-        if (keep && pos < kSegCap) {
-          sh.key[wave * kSegCap + pos] = k[e];
-          sh.idx[wave * kSegCap + pos] = x;
+      for (int q = 0; q < 4; ++q) cnt += __popcll(bal[q]);
+    };
+    if ((reinterpret_cast<uintptr_t>(row.s) & 15u) == 0u) {
+      // 16-byte loads through a descriptor over the candidates (reads past o return 0, and the keep
+      // test masks them): lane l of a 256-wide step holds keys 4l .. 4l+3, kUnroll steps in flight.
+      // A survivor's slot counts the survivors of lower lanes (all four components) and of its own
+      // lane's lower components, so every wave segment stays in index order.
+      constexpr int kUnroll = 8;
+      const BufRsrc rs = make_rsrc(row.s, static_cast<int64_t>(n) * 4);
+      for (int x0 = lo; x0 < hi; x0 += 256 * kUnroll) {
+        uint32_t k[kUnroll][4];
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (x0 + 256 * e + 4 * lane) * 4, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) k[e][q] = order_key(__uint_as_float(v[q]));
         }
-        cnt += __popcll(bal);
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) keep_step(k[e], x0 + 256 * e + 4 * lane, 4);
+      }
+    } else {
+      // rows not 16-byte aligned: one key per lane and step, kUnroll steps in flight
+      constexpr int kUnroll = 8;
+      for (int x0 = lo; x0 < hi; x0 += 64 * kUnroll) {
+        uint32_t k[kUnroll][4];
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) {
+          const int x = x0 + 64 * e + lane;
+          k[e][0] = (x < hi) ? row.key(x) : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < kUnroll; ++e) keep_step(k[e], x0 + 64 * e + lane, 1);
       }
     }
     if (lane == 0) sh.seg_cnt[wave] = cnt;

@@ -106,6 +106,24 @@ def test_block_one_selection_is_token_level():
     check_sel_rows(sel[0], sel_ref)
 
 
+def test_topk_long_rows_aligned_and_unaligned():
+    """Split top-k on rows longer than its 2048-entry direct limit, with NB = 2501 blocks: score
+    rows start at 16-byte aligned addresses only for every fourth row, so both the vector and the
+    scalar streaming paths run; every row's selection must equal the oracle's."""
+    w, x = generate_small(t_q=24, t_kv=20008, groups=2, heads=8, head_dim=64, index_dim=32,
+                          block=8, topk=256, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=9, device="cuda")
+    say("case: top-k long rows, NB = 2501")
+    prob = sg.Problem.from_workload(w)
+    _, scores = sg.index(prob, x["q_idx"], x["k_idx"])
+    sel = sg.topk(prob, scores)
+    torch.cuda.synchronize()
+    assert scores.shape[-1] == 2501
+    rows = [(0, i) for i in range(w.t_q)]
+    sel_ref, _, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0], sel_ref)
+
+
 def test_heavy_ties_and_negative_zero():
     """Constant index keys: every candidate ties, so the lowest block indices must win."""
     w, x = generate_small(t_q=600, t_kv=600, groups=2, heads=8, head_dim=128, index_dim=32,
