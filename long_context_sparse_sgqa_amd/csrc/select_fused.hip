@@ -63,7 +63,8 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   constexpr int kLds = (kSampBytes > 2 * kTileBytes) ? kSampBytes : 2 * kTileBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   __shared__ uint32_t s_thr[kRows];
-  __shared__ int s_cnt[kRows];                            // candidates appended per row
+  __shared__ uint64_t s_cnt2[kRows / 2];                  // candidates appended per row, two per word
+  int* s_cnt = reinterpret_cast<int*>(s_cnt2);
 
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
 
@@ -236,13 +237,24 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
   int c_off[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) c_off[e] = (wave * 16 + lg * 4 + e) * a.cap * 8;
+  // The counters of rows e = 0, 1 and of rows 2, 3 share a 64-bit word (low half: the even row), so
+  // one 64-bit LDS atomic takes both rows' slots; a half cannot carry into the other below 2^32.
+  unsigned long long* row_cnt2 = reinterpret_cast<unsigned long long*>(row_cnt);
   auto append = [&](const f32x4_t& c, int32_t col, bool check_causal) {
-    int pos[4];
+    bool pass[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bool pass = c[e] >= c_thr[e];
-      if (check_causal) pass = pass && col < c_o32[e];
-      pos[e] = pass ? atomicAdd(&row_cnt[e], 1) : a.cap;
+      pass[e] = c[e] >= c_thr[e];
+      if (check_causal) pass[e] = pass[e] && col < c_o32[e];
+    }
+    int pos[4];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const bool p0 = pass[2 * hlf], p1 = pass[2 * hlf + 1];
+      const unsigned long long add = (p0 ? 1ull : 0ull) | (p1 ? (1ull << 32) : 0ull);
+      const unsigned long long old = (p0 || p1) ? atomicAdd(&row_cnt2[hlf], add) : 0ull;
+      pos[2 * hlf] = p0 ? static_cast<int>(old & 0xffffffffull) : a.cap;
+      pos[2 * hlf + 1] = p1 ? static_cast<int>(old >> 32) : a.cap;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
