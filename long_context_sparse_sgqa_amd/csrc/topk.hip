@@ -306,20 +306,40 @@ __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
     if (t < Di) qs[t] = bf16_to_f32(qrow[t]);
     __syncthreads();
     const bf16_t* kb = k_blk + b * NB * Di;
-    // one block row per thread, 16 bytes (8 index dims) per load
-    for (int64_t j = t; j < o; j += kThreads) {
-      const uint4* kr = reinterpret_cast<const uint4*>(kb + j * Di);
-      float acc = 0.f;
-      for (int c8 = 0; c8 < Di / 8; ++c8) {
-        const uint4 u = kr[c8];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    // one block row per thread, 16 bytes (8 index dims) per load; four rows' loads are in flight at
+    // once (one workgroup per CU, so registers are plentiful and latency is the cost)
+    constexpr int kRowsInFlight = 4;
+    for (int64_t j0 = t; j0 < o; j0 += kThreads * kRowsInFlight) {
+      float acc[kRowsInFlight];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          acc = fmaf(qs[c8 * 8 + 2 * h], __uint_as_float(w[h] << 16), acc);
-          acc = fmaf(qs[c8 * 8 + 2 * h + 1], __uint_as_float(w[h] & 0xffff0000u), acc);
+      for (int u = 0; u < kRowsInFlight; ++u) acc[u] = 0.f;
+      for (int c0 = 0; c0 < Di / 8; c0 += 4) {
+        uint4 w4[kRowsInFlight][4];
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) {
+          const int64_t j = j0 + static_cast<int64_t>(u) * kThreads;
+          const uint4* kr = reinterpret_cast<const uint4*>(kb + (j < o ? j : 0) * Di);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w4[u][q] = (c0 + q < Di / 8) ? kr[c0 + q] : make_uint4(0u, 0u, 0u, 0u);
         }
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (c0 + q >= Di / 8) continue;
+            const uint32_t w[4] = {w4[u][q].x, w4[u][q].y, w4[u][q].z, w4[u][q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              acc[u] = fmaf(qs[(c0 + q) * 8 + 2 * h], __uint_as_float(w[h] << 16), acc[u]);
+              acc[u] = fmaf(qs[(c0 + q) * 8 + 2 * h + 1], __uint_as_float(w[h] & 0xffff0000u), acc[u]);
+            }
+          }
       }
-      srow[j] = acc;
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        const int64_t j = j0 + static_cast<int64_t>(u) * kThreads;
+        if (j < o) srow[j] = acc[u];
+      }
     }
     __syncthreads();
     const int need = NS - 1;
