@@ -48,7 +48,7 @@ size_t dtype_size(int32_t dt) { return dt == SGQA_BF16 ? 2 : 4; }
 
 // Query tokens per chunk are bounded by a fixed budget of per-chunk selection state (stored score
 // rows on the split path, candidate lists on the fused path).
-constexpr size_t kForwardChunkBudget = size_t(2) << 30;   // 2 GiB
+constexpr size_t kForwardChunkBudget = size_t(8) << 30;   // 8 GiB
 
 struct Derived {
   sgqa::Dims d;
@@ -229,11 +229,15 @@ sgqa_status for_each_chunk(const sgqa::Dims& d, int64_t chunk_tok, F&& fn) {
       SGQA_CHECK(fn(c));
       b += c.nseq;
     } else {
-      for (int64_t i0 = 0; i0 < d.Tq; i0 += chunk_tok) {
+      // as many chunks as the workspace requires, of equal size (no short last chunk whose launches
+      // would leave most of the GPU idle)
+      const int64_t nch = (d.Tq + chunk_tok - 1) / chunk_tok;
+      const int64_t per = (d.Tq + nch - 1) / nch;
+      for (int64_t i0 = 0; i0 < d.Tq; i0 += per) {
         c.b0 = b;
         c.nseq = 1;
         c.i0 = i0;
-        c.ntok = (d.Tq - i0 < chunk_tok) ? d.Tq - i0 : chunk_tok;
+        c.ntok = (d.Tq - i0 < per) ? d.Tq - i0 : per;
         SGQA_CHECK(fn(c));
       }
       b += 1;
