@@ -70,8 +70,10 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
+  // tiles in reverse order: the last tokens have the most causal blocks, so the longest workgroups
+  // are dispatched first and the launch ends on short ones
   const int64_t seq = blockIdx.x / a.tiles_per_seq;
-  const int64_t row0 = (blockIdx.x - seq * a.tiles_per_seq) * kRows;      // within the sequence
+  const int64_t row0 = (a.tiles_per_seq - 1 - (blockIdx.x - seq * a.tiles_per_seq)) * kRows;
   const int64_t rows_here = min<int64_t>(kRows, a.seq_rows - row0);
   const int64_t b = a.b0 + seq;
   const bf16_t* kb = a.k_blk + b * a.NB * DI;
