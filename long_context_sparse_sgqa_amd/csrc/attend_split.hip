@@ -168,6 +168,25 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
 
   uint32_t* out = a.ulist + gq * list_stride(a.umax);
+  // A lane meets its units in increasing order, so it carries its current range, that range's
+  // output shift and the next range's first unit, and updates them only when it crosses a start.
+  auto shift_of = [&](int r) {
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q < kRanges; ++q) v = q == r ? start[q] - below[q] : v;
+    return v;
+  };
+  auto next_start = [&](int r) {
+    uint32_t v = 0xffffffffu;
+#pragma unroll
+    for (int q = 1; q < kRanges; ++q) v = q == r + 1 ? lo[q] : v;
+    return v;
+  };
+  int rcur = 0;
+#pragma unroll
+  for (int q = 1; q < kRanges; ++q) rcur += static_cast<uint32_t>(32 * w0) >= lo[q] ? 1 : 0;
+  int shift = shift_of(rcur);
+  uint32_t nxt = next_start(rcur);
   for (int w = w0; w < w1; ++w) {
     uint32_t xt[kTok], x = 0u;
 #pragma unroll
@@ -179,16 +198,17 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
       const int bit = __builtin_ctz(x);
       x &= x - 1u;
       const uint32_t u = static_cast<uint32_t>(32 * w + bit);
-      int r = 0;
+      if (u >= nxt) {                                   // crossed a range start (rare)
+        do {
+          ++rcur;
+          nxt = next_start(rcur);
+        } while (u >= nxt);
+        shift = shift_of(rcur);
+      }
+      uint32_t chose = 0u;
 #pragma unroll
-      for (int q = 1; q < kRanges; ++q) r += u >= lo[q] ? 1 : 0;
-      int shift = 0;
-#pragma unroll
-      for (int q = 0; q < kRanges; ++q) shift = q == r ? start[q] - below[q] : shift;
-      uint32_t ent = u;
-#pragma unroll
-      for (int t = 0; t < kTok; ++t) ent |= ((xt[t] >> bit) & 1u) << (kChoseShift + t);
-      out[pos + shift] = ent;
+      for (int t = 0; t < kTok; ++t) chose |= __builtin_amdgcn_ubfe(xt[t], bit, 1) << t;
+      out[pos + shift] = u | (chose << kChoseShift);
       ++pos;
     }
   }
