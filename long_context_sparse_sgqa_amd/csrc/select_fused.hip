@@ -29,6 +29,11 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 64;          // rows per workgroup
 constexpr int kSamp = 512;         // sampled blocks per row
+// Rows with more causal blocks than this take their threshold from kSampBig samples per row, by
+// two histogram passes instead of a stored sample (which would not fit in LDS): with 512 samples
+// only a handful of them lie above a long row's threshold, and its pass count varies too much.
+constexpr int64_t kHugeO = 32768;
+constexpr int kSampBig = 4096;
 constexpr int kCols = 128;         // K_blk columns per staged tile
 
 __device__ __forceinline__ uint32_t order_key_f(float f) {
@@ -140,7 +145,116 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
 
   // ---------------- phase 1: sampled scores -> per-row threshold ----------------
   const bool sampling = o_max > a.cap;
-  if (sampling) {
+  if (sampling && o_max > kHugeO) {
+    // Long rows: kSampBig samples per row at a fixed stride.  Pass A counts each row's sampled
+    // 16-bit keys by their high byte (256 bins per row in LDS); the row's r-th largest key lies in
+    // the bin where the count from the top reaches r.  Pass B recomputes the samples and counts,
+    // within that bin, the low bytes; the same search gives the exact r-th largest 16-bit key.
+    const int64_t stride = (o_max + kSampBig - 1) / kSampBig;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);             // [kRows][256]
+    uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_thr);           // high byte, then the threshold
+    __shared__ int s_rank[kRows];                                  // rank left inside the high bin
+    auto clear_hist = [&]() {
+      for (int i = threadIdx.x; i < kRows * 256; i += 256) hist[i] = 0u;
+    };
+    // one pass over the samples; `visit(row, key16)` for every sample inside the row's causal range
+    auto sample_pass = [&](auto visit) {
+      constexpr int kBatch = 4;
+#pragma unroll 1
+      for (int n0 = 0; n0 < kSampBig / 16; n0 += kBatch) {
+        uint4 bb[kBatch][DI / 32];
+        int64_t cols[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          cols[j] = (static_cast<int64_t>(n0 + j) * 16 + lr) * stride;
+          const int64_t cc = cols[j] < a.NB ? cols[j] : a.NB - 1;
+#pragma unroll
+          for (int kc = 0; kc < DI / 32; ++kc)
+            bb[j][kc] = *reinterpret_cast<const uint4*>(kb + cc * DI + kc * 32 + lg * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < DI / 32; ++kc) c = mfma16x16x32(qa[kc], bf16x8_from_u4(bb[j][kc]), c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c_valid[e] && cols[j] < c_o[e])
+              visit(wave * 16 + lg * 4 + e, order_key_f(c[e]) >> 16);
+        }
+      }
+    };
+    // the bin of rank `r` counted from the top of a row's 256 bins: lane l holds bins 255 - 4l
+    // .. 252 - 4l; returns the bin and the rank left inside it
+    auto find_bin = [&](const uint32_t* h, int r, int* left) -> int {
+      const uint32_t b0 = h[255 - 4 * lane], b1 = h[254 - 4 * lane], b2 = h[253 - 4 * lane],
+                     b3 = h[252 - 4 * lane];
+      const int cnt = static_cast<int>(b0 + b1 + b2 + b3);
+      const int incl = wave_inclusive_scan(cnt);
+      const uint64_t hit = __ballot(incl >= r);
+      const int L = hit ? __builtin_ctzll(hit) : 63;
+      int acc = __builtin_amdgcn_readlane(incl - cnt, L);
+      const uint32_t hb[4] = {static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b0), L)),
+                              static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b1), L)),
+                              static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b2), L)),
+                              static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b3), L))};
+      int bin = 252 - 4 * L;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (acc + static_cast<int>(hb[q]) >= r) {
+          bin = 255 - 4 * L - q;
+          break;
+        }
+        acc += static_cast<int>(hb[q]);
+      }
+      *left = r - acc;
+      return bin;
+    };
+    // per-row rank r (about twice the budget passing), or 0 for rows that take every block
+    auto row_rank = [&](int local) -> int {
+      if (local >= rows_here) return 0;
+      const int64_t o = row_o(local, nullptr);
+      if (o <= a.cap || o + 1 <= a.NS) return 0;
+      const int nvalid = static_cast<int>((o + stride - 1) / stride);
+      const int need = a.NS - 1;
+      int r = static_cast<int>((2ll * need * nvalid + o - 1) / o);
+      return r < 1 ? 1 : (r > nvalid ? nvalid : r);
+    };
+    clear_hist();
+    __syncthreads();
+    sample_pass([&](int row, uint32_t k16) { atomicAdd(&hist[row * 256 + (k16 >> 8)], 1u); });
+    __syncthreads();
+#pragma unroll 1
+    for (int rloc = 0; rloc < 16; ++rloc) {
+      const int local = wave * 16 + rloc;
+      const int r = row_rank(local);
+      int left = 0;
+      const int bin = r > 0 ? find_bin(hist + local * 256, r, &left) : 0;
+      if (lane == 0) {
+        s_hi[local] = r > 0 ? static_cast<uint32_t>(bin) : 0xffffffffu;
+        s_rank[local] = left;
+      }
+    }
+    __syncthreads();
+    clear_hist();
+    __syncthreads();
+    sample_pass([&](int row, uint32_t k16) {
+      if ((k16 >> 8) == s_hi[row]) atomicAdd(&hist[row * 256 + (k16 & 255u)], 1u);
+    });
+    __syncthreads();
+#pragma unroll 1
+    for (int rloc = 0; rloc < 16; ++rloc) {
+      const int local = wave * 16 + rloc;
+      const uint32_t hi = s_hi[local];
+      uint32_t thr = 0u;
+      if (hi != 0xffffffffu) {
+        int left = 0;
+        const int lo = find_bin(hist + local * 256, s_rank[local], &left);
+        thr = ((hi << 8) | static_cast<uint32_t>(lo)) << 16;
+      }
+      if (lane == 0) s_thr[local] = thr;
+    }
+  } else if (sampling) {
     const int64_t stride = (o_max + kSamp - 1) / kSamp;
     uint16_t* samp = reinterpret_cast<uint16_t*>(lds);
     // four column steps per batch: their 16 operand loads are issued before the products (columns
