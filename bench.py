@@ -618,6 +618,16 @@ def main():
                 "launch_ms": stage_ms["attention"],
                 "work_per_launch": f"{c['attention_flops']:.4e} FLOP = 4*d*h per attended "
                                    f"(query, group, token) x {c['attended']:.4e}"}
+    elif dominant == "index_topk":
+        # fused selection: the block scores are MFMA work and are never stored; the stage time
+        # (filter, select and fallback launches) bounds the filter kernel's own time from above
+        ach = c["index_flops"] / (stage_ms["index_topk"] * 1e-3) / 1e12
+        roof = {"kernel": f"index_filter_kernel<{w.index_dim}> + select", "bound": "mfma",
+                "achieved": ach, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": ach * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
+                "launch_ms": stage_ms["index_topk"],
+                "work_per_launch": f"{c['index_flops']:.4e} FLOP = 2*d_idx per scored "
+                                   f"(query, group, block)"}
     else:
         ms = stage_ms[dominant]
         byts = {"index_topk": c["sel_bytes"], "compress": c["compress_bytes"],
