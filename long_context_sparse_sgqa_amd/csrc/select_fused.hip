@@ -437,12 +437,14 @@ struct SelectArgs {
 constexpr int kSelPer = 32;        // candidates per lane held in registers (cap <= 64 * kSelPer)
 
 // The need-th largest of the wave's keys (slots >= NE are zero), searched bit by bit below `top`
-// from the common prefix tau0.
+// from the common prefix tau0, down to bit `low`: the result is one of the keys, so its bits below
+// the lowest bit set in any key are zero.
 template <int NE>
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t tau0, int top, int need) {
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t tau0, int top, int low,
+                                                int need) {
   uint32_t tau = tau0;
 #pragma unroll 1
-  for (int bit = top; bit >= 0; --bit) {
+  for (int bit = top; bit >= low; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int c = 0;                                       // ballots counted on the scalar unit
 #pragma unroll
@@ -518,11 +520,17 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   const uint32_t diff = kmin ^ kmax;
   const int top = diff ? 31 - __clz(diff) : -1;
   const uint32_t tau0 = top >= 0 ? (kmin & ~((2u << top) - 1u)) : kmin;
+  // lowest bit set in any key (integer-valued scores leave the low mantissa bits zero)
+  uint32_t kor = 0u;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) kor |= key[e];
+  kor = wave_reduce_u32(kor, [](uint32_t x, uint32_t y) { return x | y; });
+  const int low = kor ? __builtin_ctz(kor) : 32;
   const int ne = (m + 63) >> 6;                          // register slots in use per lane
-  const uint32_t tau = ne <= 16   ? kth_largest<16>(key, tau0, top, need)
-                       : ne <= 20 ? kth_largest<20>(key, tau0, top, need)
-                       : ne <= 24 ? kth_largest<24>(key, tau0, top, need)
-                                  : kth_largest<kSelPer>(key, tau0, top, need);
+  const uint32_t tau = ne <= 16   ? kth_largest<16>(key, tau0, top, low, need)
+                       : ne <= 20 ? kth_largest<20>(key, tau0, top, low, need)
+                       : ne <= 24 ? kth_largest<24>(key, tau0, top, low, need)
+                                  : kth_largest<kSelPer>(key, tau0, top, low, need);
 
   // bitmaps over blocks 0 .. o-1: above tau, equal to tau
   const int nw = static_cast<int>((o + 31) >> 5);
