@@ -28,13 +28,15 @@ namespace {
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 64;          // rows per workgroup
-constexpr int kSamp = 512;         // sampled blocks per row
+constexpr int kSamp = 384;         // sampled blocks per row (a multiple of 64)
 // Rows with more causal blocks than this take their threshold from kSampBig samples per row, by
 // two histogram passes instead of a stored sample (which would not fit in LDS): with 512 samples
 // only a handful of them lie above a long row's threshold, and its pass count varies too much.
 constexpr int64_t kHugeO = 32768;
 constexpr int kSampBig = 4096;
-constexpr int kCols = 128;         // K_blk columns per staged tile
+// K_blk columns per staged tile: 96 (a tile is 96 x DI/8 16-byte pieces, a whole number of
+// 256-thread rounds for DI = 64 and 128); 128 for DI = 32
+template <int DI> constexpr int cols_per_tile() { return DI == 32 ? 128 : 96; }
 
 __device__ __forceinline__ uint32_t order_key_f(float f) {
   uint32_t u = __float_as_uint(f);
@@ -60,8 +62,12 @@ struct FilterArgs {
   int G, B, NS, cap;
 };
 
+// 3 workgroups per CU: 53 KB of LDS (384 samples of 64 rows, or two 96-column tiles) and at most
+// 168 registers per lane
 template <int DI>
-__global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) index_filter_kernel(FilterArgs a) {
+  constexpr int kCols = cols_per_tile<DI>();
+  static_assert((kCols * (DI / 8)) % 256 == 0, "a tile must be whole 256-thread load rounds");
   constexpr int kRowBytes = DI * 2 + 16;                  // padded LDS row of one K_blk block
   constexpr int kTileBytes = kCols * kRowBytes;
   constexpr int kSampBytes = kRows * kSamp * 2;
@@ -151,11 +157,16 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     // the bin where the count from the top reaches r.  Pass B recomputes the samples and counts,
     // within that bin, the low bytes; the same search gives the exact r-th largest 16-bit key.
     const int64_t stride = (o_max + kSampBig - 1) / kSampBig;
-    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);             // [kRows][256]
+    // [kRows][128] words of two 16-bit bin counts (bin 2w in the low half, 2w + 1 in the high
+    // half); a count never exceeds kSampBig < 2^16, so no half carries into the other
+    uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
     uint32_t* s_hi = reinterpret_cast<uint32_t*>(s_thr);           // high byte, then the threshold
     __shared__ int s_rank[kRows];                                  // rank left inside the high bin
     auto clear_hist = [&]() {
-      for (int i = threadIdx.x; i < kRows * 256; i += 256) hist[i] = 0u;
+      for (int i = threadIdx.x; i < kRows * 128; i += 256) hist[i] = 0u;
+    };
+    auto bump = [&](int row, uint32_t bin) {
+      atomicAdd(&hist[row * 128 + (bin >> 1)], 1u << (16u * (bin & 1u)));
     };
     // one pass over the samples; `visit(row, key16)` for every sample inside the row's causal range
     auto sample_pass = [&](auto visit) {
@@ -187,8 +198,8 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     // the bin of rank `r` counted from the top of a row's 256 bins: lane l holds bins 255 - 4l
     // .. 252 - 4l; returns the bin and the rank left inside it
     auto find_bin = [&](const uint32_t* h, int r, int* left) -> int {
-      const uint32_t b0 = h[255 - 4 * lane], b1 = h[254 - 4 * lane], b2 = h[253 - 4 * lane],
-                     b3 = h[252 - 4 * lane];
+      const uint32_t w_hi = h[127 - 2 * lane], w_lo = h[126 - 2 * lane];
+      const uint32_t b0 = w_hi >> 16, b1 = w_hi & 0xffffu, b2 = w_lo >> 16, b3 = w_lo & 0xffffu;
       const int cnt = static_cast<int>(b0 + b1 + b2 + b3);
       const int incl = wave_inclusive_scan(cnt);
       const uint64_t hit = __ballot(incl >= r);
@@ -222,14 +233,14 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     };
     clear_hist();
     __syncthreads();
-    sample_pass([&](int row, uint32_t k16) { atomicAdd(&hist[row * 256 + (k16 >> 8)], 1u); });
+    sample_pass([&](int row, uint32_t k16) { bump(row, k16 >> 8); });
     __syncthreads();
 #pragma unroll 1
     for (int rloc = 0; rloc < 16; ++rloc) {
       const int local = wave * 16 + rloc;
       const int r = row_rank(local);
       int left = 0;
-      const int bin = r > 0 ? find_bin(hist + local * 256, r, &left) : 0;
+      const int bin = r > 0 ? find_bin(hist + local * 128, r, &left) : 0;
       if (lane == 0) {
         s_hi[local] = r > 0 ? static_cast<uint32_t>(bin) : 0xffffffffu;
         s_rank[local] = left;
@@ -239,7 +250,7 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
     clear_hist();
     __syncthreads();
     sample_pass([&](int row, uint32_t k16) {
-      if ((k16 >> 8) == s_hi[row]) atomicAdd(&hist[row * 256 + (k16 & 255u)], 1u);
+      if ((k16 >> 8) == s_hi[row]) bump(row, k16 & 255u);
     });
     __syncthreads();
 #pragma unroll 1
@@ -249,7 +260,7 @@ __global__ void __launch_bounds__(256) index_filter_kernel(FilterArgs a) {
       uint32_t thr = 0u;
       if (hi != 0xffffffffu) {
         int left = 0;
-        const int lo = find_bin(hist + local * 256, s_rank[local], &left);
+        const int lo = find_bin(hist + local * 128, s_rank[local], &left);
         thr = ((hi << 8) | static_cast<uint32_t>(lo)) << 16;
       }
       if (lane == 0) s_thr[local] = thr;
