@@ -124,6 +124,23 @@ def test_topk_long_rows_aligned_and_unaligned():
     check_sel_rows(sel[0], sel_ref)
 
 
+@pytest.mark.parametrize("t_kv,di", [(40000, 64), (40000, 128), (300000, 128)],
+                         ids=["o5000-di64", "o5000-di128", "o37500-di128"])
+def test_sampled_threshold_every_row(t_kv, di):
+    """The fused selection's sampled thresholds on every row: about 5000 causal blocks (the
+    384-sample path and 96-column tiles) and 37 500 (past 32 768: the two-pass histogram path)."""
+    w, x = generate_small(t_q=24, t_kv=t_kv, groups=2, heads=8, head_dim=64, index_dim=di,
+                          block=8, topk=4096, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=12, device="cuda")
+    say(f"case: sampled thresholds, t_kv={t_kv}, di={di}")
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    rows = [(0, i) for i in range(w.t_q)]
+    sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0], sel_ref)
+    check_out(out[0], out_ref, fp32=False, what=f"sampled thresholds t_kv={t_kv}")
+
+
 def test_heavy_ties_and_negative_zero():
     """Constant index keys: every candidate ties, so the lowest block indices must win."""
     w, x = generate_small(t_q=600, t_kv=600, groups=2, heads=8, head_dim=128, index_dim=32,
