@@ -7,16 +7,17 @@
 // and counted in the NS = k/B budget, ties to the lower block index, ascending output.
 //
 // filter kernel (one workgroup = 4 waves = 64 rows of one sequence; a row = (query, KV group)):
-//   1. sample: scores against 512 blocks at a fixed stride (v_mfma_f32_16x16x32_bf16); per row the
-//      r-th largest sampled score, r chosen so that about twice the budget is expected to pass, is
-//      the row's threshold (kept as the top 16 bits of the order-preserving key: any threshold is
-//      correct, it only sizes the candidate list);
+//   1. sample: scores against 384 blocks at a fixed stride (v_mfma_f32_16x16x32_bf16), or 4096
+//      through two histogram passes for rows past 32768 blocks; per row the r-th largest sampled
+//      score, r chosen so that about twice the budget is expected to pass, is the row's threshold
+//      (kept as the top 16 bits of the order-preserving key: any threshold is correct, it only
+//      sizes the candidate list);
 //   2. filter: every causal score, column tiles of K_blk staged in LDS (double-buffered) and
 //      shared by the 4 waves; a passing score takes the next slot of its row from a per-row LDS
 //      counter, so a row's list is unordered.
 // select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
-//   candidates held in registers, then an ordered ballot emit of keys > tau and the lowest-indexed
-//   keys == tau.  Exact whenever at least NS-1 candidates passed (every member of the top set is
+//   candidates held in registers, then an emit in block order (two LDS bitmaps) of keys > tau and
+//   the lowest-indexed keys == tau.  Exact whenever at least NS-1 candidates passed (every member of the top set is
 //   >= tau >= threshold); rows with too few or too many (> capacity) candidates are queued for the
 //   exact fallback in topk.hip, which recomputes the full score row.
 #include "device_common.h"
@@ -30,7 +31,7 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRows = 64;          // rows per workgroup
 constexpr int kSamp = 384;         // sampled blocks per row (a multiple of 64)
 // Rows with more causal blocks than this take their threshold from kSampBig samples per row, by
-// two histogram passes instead of a stored sample (which would not fit in LDS): with 512 samples
+// two histogram passes instead of a stored sample (which would not fit in LDS): with kSamp samples
 // only a handful of them lie above a long row's threshold, and its pass count varies too much.
 constexpr int64_t kHugeO = 32768;
 constexpr int kSampBig = 4096;
