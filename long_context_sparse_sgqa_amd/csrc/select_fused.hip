@@ -442,6 +442,7 @@ struct SelectArgs {
   int32_t* sel;
   int32_t* fail_list;
   int32_t* fail_count;
+  const int32_t* seq_len;              // per-sequence key counts (nullable: every sequence is full)
   int64_t b0, i0, ntok, Tq, pos0, rows;
   int G, B, NS, cap, words, waves;     // words: bitmap words per row (ceil(NB / 32))
 };
@@ -479,7 +480,7 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   const int g = static_cast<int>(rr - tok * a.G);
   const int64_t bseq = a.b0 + tok / a.ntok;
   const int64_t i = a.i0 + tok % a.ntok;
-  const int64_t o = (a.pos0 + i) / a.B;
+  const int64_t o = (seq_pos0(a.seq_len, bseq, a.pos0, a.Tq) + i) / a.B;
   int32_t* out = a.sel + ((bseq * a.Tq + i) * a.G + g) * a.NS;
   if (o + 1 <= a.NS) {
     for (int x = lane; x < a.NS; x += 64) out[x] = (x <= o) ? x : -1;
@@ -598,6 +599,294 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   if (lane == 0) out[need] = static_cast<int32_t>(o);
 }
 
+// ------------------------------------------------------------------------------------------------
+// few rows per sequence (decode: T_q * G <= 32 rows over long rows)
+// ------------------------------------------------------------------------------------------------
+// With so few rows, one workgroup per 64 rows would leave most of the GPU idle while it streams the
+// sequence's block keys.  The thresholds come first instead (kDecSamp sampled blocks per sequence,
+// scored by kDecParts workgroups, then one wave per row ranks them), and the filter splits each
+// sequence's blocks into slabs of kDecSlab, one workgroup per slab, scoring all 32 rows of the
+// sequence at once (v_mfma_f32_32x32x16_bf16: rows are the A operand, 32 blocks per wave and
+// step).  Each wave stages
+// its passing scores in LDS, per row; when one more step could overflow a row's staging, and at the
+// end of the slab, the wave reserves room in each row's list with one global atomic per row and
+// copies its staged candidates there (no workgroup barriers).  A row's list is therefore unordered,
+// as in the filter above.
+constexpr int kDecRows = 32;
+constexpr int kDecSamp = 2048;     // sampled blocks per sequence
+constexpr int kDecSlab = 1024;     // blocks per filter workgroup: 8 steps of 32 blocks per wave
+constexpr int kDecStage = 64;      // staged candidates per wave and row (a step adds at most 32)
+
+struct DecodeArgs {
+  const bf16_t* q_idx;
+  const bf16_t* k_blk;
+  const int32_t* seq_len;      // per-sequence key counts (nullable)
+  uint32_t* thr;               // [chunk rows] threshold keys (low 16 bits clear)
+  uint64_t* cand;              // [chunk rows][cap]
+  int32_t* cnt;                // [chunk rows], zeroed by the threshold kernel
+  int32_t* fail_count;         // zeroed by the threshold kernel
+  int64_t b0, i0, Tq, pos0, NB, kblk_stride;
+  int G, B, NS, cap, seq_rows;
+};
+
+// A operand of the 32 rows: row r of a sequence is token i0 + r / G, KV group r % G (all rows of a
+// sequence share its length); rows past the sequence's rows load row 0 and are zeroed.
+template <int DI>
+__device__ __forceinline__ void dec_load_q(const DecodeArgs& a, int64_t b, int c, int h,
+                                           bf16x8_t* qa) {
+  const bool ok = c < a.seq_rows;
+  const int row = ok ? c : 0;
+  const bf16_t* qrow = a.q_idx + ((b * a.Tq + a.i0 + row / a.G) * a.G + row % a.G) * DI;
+#pragma unroll
+  for (int kc = 0; kc < DI / 16; ++kc) {
+    const uint4 u = *reinterpret_cast<const uint4*>(qrow + 16 * kc + 8 * h);
+    qa[kc] = bf16x8_from_u4(ok ? u : make_uint4(0u, 0u, 0u, 0u));
+  }
+}
+
+// Row of C register r of a lane in half h of the wave (v_mfma_f32_32x32x16 output layout).
+__device__ __forceinline__ int dec_c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Sampled keys: kDecSamp blocks per sequence at a fixed stride, split over kDecParts workgroups;
+// the top 16 bits of each sample's order key are stored per row (in the row's candidate area, which
+// the filter only writes after the thresholds are taken).
+constexpr int kDecParts = 4;
+
+__device__ __forceinline__ int64_t dec_sample_stride(int64_t o_max) {
+  return (o_max + kDecSamp - 1) / kDecSamp;
+}
+
+template <int DI>
+__global__ void __launch_bounds__(256) decode_sample_kernel(DecodeArgs a) {
+  const int64_t seq = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t b = a.b0 + seq;
+  const int64_t p0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0;
+  const int64_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
+  if (o_max <= a.cap) return;                            // every row takes every block
+  const int64_t stride = dec_sample_stride(o_max);
+  bf16x8_t qa[DI / 16];
+  dec_load_q<DI>(a, b, c, h, qa);
+  const bf16_t* kb = a.k_blk + b * a.kblk_stride * DI;
+  // 4 waves x kSteps steps x 32 samples per workgroup, all loads issued before the products
+  constexpr int kSteps = kDecSamp / (kDecParts * 4 * 32);
+  const int s_base = (static_cast<int>(blockIdx.x) * 4 + wave) * kSteps * 32;
+  uint4 kk[kSteps][DI / 16];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    const int64_t col = static_cast<int64_t>(s_base + j * 32 + c) * stride;
+    const int64_t cc = col < a.NB ? col : a.NB - 1;      // past NB: never a valid sample of a row
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc)
+      kk[j][kc] = *reinterpret_cast<const uint4*>(kb + cc * DI + 16 * kc + 8 * h);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint16_t* keys = reinterpret_cast<uint16_t*>(a.cand + seq * a.seq_rows * a.cap);
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], bf16x8_from_u4(kk[j][kc]), acc);
+    const int sidx = s_base + j * 32 + c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = dec_c_row(r, h);
+      if (row < a.seq_rows)
+        keys[static_cast<int64_t>(row) * a.cap * 4 + sidx] = static_cast<uint16_t>(order_key_f(acc[r]) >> 16);
+    }
+  }
+}
+
+// One wave per row: the row's threshold, the r-th largest of its valid samples (sample s is valid
+// for a row with o causal blocks when s * stride < o; r is chosen so that about twice the budget is
+// expected to pass, as in the filter above), by a bitwise search; rows with at most `cap` causal
+// blocks take every block.  Also clears the rows' candidate counts and the failure count.
+__global__ void __launch_bounds__(256) decode_rank_kernel(DecodeArgs a, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
+  if (rr >= rows) return;
+  const int64_t seq = rr / a.seq_rows;
+  const int row = static_cast<int>(rr - seq * a.seq_rows);
+  const int64_t b = a.b0 + seq;
+  const int64_t p0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0;
+  const int64_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
+  const int64_t o = (p0 + row / a.G) / a.B;
+  uint32_t thr = 0u;
+  if (o > a.cap) {
+    const int64_t stride = dec_sample_stride(o_max);
+    const int nvalid = static_cast<int>((o + stride - 1) / stride);
+    const int need = a.NS - 1;
+    int r = static_cast<int>((2ll * need * nvalid + o - 1) / o);
+    r = r < 1 ? 1 : (r > nvalid ? nvalid : r);
+    // lane l holds samples 8 (l + 64 e) .. 8 (l + 64 e) + 7
+    const uint4* kr = reinterpret_cast<const uint4*>(a.cand + rr * a.cap);
+    constexpr int kVec = kDecSamp / (64 * 8);
+    uint4 raw[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) raw[e] = kr[e * 64 + lane];
+    uint32_t kv[kVec * 8];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const uint32_t w[4] = {raw[e].x, raw[e].y, raw[e].z, raw[e].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int sidx = 8 * (e * 64 + lane) + q;
+        const uint32_t k16 = (q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xffffu);
+        kv[e * 8 + q] = sidx < nvalid ? k16 : 0u;
+      }
+    }
+    uint32_t prefix = 0u;
+#pragma unroll 1
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = prefix | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < kVec * 8; ++e) n += __popcll(__ballot(kv[e] >= cand));
+      if (n >= r) prefix = cand;
+    }
+    thr = prefix << 16;
+  }
+  if (lane == 0) {
+    a.thr[rr] = thr;
+    a.cnt[rr] = 0;
+  }
+}
+
+// One workgroup per (slab of kDecSlab blocks, sequence): every causal score of the sequence's rows
+// in the slab, compared with the row's threshold; passing ones become candidates.
+template <int DI>
+__global__ void __launch_bounds__(256) decode_filter_kernel(DecodeArgs a) {
+  // [wave][row][slot] staged candidates, then 64 slots per wave that lanes without a candidate
+  // write to (so that the staging stores need no branch)
+  constexpr int kWaveStage = kDecRows * kDecStage + 64;
+  __shared__ uint64_t stage[4 * kWaveStage];             // 66 KB
+  __shared__ float s_thr[kDecRows];
+  __shared__ int32_t s_o[kDecRows];
+  const int64_t seq = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t b = a.b0 + seq;
+  const int64_t rr0 = seq * a.seq_rows;
+  const int64_t p0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0;
+  const int64_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
+  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * kDecSlab;
+  const int64_t c_end = min(c_begin + kDecSlab, o_max);
+  if (c_begin >= c_end) return;                          // whole workgroup
+
+  // Lane (c, h) holds the MFMA operand of block c of the step: the k-range [16 kc + 8 h, +8) for
+  // kc = 0 .. DI/16 - 1, read through a descriptor over the sequence's block keys (blocks past its
+  // NB read 0; such columns are never causal), one step ahead, into two register sets used in turn.
+  const BufRsrc krs = make_rsrc(a.k_blk + b * a.kblk_stride * DI, a.NB * DI * 2);
+  auto load_keys = [&](int64_t col0, uint4* kk) {
+    const int base = static_cast<int>((col0 + c) * (DI * 2)) + 16 * h;   // < 2^31 (checked on the host)
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc)
+      kk[kc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, base + 32 * kc, 0, 0));
+  };
+  int64_t col0 = c_begin + 32 * wave;
+  uint4 kA[DI / 16], kB[DI / 16];
+  load_keys(col0, kA);
+  bf16x8_t qa[DI / 16];
+  dec_load_q<DI>(a, b, c, h, qa);
+  // per row: the threshold as a float (NaN past the sequence's rows: never passes) and the causal
+  // limit (0 past the rows), computed once per row
+  if (threadIdx.x < kDecRows) {
+    const int row = threadIdx.x;
+    const bool ok = row < a.seq_rows;
+    s_o[row] = ok ? static_cast<int32_t>((p0 + row / a.G) / a.B) : 0;
+    s_thr[row] = ok ? key_threshold_to_float(a.thr[rr0 + row]) : __builtin_nanf("");
+  }
+  __syncthreads();
+  float c_thr[16];
+  int32_t o_r[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    c_thr[r] = s_thr[dec_c_row(r, h)];
+    o_r[r] = s_o[dec_c_row(r, h)];
+  }
+  uint64_t* my_stage = stage + wave * kWaveStage;
+  int n_lo[16], n_hi[16];           // staged per C register: rows of lanes 0-31 / 32-63 (uniform)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) n_lo[r] = n_hi[r] = 0;
+  // every valid row's causal limit is at least o_min (row 0 has the smallest)
+  const int32_t o_min = s_o[0];
+  // Staging of one step.  A passing score's slot is its row's staged count plus the passing lanes
+  // of its half below it: mbcnt over the 64-bit ballot counts the set bits below the lane, which
+  // for the upper half includes the whole lower half (subtracted through the row base).  Lanes
+  // without a candidate store to their own dummy slot.
+  auto append = [&](const f32x16_t& acc, int32_t col, bool causal) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bool pass = acc[r] >= c_thr[r];
+      if (causal) pass = pass && col < o_r[r];
+      const uint64_t m = __ballot(pass);
+      const uint32_t lo = static_cast<uint32_t>(m), hi = static_cast<uint32_t>(m >> 32);
+      const int plo = __popc(lo);
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)));
+      const int row_base = h ? dec_c_row(r, 1) * kDecStage + n_hi[r] - plo
+                             : dec_c_row(r, 0) * kDecStage + n_lo[r];
+      const int slot = pass ? row_base + below : kDecRows * kDecStage + lane;
+      my_stage[slot] = (static_cast<uint64_t>(__float_as_uint(acc[r])) << 32) | static_cast<uint32_t>(col);
+      n_lo[r] += plo;
+      n_hi[r] += __popc(hi);
+    }
+  };
+  auto step = [&](const uint4* kcur, uint4* knext) {
+    load_keys(col0 + 128, knext);
+    const int32_t col = static_cast<int32_t>(col0 + c);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], bf16x8_from_u4(kcur[kc]), acc);
+    if (col0 + 32 <= o_min)
+      append(acc, col, false);
+    else
+      append(acc, col, true);
+    col0 += 128;
+  };
+  // this wave's staged candidates -> the rows' lists: lane l < 32 reserves room for row l, then
+  // each row's staged run is copied by the lanes below its count
+  auto flush = [&]() {
+    int n_mine = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      n_mine = lane == dec_c_row(r, 0) ? n_lo[r] : n_mine;
+      n_mine = lane == dec_c_row(r, 1) ? n_hi[r] : n_mine;
+    }
+    int base = 0;
+    if (n_mine > 0) base = atomicAdd(&a.cnt[rr0 + lane], n_mine);   // n_mine = 0 past the rows
+#pragma unroll 1
+    for (int row = 0; row < kDecRows; ++row) {
+      const int n = __builtin_amdgcn_readlane(n_mine, row);
+      if (n == 0) continue;
+      const int dst = __builtin_amdgcn_readlane(base, row) + lane;
+      if (lane < n && dst < a.cap) a.cand[(rr0 + row) * a.cap + dst] = my_stage[row * kDecStage + lane];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) n_lo[r] = n_hi[r] = 0;
+  };
+  // a step adds at most 32 candidates to a row: flush first when a row could overflow
+  auto full = [&]() {
+    int m = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = max(m, max(n_lo[r], n_hi[r]));
+    return m > kDecStage - 32;
+  };
+  while (col0 < c_end) {
+    step(kA, kB);
+    if (full()) flush();
+    if (col0 >= c_end) break;
+    step(kB, kA);
+    if (full()) flush();
+  }
+  flush();
+}
+
+
 // Rows per select workgroup: each needs two bitmaps of ceil(NB / 32) words in LDS (0: none fits).
 int select_waves(const Dims& d) {
   const int64_t per_wave = 2 * ((d.NB + 31) / 32) * static_cast<int64_t>(sizeof(uint32_t));
@@ -645,6 +934,57 @@ hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_b
   return hipGetLastError();
 }
 
+bool decode_select_supported(const Dims& d, int64_t seq_rows) {
+  // the filter addresses a sequence's block keys (and up to two slabs past them) with 32-bit offsets
+  return fused_select_supported(d) && seq_rows >= 1 && seq_rows <= kDecRows &&
+         (d.NB + 2 * kDecSlab) * d.Di * 2 < (int64_t(1) << 31);
+}
+
+hipError_t launch_decode_select(const Dims& d, const void* q_idx, const void* k_blk, uint32_t* thr,
+                                uint64_t* cand, int32_t* cnt, int32_t* fail_count, const Chunk& c,
+                                hipStream_t s) {
+  DecodeArgs a;
+  a.q_idx = static_cast<const bf16_t*>(q_idx);
+  a.k_blk = static_cast<const bf16_t*>(k_blk);
+  a.seq_len = d.seq_len;
+  a.thr = thr;
+  a.cand = cand;
+  a.cnt = cnt;
+  a.fail_count = fail_count;
+  a.b0 = c.b0;
+  a.i0 = c.i0;
+  a.Tq = d.Tq;
+  a.pos0 = d.pos0;
+  a.NB = d.NB;
+  a.kblk_stride = d.kblk_stride > 0 ? d.kblk_stride : d.NB;
+  a.G = d.G;
+  a.B = d.B;
+  a.NS = d.NS;
+  a.cap = fused_select_capacity();
+  a.seq_rows = static_cast<int>(c.ntok * d.G);
+  if (c.nseq < 1) return hipSuccess;
+  const int64_t max_o = (d.Tk - 1) / d.B;                // no row has more causal blocks
+  const unsigned slabs = static_cast<unsigned>(max_o > 0 ? (max_o + kDecSlab - 1) / kDecSlab : 1);
+  const int64_t rows = c.rows(d.G);
+  const dim3 sgrid(kDecParts, static_cast<unsigned>(c.nseq));
+  const dim3 rgrid(static_cast<unsigned>((rows + 3) / 4));
+  const dim3 fgrid(slabs, static_cast<unsigned>(c.nseq));
+  if (d.Di == 128) {
+    hipLaunchKernelGGL(decode_sample_kernel<128>, sgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_filter_kernel<128>, fgrid, dim3(256), 0, s, a);
+  } else if (d.Di == 64) {
+    hipLaunchKernelGGL(decode_sample_kernel<64>, sgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_filter_kernel<64>, fgrid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(decode_sample_kernel<32>, sgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_filter_kernel<32>, fgrid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
                                     int32_t* sel, int32_t* fail_list, int32_t* fail_count,
                                     const Chunk& c, hipStream_t s) {
@@ -654,6 +994,7 @@ hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const i
   a.sel = sel;
   a.fail_list = fail_list;
   a.fail_count = fail_count;
+  a.seq_len = d.seq_len;
   a.b0 = c.b0;
   a.i0 = c.i0;
   a.ntok = c.ntok;

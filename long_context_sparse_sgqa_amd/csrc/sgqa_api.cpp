@@ -279,10 +279,16 @@ sgqa_status select_chunked(const sgqa::Dims& d, const ForwardLayout& L, char* ws
 }
 
 // ---- decode over a paged cache ------------------------------------------------------------------
+// Decode workspace layout.
+//   candidate path : [attention workspace][internal sel][thr][cnt][fail list][fail count]
+//                    [fallback scratch][cand]
+//   score-row path : [scores][internal sel][attention workspace]
 struct DecodeDerived {
   Derived dv;
   sgqa::PagedKV pk;
   size_t scores_bytes, sel_bytes, attend_bytes;
+  bool fused;                                   // candidate-list selection (T_q * G <= 32)
+  size_t rows_bytes, scratch_bytes, cand_bytes;  // candidate path: per-row arrays, fallback, lists
 };
 
 sgqa_status derive_cache(const sgqa_problem* prob, const sgqa_cache* cache, DecodeDerived* out) {
@@ -325,10 +331,18 @@ sgqa_status derive_decode(const sgqa_problem* prob, const sgqa_cache* cache, Dec
   out->scores_bytes = out->dv.scores_bytes;
   out->sel_bytes = out->dv.sel_bytes;
   out->attend_bytes = sgqa::attend_split_bytes(d);
+  out->fused = sgqa::decode_select_supported(d, d.Tq * d.G);
+  const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G);
+  out->rows_bytes = rows * sizeof(int32_t);
+  out->scratch_bytes = out->fused ? sgqa::select_fallback_scratch_bytes(d) : 0;
+  out->cand_bytes = out->fused ? rows * sgqa::fused_select_capacity() * sizeof(uint64_t) : 0;
   return SGQA_OK;
 }
 
 size_t decode_workspace(const DecodeDerived& dd) {
+  if (dd.fused)
+    return align_up(dd.attend_bytes) + align_up(dd.sel_bytes) + 3 * align_up(dd.rows_bytes) + kAlign +
+           align_up(dd.scratch_bytes) + align_up(dd.cand_bytes);
   return align_up(dd.scores_bytes) + align_up(dd.sel_bytes) + align_up(dd.attend_bytes);
 }
 
@@ -543,17 +557,47 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
   pk.v = v_cache;
   pk.block_table = block_table;
   char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws);
-  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + align_up(dd.scores_bytes));
-  void* attend_ws = ws + align_up(dd.scores_bytes) + align_up(dd.sel_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const sgqa::Chunk c{0, d.Bt, 0, d.Tq};
-  SGQA_CHECK(mark_stage(0, s));
-  hipError_t e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
-  if (e != hipSuccess) return hip_fail(e, "indexer launch");
-  SGQA_CHECK(mark_stage(1, s));
-  e = sgqa::launch_topk(d, scores, sel, c, s);
-  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  int32_t* sel;
+  void* attend_ws;
+  hipError_t e;
+  if (dd.fused) {
+    size_t off = 0;
+    attend_ws = ws;
+    off += align_up(dd.attend_bytes);
+    sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(dd.sel_bytes);
+    uint32_t* thr = reinterpret_cast<uint32_t*>(ws + off);
+    off += align_up(dd.rows_bytes);
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(dd.rows_bytes);
+    int32_t* fail_list = reinterpret_cast<int32_t*>(ws + off);
+    off += align_up(dd.rows_bytes);
+    int32_t* fail_count = reinterpret_cast<int32_t*>(ws + off);
+    off += kAlign;
+    float* scratch = reinterpret_cast<float*>(ws + off);
+    off += align_up(dd.scratch_bytes);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + off);
+    SGQA_CHECK(mark_stage(0, s));
+    e = sgqa::launch_decode_select(d, q_idx, k_blk, thr, cand, cnt, fail_count, c, s);
+    if (e != hipSuccess) return hip_fail(e, "decode filter launch");
+    SGQA_CHECK(mark_stage(1, s));
+    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, s);
+    if (e != hipSuccess) return hip_fail(e, "candidate select launch");
+    e = sgqa::launch_select_fallback(d, q_idx, k_blk, fail_list, fail_count, scratch, sel, c, s);
+    if (e != hipSuccess) return hip_fail(e, "select fallback launch");
+  } else {
+    float* scores = reinterpret_cast<float*>(ws);
+    sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + align_up(dd.scores_bytes));
+    attend_ws = ws + align_up(dd.scores_bytes) + align_up(dd.sel_bytes);
+    SGQA_CHECK(mark_stage(0, s));
+    e = sgqa::launch_index(d, q_idx, k_blk, scores, c, s);
+    if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    SGQA_CHECK(mark_stage(1, s));
+    e = sgqa::launch_topk(d, scores, sel, c, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
   SGQA_CHECK(mark_stage(2, s));
   SGQA_CHECK(mark_stage(3, s));
   e = sgqa::launch_attend_split(d, q, nullptr, gate, sel, out, nullptr, attend_ws, s,

@@ -86,6 +86,13 @@ hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_b
 hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
                                     int32_t* sel, int32_t* fail_list, int32_t* fail_count,
                                     const Chunk& c, hipStream_t s);
+// Few rows per sequence (chunk tokens * G <= 32, e.g. decode): per-row thresholds from sampled
+// blocks (thr, one workgroup per sequence), then the filter split over slabs of each sequence's
+// blocks; fills cand / cnt like launch_index_filter (and zeroes *fail_count).
+bool decode_select_supported(const Dims& d, int64_t seq_rows);
+hipError_t launch_decode_select(const Dims& d, const void* q_idx, const void* k_blk, uint32_t* thr,
+                                uint64_t* cand, int32_t* cnt, int32_t* fail_count, const Chunk& c,
+                                hipStream_t s);
 // Exact selection of the listed rows from recomputed full score rows.
 size_t select_fallback_scratch_bytes(const Dims& d);
 hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* k_blk,

@@ -287,8 +287,9 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
 __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
     const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_blk,
     const int32_t* __restrict__ fail_list, const int32_t* __restrict__ fail_count,
-    float* __restrict__ scratch, int32_t* __restrict__ sel, int64_t NB, int Di, int NS, int B, int G,
-    int64_t Tq, int64_t pos0, int64_t b0, int64_t i0, int64_t ntok) {
+    float* __restrict__ scratch, int32_t* __restrict__ sel, int64_t NB, int64_t kblk_stride, int Di,
+    int NS, int B, int G, int64_t Tq, int64_t pos0, const int32_t* seq_len, int64_t b0, int64_t i0,
+    int64_t ntok) {
   __shared__ TopkShared sh;
   __shared__ float qs[128];
   const int nfail = *fail_count;
@@ -300,12 +301,12 @@ __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
     const int g = static_cast<int>(rr - tok * G);
     const int64_t b = b0 + tok / ntok;
     const int64_t i = i0 + tok % ntok;
-    const int64_t o = (pos0 + i) / B;
+    const int64_t o = (seq_pos0(seq_len, b, pos0, Tq) + i) / B;
     int32_t* out = sel + ((b * Tq + i) * G + g) * NS;
     const bf16_t* qrow = q_idx + ((b * Tq + i) * G + g) * Di;
     if (t < Di) qs[t] = bf16_to_f32(qrow[t]);
     __syncthreads();
-    const bf16_t* kb = k_blk + b * NB * Di;
+    const bf16_t* kb = k_blk + b * kblk_stride * Di;
     // one block row per thread, 16 bytes (8 index dims) per load; four rows' loads are in flight at
     // once (one workgroup per CU, so registers are plentiful and latency is the cost)
     constexpr int kRowsInFlight = 4;
@@ -365,8 +366,8 @@ hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* 
                                   float* scratch, int32_t* sel, const Chunk& c, hipStream_t s) {
   hipLaunchKernelGGL(select_fallback_kernel, dim3(kFallbackWorkgroups), dim3(kThreads), 0, s,
                      static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), fail_list,
-                     fail_count, scratch, sel, d.NB, d.Di, d.NS, d.B, d.G, d.Tq, d.pos0, c.b0, c.i0,
-                     c.ntok);
+                     fail_count, scratch, sel, d.NB, d.kblk_stride > 0 ? d.kblk_stride : d.NB, d.Di,
+                     d.NS, d.B, d.G, d.Tq, d.pos0, d.seq_len, c.b0, c.i0, c.ntok);
   return hipGetLastError();
 }
 

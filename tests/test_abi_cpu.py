@@ -117,8 +117,10 @@ def test_decode_workspace_size_decode_workload(lib):
     cache = sg.Cache(64 * 4097, 64, 4097)
     n = sg.decode_workspace_size(_dprob(), cache)
     rows = 64 * 4 * 8
-    scores = rows * 32769 * 4
-    assert scores + rows * 512 * 4 < n < scores + (64 << 20)   # scores, sel, lists and partials
+    cand = rows * 2048 * 8                            # candidate lists (4 * 8 rows per sequence)
+    scratch = 256 * 32769 * 4                         # fallback score rows
+    sel = rows * 512 * 4
+    assert cand + scratch + sel < n < cand + scratch + sel + (64 << 20)   # + row arrays, partials
 
 
 @pytest.mark.parametrize("cache,kw,status", [

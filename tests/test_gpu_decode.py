@@ -113,6 +113,47 @@ def test_paged_decode_small_varlen(sharp):
         assert torch.equal(o_fwd[0], out[b]), f"paged decode vs forward, sequence {b}"
 
 
+@pytest.mark.parametrize("di,ties", [(32, False), (64, False), (128, False), (128, True)],
+                         ids=["di32", "di64", "di128", "di128-ties"])
+def test_paged_decode_long_varlen(di, ties):
+    """32 rows per sequence of three lengths in one call: about 5000 causal blocks (past the
+    candidate capacity: sampled thresholds), about 2000 (every block a candidate) and about 375
+    (dense).  With ties, sequence 0's index keys are constant: every block passes its threshold,
+    the list overflows and its rows take the exact recomputation (lowest blocks win the ties)."""
+    dev = "cuda"
+    lens = [40000, 16000, 3000]
+    t_q, P, t_kv = 4, 64, 40000
+    say(f"case: paged decode long varlen di={di} ties={ties}")
+    w, x = generate_small(batch=3, t_q=t_q, t_kv=t_kv, groups=8, heads=8, head_dim=64,
+                          index_dim=di, block=8, topk=4096, dtype="bf16", index_dtype="bf16",
+                          scaled_qkv=True, seed=21, device=dev)
+    if ties:
+        x["k_idx"][0].fill_(0.5)
+    prob_kw = dict(t_q=t_q, t_kv=t_kv, kv_groups=8, heads_per_group=8, head_dim=64, index_dim=di,
+                   block=8, topk_tokens=4096, softmax_scale=w.softmax_scale)
+    max_pages = -(-t_kv // P)
+    table_cpu, num_pages = shuffled_table(lens, P, max_pages, spare=3, seed=5)
+    table = table_cpu.to(dev)
+    cache = sg.Cache(num_pages, P, max_pages)
+    prob = sg.Problem(batch=3, **prob_kw)
+    pools = sg.alloc_cache(prob, cache, dev)
+    for b, L in enumerate(lens):
+        append_each(prob_kw, cache, pools, table, x, b, L, dev)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out, sel = sg.decode(prob, cache, seq_lens, table, x["q"], x["gate"], x["q_idx"], pools,
+                         return_sel=True)
+    again = sg.decode(prob, cache, seq_lens, table, x["q"], x["gate"], x["q_idx"], pools)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again), "decode run-to-run"
+    check_decode_sel_structure(sel.cpu(), lens, t_q, 8, 512)
+    xc = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in x.items()}
+    rows = [(b, i) for b in range(3) for i in range(t_q)]
+    sel_ref, out_ref, _ = oracle.sequence_rows(xc, lens, 8, 4096, w.softmax_scale, rows)
+    check_sel_rows(torch.stack([sel[b, i] for b, i in rows]), sel_ref)
+    check_out(torch.stack([out[b, i] for b, i in rows]), out_ref, fp32=False,
+              what=f"paged decode long varlen di={di}")
+
+
 def test_paged_decode_workload():
     """The long-context decode workload: 64 sequences of 262 144 cached tokens + 4 new ones."""
     dev = "cuda"
