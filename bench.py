@@ -336,8 +336,10 @@ def main_decode(args):
     bytes_ = {
         "append": w.batch * w.t_q * (2 * w.groups * w.head_dim + w.index_dim) * 2 * 2
                   + w.batch * 2 * w.block * w.index_dim * 2,
-        "index": w.batch * nb * w.index_dim * 2 + rows * nb * 4,       # K_blk scan, score rows
-        "topk": rows * nb * 4 + rows * w.n_sel * 4,
+        # thresholds + candidate filter: one scan of the block keys (candidate lists are not
+        # counted: they are an implementation choice); select: the selection written
+        "index": w.batch * nb * w.index_dim * 2 + rows * w.index_dim * 2,
+        "topk": rows * w.n_sel * 4,
         "attn_lists": rows * w.n_sel * 4,
         "attention": kv_tokens * w.head_dim * 2 * 2 + 2 * rows * w.heads * w.head_dim * 2,
         "attn_merge": rows * w.heads * (4 * (2 * w.head_dim + 8) + 2 * 2 * w.head_dim),
@@ -348,8 +350,9 @@ def main_decode(args):
         s["frac"] = s["achieved_GBps"] * 1e9 / PEAK_HBM_BYTES
     dominant = max(stages, key=lambda s: stages[s]["ms"])
     ach = stages[dominant]["achieved_GBps"]
-    kname = {"attention": "attend_range_kernel<128, paged>", "index": "index_bf16_kernel",
-             "topk": "topk_kernel"}.get(dominant, dominant)
+    kname = {"attention": "attend_range_kernel<128, paged>",
+             "index": "decode_threshold_kernel<128> + decode_filter_kernel<128>",
+             "topk": "select_candidates_kernel + select_fallback_kernel"}.get(dominant, dominant)
     roof = {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_BYTES / 1e9,
             "unit": "GB/s", "frac": ach * 1e9 / PEAK_HBM_BYTES, "launch_ms": stages[dominant]["ms"],
             "traffic": load_traffic("attend_range_paged" if dominant == "attention" else dominant,

@@ -245,8 +245,12 @@ sgqa_status sgqa_decode_workspace_size(const sgqa_problem* prob, const sgqa_cach
  *   blocks against k_blk, top NS-1 + own block, gated attention over the selected tokens <= p).
  *   sel_out : [Bt, t_q, G, NS] int32 or NULL.   out : [Bt, t_q, G, H, D] bf16.
  *   Supported: dtype and index_dtype bf16, H == 8, D in {64, 128}, B a multiple of 8.
- * The selection runs on stored score rows ([Bt * t_q * G, ceil(t_kv / B)] fp32 in the workspace):
- * with few query rows and long rows that is the layout that spreads over the whole GPU.
+ * With t_q * G <= 32, index dim 32, 64 or 128 and NS <= 513, the selection keeps short candidate
+ * lists in the workspace, not score rows.  Per-row thresholds come from sampled blocks.  The
+ * filter splits each sequence's blocks over many workgroups.  The exact selection runs on the
+ * candidates, and rows it cannot settle are recomputed in full.  Otherwise the selection runs on
+ * stored score rows ([Bt * t_q * G, ceil(t_kv / B)] fp32 in the workspace).  The result is the
+ * same either way.
  */
 sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
                         const int32_t* seq_lens, const int32_t* block_table, const void* q,

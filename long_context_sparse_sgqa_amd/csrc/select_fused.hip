@@ -604,7 +604,7 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
 // ------------------------------------------------------------------------------------------------
 // With so few rows, one workgroup per 64 rows would leave most of the GPU idle while it streams the
 // sequence's block keys.  The thresholds come first instead (kDecSamp sampled blocks per sequence,
-// scored by kDecParts workgroups, then one wave per row ranks them), and the filter splits each
+// scored and ranked by four workgroups of 8 rows each), and the filter splits each
 // sequence's blocks into slabs of kDecSlab, one workgroup per slab, scoring all 32 rows of the
 // sequence at once (v_mfma_f32_32x32x16_bf16: rows are the A operand, 32 blocks per wave and
 // step).  Each wave stages
@@ -647,97 +647,92 @@ __device__ __forceinline__ void dec_load_q(const DecodeArgs& a, int64_t b, int c
 // Row of C register r of a lane in half h of the wave (v_mfma_f32_32x32x16 output layout).
 __device__ __forceinline__ int dec_c_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Sampled keys: kDecSamp blocks per sequence at a fixed stride, split over kDecParts workgroups;
-// the top 16 bits of each sample's order key are stored per row (in the row's candidate area, which
-// the filter only writes after the thresholds are taken).
-constexpr int kDecParts = 4;
-
-__device__ __forceinline__ int64_t dec_sample_stride(int64_t o_max) {
-  return (o_max + kDecSamp - 1) / kDecSamp;
-}
-
+// Thresholds: one workgroup per (sequence, group of 8 of its rows), 8 waves.  The group's rows are
+// A rows 0-7 of v_mfma_f32_32x32x16_bf16 (the other 24 are zero), so their scores are C registers
+// 0-3 of every lane.  kDecSamp blocks at a fixed stride are scored (each wave 8 steps of 32, loaded
+// in two batches), their 16-bit keys kept in LDS, and then each wave ranks one row: the threshold is
+// the r-th largest of the row's valid samples (sample s is valid for a row with o causal blocks when
+// s * stride < o; r is chosen so that about twice the budget is expected to pass, as in the filter
+// above).  Rows with at most `cap` causal blocks take every block.  Also clears the rows' candidate
+// counts and the failure count.  Positions fit 32 bits on this path (checked on the host).
 template <int DI>
-__global__ void __launch_bounds__(256) decode_sample_kernel(DecodeArgs a) {
-  const int64_t seq = blockIdx.y;
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_threshold_kernel(DecodeArgs a) {
+  __shared__ uint16_t samp[8 * kDecSamp];                // 32 KB
+  const int64_t seq = blockIdx.x;
+  const int grp = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int64_t b = a.b0 + seq;
-  const int64_t p0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0;
-  const int64_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
-  if (o_max <= a.cap) return;                            // every row takes every block
-  const int64_t stride = dec_sample_stride(o_max);
-  bf16x8_t qa[DI / 16];
-  dec_load_q<DI>(a, b, c, h, qa);
-  const bf16_t* kb = a.k_blk + b * a.kblk_stride * DI;
-  // 4 waves x kSteps steps x 32 samples per workgroup, all loads issued before the products
-  constexpr int kSteps = kDecSamp / (kDecParts * 4 * 32);
-  const int s_base = (static_cast<int>(blockIdx.x) * 4 + wave) * kSteps * 32;
-  uint4 kk[kSteps][DI / 16];
-#pragma unroll
-  for (int j = 0; j < kSteps; ++j) {
-    const int64_t col = static_cast<int64_t>(s_base + j * 32 + c) * stride;
-    const int64_t cc = col < a.NB ? col : a.NB - 1;      // past NB: never a valid sample of a row
-#pragma unroll
-    for (int kc = 0; kc < DI / 16; ++kc)
-      kk[j][kc] = *reinterpret_cast<const uint4*>(kb + cc * DI + 16 * kc + 8 * h);
+  const int64_t rr0 = seq * a.seq_rows;
+  const int my_row = 8 * grp + wave;                     // the row this wave ranks
+  if (seq == 0 && grp == 0 && threadIdx.x == 0) *a.fail_count = 0;
+  if (lane == 0 && my_row < a.seq_rows) a.cnt[rr0 + my_row] = 0;
+  if (8 * grp >= a.seq_rows) return;                     // whole workgroup
+  const int32_t p0 = static_cast<int32_t>(seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0);
+  const int32_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
+  if (o_max <= a.cap) {
+    if (lane == 0 && my_row < a.seq_rows) a.thr[rr0 + my_row] = 0u;
+    return;
   }
-  __builtin_amdgcn_sched_barrier(0);
-  uint16_t* keys = reinterpret_cast<uint16_t*>(a.cand + seq * a.seq_rows * a.cap);
+  const int32_t stride = (o_max + kDecSamp - 1) / kDecSamp;
+  const bf16_t* kb = a.k_blk + b * a.kblk_stride * DI;
+  constexpr int kSteps = kDecSamp / (8 * 32);
+  constexpr int kBatch = 4;
+  auto load_batch = [&](int s0, uint4 (*kk)[DI / 16]) {
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) {
-    f32x16_t acc = {};
+    for (int j = 0; j < kBatch; ++j) {
+      const int32_t col = ((wave * kSteps + s0 + j) * 32 + c) * stride;
+      const int32_t cc = col < a.NB ? col : static_cast<int32_t>(a.NB) - 1;   // never a valid sample
 #pragma unroll
-    for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], bf16x8_from_u4(kk[j][kc]), acc);
-    const int sidx = s_base + j * 32 + c;
+      for (int kc = 0; kc < DI / 16; ++kc)
+        kk[j][kc] = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(cc) * DI + 16 * kc + 8 * h);
+    }
+  };
+  uint4 kk[kBatch][DI / 16];
+  load_batch(0, kk);
+  bf16x8_t qa[DI / 16];
+  {
+    const int row = 8 * grp + c;
+    const bool ok = c < 8 && row < a.seq_rows;
+    const int rq = ok ? row : 0;
+    const bf16_t* qrow = a.q_idx + ((b * a.Tq + a.i0 + rq / a.G) * a.G + rq % a.G) * DI;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = dec_c_row(r, h);
-      if (row < a.seq_rows)
-        keys[static_cast<int64_t>(row) * a.cap * 4 + sidx] = static_cast<uint16_t>(order_key_f(acc[r]) >> 16);
+    for (int kc = 0; kc < DI / 16; ++kc) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qrow + 16 * kc + 8 * h);
+      qa[kc] = bf16x8_from_u4(ok ? u : make_uint4(0u, 0u, 0u, 0u));
     }
   }
-}
-
-// One wave per row: the row's threshold, the r-th largest of its valid samples (sample s is valid
-// for a row with o causal blocks when s * stride < o; r is chosen so that about twice the budget is
-// expected to pass, as in the filter above), by a bitwise search; rows with at most `cap` causal
-// blocks take every block.  Also clears the rows' candidate counts and the failure count.
-__global__ void __launch_bounds__(256) decode_rank_kernel(DecodeArgs a, int64_t rows) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rr = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
-  if (rr >= rows) return;
-  const int64_t seq = rr / a.seq_rows;
-  const int row = static_cast<int>(rr - seq * a.seq_rows);
-  const int64_t b = a.b0 + seq;
-  const int64_t p0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + a.i0;
-  const int64_t o_max = (p0 + (a.seq_rows - 1) / a.G) / a.B;
-  const int64_t o = (p0 + row / a.G) / a.B;
+#pragma unroll 1
+  for (int s0 = 0; s0 < kSteps; s0 += kBatch) {
+    __builtin_amdgcn_sched_barrier(0);                    // keep the batch's loads together
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int kc = 0; kc < DI / 16; ++kc) acc = mfma32x32x16(qa[kc], bf16x8_from_u4(kk[j][kc]), acc);
+      const int sidx = (wave * kSteps + s0 + j) * 32 + c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)                         // C rows 4 h + r = the group's rows
+        samp[(4 * h + r) * kDecSamp + sidx] = static_cast<uint16_t>(order_key_f(acc[r]) >> 16);
+    }
+    if (s0 + kBatch < kSteps) load_batch(s0 + kBatch, kk);
+  }
+  __syncthreads();
+  if (my_row >= a.seq_rows) return;
+  const int32_t o = (p0 + my_row / a.G) / a.B;
   uint32_t thr = 0u;
   if (o > a.cap) {
-    const int64_t stride = dec_sample_stride(o_max);
-    const int nvalid = static_cast<int>((o + stride - 1) / stride);
+    const int nvalid = (o + stride - 1) / stride;
     const int need = a.NS - 1;
-    int r = static_cast<int>((2ll * need * nvalid + o - 1) / o);
+    int r = (2 * need * nvalid + o - 1) / o;
     r = r < 1 ? 1 : (r > nvalid ? nvalid : r);
-    // lane l holds samples 8 (l + 64 e) .. 8 (l + 64 e) + 7
-    const uint4* kr = reinterpret_cast<const uint4*>(a.cand + rr * a.cap);
-    constexpr int kVec = kDecSamp / (64 * 8);
-    uint4 raw[kVec];
+    uint32_t kv[kDecSamp / 64];
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) raw[e] = kr[e * 64 + lane];
-    uint32_t kv[kVec * 8];
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const uint32_t w[4] = {raw[e].x, raw[e].y, raw[e].z, raw[e].w};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int sidx = 8 * (e * 64 + lane) + q;
-        const uint32_t k16 = (q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xffffu);
-        kv[e * 8 + q] = sidx < nvalid ? k16 : 0u;
-      }
+    for (int e = 0; e < kDecSamp / 64; ++e) {
+      const int sidx = e * 64 + lane;
+      kv[e] = sidx < nvalid ? samp[wave * kDecSamp + sidx] : 0u;
     }
     uint32_t prefix = 0u;
 #pragma unroll 1
@@ -745,15 +740,12 @@ __global__ void __launch_bounds__(256) decode_rank_kernel(DecodeArgs a, int64_t 
       const uint32_t cand = prefix | (1u << bit);
       int n = 0;
 #pragma unroll
-      for (int e = 0; e < kVec * 8; ++e) n += __popcll(__ballot(kv[e] >= cand));
+      for (int e = 0; e < kDecSamp / 64; ++e) n += __popcll(__ballot(kv[e] >= cand));
       if (n >= r) prefix = cand;
     }
     thr = prefix << 16;
   }
-  if (lane == 0) {
-    a.thr[rr] = thr;
-    a.cnt[rr] = 0;
-  }
+  if (lane == 0) a.thr[rr0 + my_row] = thr;
 }
 
 // One workgroup per (slab of kDecSlab blocks, sequence): every causal score of the sequence's rows
@@ -965,21 +957,18 @@ hipError_t launch_decode_select(const Dims& d, const void* q_idx, const void* k_
   if (c.nseq < 1) return hipSuccess;
   const int64_t max_o = (d.Tk - 1) / d.B;                // no row has more causal blocks
   const unsigned slabs = static_cast<unsigned>(max_o > 0 ? (max_o + kDecSlab - 1) / kDecSlab : 1);
-  const int64_t rows = c.rows(d.G);
-  const dim3 sgrid(kDecParts, static_cast<unsigned>(c.nseq));
-  const dim3 rgrid(static_cast<unsigned>((rows + 3) / 4));
+  // blockIdx.x = sequence: a sequence's 4 threshold workgroups are dispatched to the same XCD and
+  // share its L2 for the sampled block keys
+  const dim3 tgrid(static_cast<unsigned>(c.nseq), kDecRows / 8);
   const dim3 fgrid(slabs, static_cast<unsigned>(c.nseq));
   if (d.Di == 128) {
-    hipLaunchKernelGGL(decode_sample_kernel<128>, sgrid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_threshold_kernel<128>, tgrid, dim3(512), 0, s, a);
     hipLaunchKernelGGL(decode_filter_kernel<128>, fgrid, dim3(256), 0, s, a);
   } else if (d.Di == 64) {
-    hipLaunchKernelGGL(decode_sample_kernel<64>, sgrid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_threshold_kernel<64>, tgrid, dim3(512), 0, s, a);
     hipLaunchKernelGGL(decode_filter_kernel<64>, fgrid, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(decode_sample_kernel<32>, sgrid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(decode_rank_kernel, rgrid, dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(decode_threshold_kernel<32>, tgrid, dim3(512), 0, s, a);
     hipLaunchKernelGGL(decode_filter_kernel<32>, fgrid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
