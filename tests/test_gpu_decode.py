@@ -113,24 +113,28 @@ def test_paged_decode_small_varlen(sharp):
         assert torch.equal(o_fwd[0], out[b]), f"paged decode vs forward, sequence {b}"
 
 
-@pytest.mark.parametrize("di,ties", [(32, False), (64, False), (128, False), (128, True)],
-                         ids=["di32", "di64", "di128", "di128-ties"])
-def test_paged_decode_long_varlen(di, ties):
-    """32 rows per sequence of three lengths in one call: about 5000 causal blocks (past the
-    candidate capacity: sampled thresholds), about 2000 (every block a candidate) and about 375
-    (dense).  With ties, sequence 0's index keys are constant: every block passes its threshold,
-    the list overflows and its rows take the exact recomputation (lowest blocks win the ties)."""
+@pytest.mark.parametrize("di,t_q,groups,ties", [(32, 4, 8, False), (64, 4, 8, False),
+                                                (128, 4, 8, False), (128, 4, 8, True),
+                                                (64, 5, 6, False), (128, 8, 8, False)],
+                         ids=["di32", "di64", "di128", "di128-ties", "30rows-g6", "64rows-scores"])
+def test_paged_decode_long_varlen(di, t_q, groups, ties):
+    """Rows of three sequence lengths in one call: about 5000 causal blocks (past the candidate
+    capacity: sampled thresholds), about 2000 (every block a candidate) and about 375 (dense).
+    With ties, sequence 0's index keys are constant: every block passes its threshold, the list
+    overflows and its rows take the exact recomputation (lowest blocks win the ties).  30 rows per
+    sequence (5 tokens x 6 groups) leave the last group of 8 rows part-filled; 64 rows per sequence
+    take the stored-score selection instead of candidate lists."""
     dev = "cuda"
     lens = [40000, 16000, 3000]
-    t_q, P, t_kv = 4, 64, 40000
-    say(f"case: paged decode long varlen di={di} ties={ties}")
-    w, x = generate_small(batch=3, t_q=t_q, t_kv=t_kv, groups=8, heads=8, head_dim=64,
+    P, t_kv = 64, 40000
+    say(f"case: paged decode long varlen di={di} t_q={t_q} groups={groups} ties={ties}")
+    w, x = generate_small(batch=3, t_q=t_q, t_kv=t_kv, groups=groups, heads=8, head_dim=64,
                           index_dim=di, block=8, topk=4096, dtype="bf16", index_dtype="bf16",
                           scaled_qkv=True, seed=21, device=dev)
     if ties:
         x["k_idx"][0].fill_(0.5)
-    prob_kw = dict(t_q=t_q, t_kv=t_kv, kv_groups=8, heads_per_group=8, head_dim=64, index_dim=di,
-                   block=8, topk_tokens=4096, softmax_scale=w.softmax_scale)
+    prob_kw = dict(t_q=t_q, t_kv=t_kv, kv_groups=groups, heads_per_group=8, head_dim=64,
+                   index_dim=di, block=8, topk_tokens=4096, softmax_scale=w.softmax_scale)
     max_pages = -(-t_kv // P)
     table_cpu, num_pages = shuffled_table(lens, P, max_pages, spare=3, seed=5)
     table = table_cpu.to(dev)
