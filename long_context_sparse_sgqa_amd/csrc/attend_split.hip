@@ -278,6 +278,10 @@ struct RangeArgs {
   float2* part_ml;         // [gq][R][32 rows]  (running max in the exp2 domain, sum)
   int64_t Tq, Tk, NU, pos0, ngroups, wg_groups;
   int G, umax;
+  // fewer groups of tokens than waves per workgroup (decode): one workgroup per group of tokens,
+  // its waves the unit ranges, so that no wave is idle (else the waves are kRangeWaves
+  // consecutive groups of tokens of one range)
+  int wave_ranges;
   float scale_log2e;
   const int32_t* seq_len;      // per-sequence key counts, or null
   // paged cache (kPaged): kp / vp are the page pools, unit u of sequence b lives in page
@@ -318,15 +322,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int c = lane & 31, h = lane >> 5;                // Q row (token c/8, head c%8), lane half
   const int trow = c >> 3, head = c & 7;
-  // workgroup id: range fastest, so the range decides the XCD
-  const int r = static_cast<int>(blockIdx.x % kRanges);
-  const int64_t rest = blockIdx.x / kRanges;
-  const int64_t wgq = rest % a.wg_groups;
-  const int64_t bg = rest / a.wg_groups;
+  static_assert(kRanges == kRangeWaves, "one wave per range when the waves are the ranges");
+  int r;
+  int64_t bg, qi;
+  if (a.wave_ranges) {
+    r = wave;
+    bg = blockIdx.x / a.ngroups;
+    qi = blockIdx.x - bg * a.ngroups;
+  } else {
+    // workgroup id: range fastest, so the range decides the XCD
+    r = static_cast<int>(blockIdx.x % kRanges);
+    const int64_t rest = blockIdx.x / kRanges;
+    const int64_t wgq = rest % a.wg_groups;
+    bg = rest / a.wg_groups;
+    qi = wgq * kRangeWaves + wave;
+    if (qi >= a.ngroups) return;                         // whole wave; no workgroup barriers follow
+  }
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
-  const int64_t qi = wgq * kRangeWaves + wave;
-  if (qi >= a.ngroups) return;                           // whole wave; no workgroup barriers follow
   const int64_t gq = bg * a.ngroups + qi;
   const int64_t tok0 = kTok * qi;
   const bool rowvalid = tok0 + trow < a.Tq;
@@ -1028,6 +1041,7 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
   a.pos0 = d.pos0;
   a.ngroups = ng;
   a.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
+  a.wave_ranges = ng < kRangeWaves ? 1 : 0;
   a.G = d.G;
   a.umax = umax;
   a.scale_log2e = d.scale * (fp8 ? fp8->k_scale : 1.0f) * 1.4426950408889634f;
@@ -1045,7 +1059,7 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
     a.num_pages = paged->num_pages;
     a.ul2 = paged->page_units_log2;
   }
-  const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
+  const dim3 grid(static_cast<unsigned>(a.wave_ranges ? d.Bt * d.G * ng : d.Bt * d.G * a.wg_groups * kRanges));
   if (paged) {
     if (d.D == 128)
       hipLaunchKernelGGL((attend_range_kernel<128, true, false>), grid, dim3(256), 0, s, a);
@@ -1224,6 +1238,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   a.pos0 = d.pos0;
   a.ngroups = ng;
   a.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
+  a.wave_ranges = ng < kRangeWaves ? 1 : 0;
   a.G = d.G;
   a.umax = umax;
   a.scale_log2e = d.scale * 1.4426950408889634f;
@@ -1233,7 +1248,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   a.max_pages = a.num_pages = 0;
   a.ul2 = 0;
   a.win_m1 = 1 << 30;
-  const dim3 grid(static_cast<unsigned>(d.Bt * d.G * a.wg_groups * kRanges));
+  const dim3 grid(static_cast<unsigned>(a.wave_ranges ? d.Bt * d.G * ng : d.Bt * d.G * a.wg_groups * kRanges));
   if (d.D == 128)
     hipLaunchKernelGGL((attend_range_kernel<128, false, false>), grid, dim3(256), 0, s, a);
   else
