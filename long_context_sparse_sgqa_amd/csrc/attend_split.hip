@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   // so the four tokens cost one memory round trip, and the bitmaps are cleared meanwhile.
   constexpr int kPer = 8;
   int blk[kTok][kPer];
-  const bool in_regs = a.NS <= 64 * kPer;
+  const bool in_regs = a.NS <= 64 * kPer && U == 1;     // B = 8 (a block is one unit)
   if (in_regs) {
 #pragma unroll
     for (int t = 0; t < kTok; ++t) {
@@ -109,25 +109,38 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
     for (int t = 0; t < kTok; ++t) bm[t * a.words + w] = 0u;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  auto mark = [&](int t, int bk) {
-    const int64_t p = pos0 + tok0 + t;
-    const int64_t o = p / a.B, last_unit = p >> 3;
-    if (bk < 0 || bk > o) return;
-    for (int k = 0; k < U; ++k) {
-      const int64_t u = static_cast<int64_t>(bk) * U + k;
-      if (u <= last_unit) atomicOr(&bm[t * a.words + (u >> 5)], 1u << (u & 31));
-    }
-  };
+  // each token's own block and last unit, once per token (positions fit 32 bits: NU < 2^31 / 8),
+  // so that the unrolled marking below stays a few instructions per selection
+  int32_t o_t[kTok], lu_t[kTok];
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) {
+    const int32_t p = static_cast<int32_t>(pos0 + tok0 + t);
+    o_t[t] = p / a.B;
+    lu_t[t] = p >> 3;
+  }
   if (in_regs) {
+    // one unit per block: a selected causal block sets its unit's bit (its unit is <= the token's)
 #pragma unroll
     for (int t = 0; t < kTok; ++t)
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) mark(t, blk[t][k]);
+      for (int k = 0; k < kPer; ++k) {
+        const int bk = blk[t][k];
+        if (bk >= 0 && bk <= o_t[t]) atomicOr(&bm[t * a.words + (bk >> 5)], 1u << (bk & 31));
+      }
   } else {
+#pragma unroll 1
     for (int t = 0; t < kTok; ++t) {
       if (tok0 + t >= a.Tq) break;
       const int32_t* selrow = a.sel + ((b * a.Tq + tok0 + t) * a.G + g) * a.NS;
-      for (int e = lane; e < a.NS; e += 64) mark(t, selrow[e]);
+#pragma unroll 1
+      for (int e = lane; e < a.NS; e += 64) {
+        const int bk = selrow[e];
+        if (bk < 0 || bk > o_t[t]) continue;
+        for (int k = 0; k < U; ++k) {                    // units of the block up to the token's own
+          const int32_t u = bk * U + k;
+          if (u <= lu_t[t]) atomicOr(&bm[t * a.words + (u >> 5)], 1u << (u & 31));
+        }
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
