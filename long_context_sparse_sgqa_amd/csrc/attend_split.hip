@@ -78,7 +78,10 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gq = static_cast<int64_t>(blockIdx.x) * a.waves + wave;  // (b*G + g)*ngroups + q
   if (gq >= a.total) return;                          // whole wave; no workgroup barriers below
-  uint32_t* bm = lds + static_cast<size_t>(wave) * kTok * a.words;
+  // this wave's LDS: the 4 tokens' bitmaps, then the list being built (copied out at the end)
+  const int64_t stride = list_stride(a.umax);
+  uint32_t* bm = lds + static_cast<size_t>(wave) * (kTok * a.words + stride);
+  uint32_t* stg = bm + kTok * a.words;
   const int64_t qi = gq % a.ngroups;
   const int64_t bg = gq / a.ngroups;
   const int64_t g = bg % a.G, b = bg / a.G;
@@ -180,9 +183,11 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
 #pragma unroll
   for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
 
-  uint32_t* out = a.ulist + gq * list_stride(a.umax);
+  uint32_t* out = a.ulist + gq * stride;
   // A lane meets its units in increasing order, so it carries its current range, that range's
   // output shift and the next range's first unit, and updates them only when it crosses a start.
+  // Entries go to the LDS copy of the list: a lane's entries are one contiguous run, so stores of
+  // them straight to memory would give every entry of a store instruction its own cache line.
   auto shift_of = [&](int r) {
     int v = 0;
 #pragma unroll
@@ -221,13 +226,22 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
       uint32_t chose = 0u;
 #pragma unroll
       for (int t = 0; t < kTok; ++t) chose |= __builtin_amdgcn_ubfe(xt[t], bit, 1) << t;
-      out[pos + shift] = u | (chose << kChoseShift);
+      stg[pos + shift] = u | (chose << kChoseShift);
       ++pos;
     }
   }
   if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by none)
     const int r = lane >> 2, j = start[r] + (below[r + 1] - below[r]) + (lane & 3);
-    if (j < start[r + 1]) out[j] = 0u;
+    if (j < start[r + 1]) stg[j] = 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // the list (a multiple of 4 entries; both copies 16-byte aligned) with consecutive lanes on
+  // consecutive 16-byte pieces
+  {
+    const int n4 = start[kRanges] >> 2;
+    const uint4* src = reinterpret_cast<const uint4*>(stg);
+    uint4* dst = reinterpret_cast<uint4*>(out);
+    for (int j = lane; j < n4; j += 64) dst[j] = src[j];
   }
   int32_t* bnd = a.bounds + gq * (kRanges + 1);
   if (lane <= kRanges) {
@@ -991,9 +1005,13 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Token groups whose union bitmaps (kTok x words each) share one workgroup's LDS (0: none fits).
 int union_waves(const Dims& d) {
   const int64_t words = (d.NU + 31) / 32;
-  const int64_t per_wave = kTok * words * static_cast<int64_t>(sizeof(uint32_t));
-  const int64_t fit = (160 * 1024) / per_wave;
-  return static_cast<int>(fit >= 4 ? 4 : fit);
+  const int64_t per_wave = (kTok * words + list_stride(static_cast<int>(units_per_query(d)))) *
+                           static_cast<int64_t>(sizeof(uint32_t));
+  const int64_t fit = (160 * 1024) / per_wave;          // waves whose LDS fits one CU
+  // up to 4 waves per workgroup, but small enough that two workgroups share a CU
+  if (fit >= 8) return 4;
+  if (fit >= 2) return static_cast<int>(fit / 2);
+  return static_cast<int>(fit);
 }
 
 size_t split_bytes_for(const Dims& d, int umax) {
@@ -1146,7 +1164,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.umax = umax;
   ua.words = static_cast<int>((d.NU + 31) / 32);
   ua.waves = union_waves(d);
-  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
+  const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
   hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
                      dim3(64 * ua.waves), lds, s, ua);
   hipError_t e = hipGetLastError();
@@ -1232,7 +1250,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ua.umax = umax;
   ua.words = static_cast<int>((d.NU + 31) / 32);
   ua.waves = union_waves(d);
-  const size_t lds = static_cast<size_t>(ua.waves) * kTok * ua.words * sizeof(uint32_t);
+  const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
   hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
                      dim3(64 * ua.waves), lds, s, ua);
   e = hipGetLastError();
