@@ -545,10 +545,11 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
                        : ne <= 24 ? kth_largest<24>(key, tau0, top, low, need)
                                   : kth_largest<kSelPer>(key, tau0, top, low, need);
 
-  // bitmaps over blocks 0 .. o-1: above tau, equal to tau
+  // bitmaps over blocks 0 .. o-1: above tau, equal to tau; then this wave's copy of the output row
   const int nw = static_cast<int>((o + 31) >> 5);
-  uint32_t* bgt = bm_all + static_cast<size_t>(wave) * 2 * a.words;
+  uint32_t* bgt = bm_all + static_cast<size_t>(wave) * (2 * a.words + a.NS);
   uint32_t* beq = bgt + a.words;
+  int32_t* stg = reinterpret_cast<int32_t*>(beq + a.words);
   for (int w = lane; w < nw; w += 64) {
     bgt[w] = 0u;
     beq[w] = 0u;
@@ -587,16 +588,21 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
     bgt[w] = x;
     n_sel += __popc(x);
   }
+  // A lane's selected blocks are one contiguous run of the row: they go to the LDS copy, which is
+  // then written with consecutive lanes on consecutive entries (written straight to memory, every
+  // entry of a store instruction would take its own cache line).
   int pos = wave_inclusive_scan(n_sel) - n_sel;         // exclusive prefix over lanes
   for (int w = w0; w < w1; ++w) {
     uint32_t x = bgt[w];
     while (x) {
       const int bit = __builtin_ctz(x);
       x &= x - 1u;
-      out[pos++] = 32 * w + bit;
+      stg[pos++] = 32 * w + bit;
     }
   }
-  if (lane == 0) out[need] = static_cast<int32_t>(o);
+  if (lane == 0) stg[need] = static_cast<int32_t>(o);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int x = lane; x < a.NS; x += 64) out[x] = stg[x];
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -879,9 +885,10 @@ __global__ void __launch_bounds__(256) decode_filter_kernel(DecodeArgs a) {
 }
 
 
-// Rows per select workgroup: each needs two bitmaps of ceil(NB / 32) words in LDS (0: none fits).
+// Rows per select workgroup: each needs two bitmaps of ceil(NB / 32) words and its NS output
+// entries in LDS (0: none fits).
 int select_waves(const Dims& d) {
-  const int64_t per_wave = 2 * ((d.NB + 31) / 32) * static_cast<int64_t>(sizeof(uint32_t));
+  const int64_t per_wave = (2 * ((d.NB + 31) / 32) + d.NS) * static_cast<int64_t>(sizeof(uint32_t));
   const int64_t fit = (160 * 1024) / per_wave;
   return static_cast<int>(fit >= 4 ? 4 : fit);
 }
@@ -997,7 +1004,7 @@ hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const i
   a.words = static_cast<int>((d.NB + 31) / 32);
   a.waves = select_waves(d);
   const dim3 grid(static_cast<unsigned>((a.rows + a.waves - 1) / a.waves));
-  const size_t lds = static_cast<size_t>(a.waves) * 2 * a.words * sizeof(uint32_t);
+  const size_t lds = static_cast<size_t>(a.waves) * (2 * a.words + a.NS) * sizeof(uint32_t);
   hipLaunchKernelGGL(select_candidates_kernel, grid, dim3(64 * a.waves), lds, s, a);
   return hipGetLastError();
 }
