@@ -625,18 +625,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
   const int64_t pbase = (gq * kRanges + r) * 32 + c;
-  bf16_t* po = a.part_o + pbase * D;
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+  // The 32 x D tile is contiguous in memory, but a lane holds pieces of one row: it goes through
+  // this wave's Q slice of LDS (Q is no longer read) and out with consecutive lanes on consecutive
+  // 16-byte pieces, instead of each store instruction touching 32 rows' cache lines.
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const f32x4v v = {acc[dt][4 * i4] * inv, acc[dt][4 * i4 + 1] * inv, acc[dt][4 * i4 + 2] * inv,
                         acc[dt][4 * i4 + 3] * inv};
-      *reinterpret_cast<uint2*>(po + 32 * dt + 8 * i4 + 4 * h) =
+      *reinterpret_cast<uint2*>(sq + c * kQRow + (32 * dt + 8 * i4 + 4 * h) * 2) =
           __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4v));
     }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  {
+    unsigned char* tile = reinterpret_cast<unsigned char*>(a.part_o + (pbase - c) * D);
+#pragma unroll
+    for (int k = 0; k < (32 * D * 2) / 1024; ++k) {
+      const int off = 1024 * k + 16 * lane;
+      *reinterpret_cast<uint4*>(tile + off) =
+          *reinterpret_cast<const uint4*>(sq + (off / (2 * D)) * kQRow + off % (2 * D));
+    }
+  }
   if (h == 0) a.part_ml[pbase] = make_float2(m_run, l_tot);
 }
 
