@@ -613,11 +613,15 @@ def main():
     if dominant == "attention":
         # the library takes the range-split kernels for bf16, 8 heads per group, B a multiple of 8
         split = w.dtype == "bf16" and w.heads == 8 and w.block % 8 == 0
-        kname = f"attend_range_kernel<{w.head_dim}>" if split else f"attend_mfma_h8_kernel<{w.head_dim}>"
+        fp8 = args.kv == "fp8"
+        kname = (f"attend_range_kernel<{w.head_dim}{', fp8 K/V' if fp8 else ''}>" if split
+                 else f"attend_mfma_h8_kernel<{w.head_dim}>")
         ach = c["attention_flops"] / (stage_ms["attention"] * 1e-3) / 1e12
+        # the stored counter readings are the bf16 K/V kernel's; the fp8 variant has none
+        tkey = ("attend_range_fp8" if fp8 else "attend_range") if split else "attend_mfma"
         roof = {"kernel": kname, "bound": "mfma", "achieved": ach,
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_BF16_FLOPS,
-                "traffic": load_traffic("attend_range" if split else "attend_mfma", w.name),
+                "traffic": load_traffic(tkey, w.name),
                 "launch_ms": stage_ms["attention"],
                 "work_per_launch": f"{c['attention_flops']:.4e} FLOP = 4*d*h per attended "
                                    f"(query, group, token) x {c['attended']:.4e}"}
