@@ -30,6 +30,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSegCap = 1024;                 // per-wave candidate capacity
 constexpr int kSample = 1024;                 // sampled scores of a long row
 constexpr int kDirectMax = 2048;              // rows this short are selected straight from scores
+constexpr int kFallbackWorkgroups = 256;      // failed rows handled at once (scratch score rows)
+constexpr int kFallbackSlab = 1024;           // blocks per score-recompute workgroup
 
 struct TopkShared {
   uint32_t hist[256];
@@ -151,29 +153,18 @@ __device__ int emit_selected(const Src& src, int n, uint32_t tau, int take_eq, i
   return written;
 }
 
-__global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ scores,
-                                                        int32_t* __restrict__ sel, int64_t NB,
-                                                        int NS, int B, int G, int64_t Tq,
-                                                        int64_t pos0, const int32_t* seq_len,
-                                                        int64_t b0, int64_t i0, int64_t ntok) {
-  __shared__ TopkShared sh;
-  const int64_t rr = blockIdx.x;
-  const int64_t tok = rr / G;
-  const int g = static_cast<int>(rr - tok * G);
-  const int64_t b = b0 + tok / ntok;
-  const int64_t i = i0 + tok % ntok;
-  const int64_t p = seq_pos0(seq_len, b, pos0, Tq) + i;
-  const int64_t o = p / B;
-  int32_t* out = sel + ((b * Tq + i) * G + g) * NS;
+// The selection of one row from its stored scores (candidates 0 .. o-1), by the whole workgroup:
+// out[0 .. NS-1] ascending, the own block o last, or every causal block when o + 1 <= NS.
+__device__ void topk_row(const float* __restrict__ srow, int64_t o, int NS, int32_t* __restrict__ out,
+                         TopkShared& sh) {
   const int t = threadIdx.x;
-
   if (o + 1 <= NS) {                                 // dense: every causal block
     for (int x = t; x < NS; x += kThreads) out[x] = (x <= o) ? x : -1;
     return;
   }
   const int n = static_cast<int>(o);                 // candidates 0..o-1
   const int need = NS - 1;
-  const RowSource row{scores + rr * NB};
+  const RowSource row{srow};
   int take_eq = 0;
   uint32_t tau;
   bool done = false;
@@ -280,22 +271,100 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict_
   if (t == 0) out[need] = static_cast<int32_t>(o);   // the own block, last in ascending order
 }
 
+__global__ void __launch_bounds__(kThreads) topk_kernel(const float* __restrict__ scores,
+                                                        int32_t* __restrict__ sel, int64_t NB,
+                                                        int NS, int B, int G, int64_t Tq,
+                                                        int64_t pos0, const int32_t* seq_len,
+                                                        int64_t b0, int64_t i0, int64_t ntok) {
+  __shared__ TopkShared sh;
+  const int64_t rr = blockIdx.x;
+  const int64_t tok = rr / G;
+  const int g = static_cast<int>(rr - tok * G);
+  const int64_t b = b0 + tok / ntok;
+  const int64_t i = i0 + tok % ntok;
+  const int64_t p = seq_pos0(seq_len, b, pos0, Tq) + i;
+  topk_row(scores + rr * NB, p / B, NS, sel + ((b * Tq + i) * G + g) * NS, sh);
+}
+
 // Exact selection for rows the fused candidate filter could not settle (too few candidates passed
-// the sampled threshold, or more than the candidate capacity): the row's full score vector is
-// recomputed into a scratch row and selected as in topk_kernel.  Each workgroup walks the failure
-// list with a stride of gridDim.x; the list length is read from device memory.
+// the sampled threshold, or more than the candidate capacity).  The full score rows of the first
+// kFallbackWorkgroups failed rows are recomputed by fallback_scores_kernel, whose workgroups share
+// out (row, kFallbackSlab-block slab) items, so even one failed row is recomputed by many
+// workgroups.  select_fallback_kernel then selects each of those rows from its scores as
+// topk_kernel does (one workgroup per row), and walks any further failed rows one workgroup per
+// row, recomputing their scores itself.  The list length is read from device memory: with no
+// failed row both launches exit at once.
+
+// failed row f -> its sequence and position, and its output row
+struct FallbackRow {
+  int64_t b, i;
+  int g;
+};
+__device__ __forceinline__ FallbackRow fallback_row(int64_t rr, int G, int64_t b0, int64_t i0,
+                                                    int64_t ntok) {
+  const int64_t tok = rr / G;
+  return FallbackRow{b0 + tok / ntok, i0 + tok % ntok, static_cast<int>(rr - tok * G)};
+}
+
+__global__ void __launch_bounds__(kThreads) fallback_scores_kernel(
+    const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_blk,
+    const int32_t* __restrict__ fail_list, const int32_t* __restrict__ fail_count,
+    float* __restrict__ scratch, int64_t NB, int64_t kblk_stride, int Di, int B, int G, int64_t Tq,
+    int64_t pos0, const int32_t* seq_len, int64_t b0, int64_t i0, int64_t ntok, int64_t slabs) {
+  __shared__ float qs[128];
+  const int nfail = *fail_count;
+  const int64_t rows = nfail < kFallbackWorkgroups ? nfail : kFallbackWorkgroups;
+  const int t = threadIdx.x;
+  // items in row-major order: consecutive workgroups take consecutive slabs of one row
+  for (int64_t item = blockIdx.x; item < rows * slabs; item += gridDim.x) {
+    const int f = static_cast<int>(item / slabs);
+    const int64_t j0 = (item - f * slabs) * kFallbackSlab;
+    const FallbackRow R = fallback_row(fail_list[f], G, b0, i0, ntok);
+    const int64_t o = (seq_pos0(seq_len, R.b, pos0, Tq) + R.i) / B;
+    if (j0 >= o) continue;                                    // whole workgroup
+    const bf16_t* qrow = q_idx + ((R.b * Tq + R.i) * G + R.g) * Di;
+    __syncthreads();                                          // qs of the previous item is read
+    if (t < Di) qs[t] = bf16_to_f32(qrow[t]);
+    __syncthreads();
+    const bf16_t* kb = k_blk + R.b * kblk_stride * Di;
+    float* srow = scratch + static_cast<int64_t>(f) * NB;
+    const int64_t j1 = j0 + kFallbackSlab < o ? j0 + kFallbackSlab : o;
+    for (int64_t j = j0 + t; j < j1; j += kThreads) {
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + j * Di);
+      float acc = 0.f;
+      for (int c0 = 0; c0 < Di / 8; ++c0) {
+        const uint4 w4 = kr[c0];
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc = fmaf(qs[c0 * 8 + 2 * h], __uint_as_float(w[h] << 16), acc);
+          acc = fmaf(qs[c0 * 8 + 2 * h + 1], __uint_as_float(w[h] & 0xffff0000u), acc);
+        }
+      }
+      srow[j] = acc;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
     const bf16_t* __restrict__ q_idx, const bf16_t* __restrict__ k_blk,
     const int32_t* __restrict__ fail_list, const int32_t* __restrict__ fail_count,
     float* __restrict__ scratch, int32_t* __restrict__ sel, int64_t NB, int64_t kblk_stride, int Di,
     int NS, int B, int G, int64_t Tq, int64_t pos0, const int32_t* seq_len, int64_t b0, int64_t i0,
-    int64_t ntok) {
+    int64_t ntok, int f0) {
   __shared__ TopkShared sh;
   __shared__ float qs[128];
   const int nfail = *fail_count;
   float* srow = scratch + static_cast<int64_t>(blockIdx.x) * NB;
   const int t = threadIdx.x;
-  for (int f = blockIdx.x; f < nfail; f += gridDim.x) {
+  // this workgroup's row among the first f0, whose scores fallback_scores_kernel has written
+  if (static_cast<int>(blockIdx.x) < nfail && static_cast<int>(blockIdx.x) < f0) {
+    const FallbackRow R = fallback_row(fail_list[blockIdx.x], G, b0, i0, ntok);
+    const int64_t o = (seq_pos0(seq_len, R.b, pos0, Tq) + R.i) / B;
+    topk_row(srow, o, NS, sel + ((R.b * Tq + R.i) * G + R.g) * NS, sh);
+    __syncthreads();                                          // sh and srow are reused below
+  }
+  for (int f = f0 + static_cast<int>(blockIdx.x); f < nfail; f += gridDim.x) {
     const int64_t rr = fail_list[f];
     const int64_t tok = rr / G;
     const int g = static_cast<int>(rr - tok * G);
@@ -355,8 +424,6 @@ __global__ void __launch_bounds__(kThreads) select_fallback_kernel(
 
 }  // namespace
 
-constexpr int kFallbackWorkgroups = 256;
-
 size_t select_fallback_scratch_bytes(const Dims& d) {
   return static_cast<size_t>(kFallbackWorkgroups) * static_cast<size_t>(d.NB) * sizeof(float);
 }
@@ -364,10 +431,17 @@ size_t select_fallback_scratch_bytes(const Dims& d) {
 hipError_t launch_select_fallback(const Dims& d, const void* q_idx, const void* k_blk,
                                   const int32_t* fail_list, const int32_t* fail_count,
                                   float* scratch, int32_t* sel, const Chunk& c, hipStream_t s) {
+  const int64_t kstride = d.kblk_stride > 0 ? d.kblk_stride : d.NB;
+  const int64_t max_o = (d.Tk - 1) / d.B;               // no row has more causal blocks
+  const unsigned slabs = static_cast<unsigned>(max_o > 0 ? (max_o + kFallbackSlab - 1) / kFallbackSlab : 1);
+  hipLaunchKernelGGL(fallback_scores_kernel, dim3(kFallbackWorkgroups), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), fail_list,
+                     fail_count, scratch, d.NB, kstride, d.Di, d.B, d.G, d.Tq, d.pos0, d.seq_len, c.b0,
+                     c.i0, c.ntok, static_cast<int64_t>(slabs));
   hipLaunchKernelGGL(select_fallback_kernel, dim3(kFallbackWorkgroups), dim3(kThreads), 0, s,
                      static_cast<const bf16_t*>(q_idx), static_cast<const bf16_t*>(k_blk), fail_list,
-                     fail_count, scratch, sel, d.NB, d.kblk_stride > 0 ? d.kblk_stride : d.NB, d.Di,
-                     d.NS, d.B, d.G, d.Tq, d.pos0, d.seq_len, c.b0, c.i0, c.ntok);
+                     fail_count, scratch, sel, d.NB, kstride, d.Di, d.NS, d.B, d.G, d.Tq, d.pos0,
+                     d.seq_len, c.b0, c.i0, c.ntok, kFallbackWorkgroups);
   return hipGetLastError();
 }
 
