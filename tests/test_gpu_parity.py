@@ -141,6 +141,24 @@ def test_sampled_threshold_every_row(t_kv, di):
     check_out(out[0], out_ref, fp32=False, what=f"sampled thresholds t_kv={t_kv}")
 
 
+def test_more_failed_rows_than_wide_fallback():
+    """Constant index keys on 320 rows (40 tokens x 8 groups) of about 2500 causal blocks: every
+    block ties and passes its threshold, every candidate list overflows, and all 320 rows take the
+    exact recomputation -- 256 through the wide score recompute, the rest through the per-row loop.
+    Ties go to the lowest blocks."""
+    w, x = generate_small(t_q=40, t_kv=20000, groups=8, heads=8, head_dim=64, index_dim=64,
+                          block=8, topk=4096, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          seed=5, device="cuda")
+    x["k_idx"].fill_(0.5)
+    say("case: 320 failed rows (wide fallback + per-row loop)")
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    rows = [(0, i) for i in range(w.t_q)]
+    sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0], sel_ref)
+    check_out(out[0], out_ref, fp32=False, what="320 failed rows")
+
+
 def test_heavy_ties_and_negative_zero():
     """Constant index keys: every candidate ties, so the lowest block indices must win."""
     w, x = generate_small(t_q=600, t_kv=600, groups=2, heads=8, head_dim=128, index_dim=32,
