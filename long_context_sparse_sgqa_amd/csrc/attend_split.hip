@@ -10,13 +10,16 @@
 //     and walks the union of their selections, so a unit chosen by several of the 4 tokens is
 //     loaded once (the union of 4 tokens is ~0.84x the units that 2 pairs would load);
 //   * range r of every group goes to the workgroups numbered r mod R, which the dispatcher deals to
-//     XCDs r, r+R, ..., so each XCD's L2 caches only 1/R of a KV group's keys and values.
+//     XCDs r, r+R, ..., so each XCD's L2 caches only 1/R of a KV group's keys and values.  With
+//     fewer groups of 4 tokens than waves per workgroup (decode), a workgroup's waves take one
+//     group's R ranges instead, so that no wave idles.
 //
 // Three kernels:
 //   quad_union_kernel  per (sequence, group, 4 tokens): the sorted union of the tokens' selected
 //     8-token units, entry = unit | chosen-by-token-t << (27 + t) (B is a multiple of 8, so a unit
-//     is wholly selected by a token or not at all), built through LDS bitmaps; every range is
-//     padded to a multiple of 4 entries and its first entry recorded.
+//     is wholly selected by a token or not at all), built through LDS bitmaps into an LDS copy
+//     of the list that is written out coalesced; every range is padded to a multiple of 4
+//     entries and its first entry recorded.
 //   attend_range_kernel  one wavefront per (group of 4 tokens, range): the entries inside the
 //     range in chunks of 4 units (32 tokens).  S^T = K Q^T on D/16 MFMAs with the K rows permuted
 //     so that every lane holds the 16 scores of one row for two units; masks, online softmax in
@@ -24,7 +27,8 @@
 //     K comes from the unit-packed copy laid out for this kernel and V from the unit-packed V,
 //     so every 16-lane operand load is one 256-byte run; K is loaded two chunks and V one chunk
 //     ahead, list entries arrive by scalar loads, and Q is read from LDS.  The result per row:
-//     O / l rounded to bf16, and the running max m and sum l in fp32.
+//     O / l rounded to bf16 (the wave's tile written out coalesced through its Q slice of LDS),
+//     and the running max m and sum l in fp32.
 //   merge_ranges_kernel  per row: weight each partial by its sum rescaled to the common max,
 //     combine, apply sigmoid(gate), round to bf16.
 #include "device_common.h"

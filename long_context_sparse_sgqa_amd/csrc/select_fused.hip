@@ -17,9 +17,12 @@
 //      counter, so a row's list is unordered.
 // select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
 //   candidates held in registers, then an emit in block order (two LDS bitmaps) of keys > tau and
-//   the lowest-indexed keys == tau.  Exact whenever at least NS-1 candidates passed (every member of the top set is
-//   >= tau >= threshold); rows with too few or too many (> capacity) candidates are queued for the
-//   exact fallback in topk.hip, which recomputes the full score row.
+//   the lowest-indexed keys == tau, built in LDS and written out coalesced.  Exact whenever at
+//   least NS-1 candidates passed (every member of the top set is >= tau >= threshold); rows with
+//   too few or too many (> capacity) candidates are queued for the exact fallback in topk.hip,
+//   which recomputes the full score row.
+// Few rows per sequence (decode) take a threshold kernel and a slab-split filter instead of the
+// filter kernel (see below); they share the select kernel and the fallback.
 #include "device_common.h"
 #include "sgqa_internal.h"
 
