@@ -71,6 +71,10 @@ struct UnionArgs {
   int64_t Tq, pos0, ngroups, total;
   const int32_t* seq_len;  // per-sequence key counts, or null
   int G, NS, B, umax, words, waves;   // words: bitmap words per token (ceil(NU / 32))
+  // ranges of equal entry counts instead of equal unit spans: for launches whose attention waves
+  // take a group's ranges in one workgroup (decode), where no L2 locality across groups is to be
+  // kept and the slowest range ends the launch
+  int balance;
 };
 
 // Each selected block sets its units' bits in the token's LDS bitmap (units past the token's own
@@ -179,7 +183,7 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int nu = __builtin_amdgcn_readlane(incl, 63);
   int pos = incl - mine;
 #pragma unroll
-  for (int r = 1; r < kRanges; ++r) below[r] = wave_total(below[r]);
+  for (int r = 1; r < kRanges; ++r) below[r] = a.balance ? (r * nu) / kRanges : wave_total(below[r]);
   below[0] = 0;
   below[kRanges] = nu;
   int start[kRanges + 1];
@@ -204,11 +208,20 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
     for (int q = 1; q < kRanges; ++q) v = q == r + 1 ? lo[q] : v;
     return v;
   };
+  // Equal entry counts: a range starts at an entry position (below[r]), not at a unit.
+  auto next_below = [&](int r) {
+    int v = 0x7fffffff;
+#pragma unroll
+    for (int q = 1; q < kRanges; ++q) v = q == r + 1 ? below[q] : v;
+    return v;
+  };
   int rcur = 0;
 #pragma unroll
-  for (int q = 1; q < kRanges; ++q) rcur += static_cast<uint32_t>(32 * w0) >= lo[q] ? 1 : 0;
+  for (int q = 1; q < kRanges; ++q)
+    rcur += (a.balance ? pos >= below[q] : static_cast<uint32_t>(32 * w0) >= lo[q]) ? 1 : 0;
   int shift = shift_of(rcur);
   uint32_t nxt = next_start(rcur);
+  int nxt_pos = next_below(rcur);
   for (int w = w0; w < w1; ++w) {
     uint32_t xt[kTok], x = 0u;
 #pragma unroll
@@ -220,11 +233,12 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
       const int bit = __builtin_ctz(x);
       x &= x - 1u;
       const uint32_t u = static_cast<uint32_t>(32 * w + bit);
-      if (u >= nxt) {                                   // crossed a range start (rare)
+      if (a.balance ? pos >= nxt_pos : u >= nxt) {      // crossed a range start (rare)
         do {
           ++rcur;
           nxt = next_start(rcur);
-        } while (u >= nxt);
+          nxt_pos = next_below(rcur);
+        } while (a.balance ? pos >= nxt_pos : u >= nxt);
         shift = shift_of(rcur);
       }
       uint32_t chose = 0u;
@@ -1180,6 +1194,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.umax = umax;
   ua.words = static_cast<int>((d.NU + 31) / 32);
   ua.waves = union_waves(d);
+  ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
   const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
   hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
                      dim3(64 * ua.waves), lds, s, ua);
@@ -1266,6 +1281,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ua.umax = umax;
   ua.words = static_cast<int>((d.NU + 31) / 32);
   ua.waves = union_waves(d);
+  ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
   const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
   hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
                      dim3(64 * ua.waves), lds, s, ua);
