@@ -689,12 +689,17 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
   if (gr >= a.total_groups * 32) return;
   const int d0 = static_cast<int>(threadIdx.x % per_row) * 8;
   const int row = static_cast<int>(gr & 31);
-  const int64_t gq = gr >> 5;
-  const int64_t qi = gq % a.ngroups;
-  const int64_t bg = gq / a.ngroups;
+  // group indices fit 32 bits (fewer groups than query rows, < 2^31): 32-bit divisions, each a
+  // fraction of a 64-bit one; offsets below stay 64-bit
+  const uint32_t gq32 = static_cast<uint32_t>(gr >> 5);
+  const uint32_t ng32 = static_cast<uint32_t>(a.ngroups), G32 = static_cast<uint32_t>(a.G);
+  const uint32_t bg32 = gq32 / ng32;
+  const int64_t gq = gq32;
+  const int64_t qi = gq32 - bg32 * ng32;
   const int64_t tok = kTok * qi + (row >> 3);
   if (tok >= a.Tq) return;
-  const int64_t g = bg % a.G, b = bg / a.G;
+  const uint32_t b32 = bg32 / G32;
+  const int64_t g = bg32 - b32 * G32, b = b32;
   float2 ml[kRanges];
   float mx = -1e30f;
 #pragma unroll
