@@ -80,6 +80,10 @@ struct UnionArgs {
 // Each selected block sets its units' bits in the token's LDS bitmap (units past the token's own
 // unit are left out: t <= p); one scan over the words then emits the union in ascending unit order
 // with every token's chosen bit.
+// kVec4: the bitmap scans read 4 words per token at a time (16-byte LDS reads).  That pays for
+// long contexts, where the bitmaps' LDS size leaves few waves per CU to hide each read's latency;
+// with short bitmaps and many waves the scalar scans are faster.
+template <bool kVec4>
 __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -156,9 +160,21 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-  // each lane owns a contiguous run of words; counts below each range start and in total
-  const int per = (nw + 63) >> 6;
+  // each lane owns a contiguous run of words, whole groups of 4 (one 16-byte read per token; a
+  // token's bitmap is a multiple of 4 words, and words past the run read as 0: those past nw were
+  // never cleared); counts below each range start and in total
+  const int per = kVec4 ? ((((nw + 63) >> 6) + 3) & ~3) : ((nw + 63) >> 6);
   const int w0 = lane * per, w1 = min(w0 + per, nw);
+  auto read4 = [&](int w, uint32_t (*xt)[4]) {
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      const uint4 v = *reinterpret_cast<const uint4*>(bm + t * a.words + w);
+      xt[t][0] = w < w1 ? v.x : 0u;
+      xt[t][1] = w + 1 < w1 ? v.y : 0u;
+      xt[t][2] = w + 2 < w1 ? v.z : 0u;
+      xt[t][3] = w + 3 < w1 ? v.w : 0u;
+    }
+  };
   uint32_t lo[kRanges];
 #pragma unroll
   for (int r = 0; r < kRanges; ++r) lo[r] = range_start(r, u_end);
@@ -166,16 +182,33 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   int below[kRanges + 1];
 #pragma unroll
   for (int r = 0; r <= kRanges; ++r) below[r] = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t x = 0u;
-#pragma unroll
-    for (int t = 0; t < kTok; ++t) x |= bm[t * a.words + w];
+  auto count_word = [&](int w, uint32_t x) {
     mine += __popc(x);
 #pragma unroll
     for (int r = 1; r < kRanges; ++r) {
       const int64_t rel = static_cast<int64_t>(lo[r]) - 32 * w;   // bits of this word below lo[r]
       const uint32_t m = rel >= 32 ? 0xffffffffu : (rel <= 0 ? 0u : ((1u << rel) - 1u));
       below[r] += __popc(x & m);
+    }
+  };
+  if constexpr (kVec4) {
+    for (int w4 = w0; w4 < w1; w4 += 4) {
+      uint32_t xt4[kTok][4];
+      read4(w4, xt4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t x = 0u;
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) x |= xt4[t][k];
+        count_word(w4 + k, x);
+      }
+    }
+  } else {
+    for (int w = w0; w < w1; ++w) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) x |= bm[t * a.words + w];
+      count_word(w, x);
     }
   }
   // exclusive prefix of `mine` over the lanes, and the totals
@@ -222,13 +255,10 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   int shift = shift_of(rcur);
   uint32_t nxt = next_start(rcur);
   int nxt_pos = next_below(rcur);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t xt[kTok], x = 0u;
+  auto emit_word = [&](int w, const uint32_t* xt) {
+    uint32_t x = 0u;
 #pragma unroll
-    for (int t = 0; t < kTok; ++t) {
-      xt[t] = bm[t * a.words + w];
-      x |= xt[t];
-    }
+    for (int t = 0; t < kTok; ++t) x |= xt[t];
     while (x) {
       const int bit = __builtin_ctz(x);
       x &= x - 1u;
@@ -246,6 +276,26 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
       for (int t = 0; t < kTok; ++t) chose |= __builtin_amdgcn_ubfe(xt[t], bit, 1) << t;
       stg[pos + shift] = u | (chose << kChoseShift);
       ++pos;
+    }
+  };
+  if constexpr (kVec4) {
+    for (int w4 = w0; w4 < w1; w4 += 4) {
+      uint32_t xt4[kTok][4];
+      read4(w4, xt4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t xt[kTok];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) xt[t] = xt4[t][k];
+        emit_word(w4 + k, xt);
+      }
+    }
+  } else {
+    for (int w = w0; w < w1; ++w) {
+      uint32_t xt[kTok];
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) xt[t] = bm[t * a.words + w];
+      emit_word(w, xt);
     }
   }
   if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by none)
@@ -1038,8 +1088,12 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float4* p, int64_t n4) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Token groups whose union bitmaps (kTok x words each) share one workgroup's LDS (0: none fits).
+// Bitmap words per token in the group-list kernel: ceil(NU / 32) rounded up to a multiple of 4, so
+// that every token's bitmap starts 16-byte aligned.
+int64_t union_words(const Dims& d) { return ((d.NU + 31) / 32 + 3) & ~int64_t(3); }
+
 int union_waves(const Dims& d) {
-  const int64_t words = (d.NU + 31) / 32;
+  const int64_t words = union_words(d);
   const int64_t per_wave = (kTok * words + list_stride(static_cast<int>(units_per_query(d)))) *
                            static_cast<int64_t>(sizeof(uint32_t));
   const int64_t fit = (160 * 1024) / per_wave;          // waves whose LDS fits one CU
@@ -1197,12 +1251,15 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.NS = d.NS;
   ua.B = d.B;
   ua.umax = umax;
-  ua.words = static_cast<int>((d.NU + 31) / 32);
+  ua.words = static_cast<int>(union_words(d));
   ua.waves = union_waves(d);
   ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
   const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
-  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
-                     dim3(64 * ua.waves), lds, s, ua);
+  const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
+  if (ua.words >= 2048)                                 // contexts of 512K tokens and more
+    hipLaunchKernelGGL(quad_union_kernel<true>, ugrid, dim3(64 * ua.waves), lds, s, ua);
+  else
+    hipLaunchKernelGGL(quad_union_kernel<false>, ugrid, dim3(64 * ua.waves), lds, s, ua);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(4, s);
   if (e != hipSuccess) return e;
@@ -1284,12 +1341,15 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ua.NS = d.NS;
   ua.B = d.B;
   ua.umax = umax;
-  ua.words = static_cast<int>((d.NU + 31) / 32);
+  ua.words = static_cast<int>(union_words(d));
   ua.waves = union_waves(d);
   ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
   const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
-  hipLaunchKernelGGL(quad_union_kernel, dim3(static_cast<unsigned>((total + ua.waves - 1) / ua.waves)),
-                     dim3(64 * ua.waves), lds, s, ua);
+  const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
+  if (ua.words >= 2048)                                 // contexts of 512K tokens and more
+    hipLaunchKernelGGL(quad_union_kernel<true>, ugrid, dim3(64 * ua.waves), lds, s, ua);
+  else
+    hipLaunchKernelGGL(quad_union_kernel<false>, ugrid, dim3(64 * ua.waves), lds, s, ua);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   RangeArgs a;
