@@ -47,10 +47,9 @@ __device__ __forceinline__ int64_t page_of(const AppendArgs& a, int64_t b, int64
 // One thread per (sequence, group, touched unit, 8-wide d piece): the unit's new tokens are
 // written into K (one 16-byte run per token) and V (one 16-byte run of 8 tokens per d), tokens
 // already cached are kept and tokens past the length are zeroed.
-__global__ void __launch_bounds__(256) append_kv_kernel(AppendArgs a, int64_t total) {
+__device__ __forceinline__ void append_kv_one(const AppendArgs& a, int64_t id) {
   const int pieces = a.D / 8;
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+  {
     const int j = static_cast<int>(id % pieces);
     const int64_t r = id / pieces;
     const int uu = static_cast<int>(r % a.units_max);
@@ -60,7 +59,7 @@ __global__ void __launch_bounds__(256) append_kv_kernel(AppendArgs a, int64_t to
     const int64_t start = seq_pos0(a.seq_len, b, a.max_len - a.n_new, a.n_new);
     const int64_t end = start + a.n_new;                 // exclusive
     const int64_t u = (start >> 3) + uu;
-    if (u > ((end - 1) >> 3)) continue;
+    if (u > ((end - 1) >> 3)) return;
     const int64_t page = page_of(a, b, (u * 8) >> (a.ul2 + 3));
     const int64_t unit_elem = (((page * a.G + g) << a.ul2) | (u & ((1 << a.ul2) - 1))) * 8 * a.D;
     bf16_t* kdst = a.k_pool + unit_elem;
@@ -112,11 +111,10 @@ __global__ void __launch_bounds__(256) append_kv_kernel(AppendArgs a, int64_t to
 }
 
 // One thread per (sequence, new token, 8-wide index piece): copy into the index-key pool.
-__global__ void __launch_bounds__(256) append_kidx_kernel(AppendArgs a, int64_t total) {
+__device__ __forceinline__ void append_kidx_one(const AppendArgs& a, int64_t id) {
   const int pieces = a.Di / 8;
   const int64_t ptok = int64_t(8) << a.ul2;
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+  {
     const int j = static_cast<int>(id % pieces);
     const int64_t r = id / pieces;
     const int64_t t = r % a.n_new;
@@ -125,6 +123,19 @@ __global__ void __launch_bounds__(256) append_kidx_kernel(AppendArgs a, int64_t 
     const int64_t page = page_of(a, b, pos / ptok);
     *reinterpret_cast<uint4*>(a.kidx_pool + (page * ptok + (pos & (ptok - 1))) * a.Di + 8 * j) =
         *reinterpret_cast<const uint4*>(a.kidx_new + r * a.Di + 8 * j);
+  }
+}
+
+// K/V and index keys in one launch (they write different pools): items below kv_total are K/V
+// pieces, the rest index-key pieces.
+__global__ void __launch_bounds__(256) append_kv_kidx_kernel(AppendArgs a, int64_t kv_total,
+                                                             int64_t ki_total) {
+  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < kv_total + ki_total;
+       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (id < kv_total)
+      append_kv_one(a, id);
+    else
+      append_kidx_one(a, id - kv_total);
   }
 }
 
@@ -202,12 +213,10 @@ hipError_t launch_cache_append(const Dims& d, const PagedKV& pk, int64_t n_new, 
   a.units_max = static_cast<int>((n_new + 14) / 8);
   a.blocks_max = static_cast<int>((n_new + 2 * d.B - 2) / d.B);
   const int64_t kv_total = d.Bt * d.G * a.units_max * (d.D / 8);
-  hipLaunchKernelGGL(append_kv_kernel, dim3(grid_for(kv_total)), dim3(256), 0, s, a, kv_total);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t ki_total = d.Bt * n_new * (d.Di / 8);
-  hipLaunchKernelGGL(append_kidx_kernel, dim3(grid_for(ki_total)), dim3(256), 0, s, a, ki_total);
-  e = hipGetLastError();
+  hipLaunchKernelGGL(append_kv_kidx_kernel, dim3(grid_for(kv_total + ki_total)), dim3(256), 0, s, a,
+                     kv_total, ki_total);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t kb_total = d.Bt * a.blocks_max * (d.Di / 8);
   hipLaunchKernelGGL(append_kblk_kernel, dim3(grid_for(kb_total)), dim3(256), 0, s, a, kb_total);
