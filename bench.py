@@ -13,9 +13,13 @@ stages give the per-stage (per-kernel) durations on the stream the kernels run o
 
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline      : the dominant kernel's algorithmic work / measured duration against the MI355X peak
-  cpu_baseline  : the CPU oracle timed on a bounded sample of the same workload (this process, 1 core)
+  cpu_baseline  : the CPU oracle timed on a bounded sample of the same workload, on every usable
+                  host core (one worker process per core, at most 16) and on one core
   stages        : per-stage milliseconds and roofline fractions
   parity        : the sampled rows of the last timed step against the oracle
+  selection     : the union of each group of 4 tokens' selections (and the attention's issued MFMA
+                  work it implies), needle recall, and the token inclusion rate of B = 8, k = 4096
+                  against B = 1, k = 2048 (GPU and oracle)
 """
 from __future__ import annotations
 
@@ -150,7 +154,31 @@ def load_traffic(kernel, workload):
 # ------------------------------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ------------------------------------------------------------------------------------------------
+_POOL = {}          # state the forked oracle workers read (set before the pool forks)
+
+
+def _oracle_worker(rows):
+    import oracle
+    c = _POOL
+    sel, out, _ = oracle.forward_rows(c["x"], c["block"], c["topk"], c["scale"], rows, k_blk=c["kblk"])
+    return rows, sel, out
+
+
+def host_workers():
+    """Worker processes for the all-cores oracle run: the host cores this process may use, at most
+    16 (a GPU machine's share of its host for one GPU)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
+
+
 def cpu_baseline(w, x, out_gpu, sel_gpu, target_s, seed):
+    """The oracle on a bounded random sample of query tokens: first on one core (for about
+    target_s seconds), then the same tokens on every host core this process may use (one
+    single-threaded worker process per core, forked before any of them starts)."""
+    import multiprocessing as mp
     import torch
     import oracle
     try:
@@ -165,24 +193,38 @@ def cpu_baseline(w, x, out_gpu, sel_gpu, target_s, seed):
     # sample over the whole query range, weighted like the workload (uniform over tokens)
     cpu = {n: x[n].to("cpu") for n in ("q", "k", "v", "gate", "q_idx", "k_idx")}
     cand = rng.permutation(w.t_q)
-    toks, times = [], []
-    sels, outs = [], []
+    toks, sels, outs = [], [], []
     t_begin = time.perf_counter()
     kblk = None
     for i in cand:
-        t0 = time.perf_counter()
         sel, out, kb = oracle.forward_rows(cpu, w.block, w.topk, w.softmax_scale, [(0, int(i))],
                                            k_blk=kblk)
         if kblk is None:
             kblk = np.stack([kb[0]])        # compression done once, like one pass per forward
-        times.append(time.perf_counter() - t0)
         toks.append(int(i))
         sels.append(sel[0])
         outs.append(out[0])
         if time.perf_counter() - t_begin >= target_s and len(toks) >= 4:
             break
     elapsed = time.perf_counter() - t_begin
-    rate = len(toks) / elapsed
+    rate1 = len(toks) / elapsed
+
+    # the same tokens on every usable core (compression again, once, in the parent)
+    nw = host_workers()
+    _POOL.clear()
+    _POOL.update(x=cpu, block=w.block, topk=w.topk, scale=w.softmax_scale, kblk=None)
+    t0 = time.perf_counter()
+    _POOL["kblk"] = oracle.compress(cpu["k_idx"].to(torch.float64).numpy(), w.block)
+    pieces = [[(0, t) for t in toks[j:j + 4]] for j in range(0, len(toks), 4)]
+    sel_n = {}
+    with mp.get_context("fork").Pool(nw) as pool:
+        for rows, sel, out in pool.imap_unordered(_oracle_worker, pieces):
+            for r, (_, t) in enumerate(rows):
+                sel_n[t] = sel[r]
+    elapsed_n = time.perf_counter() - t0
+    _POOL.clear()
+    same = all(np.array_equal(sel_n[t], sels[k]) for k, t in enumerate(toks))
+
     # parity of the sampled rows against the last GPU step
     sel_ref = np.stack(sels)
     out_ref = np.stack(outs)
@@ -193,11 +235,115 @@ def cpu_baseline(w, x, out_gpu, sel_gpu, target_s, seed):
               "max_abs_err": float(np.abs(og - out_ref).max()),
               "tolerance": 1e-2 if w.dtype == "bf16" else 1e-5}
     late = sum(1 for i in toks if (pos0 + i) // w.block + 1 > w.n_sel)
-    base = {"value": rate, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(toks)} random query tokens of the {w.name} workload ({late} in the sparse "
-                      f"regime), all {w.groups} KV groups, block compression included once; "
-                      f"fp64 numpy oracle, 1 thread, {elapsed:.1f} s"}
+    sample = (f"{len(toks)} random query tokens of the {w.name} workload ({late} in the sparse "
+              f"regime), all {w.groups} KV groups, block compression included once; fp64 numpy "
+              f"oracle")
+    base = {"value": len(toks) / elapsed_n, "unit": "query-tokens/s", "cores": nw, "kind": "oracle",
+            "sample": f"{sample}, {nw} single-threaded worker processes, {elapsed_n:.2f} s",
+            "host_cpu_count": os.cpu_count(),
+            "single_core": {"value": rate1, "unit": "query-tokens/s", "cores": 1,
+                            "sample": f"{sample}, 1 thread, {elapsed:.1f} s"},
+            "all_cores_match_single_core": bool(same)}
     return base, parity
+
+
+# ------------------------------------------------------------------------------------------------
+# the selection's own figures: union of 4-token groups (issued attention work), needle recall,
+# token inclusion against the B = 1, k = 2048 selection
+# ------------------------------------------------------------------------------------------------
+def union_stats(w, sel):
+    """Per group of 4 query tokens and KV group: the distinct 8-token units of the 4 selections
+    (the attention's tile walks this union once) and the issued MFMA work, each of the 4 unit
+    ranges padded to a multiple of 4 units as the range kernel runs it."""
+    import torch
+    if w.block != 8 or w.t_q % 4:
+        return None
+    ng = w.t_q // 4
+    s = sel[0].view(ng, 4, w.groups, w.n_sel).permute(0, 2, 1, 3).reshape(ng * w.groups, 4 * w.n_sel)
+    s, _ = torch.sort(s, dim=1)
+    first = torch.ones_like(s[:, :1], dtype=torch.bool)
+    distinct = torch.cat([first, s[:, 1:] != s[:, :-1]], dim=1) & (s >= 0)
+    pos_last = torch.arange(ng, device=s.device, dtype=torch.int64) * 4 + 3 + (w.t_kv - w.t_q)
+    u_end = (pos_last // 8 + 1).repeat_interleave(w.groups).view(-1, 1)
+    rng_idx = torch.zeros_like(s, dtype=torch.int64)
+    for r in range(1, 4):
+        rng_idx += (s.to(torch.int64) >= (r * u_end) // 4).to(torch.int64)
+    chunks = torch.zeros(s.shape[0], dtype=torch.int64, device=s.device)
+    units = distinct.sum(dim=1)
+    for r in range(4):
+        n_r = (distinct & (rng_idx == r)).sum(dim=1)
+        chunks += (n_r + 3) // 4
+    del s, distinct, rng_idx
+    rows = 4 * w.heads
+    flop_per_chunk = 2 * 2 * rows * 32 * w.head_dim          # S^T and P.V, 32 rows x 32 keys x d
+    return {"union_units_per_4_tokens": float(units.double().mean().item()),
+            "union_over_one_selection": float(units.double().mean().item()) / w.n_sel,
+            "issued_chunks": int(chunks.sum().item()),
+            "issued_flops": int(chunks.sum().item()) * flop_per_chunk,
+            "definition": "distinct 8-token units of each group of 4 tokens' selections (one KV "
+                          "group); issued = S^T and P.V products of 32 rows x 32 keys x d per "
+                          "chunk of 4 units, each of the 4 unit ranges padded to whole chunks"}
+
+
+def needle_recall(w, x, sel):
+    """Fraction of planted needle blocks that the selection keeps, over every (query, group) and
+    every needle block at or before the query's own block."""
+    import torch
+    nb = x["needle_blocks"]
+    if nb.numel() == 0:
+        return None
+    pos = torch.arange(w.t_kv - w.t_q, w.t_kv, device=sel.device, dtype=torch.int64)
+    o = (pos // w.block).view(-1, 1)
+    hit = tot = 0
+    for g in range(w.groups):
+        nd = nb[g].to(sel.device)
+        s = sel[0, :, g, :].to(torch.int64)
+        kept = torch.isin(s, nd).sum()
+        causal = (nd.view(1, -1) <= o).sum()
+        hit += int(kept.item())
+        tot += int(causal.item())
+    return {"recall": hit / max(tot, 1), "needles_kept": hit, "needles_causal": tot,
+            "needles_per_group": int(nb.shape[1])}
+
+
+def inclusion_report(w, x, sel, n_tok=64):
+    """Token inclusion rate of the B = 8, k = 4096 selection against B = 1, k = 2048 over the last
+    n_tok query tokens and every KV group: mean over rows of |A_8 & A_1| / |A_1|.  The GPU figure
+    takes the forward's selection and a B = 1 index + top-k run through the C ABI; the oracle
+    recomputes both selections.  A property of the synthetic inputs (no pinned value)."""
+    import torch
+    import long_context_sparse_sgqa_amd as sg
+    import oracle
+    if w.block != 8 or w.topk != 4096 or w.t_q < n_tok:
+        return None
+    p1 = sg.Problem(1, n_tok, w.t_kv, w.groups, w.heads, w.head_dim, w.index_dim, 1, 2048,
+                    w.softmax_scale, dtype=torch.bfloat16, index_dtype=torch.bfloat16)
+    qi = x["q_idx"][:, w.t_q - n_tok:].contiguous()
+    _, sc1 = sg.index(p1, qi, x["k_idx"])
+    sel1 = sg.topk(p1, sc1)
+    torch.cuda.synchronize()
+    del sc1
+    s8 = sel[0, w.t_q - n_tok:].to("cpu").numpy().astype(np.int64)
+    s1 = sel1[0].to("cpu").numpy().astype(np.int64)
+    pos = np.arange(w.t_kv - n_tok, w.t_kv)
+    rates = np.zeros((n_tok, w.groups))
+    for i in range(n_tok):
+        for g in range(w.groups):
+            b8 = s8[i, g][s8[i, g] >= 0]
+            a8 = (b8[:, None] * 8 + np.arange(8)[None, :]).ravel()
+            a8 = a8[a8 <= pos[i]]
+            a1 = s1[i, g][s1[i, g] >= 0]
+            rates[i, g] = np.intersect1d(a8, a1).size / a1.size
+    rows = [(0, i) for i in range(w.t_q - n_tok, w.t_q)]
+    ref = oracle.inclusion_rate(x["q_idx"], x["k_idx"], rows, w.t_kv)
+    return {"rate": float(rates.mean()), "oracle_rate": float(ref.mean()),
+            "rows_equal": bool(np.array_equal(rates, ref)),
+            "sample": f"last {n_tok} query tokens x {w.groups} KV groups",
+            "definition": "mean over (query, group) of |A_8 & A_1| / |A_1|, A_8 the tokens attended "
+                          "with B = 8, k = 4096 and A_1 with B = 1, k = 2048 on the same index data",
+            "pages": "78.06 % (B = 8, k = 4096) and 79.09 % (B = 1, k = 2048) on the pages' own "
+                     "model and data, against a reference set they do not name",
+            "parity": "unpinned (a property of the synthetic inputs)"}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -648,6 +794,15 @@ def main():
     cpu, parity = (None, None)
     if args.cpu_seconds > 0 and args.kv == "bf16":
         cpu, parity = cpu_baseline(w, x, out, sel, args.cpu_seconds, args.seed)
+    selection = None
+    if args.kv == "bf16":
+        selection = {"union": union_stats(w, sel), "needles": needle_recall(w, x, sel)}
+        if args.cpu_seconds > 0:
+            selection["inclusion"] = inclusion_report(w, x, sel)
+        un = selection["union"]
+        if un is not None and "kernel" in roof and roof["kernel"].startswith("attend_range"):
+            roof["issued_flops"] = un["issued_flops"]
+            roof["issued_frac"] = un["issued_flops"] / (stage_ms["attention"] * 1e-3) / PEAK_BF16_FLOPS
 
     rec = {
         "metric": "Sparse-GQA prefill query-tokens/s at 128K ctx (index+topk+attn); % roofline"
@@ -665,6 +820,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": stages,
         "parity": parity,
+        "selection": selection,
         "algorithmic": c,
         "device": torch.cuda.get_device_name(0),
     }

@@ -207,8 +207,10 @@ sgqa_status sgqa_set_stage_events(void* const* events);
  *   (seq_lens and block_table need 4-byte alignment only; every other pointer 16 bytes.)
  * Only sgqa_cache_append writes the cache; it keeps tokens past a sequence's length inside the
  * sequence's last 8-token unit at zero.  Host-side validation covers every size; device-side
- * values (seq_lens, block_table) are clamped into range by the kernels, so a bad entry gives
- * wrong results for that sequence but never an out-of-bounds access.  Required:
+ * values (seq_lens, block_table) are clamped into range where the kernels read, and the append
+ * stores nothing for tokens whose block_table entry is outside [0, num_pages), so a bad entry
+ * gives wrong results for that sequence but never an out-of-bounds access and never a write into
+ * a page the entry does not name.  Required:
  * prob->t_q <= seq_lens[b] <= prob->t_kv <= max_pages * P for sgqa_decode (n_new instead of t_q
  * for sgqa_cache_append), block_table entries in [0, num_pages).
  * --------------------------------------------------------------------------------------------- */

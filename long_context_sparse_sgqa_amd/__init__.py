@@ -119,7 +119,8 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(_PKG_DIR, _LIB_NAME)
+    """The in-tree libsgqa.so, or the library SGQA_LIBRARY names (e.g. the host-sanitized build)."""
+    return os.environ.get("SGQA_LIBRARY") or os.path.join(_PKG_DIR, _LIB_NAME)
 
 
 def load_library():

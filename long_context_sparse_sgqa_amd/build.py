@@ -1,6 +1,13 @@
 """Build libsgqa.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
     python -m long_context_sparse_sgqa_amd.build          # compile + link
+    python -m long_context_sparse_sgqa_amd.build --host-sanitizers
+        # libsgqa_hostsan.so: the same library with AddressSanitizer and UndefinedBehaviorSanitizer
+        # on the host code only (argument validation, sizing, launch set-up); the GPU code is
+        # built as usual.  Run the CPU test tier against it with
+        #   SGQA_LIBRARY=$PWD/long_context_sparse_sgqa_amd/libsgqa_hostsan.so \
+        #   LD_PRELOAD=$(python -m long_context_sparse_sgqa_amd.build --asan-runtime) \
+        #   ASAN_OPTIONS=detect_leaks=0 python -m pytest tests -m "not gpu" -q
 The library lands next to this file; objects go to _build/ (not committed).
 """
 from __future__ import annotations
@@ -47,14 +54,39 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libsgqa.so; always rebuilds.  Returns the library path."""
+# host-only sanitizers: each -fsanitize= goes to the host compilation alone
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+                 "-fno-omit-frame-pointer", "-g"]
+HOSTSAN_LIB_PATH = os.path.join(PKG_DIR, "libsgqa_hostsan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime a host-sanitized library needs preloaded."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                       text=True, check=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang AddressSanitizer runtime was not found")
+    return path
+
+
+def build(verbose: bool = False, host_sanitizers: bool = False) -> str:
+    """Compile every source and link libsgqa.so (or libsgqa_hostsan.so with host sanitizers);
+    always rebuilds.  Returns the library path."""
+    hipcc = _hipcc()
+    bdir = os.path.join(BUILD_DIR, "hostsan") if host_sanitizers else BUILD_DIR
+    lib_path = HOSTSAN_LIB_PATH if host_sanitizers else LIB_PATH
+    extra = HOST_SANITIZE if host_sanitizers else []
+    os.makedirs(bdir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         out = _run(cmd)
@@ -64,14 +96,19 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
+    # a host-sanitized library is linked without a runtime: its sanitizer symbols resolve against
+    # the AddressSanitizer runtime preloaded into the process (which carries the UBSan handlers)
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print("built", LIB_PATH)
-    return LIB_PATH
+        print("built", lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--asan-runtime" in sys.argv:
+        print(asan_runtime())
+    else:
+        build(verbose=True, host_sanitizers="--host-sanitizers" in sys.argv)
     sys.exit(0)

@@ -39,9 +39,18 @@ struct AppendArgs {
   int blocks_max;             // blocks one sequence's new tokens can touch
 };
 
+// Page of logical page j for reading: a bad entry is clamped into the pool, which can only give
+// wrong values for sequence b.
 __device__ __forceinline__ int64_t page_of(const AppendArgs& a, int64_t b, int64_t j) {
   int64_t pg = a.block_table[b * a.max_pages + j];
   return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+}
+
+// Page of logical page j for writing, or -1 when the entry is outside [0, num_pages): the append
+// then stores nothing there, so a bad entry cannot overwrite a page another sequence owns.
+__device__ __forceinline__ int64_t page_for_write(const AppendArgs& a, int64_t b, int64_t j) {
+  const int64_t pg = a.block_table[b * a.max_pages + j];
+  return (pg < 0 || pg >= a.num_pages) ? -1 : pg;
 }
 
 // One thread per (sequence, group, touched unit, 8-wide d piece): the unit's new tokens are
@@ -60,7 +69,8 @@ __device__ __forceinline__ void append_kv_one(const AppendArgs& a, int64_t id) {
     const int64_t end = start + a.n_new;                 // exclusive
     const int64_t u = (start >> 3) + uu;
     if (u > ((end - 1) >> 3)) return;
-    const int64_t page = page_of(a, b, (u * 8) >> (a.ul2 + 3));
+    const int64_t page = page_for_write(a, b, (u * 8) >> (a.ul2 + 3));
+    if (page < 0) return;
     const int64_t unit_elem = (((page * a.G + g) << a.ul2) | (u & ((1 << a.ul2) - 1))) * 8 * a.D;
     bf16_t* kdst = a.k_pool + unit_elem;
     bf16_t* vdst = a.v_pool + unit_elem;
@@ -120,7 +130,8 @@ __device__ __forceinline__ void append_kidx_one(const AppendArgs& a, int64_t id)
     const int64_t t = r % a.n_new;
     const int64_t b = r / a.n_new;
     const int64_t pos = seq_pos0(a.seq_len, b, a.max_len - a.n_new, a.n_new) + t;
-    const int64_t page = page_of(a, b, pos / ptok);
+    const int64_t page = page_for_write(a, b, pos / ptok);
+    if (page < 0) return;
     *reinterpret_cast<uint4*>(a.kidx_pool + (page * ptok + (pos & (ptok - 1))) * a.Di + 8 * j) =
         *reinterpret_cast<const uint4*>(a.kidx_new + r * a.Di + 8 * j);
   }

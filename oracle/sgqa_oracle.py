@@ -32,7 +32,8 @@ block sums and scores are exact integers far below 2**53, so the selection is ex
 
 Parity pins: every function here is checked in tests/ against something other than itself (closed
 forms, special cases that reduce to a library routine, brute force on tiny inputs, a hand-worked
-example).  The token inclusion rate is a measured property of synthetic data: parity unpinned.
+example).  The token inclusion rate is pinned by brute force on tiny inputs; its value on the
+synthetic workloads is a measured property of those inputs, not a target.
 """
 from __future__ import annotations
 
@@ -335,7 +336,8 @@ def inclusion_rate(q_idx, k_idx, rows, t_kv: int, cfg_a=(8, 4096), cfg_b=(1, 204
     For each listed (b, i) and every group: |A_a & A_b| / |A_b|, where A_x is the set of tokens the
     query attends to under block size / token budget cfg_x.  The pages compare B=8, k=4096 against
     B=1, k=2048 (78.06 % vs 79.09 %) without naming the reference set; this takes the B=1, k=2048
-    token set as the reference.  Returns float64 [n_rows, G].  Parity unpinned (a measured property).
+    token set as the reference.  Returns float64 [n_rows, G].  Its value on synthetic data is a
+    measured property of those inputs.
     """
     t_q, G = q_idx.shape[1], q_idx.shape[2]
     pos = query_positions(t_q, t_kv)

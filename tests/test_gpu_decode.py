@@ -203,3 +203,37 @@ def test_paged_decode_workload():
     check_decode_sel_structure(sel[[0, 37]].cpu(), [w.t_kv] * 2, w.t_q, w.block, w.n_sel)
     del x, pools, out, sel, again
     torch.cuda.empty_cache()
+
+
+def test_append_skips_out_of_range_page_entries():
+    """A block_table entry outside [0, num_pages) makes the append store nothing for the tokens of
+    that logical page: every pool page keeps its bytes, including the last page, which a clamped
+    entry would have named.  The other sequence's append still lands."""
+    dev = "cuda"
+    P, t_kv = 64, 256
+    w, x = generate_small(batch=2, t_q=4, t_kv=t_kv, groups=2, heads=8, head_dim=128,
+                          index_dim=64, block=8, topk=64, dtype="bf16", index_dtype="bf16",
+                          scaled_qkv=True, seed=13, device=dev)
+    say("case: append with out-of-range block_table entries")
+    prob = sg.Problem(batch=2, t_q=4, t_kv=t_kv, kv_groups=2, heads_per_group=8, head_dim=128,
+                      index_dim=64, block=8, topk_tokens=64)
+    max_pages, num_pages = 4, 8
+    cache = sg.Cache(num_pages, P, max_pages)
+    pools = sg.alloc_cache(prob, cache, dev)
+    for name in ("k_cache", "v_cache", "kidx_cache"):
+        pools[name].view(torch.int16).fill_(0x1234)
+    table = torch.tensor([[0, 1, 2, 3], [num_pages, -1, num_pages + 5, 7]], dtype=torch.int32,
+                         device=dev)
+    before = {n: pools[n].clone() for n in ("k_cache", "v_cache", "kidx_cache")}
+    n = 100                                     # positions 0..99: logical pages 0 and 1
+    seq = torch.tensor([n, n], dtype=torch.int32, device=dev)
+    sg.cache_append(prob, cache, seq, table, x["k"][:, :, :n].contiguous(),
+                    x["v"][:, :, :n].contiguous(), x["k_idx"][:, :n].contiguous(), pools)
+    torch.cuda.synchronize()
+    for name in ("k_cache", "v_cache", "kidx_cache"):
+        # sequence 0 owns pages 0 and 1; nothing else may change
+        assert torch.equal(pools[name][2:], before[name][2:]), name
+        assert not torch.equal(pools[name][:2], before[name][:2]), name
+    # sequence 0's index keys landed where its table says
+    ki = pools["kidx_cache"].view(num_pages * P, 64)
+    assert torch.equal(ki[:n], x["k_idx"][0, :n])

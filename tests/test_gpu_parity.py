@@ -92,6 +92,55 @@ def test_small_bf16_every_row(case):
     assert torch.equal(out2, out)
 
 
+# ----------------------------------------------------------------------------------------------
+# bf16 indexer scores, element by element, and the untouched tail of every score row
+# ----------------------------------------------------------------------------------------------
+# (t_q, t_kv, block, groups, index_dim, batch): the first three have at most 32 rows per sequence
+# (index_rows32_kernel for index dims 128, 64 and 32); the others take the tiled index_bf16_kernel
+INDEX_CASES = [
+    (7, 1300, 8, 2, 128, 2),
+    (5, 900, 8, 3, 64, 1),
+    (16, 2000, 16, 2, 32, 1),
+    (300, 1001, 8, 2, 128, 1),
+    (517, 517, 8, 3, 64, 1),
+    (257, 700, 16, 2, 32, 1),
+    (401, 601, 4, 2, 128, 1),
+    (150, 700, 8, 2, 128, 3),
+]
+SENTINEL = 0x7FC0BEEF          # a NaN payload no score can take
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=lambda c: "tq%d-tk%d-B%d-G%d-di%d-b%d" % c)
+def test_index_scores_every_row_bf16(case):
+    """sgqa_index on bf16 index data: every defined score (j < p/B) equals the oracle's block score
+    exactly, and every entry j >= p/B keeps the value the buffer held before the call."""
+    t_q, t_kv, B, G, di, bt = case
+    say("case: index scores", case)
+    w, x = generate_small(batch=bt, t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=64,
+                          index_dim=di, block=B, topk=64 * B, dtype="bf16", index_dtype="bf16",
+                          scaled_qkv=True, needles=1 if (t_kv // B) >= 2 * G else 0, seed=21,
+                          device="cuda")
+    prob = sg.Problem.from_workload(w)
+    scores = torch.empty((bt, t_q, G, prob.num_blocks), dtype=torch.float32, device="cuda")
+    scores.view(torch.int32).fill_(SENTINEL)
+    k_blk, scores = sg.index(prob, x["q_idx"], x["k_idx"], scores=scores)
+    torch.cuda.synchronize()
+    kblk_ref = oracle.compress(x["k_idx"].cpu().double().numpy(), B)
+    np.testing.assert_array_equal(k_blk.cpu().double().numpy(), kblk_ref)
+    sc = scores.cpu()
+    bits = sc.view(torch.int32).numpy()
+    sc = sc.double().numpy()
+    qi = x["q_idx"].cpu().double().numpy()
+    pos = oracle.query_positions(t_q, t_kv)
+    for b in range(bt):
+        for i in range(t_q):
+            o = int(pos[i]) // B
+            for g in range(G):
+                np.testing.assert_array_equal(sc[b, i, g, :o], oracle.block_scores(qi[b, i, g], kblk_ref[b], o),
+                                              err_msg=f"row b={b} i={i} g={g}")
+                assert (bits[b, i, g, o:] == SENTINEL).all(), f"tail written at b={b} i={i} g={g}"
+
+
 def test_block_one_selection_is_token_level():
     """B = 1 (token-level, the pages' comparison setting) through index + top-k."""
     w, x = generate_small(t_q=700, t_kv=900, groups=2, heads=8, head_dim=128, index_dim=128,
@@ -203,11 +252,16 @@ def test_run_to_run_bitwise():
 # ----------------------------------------------------------------------------------------------
 # full-size workloads: sampled rows against the oracle, structural checks on every row
 # ----------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("name,n_random", [("32k", 24), ("128k", 12), ("1m", 6)])
-def test_workload_sampled_rows(name, n_random):
+@pytest.mark.parametrize("name,n_random,sharp", [("32k", 24, False), ("128k", 12, False),
+                                                ("1m", 6, False), ("128k", 12, True),
+                                                ("1m", 6, True)],
+                         ids=["32k", "128k", "1m", "128k-sharp", "1m-sharp"])
+def test_workload_sampled_rows(name, n_random, sharp):
+    """Full-size workloads on stratified sampled rows.  The "sharp" variants leave q and k unscaled,
+    so the softmax is far from uniform and a wrong weight or a dropped token shows in the output."""
     w = get_workload(name)
-    say("case:", name)
-    x = generate(w, device="cuda", seed=0)
+    say("case:", name, "sharp" if sharp else "")
+    x = generate(w, device="cuda", seed=0, sharp=sharp)
     prob = sg.Problem.from_workload(w)
     out, sel = run_forward(prob, x)
     structural_check_sel(sel, prob)
@@ -221,6 +275,46 @@ def test_workload_sampled_rows(name, n_random):
     last = sel[0, -1].cpu().numpy()
     for g in range(w.groups):
         assert set(x["needle_blocks"][g].tolist()) <= set(last[g].tolist())
+    del x, out, sel
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t_q", [64, 3])
+def test_long_context_union_every_row(t_q):
+    """Every row at 524 288 keys, where the group lists scan their bitmaps four words at a time
+    (2 048 bitmap words per token).  With t_q = 3 there is one group of tokens, so the attention's
+    waves take its unit ranges and the lists split at equal entry counts.
+
+    q = 0 makes every logit 0, so each output is sigmoid(0) = 0.5 times the mean of v over the
+    attended tokens; v is one-hot per token: dim (unit mod 64) and dim 64 + (unit // 64 mod 64).
+    Each output is then a count of attended units per residue class divided by |A|, computed
+    exactly on the device up to the bf16 rounding of the range partials and of the output
+    (relative 2^-8 at most).  A residue class holds about 8 of a row's 512 units, so one dropped
+    or extra 8-token unit moves some output by several percent of its value (or from 0 to about
+    1e-3), far outside the 2^-7 relative bar below."""
+    t_kv, G, B = 524288, 2, 8
+    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=128, index_dim=128,
+                          block=B, topk=4096, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          needles=2, seed=17, device="cuda")
+    say(f"case: long-context unions, t_kv={t_kv}, t_q={t_q}")
+    x["q"].zero_()
+    x["gate"].zero_()
+    unit = torch.arange(t_kv, device="cuda") // 8
+    v = torch.zeros((t_kv, 128), dtype=torch.bfloat16, device="cuda")
+    v[torch.arange(t_kv, device="cuda"), unit % 64] = 1.0
+    v[torch.arange(t_kv, device="cuda"), 64 + (unit // 64) % 64] = 1.0
+    x["v"] = v.expand(1, G, t_kv, 128).contiguous()
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    structural_check_sel(sel, prob)
+    rows = [(0, i) for i in range(t_q)]
+    sel_ref, out_ref, _ = oracle_rows(prob, x, rows)
+    check_sel_rows(sel[0], sel_ref)
+    got = out[0].to("cpu", torch.float64).numpy()
+    err = np.abs(got - out_ref)
+    bar = 2.0 ** -7 * np.abs(out_ref) + 1e-7
+    say(f"  max relative error {float((err / (np.abs(out_ref) + 1e-30)).max()):.3e}")
+    assert (err <= bar).all(), f"{int((err > bar).sum())} outputs outside the bar"
     del x, out, sel
     torch.cuda.empty_cache()
 

@@ -336,8 +336,44 @@ def test_attention_token_order_invariant():
 
 
 # ----------------------------------------------------------------------------------------------
-# inclusion rate (measured property; parity unpinned) -- only its definition's edge cases
+# inclusion rate (a measured property of the inputs): its definition's edge cases, and brute force
+# on tiny inputs
 # ----------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg_a,cfg_b", [((4, 16), (1, 8)), ((8, 16), (2, 12)), ((3, 9), (1, 5))])
+def test_inclusion_rate_brute_force(cfg_a, cfg_b):
+    """|A_a & A_b| / |A_b| per (query, group), with both selections taken by the O(n^2) rank count
+    (no sort), the attended sets built token by token and the ratio as an exact fraction.  The two
+    sets have different sizes, so swapping numerator and denominator roles, or the two configs,
+    fails."""
+    from fractions import Fraction
+    T = 48
+    w, inp = generate_small(t_q=20, t_kv=T, groups=2, index_dim=3, seed=31)
+    rows = [(0, i) for i in range(20)]
+    got = oracle.inclusion_rate(inp["q_idx"], inp["k_idx"], rows, T, cfg_a, cfg_b)
+    k_idx = inp["k_idx"][0].double().numpy()
+    q_idx = inp["q_idx"][0].double().numpy()
+
+    def attended(q, p, B, k):
+        nb = -(-T // B)
+        kb = [[sum(k_idx[t, c] for t in range(j * B, min(j * B + B, T))) for c in range(3)]
+              for j in range(nb)]
+        o = p // B
+        s = [sum(q[c] * kb[j][c] for c in range(3)) for j in range(o)]
+        chosen = _brute_force_selection(s, o, k // B)
+        return {t for t in range(p + 1) if t // B in chosen}
+
+    n_strict = 0
+    for r, (_, i) in enumerate(rows):
+        p = T - 20 + i
+        for g in range(2):
+            a = attended(q_idx[i, g], p, *cfg_a)
+            b = attended(q_idx[i, g], p, *cfg_b)
+            want = Fraction(len(a & b), len(b))
+            assert got[r, g] == float(want), (p, g)
+            n_strict += want < 1
+    assert n_strict > 0                      # the case exercises partial inclusion
+
+
 def test_inclusion_rate_edge_cases():
     w, inp = generate_small(t_q=64, t_kv=64, groups=2, index_dim=4, seed=2)
     rows = [(0, i) for i in range(64)]
