@@ -260,6 +260,30 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
                         const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sgqa_decode for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments and results as sgqa_decode
+ * without the workspace, which comes from a fixed scratch area inside the library instead.
+ *   - The scratch is SGQA_DECODE_NOALLOC_SCRATCH_BYTES (128 MiB) of device memory per GPU, part of
+ *     the library's code object: the runtime allocates it when the library's kernels load on a GPU,
+ *     and each GPU holds it until the process ends.  The first call on a GPU looks up its address
+ *     there (no allocation); no call allocates or frees memory.
+ *   - Problems whose sgqa_decode workspace exceeds that size are rejected with SGQA_ERR_WORKSPACE
+ *     before anything is enqueued (the 64-sequence, 262 144-token, 4-new-token decode needs about
+ *     89 MiB).
+ *   - Every call on a GPU uses that GPU's one scratch area, and each call clears what it needs, so
+ *     calls in sequence on a stream (or ordered across streams) are safe, but calls that can
+ *     overlap on one GPU (different streams without ordering, several host threads) race on the
+ *     scratch and give wrong results.  Use sgqa_decode with distinct workspaces for those.
+ *   - The scratch belongs to the device of `stream` (the current device for the null stream).
+ */
+#define SGQA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+sgqa_status sgqa_decode_noalloc(const sgqa_problem* prob, const sgqa_cache* cache,
+                                const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                                const void* gate, const void* q_idx, const void* k_cache,
+                                const void* v_cache, const void* k_blk, int32_t* sel_out,
+                                void* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Backward of step 4 (training at long context; Step 5 Preview summary on mo.ai.kr, section
  * "모델 구조와 학습 안정성").  For a fixed selection `sel` (the indexer is not differentiated) and

@@ -24,8 +24,8 @@ import torch
 
 __all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
            "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
-           "decode", "swa_workspace_size", "swa", "forward_fp8kv", "attend_backward", "SgqaError",
-           "EXPORTED_SYMBOLS"]
+           "decode", "decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES", "swa_workspace_size", "swa",
+           "forward_fp8kv", "attend_backward", "SgqaError", "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsgqa.so"
@@ -36,8 +36,12 @@ _DT = {torch.float32: SGQA_F32, torch.bfloat16: SGQA_BF16}
 EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error", "sgqa_sizes",
                     "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                     "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                    "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv",
-                    "sgqa_attend_backward_workspace_size", "sgqa_attend_backward")
+                    "sgqa_decode", "sgqa_decode_noalloc", "sgqa_swa_workspace_size", "sgqa_swa",
+                    "sgqa_forward_fp8kv", "sgqa_attend_backward_workspace_size",
+                    "sgqa_attend_backward")
+
+# scratch sgqa_decode_noalloc holds per GPU (SGQA_DECODE_NOALLOC_SCRATCH_BYTES in include/sgqa.h)
+DECODE_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class SgqaError(RuntimeError):
@@ -148,6 +152,7 @@ def load_library():
     lib.sgqa_cache_append.argtypes = [P, C, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sgqa_decode_workspace_size.argtypes = [P, C, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgqa_decode.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sgqa_decode_noalloc.argtypes = [P, C, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sgqa_swa_workspace_size.argtypes = [P, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgqa_swa.argtypes = [P, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     f32 = ctypes.c_float
@@ -157,8 +162,9 @@ def load_library():
     lib.sgqa_attend_backward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                  "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
-                 "sgqa_decode", "sgqa_swa_workspace_size", "sgqa_swa", "sgqa_forward_fp8kv",
-                 "sgqa_attend_backward_workspace_size", "sgqa_attend_backward"):
+                 "sgqa_decode", "sgqa_decode_noalloc", "sgqa_swa_workspace_size", "sgqa_swa",
+                 "sgqa_forward_fp8kv", "sgqa_attend_backward_workspace_size",
+                 "sgqa_attend_backward"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -351,6 +357,28 @@ def decode(prob: Problem, cache: Cache, seq_lens, block_table, q, gate, q_idx, p
         _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], torch.bfloat16),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return (out, sel) if return_sel else out
+
+
+def decode_noalloc(prob: Problem, cache: Cache, seq_lens, block_table, q, gate, q_idx, pools: dict,
+                   out, sel=None, stream=None):
+    """sgqa_decode without a workspace: the library's fixed per-GPU scratch serves instead, so the
+    call allocates nothing (out and sel must be given).  Calls that overlap on one GPU race on
+    that scratch."""
+    lib = load_library()
+    sh = _shapes(prob)
+    csh = _cache_shapes(prob, cache)
+    _check(lib.sgqa_decode_noalloc(
+        ctypes.byref(prob._c()), ctypes.byref(cache._c()),
+        _ptr(seq_lens, "seq_lens", csh["seq_lens"], torch.int32),
+        _ptr(block_table, "block_table", csh["block_table"], torch.int32),
+        _ptr(q, "q", sh["q"], torch.bfloat16), _ptr(gate, "gate", sh["q"], torch.bfloat16),
+        _ptr(q_idx, "q_idx", sh["q_idx"], torch.bfloat16),
+        _ptr(pools["k_cache"], "k_cache", csh["k_cache"], torch.bfloat16),
+        _ptr(pools["v_cache"], "v_cache", csh["v_cache"], torch.bfloat16),
+        _ptr(pools["k_blk"], "k_blk", csh["k_blk"], torch.bfloat16),
+        _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], torch.bfloat16),
+        _stream(stream)))
+    return out
 
 
 # ----------------------------------------------------------------------------------------------

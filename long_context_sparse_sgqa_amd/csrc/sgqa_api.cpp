@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -528,13 +529,12 @@ sgqa_status sgqa_decode_workspace_size(const sgqa_problem* prob, const sgqa_cach
   return ok();
 }
 
-sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
-                        const int32_t* seq_lens, const int32_t* block_table, const void* q,
-                        const void* gate, const void* q_idx, const void* k_cache,
-                        const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  DecodeDerived dd;
-  SGQA_CHECK(derive_decode(prob, cache, &dd));
+namespace {
+
+sgqa_status check_decode_ptrs(const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                              const void* gate, const void* q_idx, const void* k_cache,
+                              const void* v_cache, const void* k_blk, const int32_t* sel_out,
+                              const void* out) {
   SGQA_CHECK(check_ptr(seq_lens, "seq_lens", 4));
   SGQA_CHECK(check_ptr(block_table, "block_table", 4));
   SGQA_CHECK(check_ptr(q, "q"));
@@ -545,6 +545,70 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
   SGQA_CHECK(check_ptr(k_blk, "k_blk"));
   SGQA_CHECK(check_ptr(out, "out"));
   if (sel_out) SGQA_CHECK(check_ptr(sel_out, "sel_out"));
+  return SGQA_OK;
+}
+
+constexpr size_t kNoAllocScratchBytes = SGQA_DECODE_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch size");
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// Scratch of sgqa_decode_noalloc: device memory of fixed size in this module, one copy per GPU
+// (allocated by the runtime when the module loads on that GPU and held until the process ends).
+// In host code `scratch` only names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, looked up once per device with that device current and kept below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` belongs to.
+sgqa_status scratch_on_stream_device(hipStream_t stream, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SGQA_ERR_UNSUPPORTED, "device %d is outside the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SGQA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SGQA_OK;
+}
+
+}  // namespace
+
+sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
+                        const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                        const void* gate, const void* q_idx, const void* k_cache,
+                        const void* v_cache, const void* k_blk, int32_t* sel_out, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeDerived dd;
+  SGQA_CHECK(derive_decode(prob, cache, &dd));
+  SGQA_CHECK(check_decode_ptrs(seq_lens, block_table, q, gate, q_idx, k_cache, v_cache, k_blk,
+                               sel_out, out));
   SGQA_CHECK(check_ptr(workspace, "workspace"));
   const size_t need = decode_workspace(dd);
   if (workspace_bytes < need)
@@ -605,6 +669,25 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   SGQA_CHECK(mark_stage(6, s));
   return ok();
+}
+
+sgqa_status sgqa_decode_noalloc(const sgqa_problem* prob, const sgqa_cache* cache,
+                                const int32_t* seq_lens, const int32_t* block_table, const void* q,
+                                const void* gate, const void* q_idx, const void* k_cache,
+                                const void* v_cache, const void* k_blk, int32_t* sel_out,
+                                void* out, void* stream) {
+  DecodeDerived dd;
+  SGQA_CHECK(derive_decode(prob, cache, &dd));
+  SGQA_CHECK(check_decode_ptrs(seq_lens, block_table, q, gate, q_idx, k_cache, v_cache, k_blk,
+                               sel_out, out));
+  const size_t need = decode_workspace(dd);
+  if (need > kNoAllocScratchBytes)
+    return fail(SGQA_ERR_WORKSPACE, "decode needs %zu bytes of scratch; sgqa_decode_noalloc holds "
+                "%zu (use sgqa_decode with a workspace)", need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  SGQA_CHECK(scratch_on_stream_device(static_cast<hipStream_t>(stream), &ws));
+  return sgqa_decode(prob, cache, seq_lens, block_table, q, gate, q_idx, k_cache, v_cache, k_blk,
+                     sel_out, out, ws, kNoAllocScratchBytes, stream);
 }
 
 sgqa_status derive_swa(const sgqa_problem* prob, int64_t window, Derived* dv, int64_t* w_eff,

@@ -163,3 +163,24 @@ def test_decode_and_append_null_and_workspace_errors(lib):
     app[2] = 4
     app[3] = None
     assert lib.sgqa_cache_append(ctypes.byref(P), ctypes.byref(C), *app, None) == ERR_NULL
+
+
+def test_decode_noalloc_rejects_before_device_access(lib):
+    """sgqa_decode_noalloc: a problem whose decode workspace exceeds the fixed scratch is rejected
+    with ERR_WORKSPACE, and a null argument with ERR_NULL, before the scratch is looked up (bogus,
+    never dereferenced addresses; no device here)."""
+    good = 0x10000
+    big = _dprob(batch=256)
+    Cb = sg.Cache(256 * 4097, 64, 4097)
+    assert sg.decode_workspace_size(big, Cb) > sg.DECODE_NOALLOC_SCRATCH_BYTES
+    assert sg.decode_workspace_size(_dprob(), sg.Cache(64 * 4097, 64, 4097)) <= \
+        sg.DECODE_NOALLOC_SCRATCH_BYTES                 # the decode workload fits
+    # seq_lens block_table q gate q_idx k_cache v_cache k_blk sel out
+    ptrs = [good] * 10
+    st = lib.sgqa_decode_noalloc(ctypes.byref(big._c()), ctypes.byref(Cb._c()), *ptrs, None)
+    assert st == ERR_WORKSPACE
+    assert b"scratch" in lib.sgqa_last_error()
+    ptrs[9] = None
+    P = _dprob()._c()
+    C = sg.Cache(64 * 4097, 64, 4097)._c()
+    assert lib.sgqa_decode_noalloc(ctypes.byref(P), ctypes.byref(C), *ptrs, None) == ERR_NULL
