@@ -141,6 +141,35 @@ def test_index_scores_every_row_bf16(case):
                 assert (bits[b, i, g, o:] == SENTINEL).all(), f"tail written at b={b} i={i} g={g}"
 
 
+@pytest.mark.parametrize("sharp", [False, True])
+def test_bf16_output_error_budget(sharp):
+    """The bf16 forward's rounding budget, element by element.  The attention rounds each
+    probability to bf16 for the P.V product (relative 2^-9 per weight, the same rounded values
+    entering the row sum), rounds each unit range's partial O/l to bf16 before the merge (relative
+    2^-9: the merged value is a convex combination of the partials, so this adds at most
+    2^-9 max|v| over the attended tokens), and rounds the gated result once more (2^-9 |out|).
+    Bound per element: sigmoid(gate) * 2 * 2^-9 * max|v| + 2^-9 |ref|, with max|v| taken over the
+    whole (sequence, group) as an upper bound of the attended tokens' maximum, doubled for fp32
+    accumulation and the exp2 approximation."""
+    t_q, t_kv = 400, 2600
+    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=2, heads=8, head_dim=128, index_dim=128,
+                          block=8, topk=512, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          needles=2, seed=23, device="cuda", sharp=sharp)
+    prob = sg.Problem.from_workload(w)
+    out, sel = run_forward(prob, x)
+    sel_ref, out_ref, _ = oracle.forward(x, w.block, w.topk, w.softmax_scale)
+    check_sel_rows(sel, sel_ref)
+    got = out.to("cpu", torch.float64).numpy()
+    gate = x["gate"].to("cpu", torch.float64).numpy()
+    vmax = x["v"].abs().amax(dim=(2, 3)).to("cpu", torch.float64).numpy()      # [Bt, G]
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    bound = 2.0 * (sig * 2.0 * 2.0 ** -9 * vmax[:, None, :, None, None] + 2.0 ** -9 * np.abs(out_ref))
+    err = np.abs(got - out_ref)
+    ratio = float((err / bound).max())
+    say(f"  error / budget: max {ratio:.3f}, max-abs err {float(err.max()):.3e}")
+    assert ratio <= 1.0
+
+
 def test_block_one_selection_is_token_level():
     """B = 1 (token-level, the pages' comparison setting) through index + top-k."""
     w, x = generate_small(t_q=700, t_kv=900, groups=2, heads=8, head_dim=128, index_dim=128,
