@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libsgqa.so")
 
 SOURCES = ["sgqa_api.cpp", "compress.hip", "index.hip", "topk.hip", "select_fused.hip", "attend.hip",
-           "attend_split.hip", "paged.hip"]
+           "attend_split.hip", "attend_bwd.hip", "paged.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -876,29 +876,22 @@ struct BwdArgs {
   const uint32_t* ulist;
   const int32_t* bounds;
   bf16_t* dq;
-  float* dk;               // [Bt, G, Tk, D], accumulated with atomics
-  float* dv;
   int64_t Tq, Tk, NU, pos0, ngroups, total;
   int G, umax;
   float scale_log2e, scale;
 };
 
-// One wave per group of 4 tokens over its whole union (all ranges), chunks of 4 units as in the
-// forward: S^T = K Q^T and dP^T = V dO^T on the same K-row permutation, P = exp2(S scale log2e -
-// lse2) under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in registers (the forward's
-// P V product with K in the transposed unit layout); dV = P^T dO and dK = scale dS^T Q through an
-// LDS transpose of P and dS, added to dv / dk with fp32 atomics.
+// dQ, query-major: one wave per group of 4 tokens over its whole union (all ranges), chunks of 4
+// units as in the forward: S^T = K Q^T and dP^T = V dO^T on the same K-row permutation,
+// P = exp2(S scale log2e - lse2) under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in
+// registers (the forward's P V product with K in the transposed unit layout).  dK and dV are
+// accumulated key-major in attend_bwd.hip.
 template <int D>
 __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
   constexpr int H = 8;
   constexpr int kRowB = D * 2 + 16;                      // LDS row of Q / dO (bytes)
-  constexpr int kTRow = 32 * 2 + 16;                     // LDS row of Q^T / dO^T / P^T / dS^T
   __shared__ __attribute__((aligned(16))) unsigned char s_q[32 * kRowB];
   __shared__ __attribute__((aligned(16))) unsigned char s_do[32 * kRowB];
-  __shared__ __attribute__((aligned(16))) unsigned char s_qt[D * kTRow];
-  __shared__ __attribute__((aligned(16))) unsigned char s_dot[D * kTRow];
-  __shared__ __attribute__((aligned(16))) unsigned char s_p[32 * kTRow];
-  __shared__ __attribute__((aligned(16))) unsigned char s_ds[32 * kTRow];
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, h = lane >> 5;
   const int trow = c >> 3, head = c & 7;
@@ -915,8 +908,7 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
   const int e0 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1)]);
   const int e1 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1) + kRanges]);
 
-  // Q and dO rows (row-major) and their transposes into LDS; lane (c, h) copies d in
-  // [D/2 h, D/2 (h+1)) of row c
+  // Q and dO rows into LDS; lane (c, h) copies d in [D/2 h, D/2 (h+1)) of row c
   const int64_t rr = ((b * a.Tq + (rowvalid ? tok0 + trow : tok0)) * a.G + g) * H + head;
   {
     const bf16_t* qrow = a.q + rr * D;
@@ -928,12 +920,6 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
       const uint4 vo = rowvalid ? *reinterpret_cast<const uint4*>(orow + d) : make_uint4(0u, 0u, 0u, 0u);
       *reinterpret_cast<uint4*>(s_q + c * kRowB + d * 2) = vq;
       *reinterpret_cast<uint4*>(s_do + c * kRowB + d * 2) = vo;
-      const uint32_t wq[4] = {vq.x, vq.y, vq.z, vq.w}, wo[4] = {vo.x, vo.y, vo.z, vo.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *reinterpret_cast<uint16_t*>(s_qt + (d + e) * kTRow + c * 2) = static_cast<uint16_t>(wq[e >> 1] >> (16 * (e & 1)));
-        *reinterpret_cast<uint16_t*>(s_dot + (d + e) * kTRow + c * 2) = static_cast<uint16_t>(wo[e >> 1] >> (16 * (e & 1)));
-      }
     }
   }
   const float lse_c = rowvalid ? a.lse2[rr] : 0.f;
@@ -944,8 +930,6 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
   const BufRsrc krs = make_rsrc(a.kq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc ktrs = make_rsrc(a.kv + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
-  float* dkg = a.dk + (b * a.G + g) * a.Tk * D;
-  float* dvg = a.dv + (b * a.G + g) * a.Tk * D;
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
@@ -995,12 +979,11 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
       dp = mfma32x32x16(R.v[kc], ld16(s_do + c * kRowB + (16 * kc + 8 * h) * 2), dp);
     }
     const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
-    float pv[16], dsv[16];
+    float dsv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool on = (msk >> i) & 1u;
       const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2e, -lse_c)) : 0.f;
-      pv[i] = p;
       dsv[i] = p * (dp[i] - D_c);
     }
     const bf16x8_t da = pack8_bf16(dsv), db = pack8_bf16(dsv + 8);
@@ -1009,47 +992,6 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
       accq[dt] = mfma32x32x16(R.kt[2 * dt], da, accq[dt]);
       accq[dt] = mfma32x32x16(R.kt[2 * dt + 1], db, accq[dt]);
     }
-    // P^T and dS^T tiles [token m = 8 slot + t][row], bf16
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i < 8 ? h : 2 + h) + (i & 7);
-      *reinterpret_cast<bf16_t*>(s_p + m * kTRow + c * 2) = f32_to_bf16(pv[i]);
-      *reinterpret_cast<bf16_t*>(s_ds + m * kTRow + c * 2) = f32_to_bf16(dsv[i]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // dV and dK tiles: C[m][d] = sum over rows; lane (c, h) holds m = 8 (r/4) + 4h + r%4, d = 32 dt + c
-    const bf16x8_t pa0 = ld16(s_p + c * kTRow + (8 * h) * 2), pa1 = ld16(s_p + c * kTRow + (16 + 8 * h) * 2);
-    const bf16x8_t sa0 = ld16(s_ds + c * kTRow + (8 * h) * 2), sa1 = ld16(s_ds + c * kTRow + (16 + 8 * h) * 2);
-    bool live[4];
-    int32_t tokb[4];
-#pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const uint32_t e = pick4(ent4, sl);
-      live[sl] = (e >> kChoseShift) != 0u;             // some token of the group chose the unit
-      tokb[sl] = static_cast<int32_t>(e & kUnitMask) * 8;
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      f32x16_t cv = {}, ck = {};
-      cv = mfma32x32x16(pa0, ld16(s_dot + (32 * dt + c) * kTRow + (8 * h) * 2), cv);
-      cv = mfma32x32x16(pa1, ld16(s_dot + (32 * dt + c) * kTRow + (16 + 8 * h) * 2), cv);
-      ck = mfma32x32x16(sa0, ld16(s_qt + (32 * dt + c) * kTRow + (8 * h) * 2), ck);
-      ck = mfma32x32x16(sa1, ld16(s_qt + (32 * dt + c) * kTRow + (16 + 8 * h) * 2), ck);
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        if (!live[sl]) continue;                        // wave-uniform
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * sl + j;
-          const int64_t tok = tokb[sl] + 4 * h + j;
-          if (tok < a.Tk) {
-            atomicAdd(dvg + tok * D + 32 * dt + c, cv[r]);
-            atomicAdd(dkg + tok * D + 32 * dt + c, ck[r] * a.scale);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
 
   if (e0 < e1) {
@@ -1077,12 +1019,6 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
         *reinterpret_cast<uint2*>(dqr + 32 * dt + 8 * i4 + 4 * h) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
       }
   }
-}
-
-__global__ void __launch_bounds__(256) fill_zero_kernel(float4* p, int64_t n4) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1303,7 +1239,7 @@ hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, co
 size_t attend_backward_bytes(const Dims& d) {
   const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * 8;
   return 2 * packed_kv_quad_bytes(d) + attend_split_bytes(d) + 2 * align256(rows * sizeof(float)) +
-         align256(rows * d.D * sizeof(bf16_t));
+         align256(rows * d.D * sizeof(bf16_t)) + backward_dkv_bytes(d);
 }
 
 hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
@@ -1321,6 +1257,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   float* lse2 = reinterpret_cast<float*>(split + attend_split_bytes(d));
   float* Dr = reinterpret_cast<float*>(reinterpret_cast<char*>(lse2) + align256(rows * sizeof(float)));
   bf16_t* d_o = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(Dr) + align256(rows * sizeof(float)));
+  char* dkv_ws = reinterpret_cast<char*>(d_o) + align256(rows * d.D * sizeof(bf16_t));
 
   hipError_t e = launch_pack_kv_quad(d, k, v, fwd_kv, s);
   if (e != hipSuccess) return e;
@@ -1405,17 +1342,8 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dk, dv accumulate from zero
-  {
-    const int64_t n4 = d.Bt * d.G * d.Tk * d.D / 4;
-    int64_t blocks = (n4 + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(dk), n4);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<float4*>(dv), n4);
-  }
-  e = hipGetLastError();
+  // dk, dv key-major: every element written once, no atomics
+  e = launch_backward_dkv(d, q, d_o, lse2, Dr, k, v, sel, dk, dv, dkv_ws, s);
   if (e != hipSuccess) return e;
   BwdArgs ba;
   ba.q = static_cast<const bf16_t*>(q);
@@ -1428,8 +1356,6 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ba.ulist = sb.ulist;
   ba.bounds = sb.bounds;
   ba.dq = static_cast<bf16_t*>(dq);
-  ba.dk = dk;
-  ba.dv = dv;
   ba.Tq = d.Tq;
   ba.Tk = d.Tk;
   ba.NU = d.NU;

@@ -148,6 +148,13 @@ hipError_t launch_pack_kv_quad(const Dims& d, const void* k, const void* v, void
 // Backward of the gated attention step for a fixed selection (range-split constraints): dq and
 // dgate in q's layout and dtype, dk / dv as fp32 [Bt, G, Tk, D] (zeroed, then accumulated).
 size_t attend_backward_bytes(const Dims& d);
+// Key-major dK and dV of the gated attention step (attend_bwd.hip): from the selection, dO =
+// dout * sigmoid(gate) and the per-row lse2 / Dr statistics; every element of dk and dv written
+// once.  Workspace: backward_dkv_bytes(d).
+size_t backward_dkv_bytes(const Dims& d);
+hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, const float* lse2,
+                               const float* Dr, const void* k, const void* v, const int32_t* sel,
+                               float* dk, float* dv, void* ws, hipStream_t s);
 hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
                                   const void* gate, const int32_t* sel, const void* dout, void* dq,
                                   float* dk, float* dv, void* dgate, void* ws, hipStream_t s);

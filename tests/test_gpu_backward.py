@@ -53,7 +53,11 @@ def test_backward_small_every_element(case):
     g = torch.Generator(device="cuda").manual_seed(7)
     dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
     dq, dk, dv, dgate = sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout)
+    again = sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout)
     torch.cuda.synchronize()
+    # no atomics anywhere: every gradient is the same bits on every run
+    for name, a1, a2 in zip(("dq", "dk", "dv", "dgate"), (dq, dk, dv, dgate), again):
+        assert torch.equal(a1, a2), f"{name} differs between two runs"
     r_dq, r_dk, r_dv, r_dg = oracle.attention_backward(xc, sel_ref, dout.cpu(), B, w.softmax_scale)
     check("dq", dq, r_dq)
     check("dk", dk, r_dk)
