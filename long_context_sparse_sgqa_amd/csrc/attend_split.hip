@@ -875,38 +875,56 @@ struct BwdArgs {
   const bf16_t* kv;        // K, transposed unit layout [unit][d][8 tokens]
   const uint32_t* ulist;
   const int32_t* bounds;
-  bf16_t* dq;
-  int64_t Tq, Tk, NU, pos0, ngroups, total;
+  float* dq_part;          // [gq][R][(D/32) * 4 pieces][64 lanes][4], this range's sum
+  int64_t Tq, Tk, NU, pos0, ngroups, wg_groups, total;
   int G, umax;
+  int wave_ranges;         // fewer groups of tokens than waves per workgroup: waves = ranges
   float scale_log2e, scale;
 };
 
-// dQ, query-major: one wave per group of 4 tokens over its whole union (all ranges), chunks of 4
-// units as in the forward: S^T = K Q^T and dP^T = V dO^T on the same K-row permutation,
-// P = exp2(S scale log2e - lse2) under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in
-// registers (the forward's P V product with K in the transposed unit layout).  dK and dV are
-// accumulated key-major in attend_bwd.hip.
+// dQ, query-major, split into the forward's unit ranges: one wave per (group of 4 tokens, range),
+// numbered as the forward's range kernel (range fastest, so range r runs on XCDs r and r + 4 and
+// each XCD's L2 holds a quarter of a group's K and V), chunks of 4 units as in the forward:
+// S^T = K Q^T and dP^T = V dO^T on the same K-row permutation, P = exp2(S scale log2e - lse2)
+// under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in registers (the forward's P V
+// product with K in the transposed unit layout).  The range's fp32 sum is stored in the
+// accumulator's lane order (coalesced 1 KB pieces); dq_merge_kernel adds the ranges.  dK and dV
+// are accumulated key-major in attend_bwd.hip.
 template <int D>
-__global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
   constexpr int H = 8;
   constexpr int kRowB = D * 2 + 16;                      // LDS row of Q / dO (bytes)
-  __shared__ __attribute__((aligned(16))) unsigned char s_q[32 * kRowB];
-  __shared__ __attribute__((aligned(16))) unsigned char s_do[32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_qa[kRangeWaves][32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_doa[kRangeWaves][32 * kRowB];
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, h = lane >> 5;
   const int trow = c >> 3, head = c & 7;
-  const int64_t gq = blockIdx.x;
-  if (gq >= a.total) return;
-  const int64_t qi = gq % a.ngroups;
-  const int64_t bg = gq / a.ngroups;
+  int r;
+  int64_t bg, qi;
+  if (a.wave_ranges) {
+    r = wave;
+    bg = blockIdx.x / a.ngroups;
+    qi = blockIdx.x - bg * a.ngroups;
+  } else {
+    r = static_cast<int>(blockIdx.x % kRanges);
+    const int64_t rest = blockIdx.x / kRanges;
+    const int64_t wgq = rest % a.wg_groups;
+    bg = rest / a.wg_groups;
+    qi = wgq * kRangeWaves + wave;
+    if (qi >= a.ngroups) return;                         // whole wave; no workgroup barriers follow
+  }
+  unsigned char* s_q = s_qa[wave];
+  unsigned char* s_do = s_doa[wave];
+  const int64_t gq = bg * a.ngroups + qi;
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
   const int64_t tok0 = kTok * qi;
   const bool rowvalid = tok0 + trow < a.Tq;
   const int64_t pX = a.pos0 + tok0 + trow;
   const uint32_t* list = a.ulist + gq * list_stride(a.umax);
-  const int e0 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1)]);
-  const int e1 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1) + kRanges]);
+  const int e0 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1) + r]);
+  const int e1 = __builtin_amdgcn_readfirstlane(a.bounds[gq * (kRanges + 1) + r + 1]);
 
   // Q and dO rows into LDS; lane (c, h) copies d in [D/2 h, D/2 (h+1)) of row c
   const int64_t rr = ((b * a.Tq + (rowvalid ? tok0 + trow : tok0)) * a.G + g) * H + head;
@@ -1007,17 +1025,54 @@ __global__ void __launch_bounds__(64) attend_bwd_kernel(BwdArgs a) {
     }
   }
 
-  // dq = scale * acc: lane (c, h) holds d = 32 dt + 8 (i/4) + 4h + i%4 of row c
-  if (rowvalid) {
-    bf16_t* dqr = a.dq + rr * D;
+  // this range's dQ^T sum, in the accumulator's lane order: piece (dt, i4) of lane l holds
+  // d = 32 dt + 8 i4 + 4 h .. + 4 of row c (0 for a range with no entries)
+  float* part = a.dq_part + (gq * kRanges + r) * (32 * D);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float x0 = accq[dt][4 * i4] * a.scale, x1 = accq[dt][4 * i4 + 1] * a.scale;
-        const float x2 = accq[dt][4 * i4 + 2] * a.scale, x3 = accq[dt][4 * i4 + 3] * a.scale;
-        *reinterpret_cast<uint2*>(dqr + 32 * dt + 8 * i4 + 4 * h) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-      }
+    for (int i4 = 0; i4 < 4; ++i4)
+      *reinterpret_cast<float4*>(part + ((dt * 4 + i4) * 64 + lane) * 4) =
+          make_float4(accq[dt][4 * i4], accq[dt][4 * i4 + 1], accq[dt][4 * i4 + 2], accq[dt][4 * i4 + 3]);
+}
+
+// dq = scale * (sum of the ranges' partials), rounded to bf16: one thread per (group of tokens,
+// piece, lane) of the partials' layout.
+struct DqMergeArgs {
+  const float* dq_part;
+  bf16_t* dq;
+  int64_t Tq, ngroups, total;
+  int G, D;
+  float scale;
+};
+
+__global__ void __launch_bounds__(256) dq_merge_kernel(DqMergeArgs a) {
+  const int pieces = (a.D / 32) * 4;
+  const int64_t n = a.total * pieces * 64;
+  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < n;
+       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int lane = static_cast<int>(id & 63);
+    const int piece = static_cast<int>((id >> 6) % pieces);
+    const int64_t gq = (id >> 6) / pieces;
+    const int c = lane & 31, h = lane >> 5;
+    const int64_t qi = gq % a.ngroups, bg = gq / a.ngroups;
+    const int64_t tok = kTok * qi + (c >> 3);
+    if (tok >= a.Tq) continue;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int r = 0; r < kRanges; ++r) {
+      const float4 v = *reinterpret_cast<const float4*>(a.dq_part + (gq * kRanges + r) * (32 * a.D) +
+                                                        (piece * 64 + lane) * 4);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const int dt = piece >> 2, i4 = piece & 3;
+    const int64_t g = bg % a.G, b = bg / a.G;
+    const int64_t row = ((b * a.Tq + tok) * a.G + g) * 8 + (c & 7);
+    *reinterpret_cast<uint2*>(a.dq + row * a.D + 32 * dt + 8 * i4 + 4 * h) =
+        make_uint2(pack_bf16x2(s.x * a.scale, s.y * a.scale), pack_bf16x2(s.z * a.scale, s.w * a.scale));
   }
 }
 
@@ -1236,10 +1291,16 @@ hipError_t launch_attend_window(const Dims& d, int64_t window, const void* q, co
                                  nullptr, nullptr, nullptr);
 }
 
+// fp32 dq partials of the unit ranges: [groups of 4 tokens][R][32 rows x D]
+size_t dq_part_bytes(const Dims& d) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  return align256(static_cast<size_t>(d.Bt * d.G * ng) * kRanges * 32 * d.D * sizeof(float));
+}
+
 size_t attend_backward_bytes(const Dims& d) {
   const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * 8;
   return 2 * packed_kv_quad_bytes(d) + attend_split_bytes(d) + 2 * align256(rows * sizeof(float)) +
-         align256(rows * d.D * sizeof(bf16_t)) + backward_dkv_bytes(d);
+         align256(rows * d.D * sizeof(bf16_t)) + backward_dkv_bytes(d) + dq_part_bytes(d);
 }
 
 hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
@@ -1258,6 +1319,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   float* Dr = reinterpret_cast<float*>(reinterpret_cast<char*>(lse2) + align256(rows * sizeof(float)));
   bf16_t* d_o = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(Dr) + align256(rows * sizeof(float)));
   char* dkv_ws = reinterpret_cast<char*>(d_o) + align256(rows * d.D * sizeof(bf16_t));
+  float* dq_part = reinterpret_cast<float*>(dkv_ws + backward_dkv_bytes(d));
 
   hipError_t e = launch_pack_kv_quad(d, k, v, fwd_kv, s);
   if (e != hipSuccess) return e;
@@ -1355,21 +1417,41 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ba.kv = reinterpret_cast<const bf16_t*>(bwd_kv + pkv / 2);
   ba.ulist = sb.ulist;
   ba.bounds = sb.bounds;
-  ba.dq = static_cast<bf16_t*>(dq);
+  ba.dq_part = dq_part;
   ba.Tq = d.Tq;
   ba.Tk = d.Tk;
   ba.NU = d.NU;
   ba.pos0 = d.pos0;
   ba.ngroups = ng;
+  ba.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
+  ba.wave_ranges = ng < kRangeWaves ? 1 : 0;
   ba.total = total;
   ba.G = d.G;
   ba.umax = umax;
   ba.scale_log2e = d.scale * 1.4426950408889634f;
   ba.scale = d.scale;
+  const dim3 bgrid(static_cast<unsigned>(ba.wave_ranges ? d.Bt * d.G * ng : d.Bt * d.G * ba.wg_groups * kRanges));
   if (d.D == 128)
-    hipLaunchKernelGGL(attend_bwd_kernel<128>, dim3(static_cast<unsigned>(total)), dim3(64), 0, s, ba);
+    hipLaunchKernelGGL(attend_bwd_kernel<128>, bgrid, dim3(256), 0, s, ba);
   else
-    hipLaunchKernelGGL(attend_bwd_kernel<64>, dim3(static_cast<unsigned>(total)), dim3(64), 0, s, ba);
+    hipLaunchKernelGGL(attend_bwd_kernel<64>, bgrid, dim3(256), 0, s, ba);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DqMergeArgs dm;
+  dm.dq_part = dq_part;
+  dm.dq = static_cast<bf16_t*>(dq);
+  dm.Tq = d.Tq;
+  dm.ngroups = ng;
+  dm.total = total;
+  dm.G = d.G;
+  dm.D = d.D;
+  dm.scale = d.scale;
+  {
+    const int64_t n = total * (d.D / 32) * 4 * 64;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(dq_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dm);
+  }
   return hipGetLastError();
 }
 
