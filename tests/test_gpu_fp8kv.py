@@ -51,10 +51,11 @@ def test_fp8kv_small_every_row(case):
     check_out(out, out_ref, fp32=False, what="fp8 kv")
 
 
-def test_fp8kv_128k_sampled_rows():
+@pytest.mark.parametrize("sharp", [False, True], ids=["plain", "sharp"])
+def test_fp8kv_128k_sampled_rows(sharp):
     w = get_workload("128k")
-    say("case: fp8 kv 128k")
-    x = generate(w, device="cuda", seed=0)
+    say("case: fp8 kv 128k", "sharp" if sharp else "")
+    x = generate(w, device="cuda", seed=0, sharp=sharp)
     prob = sg.Problem.from_workload(w)
     k8, ks = quantize_e4m3(x["k"])
     v8, vs = quantize_e4m3(x["v"])

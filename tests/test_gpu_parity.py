@@ -282,9 +282,9 @@ def test_run_to_run_bitwise():
 # full-size workloads: sampled rows against the oracle, structural checks on every row
 # ----------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("name,n_random,sharp", [("32k", 24, False), ("128k", 12, False),
-                                                ("1m", 6, False), ("128k", 12, True),
-                                                ("1m", 6, True)],
-                         ids=["32k", "128k", "1m", "128k-sharp", "1m-sharp"])
+                                                ("1m", 6, False), ("32k", 24, True),
+                                                ("128k", 12, True), ("1m", 6, True)],
+                         ids=["32k", "128k", "1m", "32k-sharp", "128k-sharp", "1m-sharp"])
 def test_workload_sampled_rows(name, n_random, sharp):
     """Full-size workloads on stratified sampled rows.  The "sharp" variants leave q and k unscaled,
     so the softmax is far from uniform and a wrong weight or a dropped token shows in the output."""
@@ -348,10 +348,11 @@ def test_long_context_union_every_row(t_q):
     torch.cuda.empty_cache()
 
 
-def test_decode_sampled_sequences():
+@pytest.mark.parametrize("sharp", [False, True], ids=["plain", "sharp"])
+def test_decode_sampled_sequences(sharp):
     w = get_workload("decode")
-    say("case: decode")
-    x = generate(w, device="cuda", seed=0)
+    say("case: decode", "sharp" if sharp else "")
+    x = generate(w, device="cuda", seed=0, sharp=sharp)
     prob = sg.Problem.from_workload(w)
     out, sel = run_forward(prob, x)
     structural_check_sel(sel, prob)
