@@ -138,8 +138,9 @@ sgqa_status sgqa_topk(const sgqa_problem* prob, const float* scores, int32_t* se
  *             out = sigmoid(gate) * sum_t softmax_t(scale * q . k_t) v_t over the tokens t <= p
  *             of the selected blocks.  fp32 accumulation; bf16 outputs are rounded to nearest even.
  *   workspace: >= sizes.attend_workspace_bytes of device memory (a block-packed copy of v).
- *   The attention kernels need B to divide 8 or be a multiple of 8; other block sizes return
- *   SGQA_ERR_UNSUPPORTED (steps 1-3 accept any B).
+ *   Any B >= 1: blocks that are a multiple of 8 or divide 8 run on the matrix-core kernels;
+ *   other block sizes run on the plain kernel (one workgroup per (query, group), every selected
+ *   token in turn; much slower, same result up to rounding).
  */
 sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, const void* v,
                         const void* gate, const int32_t* sel, void* out, void* workspace,
@@ -293,9 +294,10 @@ sgqa_status sgqa_decode_noalloc(const sgqa_problem* prob, const sgqa_cache* cach
  *   dS_t = P_t (dO.v_t - dO.O);  dq = scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dO
  *   dq, dgate : [Bt, Tq, G, H, D] dtype (rounded to nearest even)
  *   dk, dv    : [Bt, G, Tk, D] float32, overwritten (contributions of every query head summed)
- * The forward softmax statistics are recomputed.  dk / dv are accumulated with fp32 atomics, so
- * their low bits vary from run to run.  Supported: bf16, H == 8, D in {64, 128}, B a multiple of 8,
- * topk_tokens / block within the grouped kernel (as for the range-split forward).
+ * The forward softmax statistics are recomputed.  dk / dv are accumulated key-major (every
+ * element written once) and dq from fixed-order sums, so every gradient is the same bits on every
+ * run.  Supported: bf16, H == 8, D in {64, 128}, B a multiple of 8, topk_tokens / block within the
+ * grouped kernel (as for the range-split forward).
  * --------------------------------------------------------------------------------------------- */
 sgqa_status sgqa_attend_backward_workspace_size(const sgqa_problem* prob, size_t* bytes);
 sgqa_status sgqa_attend_backward(const sgqa_problem* prob, const void* q, const void* k,

@@ -123,8 +123,6 @@ sgqa_status derive(const sgqa_problem* p, Derived* out) {
   return SGQA_OK;
 }
 
-bool attend_block_ok(const sgqa::Dims& d) { return (d.B % 8 == 0) || (8 % d.B == 0); }
-
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -421,9 +419,6 @@ sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, 
                         size_t workspace_bytes, void* stream) {
   Derived dv;
   SGQA_CHECK(derive(prob, &dv));
-  if (!attend_block_ok(dv.d))
-    return fail(SGQA_ERR_UNSUPPORTED, "attention needs block dividing 8 or a multiple of 8 (got %d)",
-                dv.d.B);
   SGQA_CHECK(check_ptr(q, "q"));
   SGQA_CHECK(check_ptr(k, "k"));
   SGQA_CHECK(check_ptr(v, "v"));
@@ -449,9 +444,6 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
   Derived dv;
   SGQA_CHECK(derive(prob, &dv));
   const sgqa::Dims& d = dv.d;
-  if (!attend_block_ok(d))
-    return fail(SGQA_ERR_UNSUPPORTED, "attention needs block dividing 8 or a multiple of 8 (got %d)",
-                d.B);
   SGQA_CHECK(check_ptr(q, "q"));
   SGQA_CHECK(check_ptr(k, "k"));
   SGQA_CHECK(check_ptr(v, "v"));

@@ -98,8 +98,8 @@ def test_null_misaligned_and_workspace_errors(lib):
     assert _call_forward(lib, prob, ptrs, 16) == ERR_WORKSPACE
     msg = lib.sgqa_last_error().decode()
     assert "workspace" in msg
-    P = sg.Problem(1, 64, 64, 2, 8, 128, 128, 3, 24)._c()   # B=3: selection fine, attention not
-    assert lib.sgqa_attend(ctypes.byref(P), *([good] * 7), 1 << 20, None) == ERR_UNSUPPORTED
+    P = sg.Problem(1, 64, 64, 2, 8, 128, 128, 3, 24)._c()   # B=3: any block size is accepted
+    assert lib.sgqa_attend(ctypes.byref(P), None, *([good] * 6), 1 << 20, None) == ERR_NULL
     assert lib.sgqa_topk(None, good, good, None) == ERR_NULL
 
 

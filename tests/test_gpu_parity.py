@@ -170,6 +170,37 @@ def test_bf16_output_error_budget(sharp):
     assert ratio <= 1.0
 
 
+# block sizes that neither divide 8 nor are multiples of 8 (the plain attention kernel), and
+# one multiple of 8 above 16 (the range kernel), through both the split calls and the forward
+OTHER_BLOCK_CASES = [
+    # t_q, t_kv, block, topk, dtype
+    (200, 700, 3, 96, "bf16"),
+    (150, 601, 5, 100, "bf16"),
+    (120, 900, 12, 144, "bf16"),
+    (130, 1000, 24, 240, "bf16"),
+    (90, 400, 3, 48, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", OTHER_BLOCK_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-%s" % c)
+def test_other_block_sizes_every_row(case):
+    t_q, t_kv, B, k, dt = case
+    say("case: block size", case)
+    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=2, heads=8, head_dim=64, index_dim=32,
+                          block=B, topk=k, dtype=dt, index_dtype=dt, scaled_qkv=dt == "bf16",
+                          needles=1, seed=29, device="cuda", sharp=True)
+    prob = sg.Problem.from_workload(w)
+    k_blk, scores, sel, out = run_split(prob, x)
+    sel_ref, out_ref, kblk_ref = oracle.forward(x, B, k, w.softmax_scale)
+    np.testing.assert_array_equal(k_blk.cpu().double().numpy(), kblk_ref)
+    check_sel_rows(sel, sel_ref)
+    structural_check_sel(sel, prob)
+    check_out(out, out_ref, fp32=dt == "f32", what=f"split B={B}")
+    out2, sel2 = run_forward(prob, x)
+    assert torch.equal(sel2, sel)
+    check_out(out2, out_ref, fp32=dt == "f32", what=f"forward B={B}")
+
+
 def test_block_one_selection_is_token_level():
     """B = 1 (token-level, the pages' comparison setting) through index + top-k."""
     w, x = generate_small(t_q=700, t_kv=900, groups=2, heads=8, head_dim=128, index_dim=128,
