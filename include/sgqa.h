@@ -25,7 +25,8 @@
  *     asynchronously on it; results are valid once the stream has been synchronised.
  *   - The caller owns every buffer, workspaces included; the library allocates no device memory,
  *     keeps no state between calls (apart from the optional stage markers armed by
- *     sgqa_set_stage_events) and never synchronises.  Inputs are read-only; outputs must not
+ *     sgqa_set_stage_events, and the fixed per-GPU scratch of sgqa_decode_noalloc, part of the
+ *     library's code object) and never synchronises.  Inputs are read-only; outputs must not
  *     alias inputs.  Concurrent calls need distinct outputs and workspaces.
  *   - Arguments are validated on the host before anything is enqueued.  On any error the call
  *     returns a non-zero sgqa_status, enqueues nothing and touches no output; sgqa_last_error()
@@ -109,7 +110,10 @@ const char* sgqa_last_error(void);
 sgqa_status sgqa_sizes(const sgqa_problem* prob, sgqa_sizes_t* out);
 
 /*
- * Steps 1-2: block compression and the indexer.
+ * Steps 1-2: block compression and the indexer.  The pages compress the shared index keys block by
+ * block and score them with an indexer per KV group (mo.ai.kr summary, section "모델 구조와 학습
+ * 안정성"; ai.info article, section "Sparse GQA punta a un contesto di 1 milione di token": blocks of
+ * eight tokens, which cut indexer and top-k cost eightfold).
  *   k_idx  : [Bt, Tk, Di] or NULL.  If non-NULL, k_blk is first written as the block sums of k_idx
  *            (fp32 accumulation, rounded to index_dtype).  If NULL, k_blk is an INPUT holding block
  *            keys computed earlier (a decode cache).
@@ -123,7 +127,9 @@ sgqa_status sgqa_index(const sgqa_problem* prob, const void* q_idx, const void* 
                        void* k_blk, float* scores, void* stream);
 
 /*
- * Step 3: per-(query, KV group) block selection from stored scores.
+ * Step 3: per-(query, KV group) block selection from stored scores.  Each KV group keeps its own
+ * top blocks; k = 4096 tokens is 512 blocks of 8 (mo.ai.kr summary and ai.info article, sections as
+ * above).
  *   scores : [Bt, Tq, G, NB] float32 as written by sgqa_index (only j < p/B is read).
  *   sel    : [Bt, Tq, G, NS] int32.  With o = p / B: if o + 1 <= NS, sel = 0..o then -1s;
  *            otherwise sel = {o} plus the NS-1 candidates j < o with the largest scores, equal
@@ -132,7 +138,9 @@ sgqa_status sgqa_index(const sgqa_problem* prob, const void* q_idx, const void* 
 sgqa_status sgqa_topk(const sgqa_problem* prob, const float* scores, int32_t* sel, void* stream);
 
 /*
- * Step 4: gated grouped-query attention over the selected tokens.
+ * Step 4: gated grouped-query attention over the selected tokens.  The full-attention layers are
+ * Sparse GQA built on Gated GQA, each KV group attending to its own selected blocks (mo.ai.kr
+ * summary, section "모델 구조와 학습 안정성").
  *   q, gate : [Bt, Tq, G, H, D];  k, v : [Bt, G, Tk, D];  sel : [Bt, Tq, G, NS] (as sgqa_topk).
  *   out     : [Bt, Tq, G, H, D]; for head j of group g, query i at p = Tk - Tq + i:
  *             out = sigmoid(gate) * sum_t softmax_t(scale * q . k_t) v_t over the tokens t <= p
@@ -147,7 +155,8 @@ sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, 
                         size_t workspace_bytes, void* stream);
 
 /*
- * Steps 1-4 in one call.
+ * Steps 1-4 in one call (the pages' Sparse GQA layer: mo.ai.kr summary, section "모델 구조와
+ * 학습 안정성").
  *   k_idx   : as in sgqa_index (NULL = k_blk already holds the block keys).
  *   k_blk   : [Bt, NB, Di] (written when k_idx != NULL).
  *   sel_out : [Bt, Tq, G, NS] or NULL (the selection is then not returned).
