@@ -13,11 +13,14 @@
 //      (kept as the top 16 bits of the order-preserving key: any threshold is correct, it only
 //      sizes the candidate list);
 //   2. filter: every causal score, column tiles of K_blk staged in LDS (double-buffered) and
-//      shared by the 4 waves; a passing score takes the next slot of its row from a per-row LDS
-//      counter, so a row's list is unordered.
+//      shared by the 4 waves; the products are taken transposed, so a lane holds one row and four
+//      consecutive blocks of it, and a passing score's slot is the row's count so far plus the
+//      passing scores before it in block order (a cross-lane prefix over the row's 4 lanes): every
+//      row's list is in ascending block order.
 // select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
-//   candidates held in registers, then an emit in block order (two LDS bitmaps) of keys > tau and
-//   the lowest-indexed keys == tau, built in LDS and written out coalesced.  Exact whenever at
+//   candidates held in registers, then the keys > tau and the lowest-indexed keys == tau, emitted
+//   in block order by a stable compaction of the sorted list (lists appended by several
+//   workgroups, as in decode, go through two LDS block bitmaps instead).  Exact whenever at
 //   least NS-1 candidates passed (every member of the top set is >= tau >= threshold); rows with
 //   too few or too many (> capacity) candidates are queued for the exact fallback in topk.hip,
 //   which recomputes the full score row.
@@ -78,8 +81,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   constexpr int kLds = (kSampBytes > 2 * kTileBytes) ? kSampBytes : 2 * kTileBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   __shared__ uint32_t s_thr[kRows];
-  __shared__ uint64_t s_cnt2[kRows / 2];                  // candidates appended per row, two per word
-  int* s_cnt = reinterpret_cast<int*>(s_cnt2);
 
   if (blockIdx.x == 0 && threadIdx.x == 0) *a.fail_count = 0;
 
@@ -115,14 +116,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
     for (int kc = 0; kc < DI / 32; ++kc) qa[kc] = a_valid ? load_bf16x8(qrow + kc * 32 + lg * 8) : zero_bf16x8();
   }
-  int64_t c_rr[4], c_o[4];
+  int64_t c_o[4];
   bool c_valid[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int local = wave * 16 + lg * 4 + e;
     c_valid[e] = local < rows_here;
-    c_o[e] = c_valid[e] ? row_o(local, &c_rr[e]) : 0;
-    if (!c_valid[e]) c_rr[e] = 0;
+    c_o[e] = c_valid[e] ? row_o(local, nullptr) : 0;
   }
 
   const int64_t ntiles = (o_max + kCols - 1) / kCols;
@@ -130,14 +130,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   // is fetched into registers before the current one is multiplied and written to LDS after it
   constexpr int kPer = kCols * (DI / 8) / 256;
   uint4 pre[kPer];
+  // K_blk of this sequence through a buffer descriptor: columns past NB read as zero
+  const BufRsrc krs = make_rsrc(kb, a.NB * DI * 2);
   auto load_tile = [&](int64_t t) {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int pc = threadIdx.x + k * 256;
       const int row = pc / (DI / 8), part = pc - row * (DI / 8);
-      const int64_t col = t * kCols + row;
-      const uint4 v = *reinterpret_cast<const uint4*>(kb + (col < a.NB ? col : a.NB - 1) * DI + part * 8);
-      pre[k] = col < a.NB ? v : make_uint4(0u, 0u, 0u, 0u);
+      const int col = static_cast<int>(t) * kCols + row;
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(krs, col * (DI * 2) + part * 16, 0, 0);
+      pre[k] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   auto store_tile = [&](int buf) {
@@ -339,67 +341,69 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     if (threadIdx.x < kRows) s_thr[threadIdx.x] = 0u;
   }
   __syncthreads();
-  // per C row e of this lane: float threshold (NaN for rows past the tile: never passes), causal
-  // limit o as 32 bits, and the row's candidate list
-  float c_thr[4];
-  int32_t c_o32[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    c_thr[e] = c_valid[e] ? key_threshold_to_float(s_thr[wave * 16 + lg * 4 + e]) : __builtin_nanf("");
-    c_o32[e] = static_cast<int32_t>(c_o[e]);
-  }
+  // Phase 2 takes the products transposed (K_blk tile as the A operand, q_idx as B), so a lane
+  // holds one row, the row of its A operand above, and four consecutive blocks of it per column step.
+  // Per lane: float threshold (NaN for rows past the tile: never passes), causal limit o as 32 bits.
+  const float r_thr = a_valid ? key_threshold_to_float(s_thr[my_local_a]) : __builtin_nanf("");
+  int64_t my_rr = 0;
+  const int32_t r_o32 = a_valid ? static_cast<int32_t>(row_o(my_local_a, &my_rr)) : 0;
 
   // ---------------- phase 2: every causal score, filtered, appended ----------------
-  // A candidate is (float bits of the score << 32 | block).  Appends take their slot from a per-row
-  // LDS counter, so a row's list is in no particular order (the select kernel orders its output).
-  if (threadIdx.x < kRows) s_cnt[threadIdx.x] = 0;
+  // A candidate is (float bits of the score << 32 | block).  A row's 4 lanes (lg = 0 .. 3, 16 lanes
+  // apart) hold 16 consecutive blocks of it per step, 4 each in lg order; a passing score's slot is
+  // the row's count so far plus the passing scores before it in block order, so every row's list
+  // comes out in ascending block order.  The lanes' exclusive prefix comes from the two cross-row
+  // swaps (16 lanes: the pair's even and odd row; 32 lanes: the lower and upper half), no LDS.
   // tiles below every row's causal limit need no per-column check
   const int64_t o_min = row_o(0, nullptr);
   const int64_t full_tiles = o_min / kCols;
   if (ntiles > 0) store_tile(0);
+  // vmcnt(0): nothing loaded before this point (q_idx rows among it) stays outstanding into the tile
+  // loops, so their only memory waits are for the next tile's loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  int* row_cnt = &s_cnt[wave * 16 + lg * 4];
   // Candidate stores go through a buffer descriptor over this workgroup's rows and are issued for
   // every lane: lanes without a candidate use an out-of-range offset, which the hardware drops.
   // With no branches around them, the number of stores per tile is fixed and the wait for the next
   // tile's loads need not wait for them.
   const BufRsrc crs = make_rsrc(a.cand + (seq * a.seq_rows + row0) * a.cap,
                                 static_cast<int64_t>(kRows) * a.cap * 8);
-  int c_off[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) c_off[e] = (wave * 16 + lg * 4 + e) * a.cap * 8;
-  // The counters of rows e = 0, 1 and of rows 2, 3 share a 64-bit word (low half: the even row), so
-  // one 64-bit LDS atomic takes both rows' slots; a half cannot carry into the other below 2^32.
-  unsigned long long* row_cnt2 = reinterpret_cast<unsigned long long*>(row_cnt);
-  auto append = [&](const f32x4_t& c, int32_t col, bool check_causal) {
+  const int r_off = my_local_a * a.cap * 8;
+  int r_count = 0;                       // the row's passing scores so far (same in its 4 lanes)
+  // A lane whose slots would run past the capacity stores none of them: its row then counts more
+  // than `cap` candidates and is recomputed exactly.
+  auto append = [&](const f32x4_t& c, int32_t cb, bool check_causal) {
     bool pass[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pass[e] = c[e] >= c_thr[e];
-      if (check_causal) pass[e] = pass[e] && col < c_o32[e];
+      pass[e] = c[e] >= r_thr;
+      if (check_causal) pass[e] = pass[e] && cb + e < r_o32;
     }
-    int pos[4];
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const bool p0 = pass[2 * hlf], p1 = pass[2 * hlf + 1];
-      const unsigned long long add = (p0 ? 1ull : 0ull) | (p1 ? (1ull << 32) : 0ull);
-      const unsigned long long old = (p0 || p1) ? atomicAdd(&row_cnt2[hlf], add) : 0ull;
-      pos[2 * hlf] = p0 ? static_cast<int>(old & 0xffffffffull) : a.cap;
-      pos[2 * hlf + 1] = p1 ? static_cast<int>(old >> 32) : a.cap;
-    }
+    const int n = static_cast<int>(pass[0]) + static_cast<int>(pass[1]) + static_cast<int>(pass[2]) +
+                  static_cast<int>(pass[3]);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(n, n, false, false);   // n of rows lg&~1, lg|1
+    const int pair = static_cast<int>(p16[0] + p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);  // pairs 0 and 1
+    int pos = r_count + ((lg & 1) ? static_cast<int>(p16[0]) : 0) + ((lg & 2) ? static_cast<int>(p32[0]) : 0);
+    r_count += static_cast<int>(p32[0] + p32[1]);
+    const bool fits = pos + n <= a.cap;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const u32x2_t v = {static_cast<uint32_t>(col), __float_as_uint(c[e])};
-      __builtin_amdgcn_raw_buffer_store_b64(v, crs, pos[e] < a.cap ? c_off[e] + pos[e] * 8 : 0x7fffffff,
-                                            0, 0);
+      const u32x2_t v = {static_cast<uint32_t>(cb + e), __float_as_uint(c[e])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, crs, pass[e] && fits ? r_off + pos * 8 : 0x7fffffff, 0, 0);
+      pos += static_cast<int>(pass[e]);
     }
   };
   // Per tile: all products first (LDS reads and MFMAs only), then the next tile's global loads,
   // then the appends (compares, LDS counters, candidate stores), then the staging of the next tile.
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // The loads are issued for every tile (past the last one they read zeros or unused blocks) and
+  // the tiles below every row's causal limit run in a loop of their own, so each loop body is
+  // straight-line code with a fixed number of stores after the loads: the staging waits for the
+  // loads only, not for the candidate stores behind them.
+  auto tile = [&](int64_t t, bool check_causal) {
     const int buf = static_cast<int>(t & 1);
     const unsigned char* src = lds + buf * kTileBytes;
-    const int32_t col0 = static_cast<int32_t>(t * kCols) + lr;
+    const int32_t col0 = static_cast<int32_t>(t * kCols) + 4 * lg;
     // B operands of step n+1 are read from LDS before the products of step n are issued
     f32x4_t sc[kCols / 16];
     uint4 opb[2][DI / 32];
@@ -415,25 +419,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
       __builtin_amdgcn_sched_barrier(0);               // keep the reads ahead of the products
       f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kc = 0; kc < DI / 32; ++kc) c = mfma16x16x32(qa[kc], bf16x8_from_u4(opb[n & 1][kc]), c);
+      for (int kc = 0; kc < DI / 32; ++kc) c = mfma16x16x32(bf16x8_from_u4(opb[n & 1][kc]), qa[kc], c);
       sc[n] = c;
     }
-    if (t + 1 < ntiles) load_tile(t + 1);
-    if (t >= full_tiles) {
+    load_tile(t + 1);
 #pragma unroll
-      for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, true);
-    } else {
-#pragma unroll
-      for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, false);
-    }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier below in t-1
+    for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, check_causal);
+    store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier that ended tile t - 1
     __syncthreads();
-  }
-  if (lr == 0) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (c_valid[e]) a.cnt[c_rr[e]] = row_cnt[e];
-  }
+  };
+  const int64_t t_full = full_tiles < ntiles ? full_tiles : ntiles;
+  int64_t t = 0;
+#pragma unroll 1
+  for (; t < t_full; ++t) tile(t, false);
+#pragma unroll 1
+  for (; t < ntiles; ++t) tile(t, true);
+  if (lg == 0 && a_valid) a.cnt[my_rr] = r_count;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -473,6 +474,10 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t* key, uint32_t ta
 // Each wave owns one row and two LDS bitmaps over the row's candidate blocks: blocks whose key is
 // above tau, and blocks whose key equals tau.  Scanning them in block order emits the selection
 // ascending, with the lowest-indexed ties taken first.
+// kSorted: every list is in ascending block order (the prefill filter), so the selected blocks are
+// emitted by a stable compaction of the list; otherwise (decode: lists appended by several
+// workgroups) through block bitmaps in LDS.
+template <bool kSorted>
 __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   extern __shared__ uint32_t bm_all[];
   const int lane = threadIdx.x & 63;
@@ -548,6 +553,36 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
                        : ne <= 24 ? kth_largest<24>(key, tau0, top, low, need)
                                   : kth_largest<kSelPer>(key, tau0, top, low, need);
 
+  if constexpr (kSorted) {
+    // Slots x = 64 e + lane are in block order: keys above tau are taken, and of the keys equal to
+    // tau the first take_eq in block order; each taking lane writes at the count of takers before
+    // it, so consecutive lanes write consecutive entries.
+    const int m_u = __builtin_amdgcn_readfirstlane(m);   // the same in every lane
+    int n_gt = 0;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e)
+      if (e * 64 < m_u) n_gt += __popcll(__ballot(key[e] > tau));
+    const int take_eq = need - n_gt;
+    int seen_eq = 0, done = 0;
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e) {
+      if (e * 64 >= m_u) continue;
+      const bool eq = key[e] == tau;
+      const uint64_t m_eq = __ballot(eq);
+      const int eq_rank = seen_eq + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                        static_cast<uint32_t>(m_eq >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m_eq), 0u)));
+      const bool take = key[e] > tau || (eq && eq_rank < take_eq);
+      const uint64_t m_take = __ballot(take);
+      const int before = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m_take >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m_take), 0u)));
+      if (take) out[done + before] = static_cast<int32_t>(col[e]);
+      done += __popcll(m_take);
+      seen_eq += __popcll(m_eq);
+    }
+    if (lane == 0) out[need] = static_cast<int32_t>(o);
+    return;
+  }
   // bitmaps over blocks 0 .. o-1: above tau, equal to tau; then this wave's copy of the output row
   const int nw = static_cast<int>((o + 31) >> 5);
   uint32_t* bgt = bm_all + static_cast<size_t>(wave) * (2 * a.words + a.NS);
@@ -901,13 +936,16 @@ int select_waves(const Dims& d) {
 int fused_select_capacity() { return 64 * kSelPer; }
 
 bool fused_select_supported(const Dims& d) {
-  // the candidate list holds about twice the budget: budgets up to 512 blocks
+  // the candidate list holds about twice the budget: budgets up to 512 blocks; the filter addresses
+  // one sequence's block keys (and a tile past them) with 32-bit byte offsets
   return d.idx_bf16 && d.NS <= 513 && (d.Di == 32 || d.Di == 64 || d.Di == 128) &&
-         select_waves(d) >= 1;
+         (d.NB + 128) * static_cast<int64_t>(d.Di) * 2 < (int64_t(1) << 31);
 }
 
 hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
                                int32_t* cnt, int32_t* fail_count, const Chunk& c, hipStream_t s) {
+  // one sequence's K_blk is addressed with 32-bit byte offsets (up to 2^31 / 256 blocks at Di = 128)
+  if ((d.NB + 128) * static_cast<int64_t>(d.Di) * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   FilterArgs a;
   a.q_idx = static_cast<const bf16_t*>(q_idx);
   a.k_blk = static_cast<const bf16_t*>(k_blk);
@@ -938,7 +976,8 @@ hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_b
 
 bool decode_select_supported(const Dims& d, int64_t seq_rows) {
   // the filter addresses a sequence's block keys (and up to two slabs past them) with 32-bit offsets
-  return fused_select_supported(d) && seq_rows >= 1 && seq_rows <= kDecRows &&
+  // (its lists are appended by several workgroups: the select orders them through LDS bitmaps)
+  return fused_select_supported(d) && select_waves(d) >= 1 && seq_rows >= 1 && seq_rows <= kDecRows &&
          (d.NB + 2 * kDecSlab) * d.Di * 2 < (int64_t(1) << 31);
 }
 
@@ -986,7 +1025,7 @@ hipError_t launch_decode_select(const Dims& d, const void* q_idx, const void* k_
 
 hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
                                     int32_t* sel, int32_t* fail_list, int32_t* fail_count,
-                                    const Chunk& c, hipStream_t s) {
+                                    const Chunk& c, bool sorted, hipStream_t s) {
   SelectArgs a;
   a.cand = cand;
   a.cnt = cnt;
@@ -1005,10 +1044,17 @@ hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const i
   a.NS = d.NS;
   a.cap = fused_select_capacity();
   a.words = static_cast<int>((d.NB + 31) / 32);
-  a.waves = select_waves(d);
-  const dim3 grid(static_cast<unsigned>((a.rows + a.waves - 1) / a.waves));
-  const size_t lds = static_cast<size_t>(a.waves) * (2 * a.words + a.NS) * sizeof(uint32_t);
-  hipLaunchKernelGGL(select_candidates_kernel, grid, dim3(64 * a.waves), lds, s, a);
+  if (sorted) {
+    a.waves = 4;
+    const dim3 grid(static_cast<unsigned>((a.rows + a.waves - 1) / a.waves));
+    hipLaunchKernelGGL(select_candidates_kernel<true>, grid, dim3(64 * a.waves), 0, s, a);
+  } else {
+    a.waves = select_waves(d);
+    if (a.waves < 1) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>((a.rows + a.waves - 1) / a.waves));
+    const size_t lds = static_cast<size_t>(a.waves) * (2 * a.words + a.NS) * sizeof(uint32_t);
+    hipLaunchKernelGGL(select_candidates_kernel<false>, grid, dim3(64 * a.waves), lds, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -269,7 +269,7 @@ sgqa_status select_chunked(const sgqa::Dims& d, const ForwardLayout& L, char* ws
   return for_each_chunk(d, chunk_tok, [&](const sgqa::Chunk& c) -> sgqa_status {
     hipError_t e = sgqa::launch_index_filter(d, q_idx, k_blk, cand, cnt, fail_count, c, s);
     if (e != hipSuccess) return hip_fail(e, "index filter launch");
-    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, s);
+    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, true, s);
     if (e != hipSuccess) return hip_fail(e, "candidate select launch");
     e = sgqa::launch_select_fallback(d, q_idx, k_blk, fail_list, fail_count, scratch, sel, c, s);
     if (e != hipSuccess) return hip_fail(e, "select fallback launch");
@@ -639,7 +639,7 @@ sgqa_status sgqa_decode(const sgqa_problem* prob, const sgqa_cache* cache,
     e = sgqa::launch_decode_select(d, q_idx, k_blk, thr, cand, cnt, fail_count, c, s);
     if (e != hipSuccess) return hip_fail(e, "decode filter launch");
     SGQA_CHECK(mark_stage(1, s));
-    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, s);
+    e = sgqa::launch_select_candidates(d, cand, cnt, sel, fail_list, fail_count, c, false, s);
     if (e != hipSuccess) return hip_fail(e, "candidate select launch");
     e = sgqa::launch_select_fallback(d, q_idx, k_blk, fail_list, fail_count, scratch, sel, c, s);
     if (e != hipSuccess) return hip_fail(e, "select fallback launch");

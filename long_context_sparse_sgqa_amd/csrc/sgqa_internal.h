@@ -78,14 +78,15 @@ hipError_t launch_topk(const Dims& d, const float* scores, int32_t* sel, const C
 int fused_select_capacity();
 bool fused_select_supported(const Dims& d);
 // Filter: per chunk row, the (score bits << 32 | block) candidates at or above a sampled
-// threshold, in no particular order, into cand + rr * capacity (count in cnt[rr], possibly
+// threshold, in ascending block order, into cand + rr * capacity (count in cnt[rr], possibly
 // > capacity).  Also zeroes *fail_count.
 hipError_t launch_index_filter(const Dims& d, const void* q_idx, const void* k_blk, uint64_t* cand,
                                int32_t* cnt, int32_t* fail_count, const Chunk& c, hipStream_t s);
-// Select from the candidates; rows it cannot settle are appended to fail_list.
+// Select from the candidates; rows it cannot settle are appended to fail_list.  `sorted`: every
+// list is in ascending block order (launch_index_filter's lists; not the decode filter's).
 hipError_t launch_select_candidates(const Dims& d, const uint64_t* cand, const int32_t* cnt,
                                     int32_t* sel, int32_t* fail_list, int32_t* fail_count,
-                                    const Chunk& c, hipStream_t s);
+                                    const Chunk& c, bool sorted, hipStream_t s);
 // Few rows per sequence (chunk tokens * G <= 32, e.g. decode): per-row thresholds from sampled
 // blocks (thr, one workgroup per sequence), then the filter split over slabs of each sequence's
 // blocks; fills cand / cnt like launch_index_filter (and zeroes *fail_count).
