@@ -16,8 +16,10 @@
 // The rows of the first products are permuted so that each lane's 16 results are exactly the
 // operand of the second products: lane l (l mod 32 = key n, l / 32 = h) gets rows of token slots
 // h (values 0..7 = heads 0..7) and 2 + h (values 8..15), and the second products take token slot
-// 2s + h's 8 heads as sum indices 8h .. 8h + 7 of step s; q and dO are therefore also read in a
-// per-token transposed copy ([token][d][8 heads]) so that those 8 heads are one 16-byte load.
+// 2s + h's 8 heads as sum indices 8h .. 8h + 7 of step s.  A step's q and dO rows are read from
+// memory once, row-major, into LDS: the first products read them row by row, the second read 4
+// heads at one d per lane through gfx950's transposing LDS read.  The next step's rows are loaded
+// into registers while the current step is computed, then written to the other LDS buffer.
 // Which tokens selected which unit comes from a bitmap per (sequence, group, unit) over the query
 // tokens, built from the selection with atomic ORs (the result does not depend on their order);
 // the tokens are walked in increasing order, so dK and dV are the same bits on every run.
@@ -60,60 +62,11 @@ __global__ void __launch_bounds__(256) mark_units_kernel(const int32_t* __restri
 }
 
 // ------------------------------------------------------------------------------------------------
-// q and dO per token transposed: [Bt, G, Tq, D, 8 heads]
-// ------------------------------------------------------------------------------------------------
-// One thread per (b, i, g, 8 consecutive d): eight 16-byte loads (one per head), an 8 x 8
-// transpose in registers, eight 16-byte stores (one per d).
-__global__ void __launch_bounds__(256) pack_heads_t_kernel(const bf16_t* __restrict__ q,
-                                                           const bf16_t* __restrict__ d_o,
-                                                           bf16_t* __restrict__ qt,
-                                                           bf16_t* __restrict__ dot, int64_t Tq,
-                                                           int G, int D, int64_t total) {
-  const int per = D / 8;
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int j = static_cast<int>(id % per);
-    const int64_t row = id / per;                // (b, i, g)
-    const int g = static_cast<int>(row % G);
-    const int64_t bi = row / G;
-    const int64_t i = bi % Tq, b = bi / Tq;
-    const int64_t dst = (((b * G + g) * Tq + i) * D + 8 * j) * kH;
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const bf16_t* src = (which ? d_o : q) + row * kH * D + 8 * j;
-      bf16_t* out = (which ? dot : qt) + dst;
-      uint32_t w[kH][4];
-#pragma unroll
-      for (int hh = 0; hh < kH; ++hh) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + hh * D);
-        w[hh][0] = v.x;
-        w[hh][1] = v.y;
-        w[hh][2] = v.z;
-        w[hh][3] = v.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = (w[2 * p][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          const uint32_t hi = (w[2 * p + 1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          o[p] = lo | (hi << 16);
-        }
-        *reinterpret_cast<uint4*>(out + e * kH) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------------
 // dK, dV per 4-unit chunk
 // ------------------------------------------------------------------------------------------------
 struct DkvArgs {
   const bf16_t* q;        // [Bt, Tq, G, 8, D]
   const bf16_t* d_o;      // dout * sigmoid(gate), q's layout
-  const bf16_t* qt;       // [Bt, G, Tq, D, 8]
-  const bf16_t* dot;
   const float* lse2;      // [Bt, Tq, G, 8], exp2 domain
   const float* Dr;        // dO . O per row
   const bf16_t* k;        // [Bt, G, Tk, D]
@@ -126,12 +79,37 @@ struct DkvArgs {
   float scale_log2e, scale;
 };
 
+// A step's q and dO rows in LDS: 32 rows (4 token slots x 8 heads) of D bf16 each, padded by 16
+// bytes (the row-major operand reads of 32 rows then fall in distinct banks), and the rows' lse2
+// and Dr; two steps in turn.
+template <int D> struct DkvLds {
+  static constexpr int kRowBytes = D * 2 + 16;
+  static constexpr int kTensorBytes = 32 * kRowBytes;
+  static constexpr int kStepBytes = 2 * kTensorBytes + 256;  // q, dO, then 32 lse2 and 32 Dr
+  static constexpr int kBytes = 2 * kStepBytes;
+  static constexpr int kPieces = D / 64;                    // 16-byte pieces per lane per token row set
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* LdsS16x4;
+
+// Transposing LDS read (16-bit elements): within each 16-lane group, lane i receives the i & 3-th
+// element of the 8 bytes read by group lane 4 j + (i >> 2), j = 0..3.  With group lane a reading
+// row base + (a >> 2), columns c + 4 (a & 3) .. + 3 of a row-major matrix, lane i gets rows
+// base .. base + 3 of column c + i.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(p));
+}
+
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) dkv_kernel(DkvArgs a) {
+  typedef DkvLds<D> L;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
   const int64_t wid = blockIdx.x;
   if (wid >= a.total) return;
   const int lane = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
+  const int gi = lane & 15, gh = (lane >> 4) & 1;        // lane in its 16-lane group, group's half
   const int64_t chunk = wid % a.nchunks;
   const int64_t bg = wid / a.nchunks;
   const int g = static_cast<int>(bg % a.G);
@@ -163,62 +141,77 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   // A-operand row of this lane in the first products: row m = lane % 32 is head
   // 4 ((m / 8) % 2) + m % 4 of token slot 2 (m / 16) + (m / 4) % 2
   const int m = n;
-  const int a_slot = 2 * (m >> 4) + ((m >> 2) & 1);
-  const int a_head = 4 * ((m >> 3) & 1) + (m & 3);
+  const int a_row = 8 * (2 * (m >> 4) + ((m >> 2) & 1)) + 4 * ((m >> 3) & 1) + (m & 3);
 
-  // one step: 4 token slots (token index, 4-bit mask of the chunk's units it selected)
-  auto step = [&](const int64_t* tok, const uint32_t* msk) {
-    auto pick = [&](int s) -> int64_t {
-      return s == 0 ? tok[0] : (s == 1 ? tok[1] : (s == 2 ? tok[2] : tok[3]));
-    };
-    auto pickm = [&](int s) -> uint32_t {
-      return s == 0 ? msk[0] : (s == 1 ? msk[1] : (s == 2 ? msk[2] : msk[3]));
-    };
-    const int64_t ta = pick(a_slot);
-    const int64_t arow = ((b * a.Tq + ta) * a.G + g) * kH + a_head;
-    bf16x8_t qa[D / 16], oa[D / 16];
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      qa[kc] = load_bf16x8(a.q + arow * D + 16 * kc + 8 * h);
-      oa[kc] = load_bf16x8(a.d_o + arow * D + 16 * kc + 8 * h);
+  // A step's rows go global -> registers -> LDS.  A token's 8 head rows are contiguous (16 D
+  // bytes): lane l moves its 16-byte pieces w = 64 p + l of each token slot's rows of q and dO.
+  u32x4_t stg_q[4][L::kPieces], stg_o[4][L::kPieces];   // vector types: kept in registers
+  float stg_r;                                         // lane l: lse2 (l < 32) or Dr of row l % 32
+  auto stage_load = [&](const int32_t* tok) __attribute__((always_inline)) {
+    {
+      const int row = lane & 31, sl = row >> 3;
+      const int32_t tk = sl == 0 ? tok[0] : (sl == 1 ? tok[1] : (sl == 2 ? tok[2] : tok[3]));
+      const int64_t r = ((b * a.Tq + tk) * a.G + g) * kH + (row & 7);
+      stg_r = lane < 32 ? a.lse2[r] : a.Dr[r];
     }
-    // rows of this lane's results: slot h (values 0..7) and slot 2 + h (8..15), heads 0..7
-    const int64_t t_lo = pick(h), t_hi = pick(2 + h);
-    const int64_t r_lo = ((b * a.Tq + t_lo) * a.G + g) * kH;
-    const int64_t r_hi = ((b * a.Tq + t_hi) * a.G + g) * kH;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int64_t row0 = ((b * a.Tq + tok[sl]) * a.G + g) * kH;
+#pragma unroll
+      for (int pc = 0; pc < L::kPieces; ++pc) {
+        const int w = 64 * pc + lane;
+        stg_q[sl][pc] = *reinterpret_cast<const u32x4_t*>(a.q + row0 * D + 8 * w);
+        stg_o[sl][pc] = *reinterpret_cast<const u32x4_t*>(a.d_o + row0 * D + 8 * w);
+      }
+    }
+  };
+  auto stage_write = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* base = lds + buf * L::kStepBytes;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+      for (int pc = 0; pc < L::kPieces; ++pc) {
+        const int w = 64 * pc + lane;
+        const int head = w / (D / 8), piece = w % (D / 8);
+        const int off = (8 * sl + head) * L::kRowBytes + 16 * piece;
+        *reinterpret_cast<u32x4_t*>(base + off) = stg_q[sl][pc];
+        *reinterpret_cast<u32x4_t*>(base + L::kTensorBytes + off) = stg_o[sl][pc];
+      }
+    }
+    reinterpret_cast<float*>(base + 2 * L::kTensorBytes)[lane] = stg_r;
+  };
+  // one step from LDS buffer `buf`: 4 token slots (token index, 4-bit mask of the chunk's units)
+  auto compute = [&](int buf, const int32_t* tok, const uint32_t* msk) __attribute__((always_inline)) {
+    const unsigned char* lq = lds + buf * L::kStepBytes;
+    const unsigned char* lo = lq + L::kTensorBytes;
+    // lse2 and Dr of this lane's result rows: slot h (values 0..7) and slot 2 + h (values 8..15)
+    const float* lr = reinterpret_cast<const float*>(lq + 2 * L::kTensorBytes);
     float lse[16], dr[16];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float4 l0 = *reinterpret_cast<const float4*>(a.lse2 + r_lo + 4 * e);
-      const float4 l1 = *reinterpret_cast<const float4*>(a.lse2 + r_hi + 4 * e);
-      const float4 d0 = *reinterpret_cast<const float4*>(a.Dr + r_lo + 4 * e);
-      const float4 d1 = *reinterpret_cast<const float4*>(a.Dr + r_hi + 4 * e);
+      const float4 l0 = reinterpret_cast<const float4*>(lr + 8 * h)[e];
+      const float4 l1 = reinterpret_cast<const float4*>(lr + 16 + 8 * h)[e];
+      const float4 d0 = reinterpret_cast<const float4*>(lr + 32 + 8 * h)[e];
+      const float4 d1 = reinterpret_cast<const float4*>(lr + 48 + 8 * h)[e];
       lse[4 * e] = l0.x; lse[4 * e + 1] = l0.y; lse[4 * e + 2] = l0.z; lse[4 * e + 3] = l0.w;
       lse[8 + 4 * e] = l1.x; lse[9 + 4 * e] = l1.y; lse[10 + 4 * e] = l1.z; lse[11 + 4 * e] = l1.w;
       dr[4 * e] = d0.x; dr[4 * e + 1] = d0.y; dr[4 * e + 2] = d0.z; dr[4 * e + 3] = d0.w;
       dr[8 + 4 * e] = d1.x; dr[9 + 4 * e] = d1.y; dr[10 + 4 * e] = d1.z; dr[11 + 4 * e] = d1.w;
     }
-    // transposed q / dO of token slot 2 s + h at d = 32 dt + n: the second products' B operand
-    bf16x8_t qtb[D / 32][2], otb[D / 32][2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t ts = pick(2 * s + h);
-      const int64_t base = ((bg * a.Tq + ts) * D + n) * kH;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        qtb[dt][s] = load_bf16x8(a.qt + base + 32 * dt * kH);
-        otb[dt][s] = load_bf16x8(a.dot + base + 32 * dt * kH);
-      }
-    }
     f32x16_t sc = {}, dp = {};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      sc = mfma32x32x16(qa[kc], kb[kc], sc);
-      dp = mfma32x32x16(oa[kc], vb[kc], dp);
+      const int off = a_row * L::kRowBytes + 2 * (16 * kc + 8 * h);
+      const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(lq + off);
+      const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(lo + off);
+      sc = mfma32x32x16(qa, kb[kc], sc);
+      dp = mfma32x32x16(oa, vb[kc], dp);
     }
     // masks: the token selected this lane's unit, and the key is at or before the token
-    const bool on_lo = ((pickm(h) >> un) & 1u) && t <= a.pos0 + t_lo;
-    const bool on_hi = ((pickm(2 + h) >> un) & 1u) && t <= a.pos0 + t_hi;
+    const int64_t t_lo = h ? tok[1] : tok[0], t_hi = h ? tok[3] : tok[2];
+    const uint32_t m_lo = h ? msk[1] : msk[0], m_hi = h ? msk[3] : msk[2];
+    const bool on_lo = ((m_lo >> un) & 1u) && t <= a.pos0 + t_lo;
+    const bool on_hi = ((m_hi >> un) & 1u) && t <= a.pos0 + t_hi;
     float pv[16], ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -229,38 +222,52 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
     const bf16x8_t p0 = pack8_bf16(pv), p1 = pack8_bf16(pv + 8);
     const bf16x8_t s0 = pack8_bf16(ds), s1 = pack8_bf16(ds + 8);
+    // second products' B operand: token slot 2 s + h's 8 heads (rows) at d = 32 dt + n, read
+    // transposed from the row-major rows (two reads of 4 heads each)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      acc_v[dt] = mfma32x32x16(p0, otb[dt][0], acc_v[dt]);
-      acc_v[dt] = mfma32x32x16(p1, otb[dt][1], acc_v[dt]);
-      acc_k[dt] = mfma32x32x16(s0, qtb[dt][0], acc_k[dt]);
-      acc_k[dt] = mfma32x32x16(s1, qtb[dt][1], acc_k[dt]);
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const int row = 8 * (2 * sp + h) + (gi >> 2);
+        const int off = row * L::kRowBytes + 2 * (32 * dt + 16 * gh + 4 * (gi & 3));
+        const s16x4_t q0 = lds_read_tr16(lq + off), q1 = lds_read_tr16(lq + off + 4 * L::kRowBytes);
+        const s16x4_t o0 = lds_read_tr16(lo + off), o1 = lds_read_tr16(lo + off + 4 * L::kRowBytes);
+        const bf16x8_t qb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8_t ob = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_v[dt] = mfma32x32x16(sp ? p1 : p0, ob, acc_v[dt]);
+        acc_k[dt] = mfma32x32x16(sp ? s1 : s0, qb, acc_k[dt]);
+      }
     }
   };
 
   // Query tokens that can select a unit of this chunk have position >= its first key.  The four
-  // units' bitmap words are read with scalar loads; the tokens are taken in increasing order.
+  // units' bitmap words are read with scalar loads; the tokens are taken in increasing order, four
+  // per step (unused slots repeat slot 0's token with no unit selected: they add nothing).
   typedef const __attribute__((address_space(4))) uint32_t* ConstU32Ptr;
   const int64_t first = chunk * 32 - a.pos0;
-  const int64_t w_lo = first > 0 ? (first >> 5) : 0;
   const uint32_t* bmc = a.bm + (bg * a.NU + chunk * 4) * a.W;
   const int nunits = static_cast<int>(a.NU - chunk * 4 < 4 ? a.NU - chunk * 4 : 4);
-  int64_t tok[4] = {0, 0, 0, 0};
-  uint32_t msk[4] = {0u, 0u, 0u, 0u};
-  int fill = 0;
-  for (int64_t w = w_lo; w < a.W; ++w) {
-    uint32_t wd[4];
+  int64_t w_next = first > 0 ? (first >> 5) : 0;      // next bitmap word to read
+  int64_t w_cur = 0;                                   // word the bits in `any` belong to
+  uint32_t wd[4] = {0u, 0u, 0u, 0u};
+  uint32_t any = 0u;
+  auto next_step = [&](int32_t* tok, uint32_t* msk) __attribute__((always_inline)) -> int {
+    int fill = 0;
+    while (fill < 4) {
+      while (any == 0u && w_next < a.W) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      wd[u] = u < nunits ? *((ConstU32Ptr)(bmc + u * a.W + w)) : 0u;
-    uint32_t any = wd[0] | wd[1] | wd[2] | wd[3];
-    while (any) {
+        for (int u = 0; u < 4; ++u)
+          wd[u] = u < nunits ? *((ConstU32Ptr)(bmc + u * a.W + w_next)) : 0u;
+        any = wd[0] | wd[1] | wd[2] | wd[3];
+        w_cur = w_next++;
+      }
+      if (any == 0u) break;
       const int bit = __builtin_ctz(any);
       any &= any - 1u;
       uint32_t mk = 0u;
 #pragma unroll
       for (int u = 0; u < 4; ++u) mk |= ((wd[u] >> bit) & 1u) << u;
-      const int64_t ti = w * 32 + bit;
+      const int32_t ti = static_cast<int32_t>(w_cur * 32 + bit);
       tok[0] = fill == 0 ? ti : tok[0];
       tok[1] = fill == 1 ? ti : tok[1];
       tok[2] = fill == 2 ? ti : tok[2];
@@ -269,14 +276,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
       msk[1] = fill == 1 ? mk : msk[1];
       msk[2] = fill == 2 ? mk : msk[2];
       msk[3] = fill == 3 ? mk : msk[3];
-      if (++fill == 4) {
-        step(tok, msk);
-        fill = 0;
-      }
+      ++fill;
     }
-  }
-  if (fill > 0) {
-    // unused slots repeat a valid token with no unit selected: they add nothing
 #pragma unroll
     for (int s = 1; s < 4; ++s) {
       if (s >= fill) {
@@ -284,7 +285,31 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         msk[s] = 0u;
       }
     }
-    step(tok, msk);
+    return fill;
+  };
+
+  // Software pipeline: step i+1's rows are loaded into registers while step i is computed from
+  // LDS, then written to the other LDS buffer.
+  int32_t tok_a[4] = {0, 0, 0, 0}, tok_b[4] = {0, 0, 0, 0};
+  uint32_t msk_a[4] = {0u, 0u, 0u, 0u}, msk_b[4] = {0u, 0u, 0u, 0u};
+  if (next_step(tok_a, msk_a) > 0) {
+    stage_load(tok_a);
+    stage_write(0);
+    int have_b = next_step(tok_b, msk_b);
+    int buf = 0;
+    while (true) {
+      if (have_b > 0) stage_load(tok_b);
+      compute(buf, tok_a, msk_a);
+      if (have_b == 0) break;
+      stage_write(buf ^ 1);
+      buf ^= 1;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        tok_a[s] = tok_b[s];
+        msk_a[s] = msk_b[s];
+      }
+      have_b = next_step(tok_b, msk_b);
+    }
   }
 
   // dV and dK rows of this chunk: lane (n, h) holds key 8 (r / 4) + 4 h + r % 4, d = 32 dt + n
@@ -316,8 +341,7 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 size_t backward_dkv_bytes(const Dims& d) {
   const int64_t W = (d.Tq + 31) / 32;
   const size_t bm = static_cast<size_t>(d.Bt * d.G * d.NU * W) * sizeof(uint32_t);
-  const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * kH;
-  return round256(bm) + 2 * round256(rows * d.D * sizeof(bf16_t));
+  return round256(bm);
 }
 
 hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, const float* lse2,
@@ -325,11 +349,7 @@ hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, co
                                float* dk, float* dv, void* ws, hipStream_t s) {
   const int64_t W = (d.Tq + 31) / 32;
   const size_t bm_bytes = round256(static_cast<size_t>(d.Bt * d.G * d.NU * W) * sizeof(uint32_t));
-  const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * kH;
-  char* p = static_cast<char*>(ws);
-  uint32_t* bm = reinterpret_cast<uint32_t*>(p);
-  bf16_t* qt = reinterpret_cast<bf16_t*>(p + bm_bytes);
-  bf16_t* dot = reinterpret_cast<bf16_t*>(p + bm_bytes + round256(rows * d.D * sizeof(bf16_t)));
+  uint32_t* bm = static_cast<uint32_t*>(ws);
 
   const int64_t n4 = static_cast<int64_t>(bm_bytes / 16);
   hipLaunchKernelGGL(fill_u32x4_zero_kernel, dim3(grid_for(n4)), dim3(256), 0, s,
@@ -341,17 +361,9 @@ hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, co
                      d.NU, W, d.G, d.NS, d.B / 8, entries);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t items = d.Bt * d.Tq * d.G * (d.D / 8);
-  hipLaunchKernelGGL(pack_heads_t_kernel, dim3(grid_for(items)), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(d_o), qt, dot, d.Tq,
-                     d.G, d.D, items);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   DkvArgs a;
   a.q = static_cast<const bf16_t*>(q);
   a.d_o = static_cast<const bf16_t*>(d_o);
-  a.qt = qt;
-  a.dot = dot;
   a.lse2 = lse2;
   a.Dr = Dr;
   a.k = static_cast<const bf16_t*>(k);
