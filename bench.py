@@ -53,6 +53,10 @@ def parse():
                     help="swa: the gated sliding-window layer on the workload's q/k/v/gate; "
                          "backward: sgqa_attend_backward for the forward's selection")
     ap.add_argument("--window", type=int, default=4096, help="sliding window (tokens) for --layer swa")
+    ap.add_argument("--bwd-stats", default="saved", choices=("saved", "recompute"),
+                    help="--layer backward: softmax statistics from the forward's saved output and "
+                         "log-sum-exp (sgqa_attend_backward_with_lse; training) or recomputed "
+                         "(sgqa_attend_backward)")
     ap.add_argument("--kv", default="bf16", choices=("bf16", "fp8"),
                     help="fp8: K and V stored as e4m3 codes with per-tensor scales (sgqa_forward_fp8kv)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -621,23 +625,33 @@ def main_backward(args):
     lib = sg.load_library()
     x = generate(w, device=dev, seed=args.seed)
     prob = sg.Problem.from_workload(w)
-    _, sel = sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"],
-                        return_sel=True)
+    out, sel, lse = sg.forward_with_lse(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"],
+                                        x["k_idx"])
     g = torch.Generator(device=dev).manual_seed(args.seed + 1)
     dout = torch.randn(x["q"].shape, generator=g, device=dev).to(torch.bfloat16)
     n = ctypes.c_size_t()
     lib.sgqa_attend_backward_workspace_size(ctypes.byref(prob._c()), ctypes.byref(n))
     ws = torch.empty(n.value, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    saved = args.bwd_stats == "saved"
+
+    def one():
+        if saved:
+            sg.attend_backward_with_lse(prob, x["q"], x["k"], x["v"], x["gate"], sel, out, lse,
+                                        dout, workspace=ws, stream=stream)
+        else:
+            sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout, workspace=ws,
+                               stream=stream)
+
     for _ in range(args.warmup):
-        sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout, workspace=ws, stream=stream)
+        one()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
         ev[j][0].record(stream)
-        sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout, workspace=ws, stream=stream)
+        one()
         ev[j][1].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -653,10 +667,14 @@ def main_backward(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded workload; dout ~ N(0,1); the forward's selection)",
         "config": {"workload": f"{w.name} attention backward", "batch": w.batch, "t_q": w.t_q,
+                   "softmax_statistics": ("saved by sgqa_forward_with_lse" if saved
+                                          else "recomputed"),
                    "t_kv": w.t_kv, "kv_groups": w.groups, "heads_per_group": w.heads,
                    "head_dim": w.head_dim, "block": w.block, "topk_tokens": w.topk,
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "sgqa_attend_backward (recompute + attend_bwd_kernel)", "bound": "mfma",
+        "roofline": {"kernel": ("sgqa_attend_backward_with_lse (dkv_kernel + attend_bwd_kernel)"
+                                if saved else "sgqa_attend_backward (recompute + dkv_kernel + "
+                                "attend_bwd_kernel)"), "bound": "mfma",
                      "achieved": ach, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": ach * 1e12 / PEAK_BF16_FLOPS, "traffic": None,
                      "work_per_launch": f"{flops:.4e} FLOP = 10*d*h per attended (query, group, token)"},

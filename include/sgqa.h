@@ -176,6 +176,21 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
                          void* stream);
 
 /*
+ * sgqa_forward for training: the same results, plus the softmax normaliser of every attention
+ * row, which sgqa_attend_backward_with_lse takes instead of recomputing the forward (training up
+ * to 1M tokens is the pages' setting: mo.ai.kr summary, section "모델 구조와 학습 안정성").
+ *   lse_out : [Bt, Tq, G, H] float32, caller-owned: ln sum_t exp(scale * q . k_t) over the tokens
+ *             the row attends to (fp32, from the kernels' exp2-domain running max and sum).
+ * Supported: the range-split configurations (bf16, H == 8, D in {64, 128}, B a multiple of 8);
+ * others return SGQA_ERR_UNSUPPORTED.  NULL lse_out: SGQA_ERR_NULL.  Workspace as sgqa_forward.
+ */
+sgqa_status sgqa_forward_with_lse(const sgqa_problem* prob, const void* q, const void* k,
+                                  const void* v, const void* gate, const void* q_idx,
+                                  const void* k_idx, void* k_blk, int32_t* sel_out, void* out,
+                                  float* lse_out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Profiling hook: stage markers for sgqa_forward.
  *   events : SGQA_STAGE_EVENTS hipEvent_t handles (passed as void*) created by the caller, or NULL
  *            to disarm.  The handles are copied; the array may be freed after the call.
@@ -313,6 +328,21 @@ sgqa_status sgqa_attend_backward(const sgqa_problem* prob, const void* q, const 
                                  const void* v, const void* gate, const int32_t* sel,
                                  const void* dout, void* dq, float* dk, float* dv, void* dgate,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same gradients from the forward's saved output and normaliser instead of a recompute:
+ *   out : [Bt, Tq, G, H, D] dtype, the forward's output (sigmoid(gate) * O);
+ *   lse : [Bt, Tq, G, H] float32, sgqa_forward_with_lse's lse_out for the same inputs.
+ * With out = sigmoid(gate) O:  dO . O = dout . out  and  dgate = dout * out * (1 - sigmoid(gate)),
+ * and P_t = exp(scale q.k_t - lse).  Other arguments, outputs, workspace size and supported
+ * configurations as sgqa_attend_backward; out and lse are only read.  Results agree with
+ * sgqa_attend_backward up to rounding (dO . O is summed from the bf16 output here).
+ */
+sgqa_status sgqa_attend_backward_with_lse(const sgqa_problem* prob, const void* q, const void* k,
+                                          const void* v, const void* gate, const int32_t* sel,
+                                          const void* out, const float* lse, const void* dout,
+                                          void* dq, float* dk, float* dv, void* dgate,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Steps 1-4 with K and V stored as fp8.  The pages run the KV cache in FP8 (trained for it: FP8

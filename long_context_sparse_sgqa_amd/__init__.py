@@ -25,7 +25,8 @@ import torch
 __all__ = ["Problem", "Cache", "load_library", "library_path", "abi_version", "sizes", "index",
            "topk", "attend", "forward", "alloc_cache", "cache_append", "decode_workspace_size",
            "decode", "decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES", "swa_workspace_size", "swa",
-           "forward_fp8kv", "attend_backward", "SgqaError", "EXPORTED_SYMBOLS"]
+           "forward_fp8kv", "attend_backward", "forward_with_lse", "attend_backward_with_lse",
+           "SgqaError", "EXPORTED_SYMBOLS"]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libsgqa.so"
@@ -38,7 +39,8 @@ EXPORTED_SYMBOLS = ("sgqa_abi_version", "sgqa_status_string", "sgqa_last_error",
                     "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
                     "sgqa_decode", "sgqa_decode_noalloc", "sgqa_swa_workspace_size", "sgqa_swa",
                     "sgqa_forward_fp8kv", "sgqa_attend_backward_workspace_size",
-                    "sgqa_attend_backward")
+                    "sgqa_attend_backward", "sgqa_forward_with_lse",
+                    "sgqa_attend_backward_with_lse")
 
 # scratch sgqa_decode_noalloc holds per GPU (SGQA_DECODE_NOALLOC_SCRATCH_BYTES in include/sgqa.h)
 DECODE_NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -160,11 +162,13 @@ def load_library():
                                        ctypes.c_size_t, vp]
     lib.sgqa_attend_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgqa_attend_backward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
+    lib.sgqa_forward_with_lse.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
+    lib.sgqa_attend_backward_with_lse.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
     for name in ("sgqa_sizes", "sgqa_index", "sgqa_topk", "sgqa_attend", "sgqa_forward",
                  "sgqa_set_stage_events", "sgqa_cache_append", "sgqa_decode_workspace_size",
                  "sgqa_decode", "sgqa_decode_noalloc", "sgqa_swa_workspace_size", "sgqa_swa",
                  "sgqa_forward_fp8kv", "sgqa_attend_backward_workspace_size",
-                 "sgqa_attend_backward"):
+                 "sgqa_attend_backward", "sgqa_forward_with_lse", "sgqa_attend_backward_with_lse"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -283,6 +287,36 @@ def forward(prob: Problem, q, k, v, gate, q_idx, k_idx, k_blk=None, out=None, se
                             _ptr(out, "out", sh["q"], prob.dtype), workspace.data_ptr(),
                             workspace.numel(), _stream(stream)))
     return (out, sel) if return_sel else out
+
+
+def forward_with_lse(prob: Problem, q, k, v, gate, q_idx, k_idx, k_blk=None, out=None, sel=None,
+                     lse=None, workspace=None, stream=None):
+    """Steps 1-4 plus the per-row softmax normaliser ln sum_t exp(scale q.k_t), float32
+    [Bt, Tq, G, H], for attend_backward_with_lse.  Returns out, sel, lse."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q.device
+    if k_blk is None:
+        k_blk = torch.empty(sh["k_blk"], dtype=prob.index_dtype, device=dev)
+    if out is None:
+        out = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    if sel is None:
+        sel = torch.empty(sh["sel"], dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty(sh["q"][:-1], dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(sizes(prob)["forward_workspace_bytes"], dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_forward_with_lse(
+        ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype),
+        _ptr(k, "k", sh["k"], prob.dtype), _ptr(v, "v", sh["k"], prob.dtype),
+        _ptr(gate, "gate", sh["q"], prob.dtype),
+        _ptr(q_idx, "q_idx", sh["q_idx"], prob.index_dtype),
+        _ptr(k_idx, "k_idx", sh["k_idx"], prob.index_dtype),
+        _ptr(k_blk, "k_blk", sh["k_blk"], prob.index_dtype),
+        _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], prob.dtype),
+        _ptr(lse, "lse", sh["q"][:-1], torch.float32), workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
+    return out, sel, lse
 
 
 # ----------------------------------------------------------------------------------------------
@@ -458,6 +492,31 @@ def attend_backward(prob: Problem, q, k, v, gate, sel, dout, workspace=None, str
         ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype), _ptr(k, "k", sh["k"], prob.dtype),
         _ptr(v, "v", sh["k"], prob.dtype), _ptr(gate, "gate", sh["q"], prob.dtype),
         _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(dout, "dout", sh["q"], prob.dtype),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dgate.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(stream)))
+    return dq, dk, dv, dgate
+
+
+def attend_backward_with_lse(prob: Problem, q, k, v, gate, sel, out, lse, dout, workspace=None,
+                             stream=None):
+    """attend_backward from the forward's saved output `out` and normaliser `lse` (as returned by
+    forward_with_lse) instead of a forward recompute.  Returns dq, dk, dv, dgate."""
+    lib = load_library()
+    sh = _shapes(prob)
+    dev = q.device
+    dq = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    dgate = torch.empty(sh["q"], dtype=prob.dtype, device=dev)
+    dk = torch.empty(sh["k"], dtype=torch.float32, device=dev)
+    dv = torch.empty(sh["k"], dtype=torch.float32, device=dev)
+    if workspace is None:
+        n = ctypes.c_size_t()
+        _check(lib.sgqa_attend_backward_workspace_size(ctypes.byref(prob._c()), ctypes.byref(n)))
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    _check(lib.sgqa_attend_backward_with_lse(
+        ctypes.byref(prob._c()), _ptr(q, "q", sh["q"], prob.dtype), _ptr(k, "k", sh["k"], prob.dtype),
+        _ptr(v, "v", sh["k"], prob.dtype), _ptr(gate, "gate", sh["q"], prob.dtype),
+        _ptr(sel, "sel", sh["sel"], torch.int32), _ptr(out, "out", sh["q"], prob.dtype),
+        _ptr(lse, "lse", sh["q"][:-1], torch.float32), _ptr(dout, "dout", sh["q"], prob.dtype),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dgate.data_ptr(), workspace.data_ptr(),
         workspace.numel(), _stream(stream)))
     return dq, dk, dv, dgate

@@ -484,13 +484,14 @@ hipError_t launch_pack_kv_quad(const Dims& d, const void* k, const void* v, void
 
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
                                 const void* gate, const int32_t* sel, void* out, void* workspace,
-                                hipStream_t s, StageMark mark) {
+                                hipStream_t s, StageMark mark, float* lse) {
   const bf16_t* kp = static_cast<const bf16_t*>(workspace);
   const bf16_t* vp = kp + attend_packed_kv_bytes(d) / 2 / sizeof(bf16_t);
   if (attend_split_supported(d)) {
     char* rest = static_cast<char*>(workspace) + attend_packed_kv_bytes(d);
-    return launch_attend_split(d, q, kp, gate, sel, out, vp, rest, s, mark);
+    return launch_attend_split(d, q, kp, gate, sel, out, vp, rest, s, mark, nullptr, nullptr, lse);
   }
+  if (lse) return hipErrorInvalidValue;
   if (mark) {
     const hipError_t e = mark(4, s);
     if (e != hipSuccess) return e;

@@ -728,6 +728,7 @@ struct MergeArgs {
   const float2* part_ml;
   const bf16_t* gate;
   bf16_t* out;
+  float* lse;              // nullable: per row ln sum_t exp(scale q.k_t) (natural log)
   int64_t Tq, ngroups, total_groups;
   int G, D;
 };
@@ -773,7 +774,10 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
     }
   }
   const float inv = 1.f / L;
-  const int64_t obase = (((b * a.Tq + tok) * a.G + g) * 8 + (row & 7)) * a.D + d0;
+  const int64_t orow = ((b * a.Tq + tok) * a.G + g) * 8 + (row & 7);
+  const int64_t obase = orow * a.D + d0;
+  // the partials' m are in the exp2 domain of the scaled logits: lse = (m + log2 l) ln 2
+  if (a.lse && d0 == 0) a.lse[orow] = (mx + __builtin_amdgcn_logf(L)) * 0.6931471805599453f;
   const uint4 gw = *reinterpret_cast<const uint4*>(a.gate + obase);
   const uint32_t gv[4] = {gw.x, gw.y, gw.z, gw.w};
   uint32_t ov[4];
@@ -860,6 +864,56 @@ __global__ void __launch_bounds__(256) merge_stats_kernel(StatsArgs a) {
     *reinterpret_cast<uint2*>(a.dgate + base) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
     if (d0 == 0) {
       a.lse2[rr] = mx + __builtin_amdgcn_logf(L);    // v_log_f32 is log2
+      a.Dr[rr] = part;
+    }
+  }
+}
+
+// The same statistics from the forward's saved output and log-sum-exp: with out = sigmoid(gate) O,
+// dO . O = dout . out and dgate = dout * out * (1 - sigmoid(gate)); lse2 = lse log2(e).  One
+// thread per (row, 4 d); a row's threads are consecutive lanes.
+struct SavedStatsArgs {
+  const bf16_t* out;
+  const float* lse;
+  const bf16_t* gate;
+  const bf16_t* dout;
+  bf16_t* d_o;
+  bf16_t* dgate;
+  float* lse2;
+  float* Dr;
+  int64_t rows;
+  int D;
+};
+
+__global__ void __launch_bounds__(256) saved_stats_kernel(SavedStatsArgs a) {
+  const int per_row = a.D / 4;                       // 16 or 32 lanes per row, aligned in a wave
+  const int64_t total = a.rows * per_row;
+  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
+       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int d0 = static_cast<int>(id % per_row) * 4;
+    const int64_t rr = id / per_row;
+    const int64_t base = rr * a.D + d0;
+    const uint2 ow = *reinterpret_cast<const uint2*>(a.out + base);
+    const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + base);
+    const uint2 dw = *reinterpret_cast<const uint2*>(a.dout + base);
+    const uint32_t o2[2] = {ow.x, ow.y}, g2[2] = {gw.x, gw.y}, d2[2] = {dw.x, dw.y};
+    float dO[4], dg[4], part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sh = 16 * (e & 1);
+      const float ov = bf16_to_f32(static_cast<bf16_t>((o2[e >> 1] >> sh) & 0xffffu));
+      const float gv = bf16_to_f32(static_cast<bf16_t>((g2[e >> 1] >> sh) & 0xffffu));
+      const float dv = bf16_to_f32(static_cast<bf16_t>((d2[e >> 1] >> sh) & 0xffffu));
+      const float sg = 1.f / (1.f + __expf(-gv));
+      dO[e] = dv * sg;
+      dg[e] = dv * ov * (1.f - sg);
+      part += dv * ov;
+    }
+    for (int m = per_row / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+    *reinterpret_cast<uint2*>(a.d_o + base) = make_uint2(pack_bf16x2(dO[0], dO[1]), pack_bf16x2(dO[2], dO[3]));
+    *reinterpret_cast<uint2*>(a.dgate + base) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+    if (d0 == 0) {
+      a.lse2[rr] = a.lse[rr] * 1.4426950408889634f;
       a.Dr[rr] = part;
     }
   }
@@ -1135,7 +1189,8 @@ SplitBuffers split_buffers(const Dims& d, int umax, void* ws) {
 hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* packed_k,
                                    const void* gate, void* out, const void* packed_v,
                                    const SplitBuffers& sb, int umax, int win_m1, hipStream_t s,
-                                   StageMark mark, const PagedKV* paged, const Fp8Scales* fp8) {
+                                   StageMark mark, const PagedKV* paged, const Fp8Scales* fp8,
+                                   float* lse = nullptr) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   RangeArgs a;
@@ -1196,6 +1251,7 @@ hipError_t launch_ranges_and_merge(const Dims& d, const void* q, const void* pac
   m.part_ml = sb.part_ml;
   m.gate = static_cast<const bf16_t*>(gate);
   m.out = static_cast<bf16_t*>(out);
+  m.lse = lse;
   m.Tq = d.Tq;
   m.ngroups = ng;
   m.total_groups = total;
@@ -1223,7 +1279,7 @@ size_t attend_split_bytes(const Dims& d) {
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark,
-                               const PagedKV* paged, const Fp8Scales* fp8) {
+                               const PagedKV* paged, const Fp8Scales* fp8, float* lse) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
@@ -1255,7 +1311,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   if (e == hipSuccess && mark) e = mark(4, s);
   if (e != hipSuccess) return e;
   return launch_ranges_and_merge(d, q, packed_k, gate, out, packed_v, sb, umax, 1 << 30, s, mark,
-                                 paged, fp8);
+                                 paged, fp8, lse);
 }
 
 bool attend_window_supported(const Dims& d) {
@@ -1303,9 +1359,72 @@ size_t attend_backward_bytes(const Dims& d) {
          align256(rows * d.D * sizeof(bf16_t)) + backward_dkv_bytes(d) + dq_part_bytes(d);
 }
 
+// The gradient kernels of the backward, once dO, lse2 and Dr are in place: dk, dv key-major
+// (every element written once, no atomics), then dq per unit range and the merge of the ranges.
+static hipError_t launch_backward_grads(const Dims& d, const void* q, const void* k, const void* v,
+                                        const int32_t* sel, void* dq, float* dk, float* dv,
+                                        const bf16_t* d_o, const float* lse2, const float* Dr,
+                                        const char* fwd_kv, const char* bwd_kv,
+                                        const SplitBuffers& sb, char* dkv_ws, float* dq_part,
+                                        hipStream_t s) {
+  const int64_t ng = (d.Tq + kTok - 1) / kTok;
+  const int64_t total = d.Bt * d.G * ng;
+  const int umax = static_cast<int>(units_per_query(d));
+  const size_t pkv = packed_kv_quad_bytes(d);
+  hipError_t e = launch_backward_dkv(d, q, d_o, lse2, Dr, k, v, sel, dk, dv, dkv_ws, s);
+  if (e != hipSuccess) return e;
+  BwdArgs ba;
+  ba.q = static_cast<const bf16_t*>(q);
+  ba.d_o = d_o;
+  ba.lse2 = lse2;
+  ba.Dr = Dr;
+  ba.kq = reinterpret_cast<const bf16_t*>(fwd_kv);
+  ba.vq = reinterpret_cast<const bf16_t*>(bwd_kv);
+  ba.kv = reinterpret_cast<const bf16_t*>(bwd_kv + pkv / 2);
+  ba.ulist = sb.ulist;
+  ba.bounds = sb.bounds;
+  ba.dq_part = dq_part;
+  ba.Tq = d.Tq;
+  ba.Tk = d.Tk;
+  ba.NU = d.NU;
+  ba.pos0 = d.pos0;
+  ba.ngroups = ng;
+  ba.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
+  ba.wave_ranges = ng < kRangeWaves ? 1 : 0;
+  ba.total = total;
+  ba.G = d.G;
+  ba.umax = umax;
+  ba.scale_log2e = d.scale * 1.4426950408889634f;
+  ba.scale = d.scale;
+  const dim3 bgrid(static_cast<unsigned>(ba.wave_ranges ? d.Bt * d.G * ng : d.Bt * d.G * ba.wg_groups * kRanges));
+  if (d.D == 128)
+    hipLaunchKernelGGL(attend_bwd_kernel<128>, bgrid, dim3(256), 0, s, ba);
+  else
+    hipLaunchKernelGGL(attend_bwd_kernel<64>, bgrid, dim3(256), 0, s, ba);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DqMergeArgs dm;
+  dm.dq_part = dq_part;
+  dm.dq = static_cast<bf16_t*>(dq);
+  dm.Tq = d.Tq;
+  dm.ngroups = ng;
+  dm.total = total;
+  dm.G = d.G;
+  dm.D = d.D;
+  dm.scale = d.scale;
+  {
+    const int64_t n = total * (d.D / 32) * 4 * 64;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(dq_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dm);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
                                   const void* gate, const int32_t* sel, const void* dout, void* dq,
-                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s) {
+                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s,
+                                  const void* saved_out, const float* saved_lse) {
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
@@ -1351,6 +1470,28 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
     hipLaunchKernelGGL(quad_union_kernel<false>, ugrid, dim3(64 * ua.waves), lds, s, ua);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (saved_out) {
+    // statistics from the forward's output and log-sum-exp: no forward recompute
+    SavedStatsArgs st;
+    st.out = static_cast<const bf16_t*>(saved_out);
+    st.lse = saved_lse;
+    st.gate = static_cast<const bf16_t*>(gate);
+    st.dout = static_cast<const bf16_t*>(dout);
+    st.d_o = d_o;
+    st.dgate = static_cast<bf16_t*>(dgate);
+    st.lse2 = lse2;
+    st.Dr = Dr;
+    st.rows = static_cast<int64_t>(rows);
+    st.D = d.D;
+    const int64_t items = st.rows * (d.D / 4);
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(saved_stats_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, st);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_backward_grads(d, q, k, v, sel, dq, dk, dv, d_o, lse2, Dr, fwd_kv, bwd_kv, sb,
+                                 dkv_ws, dq_part, s);
+  }
   RangeArgs a;
   a.q = static_cast<const bf16_t*>(q);
   a.kp = reinterpret_cast<const bf16_t*>(fwd_kv);
@@ -1404,55 +1545,8 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dk, dv key-major: every element written once, no atomics
-  e = launch_backward_dkv(d, q, d_o, lse2, Dr, k, v, sel, dk, dv, dkv_ws, s);
-  if (e != hipSuccess) return e;
-  BwdArgs ba;
-  ba.q = static_cast<const bf16_t*>(q);
-  ba.d_o = d_o;
-  ba.lse2 = lse2;
-  ba.Dr = Dr;
-  ba.kq = reinterpret_cast<const bf16_t*>(fwd_kv);
-  ba.vq = reinterpret_cast<const bf16_t*>(bwd_kv);
-  ba.kv = reinterpret_cast<const bf16_t*>(bwd_kv + pkv / 2);
-  ba.ulist = sb.ulist;
-  ba.bounds = sb.bounds;
-  ba.dq_part = dq_part;
-  ba.Tq = d.Tq;
-  ba.Tk = d.Tk;
-  ba.NU = d.NU;
-  ba.pos0 = d.pos0;
-  ba.ngroups = ng;
-  ba.wg_groups = (ng + kRangeWaves - 1) / kRangeWaves;
-  ba.wave_ranges = ng < kRangeWaves ? 1 : 0;
-  ba.total = total;
-  ba.G = d.G;
-  ba.umax = umax;
-  ba.scale_log2e = d.scale * 1.4426950408889634f;
-  ba.scale = d.scale;
-  const dim3 bgrid(static_cast<unsigned>(ba.wave_ranges ? d.Bt * d.G * ng : d.Bt * d.G * ba.wg_groups * kRanges));
-  if (d.D == 128)
-    hipLaunchKernelGGL(attend_bwd_kernel<128>, bgrid, dim3(256), 0, s, ba);
-  else
-    hipLaunchKernelGGL(attend_bwd_kernel<64>, bgrid, dim3(256), 0, s, ba);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  DqMergeArgs dm;
-  dm.dq_part = dq_part;
-  dm.dq = static_cast<bf16_t*>(dq);
-  dm.Tq = d.Tq;
-  dm.ngroups = ng;
-  dm.total = total;
-  dm.G = d.G;
-  dm.D = d.D;
-  dm.scale = d.scale;
-  {
-    const int64_t n = total * (d.D / 32) * 4 * 64;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(dq_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dm);
-  }
-  return hipGetLastError();
+  return launch_backward_grads(d, q, k, v, sel, dq, dk, dv, d_o, lse2, Dr, fwd_kv, bwd_kv, sb, dkv_ws,
+                               dq_part, s);
 }
 
 }  // namespace sgqa

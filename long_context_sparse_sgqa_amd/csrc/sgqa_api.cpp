@@ -437,13 +437,24 @@ sgqa_status sgqa_attend(const sgqa_problem* prob, const void* q, const void* k, 
   return ok();
 }
 
-sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k, const void* v,
+}  // extern "C"
+
+namespace {
+
+// sgqa_forward, and with lse_out != NULL its per-row log-sum-exp (range-split path only).
+sgqa_status forward_impl(const sgqa_problem* prob, const void* q, const void* k, const void* v,
                          const void* gate, const void* q_idx, const void* k_idx, void* k_blk,
-                         int32_t* sel_out, void* out, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int32_t* sel_out, void* out, float* lse_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   Derived dv;
   SGQA_CHECK(derive(prob, &dv));
   const sgqa::Dims& d = dv.d;
+  if (lse_out) {
+    SGQA_CHECK(check_ptr(lse_out, "lse_out", 4));
+    if (!sgqa::attend_split_supported(d))
+      return fail(SGQA_ERR_UNSUPPORTED,
+                  "lse output needs the range-split attention (bf16, H = 8, D in {64, 128}, B a multiple of 8)");
+  }
   SGQA_CHECK(check_ptr(q, "q"));
   SGQA_CHECK(check_ptr(k, "k"));
   SGQA_CHECK(check_ptr(v, "v"));
@@ -476,10 +487,32 @@ sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k,
   if (e != hipSuccess) return hip_fail(e, "k/v packing launch");
   SGQA_CHECK(mark_stage(3, s));
   e = sgqa::launch_attend_packed(d, q, k, v, gate, sel, out, attend_ws, s,
-                                 g_stage_armed ? mark_stage_hip : nullptr);
+                                 g_stage_armed ? mark_stage_hip : nullptr, lse_out);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   SGQA_CHECK(mark_stage(6, s));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sgqa_status sgqa_forward(const sgqa_problem* prob, const void* q, const void* k, const void* v,
+                         const void* gate, const void* q_idx, const void* k_idx, void* k_blk,
+                         int32_t* sel_out, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return forward_impl(prob, q, k, v, gate, q_idx, k_idx, k_blk, sel_out, out, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+sgqa_status sgqa_forward_with_lse(const sgqa_problem* prob, const void* q, const void* k,
+                                  const void* v, const void* gate, const void* q_idx,
+                                  const void* k_idx, void* k_blk, int32_t* sel_out, void* out,
+                                  float* lse_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!lse_out) return fail(SGQA_ERR_NULL, "lse_out is NULL");
+  return forward_impl(prob, q, k, v, gate, q_idx, k_idx, k_blk, sel_out, out, lse_out, workspace,
+                      workspace_bytes, stream);
 }
 
 sgqa_status sgqa_cache_append(const sgqa_problem* prob, const sgqa_cache* cache,
@@ -822,6 +855,36 @@ sgqa_status sgqa_attend_backward(const sgqa_problem* prob, const void* q, const 
                 workspace_bytes);
   hipError_t e = sgqa::launch_attend_backward(d.d, q, k, v, gate, sel, dout, dq, dk, dv, dgate,
                                               workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
+}
+
+sgqa_status sgqa_attend_backward_with_lse(const sgqa_problem* prob, const void* q, const void* k,
+                                          const void* v, const void* gate, const int32_t* sel,
+                                          const void* out, const float* lse, const void* dout,
+                                          void* dq, float* dk, float* dv, void* dgate,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  Derived d;
+  size_t need;
+  SGQA_CHECK(derive_backward(prob, &d, &need));
+  SGQA_CHECK(check_ptr(q, "q"));
+  SGQA_CHECK(check_ptr(k, "k"));
+  SGQA_CHECK(check_ptr(v, "v"));
+  SGQA_CHECK(check_ptr(gate, "gate"));
+  SGQA_CHECK(check_ptr(sel, "sel"));
+  SGQA_CHECK(check_ptr(out, "out"));
+  SGQA_CHECK(check_ptr(lse, "lse", 4));
+  SGQA_CHECK(check_ptr(dout, "dout"));
+  SGQA_CHECK(check_ptr(dq, "dq"));
+  SGQA_CHECK(check_ptr(dk, "dk"));
+  SGQA_CHECK(check_ptr(dv, "dv"));
+  SGQA_CHECK(check_ptr(dgate, "dgate"));
+  SGQA_CHECK(check_ptr(workspace, "workspace"));
+  if (workspace_bytes < need)
+    return fail(SGQA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
+                workspace_bytes);
+  hipError_t e = sgqa::launch_attend_backward(d.d, q, k, v, gate, sel, dout, dq, dk, dv, dgate,
+                                              workspace, static_cast<hipStream_t>(stream), out, lse);
   if (e != hipSuccess) return hip_fail(e, "attention backward launch");
   return ok();
 }

@@ -119,16 +119,19 @@ hipError_t launch_pack_kv(const Dims& d, const void* k, const void* v, void* wor
 // Optional profiling marker: called with index 4 once the attention inputs are ready (pair-union
 // lists built on the range-split path) and 5 after the main attention kernel.
 using StageMark = hipError_t (*)(int index, hipStream_t s);
+// lse (nullable): per row ln sum_t exp(scale q.k_t), written on the range-split path only
+// (attend_split_supported; hipErrorInvalidValue otherwise).
 hipError_t launch_attend_packed(const Dims& d, const void* q, const void* k, const void* v,
                                 const void* gate, const int32_t* sel, void* out, void* workspace,
-                                hipStream_t s, StageMark mark = nullptr);
+                                hipStream_t s, StageMark mark = nullptr, float* lse = nullptr);
 // With `paged`, K and V come from the paged cache (packed_k / packed_v are ignored) and query
 // positions follow d.seq_len.  With `fp8`, packed_k / packed_v hold fp8 copies
 // (launch_pack_kv_fp8).
 hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_k,
                                const void* gate, const int32_t* sel, void* out,
                                const void* packed_v, void* ws, hipStream_t s, StageMark mark,
-                               const PagedKV* paged = nullptr, const Fp8Scales* fp8 = nullptr);
+                               const PagedKV* paged = nullptr, const Fp8Scales* fp8 = nullptr,
+                               float* lse = nullptr);
 // fp8 e4m3 K and V ([Bt, G, Tk, D] bytes) packed per 8-token unit for the range kernel: bytes of
 // one copy, and the packing of both into `packed` (K copy, then V copy at packed_kv_fp8_bytes / 2).
 size_t packed_kv_fp8_bytes(const Dims& d);
@@ -156,9 +159,12 @@ size_t backward_dkv_bytes(const Dims& d);
 hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, const float* lse2,
                                const float* Dr, const void* k, const void* v, const int32_t* sel,
                                float* dk, float* dv, void* ws, hipStream_t s);
+// With saved_out / saved_lse (the forward's output and natural-log lse per row, both or neither)
+// the softmax statistics come from them instead of a forward recompute.
 hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, const void* v,
                                   const void* gate, const int32_t* sel, const void* dout, void* dq,
-                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s);
+                                  float* dk, float* dv, void* dgate, void* ws, hipStream_t s,
+                                  const void* saved_out = nullptr, const float* saved_lse = nullptr);
 // Both of the above.
 hipError_t launch_attend(const Dims& d, const void* q, const void* k, const void* v,
                          const void* gate, const int32_t* sel, void* out, void* workspace,

@@ -21,4 +21,5 @@ from .sgqa_oracle import (  # noqa: F401
     window_rows,
     e4m3_decode,
     attention_backward,
+    attention_lse,
 )

@@ -305,6 +305,32 @@ def attention_backward(inputs, sel, dout, block: int, scale: float):
     return dq, dk, dv, dgate
 
 
+def attention_lse(inputs, sel, block: int, scale: float, rows):
+    """Softmax normaliser of every attention row for the listed query tokens: per (b, i, g, head)
+    ln sum_t exp(scale q.k_t) over the attended tokens t (those of the selected blocks at or before
+    the query's position), the quantity a training forward keeps for its backward (training at
+    long context: Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성").
+    inputs: q, k as for forward_rows; sel [Bt, Tq, G, n_sel]; rows: query token indices.
+    Returns float64 [Bt, len(rows), G, H] (max-shifted sum, so large logits do not overflow)."""
+    q, k = inputs["q"], inputs["k"]
+    sel = np.asarray(sel)
+    bt, t_q, G, h, _ = q.shape
+    t_kv = k.shape[2]
+    pos = query_positions(t_q, t_kv)
+    out = np.zeros((bt, len(rows), G, h))
+    for b in range(bt):
+        for r, i in enumerate(rows):
+            p = int(pos[i])
+            for g in range(G):
+                toks = attended_tokens(sel[b, i, g], block, p, t_kv)
+                kk = _rows64(k, b, g, toks)                            # [n, d]
+                qq = _np64(q[b, i, g])                                 # [h, d]
+                s = scale * (qq @ kk.T)                                # [h, n]
+                m = s.max(axis=1, keepdims=True)
+                out[b, r, g] = (m[:, 0] + np.log(np.exp(s - m).sum(axis=1)))
+    return out
+
+
 def window_rows(inputs, window: int, scale: float, rows):
     """Gated sliding-window attention (the efficient layers the pages interleave three to one with
     Sparse GQA; Step 5 Preview summary on mo.ai.kr, section "모델 구조와 학습 안정성").  The pages

@@ -529,3 +529,62 @@ def test_attention_backward_single_token_closed_form():
     assert np.abs(dq).max() == 0.0 and np.abs(dk).max() == 0.0
     np.testing.assert_allclose(dv[0, 0, 0], (0.5 * sg).sum(axis=0), rtol=0, atol=1e-15)
     np.testing.assert_allclose(dgate[0, 0, 0], 0.5 * v0[None, :] * sg * (1 - sg), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------------------------
+# softmax normaliser (log-sum-exp) a training forward keeps for the backward
+# ----------------------------------------------------------------------------------------------
+def test_lse_equals_masked_torch_logsumexp():
+    """torch.logsumexp (fp64) of the scaled logits under the selection's token mask, -inf
+    elsewhere, equals the oracle's per-row normaliser."""
+    w, inp = generate_small(t_q=20, t_kv=52, groups=2, heads=3, head_dim=8, index_dim=4, block=4,
+                            topk=16, seed=41)
+    sel, _, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    rows = list(range(w.t_q))
+    lse = oracle.attention_lse(inp, sel, w.block, w.softmax_scale, rows)
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv)
+    q64, k64 = inp["q"].to(torch.float64), inp["k"].to(torch.float64)
+    for g in range(w.groups):
+        mask = torch.zeros(w.t_q, w.t_kv, dtype=torch.bool)
+        for i in range(w.t_q):
+            toks = oracle.attended_tokens(sel[0, i, g], w.block, int(pos[i]), w.t_kv)
+            mask[i, torch.from_numpy(toks)] = True
+        s = w.softmax_scale * torch.einsum("ihd,td->iht", q64[0, :, g], k64[0, g])
+        s = s.masked_fill(~mask[:, None, :], float("-inf"))
+        ref = torch.logsumexp(s, dim=-1).numpy()
+        np.testing.assert_allclose(lse[0, :, g], ref, rtol=0, atol=1e-12)
+
+
+def test_lse_closed_forms():
+    """q = 0: every logit is 0, so lse = ln(number of attended tokens); a query at position 0
+    attends token 0 only, so lse = scale q.k_0."""
+    w, inp = generate_small(t_q=12, t_kv=12, groups=1, heads=2, head_dim=8, index_dim=4, block=4,
+                            topk=64, seed=42)                         # dense: every past token
+    sel, _, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    zero = dict(inp, q=torch.zeros_like(inp["q"]))
+    lse0 = oracle.attention_lse(zero, sel, w.block, w.softmax_scale, list(range(w.t_q)))
+    expect = np.log(np.arange(1, w.t_q + 1, dtype=np.float64))        # query i attends 0..i
+    np.testing.assert_allclose(lse0[0, :, 0], np.repeat(expect[:, None], 2, axis=1), rtol=0,
+                               atol=1e-14)
+    lse = oracle.attention_lse(inp, sel, w.block, w.softmax_scale, [0])
+    q0 = inp["q"].to(torch.float64).numpy()[0, 0, 0]                  # [h, d]
+    k0 = inp["k"].to(torch.float64).numpy()[0, 0, 0]
+    np.testing.assert_allclose(lse[0, 0, 0], w.softmax_scale * (q0 @ k0), rtol=0, atol=1e-14)
+
+
+def test_lse_normalises_the_attention():
+    """sum_t exp(s_t - lse) = 1, and sum_t exp(s_t - lse) v_t is the ungated attention output."""
+    w, inp = generate_small(t_q=9, t_kv=40, groups=2, heads=2, head_dim=8, index_dim=4, block=4,
+                            topk=12, seed=43)
+    sel, out, _ = oracle.forward(inp, w.block, w.topk, w.softmax_scale)
+    lse = oracle.attention_lse(inp, sel, w.block, w.softmax_scale, list(range(w.t_q)))
+    pos = np.arange(w.t_kv - w.t_q, w.t_kv)
+    q, k, v = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v"))
+    sg = torch.sigmoid(inp["gate"].to(torch.float64)).numpy()
+    for i in range(w.t_q):
+        for g in range(w.groups):
+            toks = oracle.attended_tokens(sel[0, i, g], w.block, int(pos[i]), w.t_kv)
+            p = np.exp(w.softmax_scale * (q[0, i, g] @ k[0, g, toks].T) - lse[0, i, g][:, None])
+            np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(p @ v[0, g, toks] * sg[0, i, g], out[0, i, g], rtol=0,
+                                       atol=1e-13)
