@@ -926,7 +926,6 @@ struct BwdArgs {
   const float* Dr;
   const bf16_t* kq;        // K, 4-token operand layout (kq_offset)
   const bf16_t* vq;        // V, same layout
-  const bf16_t* kv;        // K, transposed unit layout [unit][d][8 tokens]
   const uint32_t* ulist;
   const int32_t* bounds;
   float* dq_part;          // [gq][R][(D/32) * 4 pieces][64 lanes][4], this range's sum
@@ -941,7 +940,9 @@ struct BwdArgs {
 // each XCD's L2 holds a quarter of a group's K and V), chunks of 4 units as in the forward:
 // S^T = K Q^T and dP^T = V dO^T on the same K-row permutation, P = exp2(S scale log2e - lse2)
 // under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in registers (the forward's P V
-// product with K in the transposed unit layout).  The range's fp32 sum is stored in the
+// product).  The K^T operand (8 keys at one d per lane) is not gathered again: the chunk's K rows,
+// already in registers for S^T, go to the wave's LDS, and gfx950's transposing LDS read returns
+// them 4 rows of one column per lane.  The range's fp32 sum is stored in the
 // accumulator's lane order (coalesced 1 KB pieces); dq_merge_kernel adds the ranges.  dK and dV
 // are accumulated key-major in attend_bwd.hip.
 template <int D>
@@ -950,6 +951,7 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
   constexpr int kRowB = D * 2 + 16;                      // LDS row of Q / dO (bytes)
   __shared__ __attribute__((aligned(16))) unsigned char s_qa[kRangeWaves][32 * kRowB];
   __shared__ __attribute__((aligned(16))) unsigned char s_doa[kRangeWaves][32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_ka[kRangeWaves][32 * kRowB];   // chunk's K
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, h = lane >> 5;
@@ -970,6 +972,7 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
   }
   unsigned char* s_q = s_qa[wave];
   unsigned char* s_do = s_doa[wave];
+  unsigned char* s_k = s_ka[wave];
   const int64_t gq = bg * a.ngroups + qi;
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
@@ -1001,7 +1004,6 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
 
   const BufRsrc krs = make_rsrc(a.kq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
-  const BufRsrc ktrs = make_rsrc(a.kv + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef const __attribute__((address_space(4))) u32x4* ConstQuadPtr;
@@ -1010,25 +1012,30 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
   };
   const int kslot = kq_slot(c), ktok = kq_tok(c);
   struct Ops {
-    bf16x8_t k[D / 16], v[D / 16], kt[D / 16];
+    bf16x8_t k[D / 16], v[D / 16];
   };
   auto load_ops = [&](int cpos, uint32_t* ent4, Ops& R) {
     const u32x4 w = *((ConstQuadPtr)(list + cpos));
 #pragma unroll
     for (int j = 0; j < 4; ++j) ent4[j] = cpos < e1 ? w[j] : 0u;
     const int u = static_cast<int>(pick4(ent4, kslot) & kUnitMask);
-    const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
-    const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
       R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
       R.v[kc] = buffer_load_bf16x8(vrs, kq_offset(u, D, kc, ktok, h));
     }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      R.kt[2 * dt] = buffer_load_bf16x8(ktrs, (ua * D + 32 * dt + c) * 16);
-      R.kt[2 * dt + 1] = buffer_load_bf16x8(ktrs, (ub * D + 32 * dt + c) * 16);
-    }
+  };
+  // K^T operand of unit slot `sl` at d = 32 dt + c: the slot's 8 token rows of one column, as two
+  // transposing reads of 4 rows (16-lane group lane i reads row 4 half + i / 4 of the slot at
+  // columns 32 dt + 16 ((lane / 16) % 2) + 4 (i % 4) .. + 3, and receives column 32 dt + c)
+  const int gi = lane & 15, gh = (lane >> 4) & 1;
+  auto kt_operand = [&](int sl, int dt) -> bf16x8_t {
+    const unsigned char* p = s_k + (8 * sl + (gi >> 2)) * kRowB + 2 * (32 * dt + 16 * gh + 4 * (gi & 3));
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* LdsS16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(p + 4 * kRowB));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto row_mask = [&](uint32_t ent) -> uint32_t {
     const bool chose = (ent >> (kChoseShift + trow)) & 1u;
@@ -1059,10 +1066,15 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
       dsv[i] = p * (dp[i] - D_c);
     }
     const bf16x8_t da = pack8_bf16(dsv), db = pack8_bf16(dsv + 8);
+    // the chunk's K rows (lane (c, h): row 8 slot + token of A row c, d = 16 kc + 8 h .. + 8) to
+    // LDS; this wave alone reads them, after these writes in program order
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      *reinterpret_cast<bf16x8_t*>(s_k + (8 * kslot + ktok) * kRowB + 2 * (16 * kc + 8 * h)) = R.k[kc];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      accq[dt] = mfma32x32x16(R.kt[2 * dt], da, accq[dt]);
-      accq[dt] = mfma32x32x16(R.kt[2 * dt + 1], db, accq[dt]);
+      accq[dt] = mfma32x32x16(kt_operand(h, dt), da, accq[dt]);
+      accq[dt] = mfma32x32x16(kt_operand(2 + h, dt), db, accq[dt]);
     }
   };
 
@@ -1370,7 +1382,6 @@ static hipError_t launch_backward_grads(const Dims& d, const void* q, const void
   const int64_t ng = (d.Tq + kTok - 1) / kTok;
   const int64_t total = d.Bt * d.G * ng;
   const int umax = static_cast<int>(units_per_query(d));
-  const size_t pkv = packed_kv_quad_bytes(d);
   hipError_t e = launch_backward_dkv(d, q, d_o, lse2, Dr, k, v, sel, dk, dv, dkv_ws, s);
   if (e != hipSuccess) return e;
   BwdArgs ba;
@@ -1380,7 +1391,6 @@ static hipError_t launch_backward_grads(const Dims& d, const void* q, const void
   ba.Dr = Dr;
   ba.kq = reinterpret_cast<const bf16_t*>(fwd_kv);
   ba.vq = reinterpret_cast<const bf16_t*>(bwd_kv);
-  ba.kv = reinterpret_cast<const bf16_t*>(bwd_kv + pkv / 2);
   ba.ulist = sb.ulist;
   ba.bounds = sb.bounds;
   ba.dq_part = dq_part;
@@ -1431,7 +1441,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   const size_t pkv = packed_kv_quad_bytes(d);
   char* p = static_cast<char*>(ws);
   char* fwd_kv = p;                  // K in the operand layout, V transposed (the forward's copies)
-  char* bwd_kv = p + pkv;            // V in the operand layout, K transposed
+  char* bwd_kv = p + pkv;            // V in the operand layout (and K transposed, unused)
   char* split = bwd_kv + pkv;
   const size_t rows = static_cast<size_t>(d.Bt * d.Tq * d.G) * 8;
   float* lse2 = reinterpret_cast<float*>(split + attend_split_bytes(d));
