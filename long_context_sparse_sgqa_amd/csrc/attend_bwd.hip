@@ -20,9 +20,10 @@
 // memory once, row-major, into LDS: the first products read them row by row, the second read 4
 // heads at one d per lane through gfx950's transposing LDS read.  The next step's rows are loaded
 // into registers while the current step is computed, then written to the other LDS buffer.
-// Which tokens selected which unit comes from a bitmap per (sequence, group, unit) over the query
-// tokens, built from the selection with atomic ORs (the result does not depend on their order);
-// the tokens are walked in increasing order, so dK and dV are the same bits on every run.
+// Which tokens selected which unit comes from bitmaps over the query tokens, word-major (for each
+// 32-token word, one word per unit), built per word in LDS from the 32 tokens' selections (OR
+// does not depend on the order) and written out whole; the tokens are walked in increasing
+// order, so dK and dV are the same bits on every run.
 #include "device_common.h"
 #include "sgqa_internal.h"
 
@@ -32,33 +33,44 @@ namespace {
 constexpr int kH = 8;          // heads per group (the split kernels' shape)
 
 // ------------------------------------------------------------------------------------------------
-// selection -> per-unit token bitmaps
+// selection -> token bitmaps per unit, word-major: bm[b, g, w, u] has bit i set when query token
+// 32 w + i selected a block holding unit u (rows of NU4 = NU rounded up to 4 words)
 // ------------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) fill_u32x4_zero_kernel(uint4* p, int64_t n4) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
+constexpr int kMarkTile = 16384;        // units per workgroup: a 64 KiB LDS row of words
 
-// One thread per selection entry: every unit of a selected block gets the query token's bit.
+// One workgroup per (sequence, group, word w, tile of units): the 32 tokens' selections set bits
+// in an LDS copy of the row with LDS atomic ORs (the result does not depend on their order), and
+// the row is written out whole, coalesced: no global atomics and no separate zero fill.
 __global__ void __launch_bounds__(256) mark_units_kernel(const int32_t* __restrict__ sel,
                                                          uint32_t* __restrict__ bm, int64_t Tq,
-                                                         int64_t NU, int64_t W, int G, int NS,
-                                                         int U, int64_t total) {
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < total;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int32_t blk = sel[id];
+                                                         int64_t NU, int64_t NU4, int64_t W, int G,
+                                                         int NS, int U, int tiles) {
+  __shared__ uint32_t row[kMarkTile];
+  const int64_t id = blockIdx.x;
+  const int tile = static_cast<int>(id % tiles);
+  const int64_t bgw = id / tiles;
+  const int64_t w = bgw % W, bg = bgw / W;
+  const int g = static_cast<int>(bg % G);
+  const int64_t b = bg / G;
+  const int64_t u0 = static_cast<int64_t>(tile) * kMarkTile;
+  const int n = static_cast<int>(NU4 - u0 < kMarkTile ? NU4 - u0 : kMarkTile);
+  for (int x = threadIdx.x; x < n; x += 256) row[x] = 0u;
+  __syncthreads();
+  // 32 tokens x NS entries; consecutive threads take consecutive entries of one token
+  for (int e = threadIdx.x; e < 32 * NS; e += 256) {
+    const int i = e / NS, j = e - i * NS;
+    const int64_t t = 32 * w + i;
+    if (t >= Tq) continue;
+    const int32_t blk = sel[((b * Tq + t) * G + g) * NS + j];
     if (blk < 0) continue;
-    const int64_t row = id / NS;                 // (b, i, g)
-    const int g = static_cast<int>(row % G);
-    const int64_t bi = row / G;
-    const int64_t i = bi % Tq, b = bi / Tq;
-    const uint32_t bit = 1u << (i & 31);
-    for (int u = 0; u < U; ++u) {
-      const int64_t unit = static_cast<int64_t>(blk) * U + u;
-      if (unit < NU) atomicOr(bm + ((b * G + g) * NU + unit) * W + (i >> 5), bit);
+    for (int uu = 0; uu < U; ++uu) {
+      const int64_t unit = static_cast<int64_t>(blk) * U + uu - u0;
+      if (unit >= 0 && unit < n && unit + u0 < NU) atomicOr(&row[unit], 1u << i);
     }
   }
+  __syncthreads();
+  uint32_t* dst = bm + (bg * W + w) * NU4 + u0;
+  for (int x = threadIdx.x; x < n; x += 256) dst[x] = row[x];
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -71,10 +83,10 @@ struct DkvArgs {
   const float* Dr;        // dO . O per row
   const bf16_t* k;        // [Bt, G, Tk, D]
   const bf16_t* v;
-  const uint32_t* bm;     // [Bt, G, NU, W]
+  const uint32_t* bm;     // [Bt, G, W, NU4] (word-major)
   float* dk;              // [Bt, G, Tk, D]
   float* dv;
-  int64_t Tq, Tk, NU, pos0, W, nchunks, total;
+  int64_t Tq, Tk, NU, NU4, pos0, W, nchunks, total;
   int G;
   float scale_log2e, scale;
 };
@@ -241,23 +253,38 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
 
   // Query tokens that can select a unit of this chunk have position >= its first key.  The four
-  // units' bitmap words are read with scalar loads; the tokens are taken in increasing order, four
-  // per step (unused slots repeat slot 0's token with no unit selected: they add nothing).
-  typedef const __attribute__((address_space(4))) uint32_t* ConstU32Ptr;
+  // units' words of each token word are one 16-byte scalar load (units past NU read 0); the
+  // tokens are taken in increasing order, four per step (unused slots repeat slot 0's token with
+  // no unit selected: they add nothing).
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) u32x4v* ConstU32x4Ptr;
   const int64_t first = chunk * 32 - a.pos0;
-  const uint32_t* bmc = a.bm + (bg * a.NU + chunk * 4) * a.W;
-  const int nunits = static_cast<int>(a.NU - chunk * 4 < 4 ? a.NU - chunk * 4 : 4);
+  const uint32_t* bmc = a.bm + bg * a.W * a.NU4 + chunk * 4;
   int64_t w_next = first > 0 ? (first >> 5) : 0;      // next bitmap word to read
   int64_t w_cur = 0;                                   // word the bits in `any` belong to
   uint32_t wd[4] = {0u, 0u, 0u, 0u};
   uint32_t any = 0u;
+  // the next 4 token words' unit words, loaded together (four independent scalar loads) so that
+  // the scan waits for memory once per 4 words rather than once per word
+  u32x4v look[4];
+  int look_i = 4;
+  auto refill = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      look[k] = w_next + k < a.W ? *((ConstU32x4Ptr)(bmc + (w_next + k) * a.NU4)) : u32x4v{0u, 0u, 0u, 0u};
+    look_i = 0;
+  };
   auto next_step = [&](int32_t* tok, uint32_t* msk) __attribute__((always_inline)) -> int {
     int fill = 0;
     while (fill < 4) {
       while (any == 0u && w_next < a.W) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          wd[u] = u < nunits ? *((ConstU32Ptr)(bmc + u * a.W + w_next)) : 0u;
+        if (look_i == 4) refill();
+        const u32x4v q4 = look_i == 0 ? look[0] : (look_i == 1 ? look[1] : (look_i == 2 ? look[2] : look[3]));
+        ++look_i;
+        wd[0] = q4[0];
+        wd[1] = q4[1];
+        wd[2] = q4[2];
+        wd[3] = q4[3];
         any = wd[0] | wd[1] | wd[2] | wd[3];
         w_cur = w_next++;
       }
@@ -327,39 +354,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
 }
 
-unsigned grid_for(int64_t total) {
-  int64_t blocks = (total + 255) / 256;
-  if (blocks < 1) blocks = 1;
-  if (blocks > 65536) blocks = 65536;
-  return static_cast<unsigned>(blocks);
-}
-
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
 size_t backward_dkv_bytes(const Dims& d) {
-  const int64_t W = (d.Tq + 31) / 32;
-  const size_t bm = static_cast<size_t>(d.Bt * d.G * d.NU * W) * sizeof(uint32_t);
+  const int64_t W = (d.Tq + 31) / 32, NU4 = (d.NU + 3) / 4 * 4;
+  const size_t bm = static_cast<size_t>(d.Bt * d.G * W * NU4) * sizeof(uint32_t);
   return round256(bm);
 }
 
 hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, const float* lse2,
                                const float* Dr, const void* k, const void* v, const int32_t* sel,
                                float* dk, float* dv, void* ws, hipStream_t s) {
-  const int64_t W = (d.Tq + 31) / 32;
-  const size_t bm_bytes = round256(static_cast<size_t>(d.Bt * d.G * d.NU * W) * sizeof(uint32_t));
+  const int64_t W = (d.Tq + 31) / 32, NU4 = (d.NU + 3) / 4 * 4;
   uint32_t* bm = static_cast<uint32_t*>(ws);
-
-  const int64_t n4 = static_cast<int64_t>(bm_bytes / 16);
-  hipLaunchKernelGGL(fill_u32x4_zero_kernel, dim3(grid_for(n4)), dim3(256), 0, s,
-                     reinterpret_cast<uint4*>(bm), n4);
+  const int tiles = static_cast<int>((NU4 + kMarkTile - 1) / kMarkTile);
+  const int64_t wgs = d.Bt * d.G * W * tiles;
+  if (wgs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mark_units_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, s, sel, bm,
+                     d.Tq, d.NU, NU4, W, d.G, d.NS, d.B / 8, tiles);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t entries = d.Bt * d.Tq * d.G * d.NS;
-  hipLaunchKernelGGL(mark_units_kernel, dim3(grid_for(entries)), dim3(256), 0, s, sel, bm, d.Tq,
-                     d.NU, W, d.G, d.NS, d.B / 8, entries);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   DkvArgs a;
   a.q = static_cast<const bf16_t*>(q);
@@ -374,6 +389,7 @@ hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, co
   a.Tq = d.Tq;
   a.Tk = d.Tk;
   a.NU = d.NU;
+  a.NU4 = NU4;
   a.pos0 = d.pos0;
   a.W = W;
   a.nchunks = (d.NU + 3) / 4;
