@@ -607,19 +607,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(k_op(K, kc), q_operand(kc), s);
     refill();
-    const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
-    // masked scores become -inf: a sign-extended bit field (all ones when the bit is set) selects
-    // between the score and -inf in one bitwise op (two VALU ops per score)
+    const uint32_t mlo = row_mask(pick4(ent4, h)), mhi = row_mask(pick4(ent4, 2 + h));
+    // Values 0..7 of a lane are the 8 keys of one unit, 8..15 those of another, so each half is
+    // wholly attended or wholly masked except for the unit that holds the query's own position
+    // (and a sliding window's first unit).  Without such a partial unit anywhere in the wave, a
+    // half's mask is a choice of its max and of its exp2 bias (-inf: probability 0); otherwise
+    // masked scores become -inf one by one (a sign-extended bit field selects the score or -inf).
+    const bool partial = (mlo != 0u && mlo != 0xffu) || (mhi != 0u && mhi != 0xffu);
+    const bool whole = !__ballot(partial);               // wave-uniform
     float t[16];
+    float mx;
+    if (whole) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(msk), i, 1));
-      t[i] = __uint_as_float((__float_as_uint(s[i]) & m) | (~m & 0xff800000u));
+      for (int i = 0; i < 16; ++i) t[i] = s[i];
+      float mxa = fmaxf(fmaxf(t[0], t[1]), t[2]), mxb = fmaxf(fmaxf(t[8], t[9]), t[10]);
+      mxa = fmaxf(fmaxf(mxa, t[3]), t[4]);
+      mxb = fmaxf(fmaxf(mxb, t[11]), t[12]);
+      mxa = fmaxf(fmaxf(mxa, t[5]), t[6]);
+      mxb = fmaxf(fmaxf(mxb, t[13]), t[14]);
+      mxa = fmaxf(mxa, t[7]);
+      mxb = fmaxf(mxb, t[15]);
+      mx = fmaxf(mlo ? mxa : -__builtin_inff(), mhi ? mxb : -__builtin_inff());
+    } else {
+      const uint32_t msk = mlo | (mhi << 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(msk), i, 1));
+        t[i] = __uint_as_float((__float_as_uint(s[i]) & m) | (~m & 0xff800000u));
+      }
+      mx = fmaxf(fmaxf(t[0], t[1]), t[2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, t[i]), t[i + 1]);
+      mx = fmaxf(mx, t[15]);
     }
-    float mx = fmaxf(fmaxf(t[0], t[1]), t[2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, t[i]), t[i + 1]);
-    mx = fmaxf(mx, t[15]);
     mx = max_with_other_half(mx);
     const float m_new = fmaxf(m_run, mx * a.scale_log2e);
     if (__ballot(m_new > m_run + kLazyRescaleLog2)) {   // a row's max grew by > margin: rescale all
@@ -629,9 +649,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
       m_run = m_new;
     }
+    // exp2 bias of each half: -m_run, or -inf for a masked half on the whole-unit path (the
+    // per-score path has already put -inf into the masked scores)
+    const float blo = (!whole || mlo) ? -m_run : -__builtin_inff();
+    const float bhi = (!whole || mhi) ? -m_run : -__builtin_inff();
     float pv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(t[i], a.scale_log2e, -m_run));
+    for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(t[i], a.scale_log2e, i < 8 ? blo : bhi));
     const bf16x8_t pa = pack8_bf16(pv), pb = pack8_bf16(pv + 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
