@@ -101,3 +101,39 @@ def test_saved_backward_32k_sampled_rows_and_sums():
     assert err_k <= 2e-2 * float(dk.double().abs().sum(dim=2).max())
     del x, out, sel, lse, dq, dk, dv, dgate
     torch.cuda.empty_cache()
+
+
+def test_backward_long_context_every_row():
+    """524 288 keys (the group lists' four-word bitmap scans, 65 536 units per group): both
+    backward entry points against the oracle on every dq and dgate row and on every element of dk
+    and dv (keys no query selected must come out exactly 0)."""
+    t_q, t_kv, G, B, k = 64, 524288, 2, 8, 4096
+    say(f"case: backward at t_kv={t_kv}, t_q={t_q}")
+    w, x = generate_small(t_q=t_q, t_kv=t_kv, groups=G, heads=8, head_dim=128, index_dim=128,
+                          block=B, topk=k, dtype="bf16", index_dtype="bf16", scaled_qkv=True,
+                          needles=2, seed=29, device="cuda")
+    prob = sg.Problem.from_workload(w)
+    out, sel, lse = sg.forward_with_lse(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"],
+                                        x["k_idx"])
+    g = torch.Generator(device="cuda").manual_seed(11)
+    dout = torch.randn(x["q"].shape, generator=g, device="cuda").to(torch.bfloat16)
+    grads = {
+        "recompute": sg.attend_backward(prob, x["q"], x["k"], x["v"], x["gate"], sel, dout),
+        "saved lse": sg.attend_backward_with_lse(prob, x["q"], x["k"], x["v"], x["gate"], sel, out,
+                                                 lse, dout),
+    }
+    torch.cuda.synchronize()
+    xc = {n: x[n].cpu() for n in ("q", "k", "v", "gate")}
+    sel_c = sel.cpu().numpy()
+    check_lse("lse", lse, oracle.attention_lse(xc, sel_c, B, w.softmax_scale, list(range(t_q))))
+    r_dq, r_dk, r_dv, r_dg = oracle.attention_backward(xc, sel_c, dout.cpu(), B, w.softmax_scale)
+    for name, (dq, dk, dv, dgate) in grads.items():
+        say(f"  {name}:")
+        check("dq", dq, r_dq)
+        check("dk", dk, r_dk)
+        check("dv", dv, r_dv)
+        check("dgate", dgate, r_dg)
+        untouched = torch.from_numpy((r_dv == 0).all(axis=-1))           # [Bt, G, Tk]
+        assert bool((dv.cpu()[untouched] == 0).all()) and bool((dk.cpu()[untouched] == 0).all())
+    del x, out, sel, lse, grads
+    torch.cuda.empty_cache()
