@@ -789,8 +789,10 @@ __global__ void __launch_bounds__(256) merge_ranges_kernel(MergeArgs a) {
     const int64_t pb = (gq * kRanges + r) * 32 + row;
     const float w = ml[r].y * __builtin_amdgcn_exp2f(ml[r].x - mx);   // partial sum at the common max
     L += w;
-    const uint4 pw = *reinterpret_cast<const uint4*>(a.part_o + pb * a.D + d0);
-    const uint32_t pv[4] = {pw.x, pw.y, pw.z, pw.w};
+    // each partial is read exactly once, so it is loaded with the streaming (non-temporal) hint
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 pw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + pb * a.D + d0));
+    const uint32_t pv[4] = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       o[2 * j] += bf16_to_f32(static_cast<bf16_t>(pv[j] & 0xffffu)) * w;
