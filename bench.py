@@ -39,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+# L2 read bandwidth, derived: 8 XCDs x 16 channels x 128 B per clock at 2.4 GHz
+PEAK_L2_BYTES = 8 * 16 * 128 * 2.4e9
 STAGES = ("compress", "index_topk", "pack_kv", "attn_lists", "attention", "attn_merge")
 N_MARKS = len(STAGES) + 1
 
@@ -821,6 +823,13 @@ def main():
         if un is not None and "kernel" in roof and roof["kernel"].startswith("attend_range"):
             roof["issued_flops"] = un["issued_flops"]
             roof["issued_frac"] = un["issued_flops"] / (stage_ms["attention"] * 1e-3) / PEAK_BF16_FLOPS
+            # what bounds the kernel: its K/V gathers (K and V of every unit of every issued chunk)
+            # through the L2, against the L2's derived read bandwidth
+            gathered = un["issued_chunks"] * 4 * 8 * w.head_dim * 2 * 2
+            rate = gathered / (stage_ms["attention"] * 1e-3)
+            roof["gathered_bytes"] = gathered
+            roof["gather_TBps"] = rate / 1e12
+            roof["gather_frac_of_l2_peak"] = rate / PEAK_L2_BYTES
 
     rec = {
         "metric": "Sparse-GQA prefill query-tokens/s at 128K ctx (index+topk+attn); % roofline"
