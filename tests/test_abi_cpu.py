@@ -103,6 +103,54 @@ def test_null_misaligned_and_workspace_errors(lib):
     assert lib.sgqa_topk(None, good, good, None) == ERR_NULL
 
 
+def test_training_entry_points_reject_before_device_access(lib):
+    """sgqa_forward_with_lse, sgqa_attend_backward and sgqa_attend_backward_with_lse: bogus (never
+    dereferenced) addresses; every null argument, a misaligned lse and a short workspace are
+    rejected on the host, and so are problems outside the backward's kernels."""
+    good = 0x10000
+    P = sg.Problem(1, 64, 64, 2, 8, 128, 128, 8, 32)._c()
+    need = ctypes.c_size_t()
+    assert lib.sgqa_attend_backward_workspace_size(ctypes.byref(P), ctypes.byref(need)) == OK
+    assert need.value > 0
+    # q k v gate sel dout dq dk dv dgate workspace
+    for i in range(11):
+        args = [good] * 11
+        args[i] = None
+        assert lib.sgqa_attend_backward(ctypes.byref(P), *args, need.value, None) == ERR_NULL, i
+    assert lib.sgqa_attend_backward(ctypes.byref(P), *([good] * 11), need.value - 1, None) == ERR_WORKSPACE
+    # q k v gate sel out lse dout dq dk dv dgate workspace
+    for i in range(13):
+        args = [good] * 13
+        args[i] = None
+        assert lib.sgqa_attend_backward_with_lse(ctypes.byref(P), *args, need.value, None) == ERR_NULL, i
+    args = [good] * 13
+    args[6] = good + 2                                   # lse: fp32, 4-byte aligned
+    assert lib.sgqa_attend_backward_with_lse(ctypes.byref(P), *args, need.value, None) == ERR_ALIGN
+    assert lib.sgqa_attend_backward_with_lse(ctypes.byref(P), *([good] * 13), need.value - 1,
+                                             None) == ERR_WORKSPACE
+    for kw in (dict(heads_per_group=4), dict(block=4), dict(head_dim=96)):
+        base = dict(batch=1, t_q=64, t_kv=64, kv_groups=2, heads_per_group=8, head_dim=128,
+                    index_dim=128, block=8, topk_tokens=32)
+        base.update(kw)
+        Pu = sg.Problem(**base)._c()
+        assert lib.sgqa_attend_backward_workspace_size(ctypes.byref(Pu), ctypes.byref(need)) in (
+            ERR_UNSUPPORTED, ERR_SHAPE), kw
+    # forward with lse: q k v gate q_idx k_idx k_blk sel out lse workspace
+    Pf = sg.Problem(1, 64, 64, 2, 8, 128, 128, 8, 32)
+    ws = sg.sizes(Pf)["forward_workspace_bytes"]
+    args = [good] * 11
+    args[9] = None
+    assert lib.sgqa_forward_with_lse(ctypes.byref(Pf._c()), *args, ws, None) == ERR_NULL
+    args[9] = good + 2
+    assert lib.sgqa_forward_with_lse(ctypes.byref(Pf._c()), *args, ws, None) == ERR_ALIGN
+    args[9] = good
+    assert lib.sgqa_forward_with_lse(ctypes.byref(Pf._c()), *args, 16, None) == ERR_WORKSPACE
+    # the normaliser needs the range-split attention: B = 4 takes the pair kernel instead
+    Pb = sg.Problem(1, 64, 64, 2, 8, 128, 128, 4, 32)
+    wsb = sg.sizes(Pb)["forward_workspace_bytes"]
+    assert lib.sgqa_forward_with_lse(ctypes.byref(Pb._c()), *([good] * 11), wsb, None) == ERR_UNSUPPORTED
+
+
 # ----------------------------------------------------------------------------------------------
 # decode over a paged cache: host-side validation and sizes
 # ----------------------------------------------------------------------------------------------
