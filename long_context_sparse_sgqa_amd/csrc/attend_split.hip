@@ -77,13 +77,22 @@ struct UnionArgs {
   int balance;
 };
 
+// LDS words per wave of the group-list kernel: the four bitmaps and the list, one after the other,
+// or overlapping when the bitmaps' words are held in registers.
+__host__ __device__ constexpr int64_t union_lds_words(int64_t words, int64_t stride, bool overlap) {
+  return overlap ? (kTok * words > stride ? kTok * words : stride) : kTok * words + stride;
+}
+
 // Each selected block sets its units' bits in the token's LDS bitmap (units past the token's own
 // unit are left out: t <= p); one scan over the words then emits the union in ascending unit order
 // with every token's chosen bit.
 // kVec4: the bitmap scans read 4 words per token at a time (16-byte LDS reads).  That pays for
 // long contexts, where the bitmaps' LDS size leaves few waves per CU to hide each read's latency;
 // with short bitmaps and many waves the scalar scans are faster.
-template <bool kVec4>
+// kRegW > 0 (scalar scans, at most 64 kRegW words per token): each lane keeps its words of the four
+// bitmaps in registers from the counting pass on, so the list is built in LDS over the bitmaps
+// and a wave needs only max(4 words, list stride) words of LDS.
+template <bool kVec4, int kRegW>
 __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
@@ -92,8 +101,8 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   if (gq >= a.total) return;                          // whole wave; no workgroup barriers below
   // this wave's LDS: the 4 tokens' bitmaps, then the list being built (copied out at the end)
   const int64_t stride = list_stride(a.umax);
-  uint32_t* bm = lds + static_cast<size_t>(wave) * (kTok * a.words + stride);
-  uint32_t* stg = bm + kTok * a.words;
+  uint32_t* bm = lds + static_cast<size_t>(wave) * union_lds_words(a.words, stride, kRegW > 0);
+  uint32_t* stg = kRegW > 0 ? bm : bm + kTok * a.words;
   const int64_t qi = gq % a.ngroups;
   const int64_t bg = gq / a.ngroups;
   const int64_t g = bg % a.G, b = bg / a.G;
@@ -191,6 +200,7 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
       below[r] += __popc(x & m);
     }
   };
+  uint32_t xr[kTok][kRegW > 0 ? kRegW : 1];
   if constexpr (kVec4) {
     for (int w4 = w0; w4 < w1; w4 += 4) {
       uint32_t xt4[kTok][4];
@@ -203,6 +213,20 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
         count_word(w4 + k, x);
       }
     }
+  } else if constexpr (kRegW > 0) {
+#pragma unroll
+    for (int k = 0; k < kRegW; ++k) {
+      const int w = w0 + k;
+      uint32_t x = 0u;
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        xr[t][k] = w < w1 ? bm[t * a.words + w] : 0u;
+        x |= xr[t][k];
+      }
+      count_word(w, x);
+    }
+    // every lane's words are in registers: the list may now overwrite the bitmaps
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   } else {
     for (int w = w0; w < w1; ++w) {
       uint32_t x = 0u;
@@ -289,6 +313,14 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
         for (int t = 0; t < kTok; ++t) xt[t] = xt4[t][k];
         emit_word(w4 + k, xt);
       }
+    }
+  } else if constexpr (kRegW > 0) {
+#pragma unroll
+    for (int k = 0; k < kRegW; ++k) {
+      uint32_t xt[kTok];
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) xt[t] = xr[t][k];
+      if (w0 + k < w1) emit_word(w0 + k, xt);
     }
   } else {
     for (int w = w0; w < w1; ++w) {
@@ -1175,15 +1207,33 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // that every token's bitmap starts 16-byte aligned.
 int64_t union_words(const Dims& d) { return ((d.NU + 31) / 32 + 3) & ~int64_t(3); }
 
+// Bitmap words each lane holds in registers in the group-list kernel (0: the 16-byte scans of
+// long contexts, whose bitmaps stay in LDS beside the list).
+int union_per_lane(int64_t words) { return words <= 64 * 8 ? 8 : 0; }
+
 int union_waves(const Dims& d) {
   const int64_t words = union_words(d);
-  const int64_t per_wave = (kTok * words + list_stride(static_cast<int>(units_per_query(d)))) *
+  const int64_t per_wave = union_lds_words(words, list_stride(static_cast<int>(units_per_query(d))),
+                                           union_per_lane(words) > 0) *
                            static_cast<int64_t>(sizeof(uint32_t));
   const int64_t fit = (160 * 1024) / per_wave;          // waves whose LDS fits one CU
   // up to 4 waves per workgroup, but small enough that two workgroups share a CU
   if (fit >= 8) return 4;
   if (fit >= 2) return static_cast<int>(fit / 2);
   return static_cast<int>(fit);
+}
+
+void launch_quad_union(const UnionArgs& ua, int64_t total, hipStream_t s) {
+  const int per = union_per_lane(ua.words);
+  const size_t lds = static_cast<size_t>(ua.waves) *
+                     union_lds_words(ua.words, list_stride(ua.umax), per > 0) * sizeof(uint32_t);
+  const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
+  if (per == 8)                                         // contexts up to 128K tokens
+    hipLaunchKernelGGL((quad_union_kernel<false, 8>), ugrid, dim3(64 * ua.waves), lds, s, ua);
+  else if (ua.words >= 2048)                            // contexts of 512K tokens and more
+    hipLaunchKernelGGL((quad_union_kernel<true, 0>), ugrid, dim3(64 * ua.waves), lds, s, ua);
+  else
+    hipLaunchKernelGGL((quad_union_kernel<false, 0>), ugrid, dim3(64 * ua.waves), lds, s, ua);
 }
 
 size_t split_bytes_for(const Dims& d, int umax) {
@@ -1339,12 +1389,7 @@ hipError_t launch_attend_split(const Dims& d, const void* q, const void* packed_
   ua.words = static_cast<int>(union_words(d));
   ua.waves = union_waves(d);
   ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
-  const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
-  const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
-  if (ua.words >= 2048)                                 // contexts of 512K tokens and more
-    hipLaunchKernelGGL(quad_union_kernel<true>, ugrid, dim3(64 * ua.waves), lds, s, ua);
-  else
-    hipLaunchKernelGGL(quad_union_kernel<false>, ugrid, dim3(64 * ua.waves), lds, s, ua);
+  launch_quad_union(ua, total, s);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && mark) e = mark(4, s);
   if (e != hipSuccess) return e;
@@ -1498,12 +1543,7 @@ hipError_t launch_attend_backward(const Dims& d, const void* q, const void* k, c
   ua.words = static_cast<int>(union_words(d));
   ua.waves = union_waves(d);
   ua.balance = ng < kRangeWaves ? 1 : 0;                // as the attention's wave_ranges
-  const size_t lds = static_cast<size_t>(ua.waves) * (kTok * ua.words + list_stride(umax)) * sizeof(uint32_t);
-  const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
-  if (ua.words >= 2048)                                 // contexts of 512K tokens and more
-    hipLaunchKernelGGL(quad_union_kernel<true>, ugrid, dim3(64 * ua.waves), lds, s, ua);
-  else
-    hipLaunchKernelGGL(quad_union_kernel<false>, ugrid, dim3(64 * ua.waves), lds, s, ua);
+  launch_quad_union(ua, total, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (saved_out) {
