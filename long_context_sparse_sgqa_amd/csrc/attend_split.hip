@@ -19,7 +19,9 @@
 //     8-token units, entry = unit | chosen-by-token-t << (27 + t) (B is a multiple of 8, so a unit
 //     is wholly selected by a token or not at all), built through LDS bitmaps into an LDS copy
 //     of the list that is written out coalesced; every range is padded to a multiple of 4
-//     entries and its first entry recorded.
+//     entries and its first entry recorded.  Past 128K tokens (with B = 8 and at most 512
+//     selected blocks) quad_union_merge_kernel builds the same list by merging the tokens'
+//     ascending selections instead of through bitmaps.
 //   attend_range_kernel  one wavefront per (group of 4 tokens, range): the entries inside the
 //     range in chunks of 4 units (32 tokens).  S^T = K Q^T on D/16 MFMAs with the K rows permuted
 //     so that every lane holds the 16 scores of one row for two units; masks, online softmax in
@@ -337,6 +339,134 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // the list (a multiple of 4 entries; both copies 16-byte aligned) with consecutive lanes on
   // consecutive 16-byte pieces
+  {
+    const int n4 = start[kRanges] >> 2;
+    const uint4* src = reinterpret_cast<const uint4*>(stg);
+    uint4* dst = reinterpret_cast<uint4*>(out);
+    for (int j = lane; j < n4; j += 64) dst[j] = src[j];
+  }
+  int32_t* bnd = a.bounds + gq * (kRanges + 1);
+  if (lane <= kRanges) {
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q <= kRanges; ++q) v = q == lane ? start[q] : v;
+    bnd[lane] = v;
+  }
+}
+
+// Long contexts with B = 8 (a block is one unit) and at most 512 selected blocks, ranges of equal
+// unit spans: the union by merging the 4 tokens' selections, which arrive in ascending block
+// order, instead of through bitmaps (which at 1M tokens take 64 KiB of LDS per group of tokens).
+// Lane l owns the units [l u_end / 64, (l + 1) u_end / 64), so lanes 16 r .. 16 r + 15 own range
+// r: it finds each selection's run in its span by binary search, counts the distinct units of
+// the four runs by a 4-way merge, and after a prefix over the lanes merges them again into the
+// LDS copy of the list.  Searches and merges are bounded by the list indices, so any input stays
+// in bounds.
+constexpr int kMergeSel = 512;                  // selected blocks per token held in LDS
+__global__ void __launch_bounds__(256) quad_union_merge_kernel(UnionArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gq = static_cast<int64_t>(blockIdx.x) * a.waves + wave;
+  if (gq >= a.total) return;                          // whole wave; no workgroup barriers below
+  const int64_t stride = list_stride(a.umax);
+  int32_t* L = reinterpret_cast<int32_t*>(lds + static_cast<size_t>(wave) * (kTok * kMergeSel + stride));
+  uint32_t* stg = reinterpret_cast<uint32_t*>(L + kTok * kMergeSel);
+  const int64_t qi = gq % a.ngroups;
+  const int64_t bg = gq / a.ngroups;
+  const int64_t g = bg % a.G, b = bg / a.G;
+  const int64_t tok0 = kTok * qi;
+  const int64_t pos0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq);
+  const int64_t u_end = group_u_end(pos0, tok0, a.Tq);
+  // the selections, blocks past a token's own (or of tokens past Tq, or -1 padding) as INT_MAX
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) {
+    const int64_t tt = tok0 + t < a.Tq ? tok0 + t : tok0;
+    const int32_t* selrow = a.sel + ((b * a.Tq + tt) * a.G + g) * a.NS;
+    const int32_t o_t = static_cast<int32_t>((pos0 + tok0 + t) >> 3);
+#pragma unroll
+    for (int k = 0; k < kMergeSel / 64; ++k) {
+      const int e = lane + 64 * k;
+      const int bk = (e < a.NS && tok0 + t < a.Tq) ? selrow[e] : -1;
+      L[t * kMergeSel + e] = (bk >= 0 && bk <= o_t) ? bk : 0x7fffffff;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // first index of each selection at or above a unit (binary search over the 512 entries)
+  auto lower = [&](int t, int32_t v) {
+    int lo = 0, hi = kMergeSel;
+#pragma unroll 1
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L[t * kMergeSel + mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  const int32_t c0 = static_cast<int32_t>((lane * u_end) >> 6);
+  const int32_t c1 = static_cast<int32_t>(((lane + 1) * u_end) >> 6);
+  int p0[kTok], p1[kTok];
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) {
+    p0[t] = lower(t, c0);
+    p1[t] = lower(t, c1);
+  }
+  // 4-way merge of the lane's runs; `visit(unit, chosen bits)` per distinct unit
+  auto merge = [&](auto visit) {
+    int i[kTok];
+    int32_t hd[kTok];
+#pragma unroll
+    for (int t = 0; t < kTok; ++t) {
+      i[t] = p0[t];
+      hd[t] = i[t] < p1[t] ? L[t * kMergeSel + i[t]] : 0x7fffffff;
+    }
+#pragma unroll 1
+    while (true) {
+      int32_t m = hd[0];
+#pragma unroll
+      for (int t = 1; t < kTok; ++t) m = min(m, hd[t]);
+      if (m == 0x7fffffff) break;
+      uint32_t chose = 0u;
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        if (hd[t] == m) {
+          chose |= 1u << t;
+#pragma unroll 1
+          while (i[t] < p1[t] && L[t * kMergeSel + i[t]] == m) ++i[t];   // duplicates included
+          hd[t] = i[t] < p1[t] ? L[t * kMergeSel + i[t]] : 0x7fffffff;
+        }
+      }
+      visit(static_cast<uint32_t>(m), chose);
+    }
+  };
+  int mine = 0;
+  merge([&](uint32_t, uint32_t) { ++mine; });
+  // lanes 16 r .. 16 r + 15 are range r: the counts below each range start from the lane prefix
+  const int incl = wave_inclusive_scan(mine);
+  const int nu = __builtin_amdgcn_readlane(incl, 63);
+  int pos = incl - mine;
+  int below[kRanges + 1];
+  below[0] = 0;
+#pragma unroll
+  for (int r = 1; r < kRanges; ++r) below[r] = __builtin_amdgcn_readlane(pos, 16 * r);
+  below[kRanges] = nu;
+  int start[kRanges + 1];
+  start[0] = 0;
+#pragma unroll
+  for (int r = 0; r < kRanges; ++r) start[r + 1] = start[r] + ((below[r + 1] - below[r] + 3) & ~3);
+  const int rl = lane >> 4;
+  int shift = 0;
+#pragma unroll
+  for (int q = 0; q < kRanges; ++q) shift = q == rl ? start[q] - below[q] : shift;
+  merge([&](uint32_t u, uint32_t chose) {
+    stg[pos + shift] = u | (chose << kChoseShift);
+    ++pos;
+  });
+  if (lane < 4 * kRanges) {                      // padding entries (unit 0, chosen by none)
+    const int r = lane >> 2, j = start[r] + (below[r + 1] - below[r]) + (lane & 3);
+    if (j < start[r + 1]) stg[j] = 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint32_t* out = a.ulist + gq * stride;
   {
     const int n4 = start[kRanges] >> 2;
     const uint4* src = reinterpret_cast<const uint4*>(stg);
@@ -1225,6 +1355,18 @@ int union_waves(const Dims& d) {
 
 void launch_quad_union(const UnionArgs& ua, int64_t total, hipStream_t s) {
   const int per = union_per_lane(ua.words);
+  if (per == 0 && ua.B == 8 && ua.NS <= kMergeSel && !ua.balance) {
+    // LDS per wave: the 4 selections and the list; 4 waves per workgroup when 8 fit on a CU
+    const int64_t per_wave = (kTok * kMergeSel + list_stride(ua.umax)) * static_cast<int64_t>(sizeof(uint32_t));
+    const int64_t fit = (160 * 1024) / per_wave;
+    const int waves = fit >= 8 ? 4 : (fit >= 2 ? static_cast<int>(fit / 2) : 1);
+    UnionArgs um = ua;
+    um.waves = waves;
+    const dim3 ugrid(static_cast<unsigned>((total + waves - 1) / waves));
+    hipLaunchKernelGGL(quad_union_merge_kernel, ugrid, dim3(64 * waves),
+                       static_cast<size_t>(waves * per_wave), s, um);
+    return;
+  }
   const size_t lds = static_cast<size_t>(ua.waves) *
                      union_lds_words(ua.words, list_stride(ua.umax), per > 0) * sizeof(uint32_t);
   const dim3 ugrid(static_cast<unsigned>((total + ua.waves - 1) / ua.waves));
