@@ -15,8 +15,8 @@
 //   2. filter: every causal score, column tiles of K_blk staged in LDS (double-buffered) and
 //      shared by the 4 waves; the products are taken transposed, so a lane holds one row and four
 //      consecutive blocks of it, and a passing score's slot is the row's count so far plus the
-//      passing scores before it in block order (a cross-lane prefix over the row's 4 lanes): every
-//      row's list is in ascending block order.
+//      passing scores before it in block order (a cross-lane prefix over the row's 4 lanes, taken
+//      for three column steps at once): every row's list is in ascending block order.
 // select kernel (one wave per row): the (NS-1)-th largest key tau by a bitwise search over the
 //   candidates held in registers, then the keys > tau and the lowest-indexed keys == tau, emitted
 //   in block order by a stable compaction of the sorted list (lists appended by several
@@ -370,29 +370,50 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
                                 static_cast<int64_t>(kRows) * a.cap * 8);
   const int r_off = my_local_a * a.cap * 8;
   int r_count = 0;                       // the row's passing scores so far (same in its 4 lanes)
-  // A lane whose slots would run past the capacity stores none of them: its row then counts more
-  // than `cap` candidates and is recomputed exactly.
-  auto append = [&](const f32x4_t& c, int32_t cb, bool check_causal) {
-    bool pass[4];
+  // Appends of kGrp consecutive column steps at once.  Each lane's pass counts of the steps are
+  // packed one byte per step (at most 4 per lane, 16 per row and step: no byte carries into the
+  // next), so one pair of cross-row swaps gives every step's exclusive prefix over the row's 4
+  // lanes and its total.  A row whose list would run past the capacity in the group stores none
+  // of the group's candidates: it then counts more than `cap` and is recomputed exactly.
+  constexpr int kSteps = kCols / 16;
+  constexpr int kGrp = kSteps / 2;
+  auto append_group = [&](const f32x4_t* c, int32_t cb0, bool check_causal) {
+    bool pass[kGrp][4];
+    int nn[kGrp];
+    uint32_t packed = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pass[e] = c[e] >= r_thr;
-      if (check_causal) pass[e] = pass[e] && cb + e < r_o32;
-    }
-    const int n = static_cast<int>(pass[0]) + static_cast<int>(pass[1]) + static_cast<int>(pass[2]) +
-                  static_cast<int>(pass[3]);
-    const auto p16 = __builtin_amdgcn_permlane16_swap(n, n, false, false);   // n of rows lg&~1, lg|1
-    const int pair = static_cast<int>(p16[0] + p16[1]);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);  // pairs 0 and 1
-    int pos = r_count + ((lg & 1) ? static_cast<int>(p16[0]) : 0) + ((lg & 2) ? static_cast<int>(p32[0]) : 0);
-    r_count += static_cast<int>(p32[0] + p32[1]);
-    const bool fits = pos + n <= a.cap;
+    for (int q = 0; q < kGrp; ++q) {
+      nn[q] = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const u32x2_t v = {static_cast<uint32_t>(cb + e), __float_as_uint(c[e])};
-      __builtin_amdgcn_raw_buffer_store_b64(v, crs, pass[e] && fits ? r_off + pos * 8 : 0x7fffffff, 0, 0);
-      pos += static_cast<int>(pass[e]);
+      for (int e = 0; e < 4; ++e) {
+        pass[q][e] = c[q][e] >= r_thr;
+        if (check_causal) pass[q][e] = pass[q][e] && cb0 + 16 * q + e < r_o32;
+        nn[q] += static_cast<int>(pass[q][e]);
+      }
+      packed |= static_cast<uint32_t>(nn[q]) << (8 * q);
     }
+    const auto p16 = __builtin_amdgcn_permlane16_swap(packed, packed, false, false);
+    const uint32_t pair = p16[0] + p16[1];
+    const auto p32 = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+    const uint32_t excl = ((lg & 1) ? p16[0] : 0u) + ((lg & 2) ? p32[0] : 0u);
+    const uint32_t tot = p32[0] + p32[1];
+    uint32_t all = 0u;
+#pragma unroll
+    for (int q = 0; q < kGrp; ++q) all += (tot >> (8 * q)) & 0xffu;
+    const bool fits = r_count + static_cast<int>(all) <= a.cap;
+    int base = r_count;
+#pragma unroll
+    for (int q = 0; q < kGrp; ++q) {
+      int pos = base + static_cast<int>((excl >> (8 * q)) & 0xffu);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x2_t v = {static_cast<uint32_t>(cb0 + 16 * q + e), __float_as_uint(c[q][e])};
+        __builtin_amdgcn_raw_buffer_store_b64(v, crs, pass[q][e] && fits ? r_off + pos * 8 : 0x7fffffff, 0, 0);
+        pos += static_cast<int>(pass[q][e]);
+      }
+      base += static_cast<int>((tot >> (8 * q)) & 0xffu);
+    }
+    r_count = base;
   };
   // Per tile: all products first (LDS reads and MFMAs only), then the next tile's global loads,
   // then the appends (compares, LDS counters, candidate stores), then the staging of the next tile.
@@ -424,7 +445,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     }
     load_tile(t + 1);
 #pragma unroll
-    for (int n = 0; n < kCols / 16; ++n) append(sc[n], col0 + n * 16, check_causal);
+    for (int n = 0; n < kSteps; n += kGrp) append_group(sc + n, col0 + n * 16, check_causal);
     store_tile(buf ^ 1);   // buf ^ 1 was released by the barrier that ended tile t - 1
     __syncthreads();
   };
