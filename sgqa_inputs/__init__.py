@@ -17,7 +17,16 @@ to 1,048,576 tokens.  The pages publish no dataset, so every tensor is synthetic
   every index key of a needle block gets +2 u_g and every index query of group g gets +2 u_g, both
   clamped to [-4, 4], so later queries of group g correlate with that group's needle blocks.
 
-Draw order (one generator, fixed seed): q, k, v, gate, k_idx, q_idx, u, needle blocks.
+* "drift" (the 128k-drift workload only): adjacent tokens' index queries are correlated.  Along
+  the tokens of each (sequence, group), every component of the index query keeps the previous
+  token's value unless it is redrawn, with probability q_idx_redraw; a redrawn component takes the
+  uniform draw above for that token (needle bias included).  The pages' premise for grouping
+  adjacent query tokens is that their selections overlap; with independent queries (every other
+  workload) two tokens share about 142 of their 512 blocks, with q_idx_redraw = 0.05 adjacent
+  tokens share about 370.
+
+Draw order (one generator, fixed seed): q, k, v, gate, k_idx, q_idx, u, needle blocks, then the
+drift's redraw mask (only when q_idx_redraw < 1).
 Large tensors are drawn in slices along their outermost axis so that fp32 temporaries stay small;
 the slicing is part of the recipe, so a given (workload, device, seed) always yields the same bits.
 """
@@ -49,6 +58,7 @@ class Workload:
     needles: int          # planted needle blocks per KV group (0 = none)
     scaled_qkv: bool      # q, k, v drawn as N(0,1)/sqrt(d) when True
     description: str = ""
+    q_idx_redraw: float = 1.0   # per token and component: probability of a fresh index query value
 
     @property
     def num_blocks(self) -> int:
@@ -85,6 +95,12 @@ WORKLOADS: Dict[str, Workload] = {
         block=8, topk=4096, dtype="bf16", index_dtype="bf16", needles=64, scaled_qkv=True,
         description="decode, 4 query tokens (MTP-3) per sequence after 262144 cached tokens, "
                     "64 sequences, 8 KV groups x 8 heads, d=128, bf16, B=8, k=4096"),
+    "128k-drift": Workload(
+        "128k-drift", batch=1, t_q=131072, t_kv=131072, groups=8, heads=8, head_dim=128,
+        index_dim=128, block=8, topk=4096, dtype="bf16", index_dtype="bf16", needles=64,
+        scaled_qkv=True, q_idx_redraw=0.05,
+        description="128K prefill as 128k, with drifting index queries (each component redrawn "
+                    "with probability 0.05 per token): adjacent tokens select overlapping blocks"),
     "1m": Workload(
         "1m", batch=1, t_q=8192, t_kv=1048576, groups=8, heads=8, head_dim=128, index_dim=128,
         block=8, topk=4096, dtype="bf16", index_dtype="bf16", needles=64, scaled_qkv=True,
@@ -182,6 +198,17 @@ def generate(w: Workload, device="cpu", seed: int = 0, sharp: bool = False) -> D
             # every index query of group g: +2 u_g, clamped
             qs = q_idx[:, :, g, :].to(torch.float32) + 2.0 * u[g]
             q_idx[:, :, g, :] = qs.clamp_(-4, 4).to(idt)
+    if w.q_idx_redraw < 1.0:
+        # token i takes, per component, the value drawn at the last token <= i whose component was
+        # redrawn (token 0 always is)
+        redraw = torch.rand((B, Tq, G, Di), generator=gen, device=dev) < w.q_idx_redraw
+        redraw[:, 0] = True
+        tok = torch.arange(Tq, device=dev, dtype=torch.int64).view(1, Tq, 1, 1)
+        src = torch.where(redraw, tok, torch.zeros((), dtype=torch.int64, device=dev))
+        del redraw
+        src = torch.cummax(src, dim=1).values
+        q_idx = torch.gather(q_idx, 1, src)
+        del src
     return {"q": q, "k": k, "v": v, "gate": gate, "q_idx": q_idx, "k_idx": k_idx,
             "needle_blocks": needle_blocks}
 

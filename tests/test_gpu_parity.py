@@ -314,8 +314,10 @@ def test_run_to_run_bitwise():
 # ----------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("name,n_random,sharp", [("32k", 24, False), ("128k", 12, False),
                                                 ("1m", 6, False), ("32k", 24, True),
-                                                ("128k", 12, True), ("1m", 6, True)],
-                         ids=["32k", "128k", "1m", "32k-sharp", "128k-sharp", "1m-sharp"])
+                                                ("128k", 12, True), ("1m", 6, True),
+                                                ("128k-drift", 12, False)],
+                         ids=["32k", "128k", "1m", "32k-sharp", "128k-sharp", "1m-sharp",
+                              "128k-drift"])
 def test_workload_sampled_rows(name, n_random, sharp):
     """Full-size workloads on stratified sampled rows.  The "sharp" variants leave q and k unscaled,
     so the softmax is far from uniform and a wrong weight or a dropped token shows in the output."""
@@ -341,9 +343,10 @@ def test_workload_sampled_rows(name, n_random, sharp):
 
 @pytest.mark.parametrize("t_q", [64, 3])
 def test_long_context_union_every_row(t_q):
-    """Every row at 524 288 keys, where the group lists scan their bitmaps four words at a time
-    (2 048 bitmap words per token).  With t_q = 3 there is one group of tokens, so the attention's
-    waves take its unit ranges and the lists split at equal entry counts.
+    """Every row at 524 288 keys.  With t_q = 64 the group lists come from merging the tokens'
+    selections (contexts past 128K tokens); with t_q = 3 there is one group of tokens, so the
+    attention's waves take its unit ranges, the lists split at equal entry counts and they are
+    built through bitmaps scanned four words at a time (2 048 words per token).
 
     q = 0 makes every logit 0, so each output is sigmoid(0) = 0.5 times the mean of v over the
     attended tokens; v is one-hot per token: dim (unit mod 64) and dim 64 + (unit // 64 mod 64).

@@ -38,3 +38,21 @@ def test_workloads_match_descriptions():
     assert WORKLOADS["128k"].num_blocks == 16384
     assert WORKLOADS["1m"].t_kv - WORKLOADS["1m"].t_q == 1040384
     assert WORKLOADS["decode"].t_kv == 262144 + 4 and WORKLOADS["decode"].t_q == 4
+
+
+def test_drifting_index_queries():
+    """q_idx_redraw < 1: along the tokens, a component keeps the previous token's value unless
+    redrawn; the first token is the plain draw, and every other tensor is drawn as without drift."""
+    w = get_workload("tiny").replace(q_idx_redraw=0.05)
+    plain = generate(get_workload("tiny"), seed=3)
+    x = generate(w, seed=3)
+    for n in ("q", "k", "v", "gate", "k_idx"):
+        assert torch.equal(x[n], plain[n]), n
+    q = x["q_idx"]
+    assert torch.equal(q[:, 0], plain["q_idx"][:, 0])
+    same = (q[:, 1:] == q[:, :-1]).double().mean().item()
+    assert 0.9 < same < 0.99                     # about 95 % of components carried over
+    changed = q[:, 1:] != q[:, :-1]
+    # a component that changed takes that token's own plain draw
+    assert torch.equal(q[:, 1:][changed], plain["q_idx"][:, 1:][changed])
+    assert torch.equal(x["q_idx"], generate(w, seed=3)["q_idx"])
