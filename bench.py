@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-sensitivity", dest="sensitivity", action="store_false",
+                    help="128k only: skip the extra timing of the 128k-drift workload (index queries "
+                         "of adjacent tokens correlated), reported under \"sensitivity\"")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a device buffer of this many MiB twice (a "
                          "device-to-device blit of known size, for scaling HBM byte counters)")
@@ -685,6 +688,52 @@ def main_backward(args):
     print(json.dumps(rec), flush=True)
 
 
+def drift_sensitivity(args, lib, sg, out, sel, k_blk, ws, stream):
+    """The same forward on the 128k-drift workload: the 128k shapes with index queries that drift
+    along the tokens (each component redrawn with probability 0.05 per token), so that adjacent
+    tokens select overlapping blocks, the premise of grouping adjacent query tokens.  Not the
+    headline: `value` is measured on the independent-query workload."""
+    import torch
+    from sgqa_inputs import generate, get_workload
+    w = get_workload("128k-drift")
+    dev = out.device
+    x = generate(w, device=dev, seed=args.seed)
+    prob = sg.Problem.from_workload(w)
+
+    def step():
+        sg.forward(prob, x["q"], x["k"], x["v"], x["gate"], x["q_idx"], x["k_idx"], k_blk=k_blk,
+                   out=out, sel=sel, workspace=ws, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    n = 3
+    ev = HipEvents()
+    marks = [[ev.create() for _ in range(N_MARKS)] for _ in range(n)]
+    arr_t = ctypes.c_void_p * N_MARKS
+    t0 = time.perf_counter()
+    for k in range(n):
+        lib.sgqa_set_stage_events(arr_t(*[m.value for m in marks[k]]))
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / n
+    lib.sgqa_set_stage_events(None)
+    stage_ms = {s: sum(ev.elapsed_ms(m[j], m[j + 1]) for m in marks) / n for j, s in enumerate(STAGES)}
+    ev.destroy()
+    c = algorithmic_counts(w)
+    un = union_stats(w, sel)
+    att_ms = stage_ms["attention"]
+    rec = {"workload": w.name, "description": w.description, "steps": n,
+           "ms_per_step": wall_ms, "query_tokens_per_s": prob.batch * prob.t_q / (wall_ms / 1e3),
+           "stages_ms": stage_ms,
+           "attention_frac_of_mfma_peak": c["attention_flops"] / (att_ms * 1e-3) / PEAK_BF16_FLOPS}
+    if un is not None:
+        rec["union_units_per_4_tokens"] = un["union_units_per_4_tokens"]
+        rec["union_over_one_selection"] = un["union_over_one_selection"]
+    del x
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -851,6 +900,10 @@ def main():
         "algorithmic": c,
         "device": torch.cuda.get_device_name(0),
     }
+    if args.sensitivity and args.workload == "128k" and args.kv == "bf16":
+        del x
+        torch.cuda.empty_cache()
+        rec["sensitivity"] = drift_sensitivity(args, lib, sg, out, sel, k_blk, ws, stream)
     print(json.dumps(rec), flush=True)
 
     if args.copy_calibration_mib > 0:
