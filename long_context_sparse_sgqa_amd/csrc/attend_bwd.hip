@@ -56,16 +56,28 @@ __global__ void __launch_bounds__(256) mark_units_kernel(const int32_t* __restri
   const int n = static_cast<int>(NU4 - u0 < kMarkTile ? NU4 - u0 : kMarkTile);
   for (int x = threadIdx.x; x < n; x += 256) row[x] = 0u;
   __syncthreads();
-  // 32 tokens x NS entries; consecutive threads take consecutive entries of one token
-  for (int e = threadIdx.x; e < 32 * NS; e += 256) {
-    const int i = e / NS, j = e - i * NS;
-    const int64_t t = 32 * w + i;
-    if (t >= Tq) continue;
-    const int32_t blk = sel[((b * Tq + t) * G + g) * NS + j];
-    if (blk < 0) continue;
-    for (int uu = 0; uu < U; ++uu) {
-      const int64_t unit = static_cast<int64_t>(blk) * U + uu - u0;
-      if (unit >= 0 && unit < n && unit + u0 < NU) atomicOr(&row[unit], 1u << i);
+  // 32 tokens x NS entries; consecutive threads take consecutive entries of one token.  Each
+  // thread loads kBatch entries before it marks any, so their loads are in flight together.
+  constexpr int kBatch = 8;
+  const int n_e = 32 * NS;
+  const int32_t* sw = sel + ((b * Tq + 32 * w) * G + g) * NS;   // token 32 w, entry 0
+  for (int e0 = 0; e0 < n_e; e0 += 256 * kBatch) {
+    int32_t blk[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int e = e0 + 256 * k + threadIdx.x;
+      const int i = e / NS;
+      const bool ok = e < n_e && 32 * w + i < Tq;
+      blk[k] = ok ? sw[static_cast<int64_t>(i) * G * NS + (e - i * NS)] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (blk[k] < 0) continue;
+      const int i = (e0 + 256 * k + threadIdx.x) / NS;
+      for (int uu = 0; uu < U; ++uu) {
+        const int64_t unit = static_cast<int64_t>(blk[k]) * U + uu - u0;
+        if (unit >= 0 && unit < n && unit + u0 < NU) atomicOr(&row[unit], 1u << i);
+      }
     }
   }
   __syncthreads();
@@ -86,7 +98,8 @@ struct DkvArgs {
   const uint32_t* bm;     // [Bt, G, W, NU4] (word-major)
   float* dk;              // [Bt, G, Tk, D]
   float* dv;
-  int64_t Tq, Tk, NU, NU4, pos0, W, nchunks, total;
+  int64_t Tq, Tk, NU, NU4, pos0, W, total;
+  int64_t BG;             // Bt * G: wave w takes chunk w / BG of (sequence, group) w % BG
   int G;
   float scale_log2e, scale;
 };
@@ -122,8 +135,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int lane = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
   const int gi = lane & 15, gh = (lane >> 4) & 1;        // lane in its 16-lane group, group's half
-  const int64_t chunk = wid % a.nchunks;
-  const int64_t bg = wid / a.nchunks;
+  // (sequence, group) fastest: with 8 of them, the XCD that runs a wave (workgroup index mod 8)
+  // always serves the same group, and its L2 holds only that group's q and dO rows
+  const int64_t chunk = wid / a.BG;
+  const int64_t bg = wid - chunk * a.BG;
   const int g = static_cast<int>(bg % a.G);
   const int64_t b = bg / a.G;
   const int64_t t = chunk * 32 + n;                      // this lane's key (kv column / dK row n)
@@ -392,8 +407,8 @@ hipError_t launch_backward_dkv(const Dims& d, const void* q, const void* d_o, co
   a.NU4 = NU4;
   a.pos0 = d.pos0;
   a.W = W;
-  a.nchunks = (d.NU + 3) / 4;
-  a.total = d.Bt * d.G * a.nchunks;
+  a.BG = d.Bt * d.G;
+  a.total = a.BG * ((d.NU + 3) / 4);
   a.G = d.G;
   a.scale_log2e = d.scale * 1.4426950408889634f;
   a.scale = d.scale;

@@ -1290,8 +1290,11 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
           make_float4(accq[dt][4 * i4], accq[dt][4 * i4 + 1], accq[dt][4 * i4 + 2], accq[dt][4 * i4 + 3]);
 }
 
-// dq = scale * (sum of the ranges' partials), rounded to bf16: one thread per (group of tokens,
-// piece, lane) of the partials' layout.
+// dq = scale * (sum of the ranges' partials), rounded to bf16.  One workgroup per (group of
+// tokens, 4 of its D / 8 pieces), wave w taking piece 4 j + w, a lane its (row, 4 d) of the
+// partials' layout.  Group indices fit 32 bits (there are fewer groups than query rows): the
+// workgroup's indices come from 32-bit divisions on the scalar unit, with no per-lane 64-bit
+// division.
 struct DqMergeArgs {
   const float* dq_part;
   bf16_t* dq;
@@ -1301,33 +1304,27 @@ struct DqMergeArgs {
 };
 
 __global__ void __launch_bounds__(256) dq_merge_kernel(DqMergeArgs a) {
-  const int pieces = (a.D / 32) * 4;
-  const int64_t n = a.total * pieces * 64;
-  for (int64_t id = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; id < n;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int lane = static_cast<int>(id & 63);
-    const int piece = static_cast<int>((id >> 6) % pieces);
-    const int64_t gq = (id >> 6) / pieces;
-    const int c = lane & 31, h = lane >> 5;
-    const int64_t qi = gq % a.ngroups, bg = gq / a.ngroups;
-    const int64_t tok = kTok * qi + (c >> 3);
-    if (tok >= a.Tq) continue;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  const uint32_t wgs = static_cast<uint32_t>(a.D / 32);           // workgroups per group of tokens
+  const uint32_t gq32 = blockIdx.x / wgs;
+  const int piece = static_cast<int>(blockIdx.x - gq32 * wgs) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  const uint32_t ng32 = static_cast<uint32_t>(a.ngroups), G32 = static_cast<uint32_t>(a.G);
+  const uint32_t bg32 = gq32 / ng32, qi32 = gq32 - bg32 * ng32;
+  const int64_t tok = kTok * static_cast<int64_t>(qi32) + (c >> 3);
+  if (tok >= a.Tq) return;
+  const int64_t gq = gq32;
+  // each partial is read exactly once: streaming (non-temporal) loads
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < kRanges; ++r) {
-      const float4 v = *reinterpret_cast<const float4*>(a.dq_part + (gq * kRanges + r) * (32 * a.D) +
-                                                        (piece * 64 + lane) * 4);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
-    }
-    const int dt = piece >> 2, i4 = piece & 3;
-    const int64_t g = bg % a.G, b = bg / a.G;
-    const int64_t row = ((b * a.Tq + tok) * a.G + g) * 8 + (c & 7);
-    *reinterpret_cast<uint2*>(a.dq + row * a.D + 32 * dt + 8 * i4 + 4 * h) =
-        make_uint2(pack_bf16x2(s.x * a.scale, s.y * a.scale), pack_bf16x2(s.z * a.scale, s.w * a.scale));
-  }
+  for (int r = 0; r < kRanges; ++r)
+    s += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
+        a.dq_part + (gq * kRanges + r) * (32 * a.D) + (piece * 64 + lane) * 4));
+  const int dt = piece >> 2, i4 = piece & 3;
+  const uint32_t b32 = bg32 / G32, g32 = bg32 - b32 * G32;
+  const int64_t row = ((static_cast<int64_t>(b32) * a.Tq + tok) * a.G + g32) * 8 + (c & 7);
+  *reinterpret_cast<uint2*>(a.dq + row * a.D + 32 * dt + 8 * i4 + 4 * h) =
+      make_uint2(pack_bf16x2(s[0] * a.scale, s[1] * a.scale), pack_bf16x2(s[2] * a.scale, s[3] * a.scale));
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1636,9 +1633,8 @@ static hipError_t launch_backward_grads(const Dims& d, const void* q, const void
   dm.D = d.D;
   dm.scale = d.scale;
   {
-    const int64_t n = total * (d.D / 32) * 4 * 64;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    const int64_t blocks = total * (d.D / 32);
+    if (total >= (int64_t(1) << 31) || blocks * 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(dq_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dm);
   }
   return hipGetLastError();

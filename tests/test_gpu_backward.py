@@ -36,9 +36,14 @@ BWD_CASES = [
     (100, 333, 16, 128, 2, 64, True, 128, 2),
     (7, 1300, 8, 256, 2, 128, False, 128, 1),
 ]
+# a long token walk for the key-major dK/dV kernel (130 bitmap words per chunk, read four at a
+# time) behind a prefix that is not a whole number of 32-key chunks
+LONG_CASES = [
+    (4160, 4460, 8, 256, 2, 64, False, 128, 1),
+]
 
 
-@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d%s-d%d-b%d" % (
+@pytest.mark.parametrize("case", BWD_CASES + LONG_CASES, ids=lambda c: "tq%d-tk%d-B%d-k%d-G%d%s-d%d-b%d" % (
     c[0], c[1], c[2], c[3], c[4], "-sharp" if c[6] else "", c[7], c[8]))
 def test_backward_small_every_element(case):
     t_q, t_kv, B, k, G, di, sharp, d, bt = case
