@@ -1130,15 +1130,15 @@ struct BwdArgs {
 // under the forward's masks, dS = P (dP - Dr); dQ^T += K^T dS^T in registers (the forward's P V
 // product).  The K^T operand (8 keys at one d per lane) is not gathered again: the chunk's K rows,
 // already in registers for S^T, go to the wave's LDS, and gfx950's transposing LDS read returns
-// them 4 rows of one column per lane.  The range's fp32 sum is stored in the
-// accumulator's lane order (coalesced 1 KB pieces); dq_merge_kernel adds the ranges.  dK and dV
-// are accumulated key-major in attend_bwd.hip.
+// them 4 rows of one column per lane.  Two waves per SIMD (240 registers, 8.5 KiB of LDS per
+// wave): the Q^T and dO^T operands stay in registers for the whole walk, and one K/V register
+// set is refilled with the next chunk as soon as S^T and dP^T have consumed it.  The range's fp32
+// sum is stored in the accumulator's lane order (coalesced 1 KB pieces); dq_merge_kernel adds the
+// ranges.  dK and dV are accumulated key-major in attend_bwd.hip.
 template <int D>
-__global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attend_bwd_kernel(BwdArgs a) {
   constexpr int H = 8;
-  constexpr int kRowB = D * 2 + 16;                      // LDS row of Q / dO (bytes)
-  __shared__ __attribute__((aligned(16))) unsigned char s_qa[kRangeWaves][32 * kRowB];
-  __shared__ __attribute__((aligned(16))) unsigned char s_doa[kRangeWaves][32 * kRowB];
+  constexpr int kRowB = D * 2 + 16;                      // LDS row of K (bytes)
   __shared__ __attribute__((aligned(16))) unsigned char s_ka[kRangeWaves][32 * kRowB];   // chunk's K
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1158,8 +1158,6 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
     qi = wgq * kRangeWaves + wave;
     if (qi >= a.ngroups) return;                         // whole wave; no workgroup barriers follow
   }
-  unsigned char* s_q = s_qa[wave];
-  unsigned char* s_do = s_doa[wave];
   unsigned char* s_k = s_ka[wave];
   const int64_t gq = bg * a.ngroups + qi;
   const int g = static_cast<int>(bg % a.G);
@@ -1173,22 +1171,19 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
 
   // Q and dO rows into LDS; lane (c, h) copies d in [D/2 h, D/2 (h+1)) of row c
   const int64_t rr = ((b * a.Tq + (rowvalid ? tok0 + trow : tok0)) * a.G + g) * H + head;
+  // Q^T and dO^T operands of d-slice kc in registers: lane (c, h) holds row c, d = 16 kc + 8 h .. + 8
+  bf16x8_t qop[D / 16], oop[D / 16];
   {
     const bf16_t* qrow = a.q + rr * D;
     const bf16_t* orow = a.d_o + rr * D;
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const int d = (D / 2) * h + 8 * k;
-      const uint4 vq = rowvalid ? *reinterpret_cast<const uint4*>(qrow + d) : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 vo = rowvalid ? *reinterpret_cast<const uint4*>(orow + d) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(s_q + c * kRowB + d * 2) = vq;
-      *reinterpret_cast<uint4*>(s_do + c * kRowB + d * 2) = vo;
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qop[kc] = rowvalid ? load_bf16x8(qrow + 16 * kc + 8 * h) : zero_bf16x8();
+      oop[kc] = rowvalid ? load_bf16x8(orow + 16 * kc + 8 * h) : zero_bf16x8();
     }
   }
   const float lse_c = rowvalid ? a.lse2[rr] : 0.f;
   const float D_c = rowvalid ? a.Dr[rr] : 0.f;
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  auto ld16 = [](const unsigned char* p) -> bf16x8_t { return bf16x8_from_u4(*reinterpret_cast<const uint4*>(p)); };
 
   const BufRsrc krs = make_rsrc(a.kq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
   const BufRsrc vrs = make_rsrc(a.vq + (b * a.G + g) * a.NU * D * 8, a.NU * D * 16);
@@ -1238,44 +1233,39 @@ __global__ void __launch_bounds__(256) attend_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) accq[dt][i] = 0.f;
 
-  auto chunk = [&](const Ops& R, const uint32_t* ent4) {
-    f32x16_t s = {}, dp = {};
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      s = mfma32x32x16(R.k[kc], ld16(s_q + c * kRowB + (16 * kc + 8 * h) * 2), s);
-      dp = mfma32x32x16(R.v[kc], ld16(s_do + c * kRowB + (16 * kc + 8 * h) * 2), dp);
-    }
-    const uint32_t msk = row_mask(pick4(ent4, h)) | (row_mask(pick4(ent4, 2 + h)) << 8);
-    float dsv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool on = (msk >> i) & 1u;
-      const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2e, -lse_c)) : 0.f;
-      dsv[i] = p * (dp[i] - D_c);
-    }
-    const bf16x8_t da = pack8_bf16(dsv), db = pack8_bf16(dsv + 8);
-    // the chunk's K rows (lane (c, h): row 8 slot + token of A row c, d = 16 kc + 8 h .. + 8) to
-    // LDS; this wave alone reads them, after these writes in program order
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      *reinterpret_cast<bf16x8_t*>(s_k + (8 * kslot + ktok) * kRowB + 2 * (16 * kc + 8 * h)) = R.k[kc];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      accq[dt] = mfma32x32x16(kt_operand(h, dt), da, accq[dt]);
-      accq[dt] = mfma32x32x16(kt_operand(2 + h, dt), db, accq[dt]);
-    }
-  };
-
+  // One register set: S^T and dP^T consume the chunk's K and V, its K rows go to LDS, and the
+  // next chunk's K and V are loaded into the same registers while dS and dQ^T are computed.
   if (e0 < e1) {
-    uint32_t entA[4], entB[4];
-    Ops A, B;
-    load_ops(e0, entA, A);
-    for (int cpos = e0; cpos < e1; cpos += 8) {
-      if (cpos + 4 < e1) load_ops(cpos + 4, entB, B);
-      chunk(A, entA);
-      if (cpos + 4 >= e1) break;
-      if (cpos + 8 < e1) load_ops(cpos + 8, entA, A);
-      chunk(B, entB);
+    uint32_t ent[4];
+    Ops R;
+    load_ops(e0, ent, R);
+    for (int cpos = e0; cpos < e1; cpos += 4) {
+      f32x16_t s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        s = mfma32x32x16(R.k[kc], qop[kc], s);
+        dp = mfma32x32x16(R.v[kc], oop[kc], dp);
+      }
+      // the chunk's K rows (lane (c, h): row 8 slot + token of A row c, d = 16 kc + 8 h .. + 8) to
+      // LDS; this wave alone reads them, after these writes in program order
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc)
+        *reinterpret_cast<bf16x8_t*>(s_k + (8 * kslot + ktok) * kRowB + 2 * (16 * kc + 8 * h)) = R.k[kc];
+      const uint32_t msk = row_mask(pick4(ent, h)) | (row_mask(pick4(ent, 2 + h)) << 8);
+      if (cpos + 4 < e1) load_ops(cpos + 4, ent, R);
+      float dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool on = (msk >> i) & 1u;
+        const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2e, -lse_c)) : 0.f;
+        dsv[i] = p * (dp[i] - D_c);
+      }
+      const bf16x8_t da = pack8_bf16(dsv), db = pack8_bf16(dsv + 8);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        accq[dt] = mfma32x32x16(kt_operand(h, dt), da, accq[dt]);
+        accq[dt] = mfma32x32x16(kt_operand(2 + h, dt), db, accq[dt]);
+      }
     }
   }
 
