@@ -36,6 +36,13 @@ COMMON_FLAGS = [
     "-I", os.path.join(REPO_DIR, "include"), "-I", CSRC,
 ]
 
+# Per-source flags.  The key-major dK/dV kernel needs more than the 256 architectural VGPRs; left to
+# its heuristics the compiler keeps the dK/dV sums in VGPRs between steps and moves all 128 of them
+# to accumulation registers for every step's products.  Matrix-core ops on VGPRs avoid that move.
+SOURCE_FLAGS = {
+    "attend_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -86,7 +93,8 @@ def build(verbose: bool = False, host_sanitizers: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         out = _run(cmd)
