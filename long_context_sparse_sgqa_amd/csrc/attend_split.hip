@@ -665,11 +665,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // K and V the registers hold the raw bytes (one 16-byte load covers two operands) and are
   // converted to bf16 right before the products.
   const int kslot = kq_slot(c), ktok = kq_tok(c);
-  struct KRegs {
+  // One register set holds either a chunk's K operands or its V operands (the same size): the
+  // pipeline below rotates three sets through both roles.
+  struct OpRegs {
     bf16x8_t k[kFp8 ? 1 : D / 16];
     uint4 r[kFp8 ? D / 32 : 1];
   };
-  auto load_k = [&](const uint32_t* ent4, const uint32_t* pu4, KRegs& R) {
+  auto load_k = [&](const uint32_t* ent4, const uint32_t* pu4, OpRegs& R) {
     if constexpr (kFp8) {
       // fp8 unit layout: bytes ((m * 8 + t) * 2 + h) * 16 hold d 32m + 8h + [0, 8) then
       // 32m + 16 + 8h + [0, 8) of token t
@@ -688,7 +690,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int kc = 0; kc < D / 16; ++kc) R.k[kc] = buffer_load_bf16x8(krs, kq_offset(u, D, kc, ktok, h));
     }
   };
-  auto k_op = [&](const KRegs& K, int kc) -> bf16x8_t {
+  auto k_op = [&](const OpRegs& K, int kc) -> bf16x8_t {
     if constexpr (kFp8) {
       const uint4 w = K.r[kc >> 1];
       return (kc & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
@@ -697,11 +699,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
   // V^T operands of d-tile dt for the units of slot h (first product) and slot 2 + h (second).
-  struct VRegs {
-    bf16x8_t v[kFp8 ? 1 : D / 16];
-    uint4 r[kFp8 ? D / 32 : 1];
-  };
-  auto load_v = [&](const uint32_t* ent4, const uint32_t* pu4, VRegs& R) {
+  auto load_v = [&](const uint32_t* ent4, const uint32_t* pu4, OpRegs& R) {
     if constexpr (kFp8) {
       // fp8 unit layout: bytes (n * 32 + c) * 16 hold tokens 0..7 of d 64n + c, then of 64n + 32 + c
       const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
@@ -718,26 +716,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const bf16_t* vb = a.vp + static_cast<uint64_t>(pick4(pu4, 2 + h)) * (D * 8) + c * 8;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        R.v[2 * dt] = load_bf16x8(va + 256 * dt);
-        R.v[2 * dt + 1] = load_bf16x8(vb + 256 * dt);
+        R.k[2 * dt] = load_bf16x8(va + 256 * dt);
+        R.k[2 * dt + 1] = load_bf16x8(vb + 256 * dt);
       }
     } else {
       const int ua = static_cast<int>(pick4(ent4, h) & kUnitMask);
       const int ub = static_cast<int>(pick4(ent4, 2 + h) & kUnitMask);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        R.v[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
-        R.v[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
+        R.k[2 * dt] = buffer_load_bf16x8(vrs, (ua * D + 32 * dt + c) * 16);
+        R.k[2 * dt + 1] = buffer_load_bf16x8(vrs, (ub * D + 32 * dt + c) * 16);
       }
     }
   };
   // operand of d-tile dt, unit slot h (sb = 0) or 2 + h (sb = 1)
-  auto v_op = [&](const VRegs& V, int dt, int sb) -> bf16x8_t {
+  auto v_op = [&](const OpRegs& V, int dt, int sb) -> bf16x8_t {
     if constexpr (kFp8) {
       const uint4 w = V.r[(dt >> 1) * 2 + sb];
       return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
     } else {
-      return V.v[2 * dt + sb];
+      return V.k[2 * dt + sb];
     }
   };
 
@@ -760,15 +758,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // one chunk: S^T = K Q^T, masks, online softmax, O^T += V^T P^T.  `refill` runs once S has
-  // consumed K, to reuse its registers.  Masked scores become -inf by adding a bias built from the
+  // one chunk: S^T = K Q^T, masks, online softmax, O^T += V^T P^T.  `after_s` runs once S has
+  // consumed K and `after_pv` once the P.V products have consumed V, to reuse their registers.  Masked scores become -inf by adding a bias built from the
   // mask bit; the scale enters through one fma in the exp2 argument; the row sum adds the bf16
   // probabilities the product uses, two at a time.
-  auto chunk = [&](const KRegs& K, const VRegs& V, const uint32_t* ent4, auto refill) {
+  auto chunk = [&](const OpRegs& K, const OpRegs& V, const uint32_t* ent4, auto after_s, auto after_pv) {
     f32x16_t s = {};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(k_op(K, kc), q_operand(kc), s);
-    refill();
+    after_s();
     const uint32_t mlo = row_mask(pick4(ent4, h)), mhi = row_mask(pick4(ent4, 2 + h));
     // Values 0..7 of a lane are the 8 keys of one unit, 8..15 those of another, so each half is
     // wholly attended or wholly masked except for the unit that holds the query's own position
@@ -831,28 +829,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       acc[dt] = mfma32x32x16(v_op(V, dt, 0), pa, acc[dt]);
       acc[dt] = mfma32x32x16(v_op(V, dt, 1), pb, acc[dt]);
     }
+    after_pv();
   };
 
   // Software pipeline over chunks of 4 units (past the range's end the loads fetch unit 0 and are
-  // masked out): K is loaded two chunks ahead and V one chunk ahead, two register sets each.  Per
-  // chunk x: V(x+4) is issued first, then K(x+8) once S(x) has freed its set; the compiler's vmcnt
-  // waits then leave up to three chunks' worth of K/V in flight.
-  if (e0 < e1) {
-    uint32_t ec[4], e1c[4], e2c[4], e3c[4];           // entries of chunks x, x+4, x+8, x+12
-    uint32_t pc[4], p1c[4], p2c[4], p3c[4];           // their pool units (paged cache)
+  // masked out).  Three register sets take turns as K and V: in chunk x, once S(x) has consumed
+  // K(x) its set receives V(x+1), and once P.V has consumed V(x) that set receives K(x+2).  Every
+  // load is thus issued about one chunk before its use, and the compiler's vmcnt waits leave two
+  // sets' loads in flight at each product.  The sets' roles repeat every three chunks.
+  // On a paged cache the page lookups leave no room for this rotation (it would spill registers):
+  // there K is loaded two chunks ahead into two sets and V at the start of its chunk.
+  if (kPaged && e0 < e1) {
+    uint32_t ec[4], e1c[4], e2c[4], e3c[4];
+    uint32_t pc[4], p1c[4], p2c[4], p3c[4];
     chunk_entries(e0, ec, pc);
     chunk_entries(e0 + 4, e1c, p1c);
     chunk_entries(e0 + 8, e2c, p2c);
-    KRegs kA, kB;
-    VRegs v0;
+    OpRegs kA, kB, v0;
     load_k(ec, pc, kA);
     load_k(e1c, p1c, kB);
-    int nx = e0 + 12;                                  // next chunk whose entries are read
-    auto step = [&](KRegs& K) {
-      chunk_entries(nx, e3c, p3c);                     // entries a chunk ahead of their use
+    int nx = e0 + 12;
+    auto step = [&](OpRegs& K) {
+      chunk_entries(nx, e3c, p3c);
       nx += 4;
       load_v(ec, pc, v0);
-      chunk(K, v0, ec, [&] { load_k(e2c, p2c, K); });
+      chunk(K, v0, ec, [&] { load_k(e2c, p2c, K); }, [] {});
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ec[j] = e1c[j];
@@ -863,15 +864,49 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         p2c[j] = p3c[j];
       }
     };
-    // the loop body is one period of the register rotation, so every trip enters with the same
-    // loads in flight; the first chunk and the tail run outside it
     step(kA);
-    int rem = (e1 - e0 - 4) >> 2;                      // chunks left
+    int rem = (e1 - e0 - 4) >> 2;
     for (; rem >= 2; rem -= 2) {
       step(kB);
       step(kA);
     }
     if (rem >= 1) step(kB);
+  } else if (e0 < e1) {
+    uint32_t ec[4], e1c[4], e2c[4], e3c[4];           // entries of chunks x, x+4, x+8, x+12
+    uint32_t pc[4], p1c[4], p2c[4], p3c[4];           // their pool units (paged cache)
+    chunk_entries(e0, ec, pc);
+    chunk_entries(e0 + 4, e1c, p1c);
+    chunk_entries(e0 + 8, e2c, p2c);
+    OpRegs rA, rB, rC;
+    load_k(ec, pc, rA);
+    load_v(ec, pc, rB);
+    load_k(e1c, p1c, rC);
+    int nx = e0 + 12;                                  // next chunk whose entries are read
+    // K(x) in Kc, V(x) in Vc (K(x+1) is in the third set)
+    auto step = [&](OpRegs& Kc, OpRegs& Vc) {
+      chunk_entries(nx, e3c, p3c);                     // entries a chunk ahead of their use
+      nx += 4;
+      chunk(Kc, Vc, ec, [&] { load_v(e1c, p1c, Kc); }, [&] { load_k(e2c, p2c, Vc); });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ec[j] = e1c[j];
+        e1c[j] = e2c[j];
+        e2c[j] = e3c[j];
+        pc[j] = p1c[j];
+        p1c[j] = p2c[j];
+        p2c[j] = p3c[j];
+      }
+    };
+    // the loop body is one period of the rotation, so every trip enters with the same loads in
+    // flight; the tail runs outside it
+    int rem = (e1 - e0) >> 2;                          // chunks
+    for (; rem >= 3; rem -= 3) {
+      step(rA, rB);
+      step(rC, rA);
+      step(rB, rC);
+    }
+    if (rem >= 1) step(rA, rB);
+    if (rem >= 2) step(rC, rA);
   }
 
   // partial of this range: O / l in bf16 (0 for a row with nothing in the range), and the running
