@@ -105,9 +105,12 @@ __global__ void __launch_bounds__(256) quad_union_kernel(UnionArgs a) {
   const int64_t stride = list_stride(a.umax);
   uint32_t* bm = lds + static_cast<size_t>(wave) * union_lds_words(a.words, stride, kRegW > 0);
   uint32_t* stg = kRegW > 0 ? bm : bm + kTok * a.words;
-  const int64_t qi = gq % a.ngroups;
-  const int64_t bg = gq / a.ngroups;
-  const int64_t g = bg % a.G, b = bg / a.G;
+  // group indices fit 32 bits (fewer groups than rows, < 2^31): 32-bit divisions, a fraction of
+  // a 64-bit division's scalar instructions at one short-lived wave per group of tokens
+  const uint32_t gq32 = static_cast<uint32_t>(gq), ng32 = static_cast<uint32_t>(a.ngroups);
+  const uint32_t bg32 = gq32 / ng32, b32 = bg32 / static_cast<uint32_t>(a.G);
+  const int64_t qi = gq32 - bg32 * ng32;
+  const int64_t g = bg32 - b32 * static_cast<uint32_t>(a.G), b = b32;
   const int64_t tok0 = kTok * qi;
   const int64_t pos0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq);
   const int64_t u_end = group_u_end(pos0, tok0, a.Tq);
@@ -372,9 +375,12 @@ __global__ void __launch_bounds__(256) quad_union_merge_kernel(UnionArgs a) {
   const int64_t stride = list_stride(a.umax);
   int32_t* L = reinterpret_cast<int32_t*>(lds + static_cast<size_t>(wave) * (kTok * kMergeSel + stride));
   uint32_t* stg = reinterpret_cast<uint32_t*>(L + kTok * kMergeSel);
-  const int64_t qi = gq % a.ngroups;
-  const int64_t bg = gq / a.ngroups;
-  const int64_t g = bg % a.G, b = bg / a.G;
+  // group indices fit 32 bits (fewer groups than rows, < 2^31): 32-bit divisions, a fraction of
+  // a 64-bit division's scalar instructions at one short-lived wave per group of tokens
+  const uint32_t gq32 = static_cast<uint32_t>(gq), ng32 = static_cast<uint32_t>(a.ngroups);
+  const uint32_t bg32 = gq32 / ng32, b32 = bg32 / static_cast<uint32_t>(a.G);
+  const int64_t qi = gq32 - bg32 * ng32;
+  const int64_t g = bg32 - b32 * static_cast<uint32_t>(a.G), b = b32;
   const int64_t tok0 = kTok * qi;
   const int64_t pos0 = seq_pos0(a.seq_len, b, a.pos0, a.Tq);
   const int64_t u_end = group_u_end(pos0, tok0, a.Tq);

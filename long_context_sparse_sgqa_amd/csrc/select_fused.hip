@@ -503,13 +503,21 @@ __global__ void __launch_bounds__(256) select_candidates_kernel(SelectArgs a) {
   extern __shared__ uint32_t bm_all[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rr = static_cast<int64_t>(blockIdx.x) * a.waves + wave;
-  if (rr >= a.rows) return;                           // whole wave; no workgroup barriers below
-  const int64_t tok = rr / a.G;
-  const int g = static_cast<int>(rr - tok * a.G);
-  const int64_t bseq = a.b0 + tok / a.ntok;
-  const int64_t i = a.i0 + tok % a.ntok;
-  const int64_t o = (seq_pos0(a.seq_len, bseq, a.pos0, a.Tq) + i) / a.B;
+  // Row indices fit 32 bits (fewer than 2^31 rows), so the row's token, group and sequence come
+  // from 32-bit divisions: a 64-bit division is a long scalar routine, and at one wave per row
+  // these divisions were about a third of the kernel's scalar instructions.
+  const uint32_t rr32 = blockIdx.x * static_cast<uint32_t>(a.waves) + static_cast<uint32_t>(wave);
+  if (rr32 >= a.rows) return;                         // whole wave; no workgroup barriers below
+  const int64_t rr = rr32;
+  const uint32_t G32 = static_cast<uint32_t>(a.G), nt32 = static_cast<uint32_t>(a.ntok);
+  const uint32_t tok32 = rr32 / G32;
+  const int g = static_cast<int>(rr32 - tok32 * G32);
+  const uint32_t sq32 = tok32 / nt32;
+  const int64_t bseq = a.b0 + sq32;
+  const int64_t i = a.i0 + (tok32 - sq32 * nt32);
+  const int64_t p = seq_pos0(a.seq_len, bseq, a.pos0, a.Tq) + i;
+  const int64_t o = p <= 0xffffffffll ? static_cast<int64_t>(static_cast<uint32_t>(p) / static_cast<uint32_t>(a.B))
+                                      : p / a.B;
   int32_t* out = a.sel + ((bseq * a.Tq + i) * a.G + g) * a.NS;
   if (o + 1 <= a.NS) {
     for (int x = lane; x < a.NS; x += 64) out[x] = (x <= o) ? x : -1;
