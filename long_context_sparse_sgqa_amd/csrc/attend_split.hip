@@ -607,6 +607,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t tok0 = kTok * qi;
   const bool rowvalid = tok0 + trow < a.Tq;
   const int64_t pX = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + tok0 + trow;
+  // Units holding the group's tokens' own positions (wave-uniform): only there can a row attend to
+  // part of a unit (or, with a sliding window, at its start: windowed launches check every chunk).
+  const int64_t pfirst = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + tok0;
+  const int64_t plast = pfirst + (tok0 + kTok - 1 < a.Tq ? kTok - 1 : a.Tq - 1 - tok0);
+  const uint32_t own_lo = static_cast<uint32_t>(pfirst >> 3), own_hi = static_cast<uint32_t>(plast >> 3);
+  const bool windowed = a.win_m1 < (1 << 29);
 
   const uint32_t* list = a.ulist + gq * list_stride(a.umax);
   const int32_t* bnd = a.bounds + gq * (kRanges + 1);
@@ -773,14 +779,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) s = mfma32x32x16(k_op(K, kc), q_operand(kc), s);
     after_s();
-    const uint32_t mlo = row_mask(pick4(ent4, h)), mhi = row_mask(pick4(ent4, 2 + h));
     // Values 0..7 of a lane are the 8 keys of one unit, 8..15 those of another, so each half is
     // wholly attended or wholly masked except for the unit that holds the query's own position
     // (and a sliding window's first unit).  Without such a partial unit anywhere in the wave, a
     // half's mask is a choice of its max and of its exp2 bias (-inf: probability 0); otherwise
     // masked scores become -inf one by one (a sign-extended bit field selects the score or -inf).
-    const bool partial = (mlo != 0u && mlo != 0xffu) || (mhi != 0u && mhi != 0xffu);
-    const bool whole = !__ballot(partial);               // wave-uniform
+    // Whether the chunk can hold a partial unit at all is decided on the scalar unit from the
+    // chunk's units: a token chooses no unit past its own, and every unit before it is wholly in
+    // its past, so away from the group's own units a half's mask is its token's chosen bit.
+    uint32_t mlo, mhi;
+    bool whole;
+    bool near_own = windowed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = ent4[j] & kUnitMask;
+      near_own = near_own || (u >= own_lo && u <= own_hi);
+    }
+    if (!near_own) {
+      mlo = (pick4(ent4, h) >> (kChoseShift + trow)) & 1u;       // nonzero: the whole unit
+      mhi = (pick4(ent4, 2 + h) >> (kChoseShift + trow)) & 1u;
+      whole = true;
+    } else {
+      mlo = row_mask(pick4(ent4, h));
+      mhi = row_mask(pick4(ent4, 2 + h));
+      const bool partial = (mlo != 0u && mlo != 0xffu) || (mhi != 0u && mhi != 0xffu);
+      whole = !__ballot(partial);                        // wave-uniform
+    }
     float t[16];
     float mx;
     if (whole) {
