@@ -610,8 +610,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Units holding the group's tokens' own positions (wave-uniform): only there can a row attend to
   // part of a unit (or, with a sliding window, at its start: windowed launches check every chunk).
   const int64_t pfirst = seq_pos0(a.seq_len, b, a.pos0, a.Tq) + tok0;
-  const int64_t plast = pfirst + (tok0 + kTok - 1 < a.Tq ? kTok - 1 : a.Tq - 1 - tok0);
-  const uint32_t own_lo = static_cast<uint32_t>(pfirst >> 3), own_hi = static_cast<uint32_t>(plast >> 3);
+  const uint32_t own_lo = static_cast<uint32_t>(pfirst >> 3);
   const bool windowed = a.win_m1 < (1 << 29);
 
   const uint32_t* list = a.ulist + gq * list_stride(a.umax);
@@ -787,21 +786,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Whether the chunk can hold a partial unit at all is decided on the scalar unit from the
     // chunk's units: a token chooses no unit past its own, and every unit before it is wholly in
     // its past, so away from the group's own units a half's mask is its token's chosen bit.
-    uint32_t mlo, mhi;
-    bool whole;
-    bool near_own = windowed;
+    // The chosen bits become lane masks there: lanes 8t .. 8t + 7 of each half are token t's rows,
+    // so a unit's 4 chosen bits spread to one byte each (bit t -> byte t) give the half's 32 lanes.
+    bool keep_lo, keep_hi, whole;
+    uint32_t msk = 0u;                                   // per-score masks (partial chunks only)
+    // (no list entry lies past the last token's own unit, and padding entries are unit 0, so the
+    // chunk's largest unit decides)
+    uint32_t umax4 = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t u = ent4[j] & kUnitMask;
-      near_own = near_own || (u >= own_lo && u <= own_hi);
-    }
+    for (int j = 0; j < 4; ++j) umax4 = max(umax4, ent4[j] & kUnitMask);
+    const bool near_own = windowed || umax4 >= own_lo;
     if (!near_own) {
-      mlo = (pick4(ent4, h) >> (kChoseShift + trow)) & 1u;       // nonzero: the whole unit
-      mhi = (pick4(ent4, 2 + h) >> (kChoseShift + trow)) & 1u;
+      auto lanes = [](uint32_t ent) -> uint64_t {
+        const uint32_t c4 = (ent >> kChoseShift) & 0xfu;
+        return static_cast<uint64_t>(((c4 * 0x00204081u) & 0x01010101u) * 0xffu);
+      };
+      keep_lo = __builtin_amdgcn_inverse_ballot_w64(lanes(ent4[0]) | (lanes(ent4[1]) << 32));
+      keep_hi = __builtin_amdgcn_inverse_ballot_w64(lanes(ent4[2]) | (lanes(ent4[3]) << 32));
       whole = true;
     } else {
-      mlo = row_mask(pick4(ent4, h));
-      mhi = row_mask(pick4(ent4, 2 + h));
+      const uint32_t mlo = row_mask(pick4(ent4, h)), mhi = row_mask(pick4(ent4, 2 + h));
+      keep_lo = mlo != 0u;
+      keep_hi = mhi != 0u;
+      msk = mlo | (mhi << 8);
       const bool partial = (mlo != 0u && mlo != 0xffu) || (mhi != 0u && mhi != 0xffu);
       whole = !__ballot(partial);                        // wave-uniform
     }
@@ -817,9 +824,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       mxb = fmaxf(fmaxf(mxb, t[13]), t[14]);
       mxa = fmaxf(mxa, t[7]);
       mxb = fmaxf(mxb, t[15]);
-      mx = fmaxf(mlo ? mxa : -__builtin_inff(), mhi ? mxb : -__builtin_inff());
+      mx = fmaxf(keep_lo ? mxa : -__builtin_inff(), keep_hi ? mxb : -__builtin_inff());
     } else {
-      const uint32_t msk = mlo | (mhi << 8);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(msk), i, 1));
@@ -841,8 +847,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // exp2 bias of each half: -m_run, or -inf for a masked half on the whole-unit path (the
     // per-score path has already put -inf into the masked scores)
-    const float blo = (!whole || mlo) ? -m_run : -__builtin_inff();
-    const float bhi = (!whole || mhi) ? -m_run : -__builtin_inff();
+    const float blo = (!whole || keep_lo) ? -m_run : -__builtin_inff();
+    const float bhi = (!whole || keep_hi) ? -m_run : -__builtin_inff();
     float pv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(t[i], a.scale_log2e, i < 8 ? blo : bhi));
