@@ -362,10 +362,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   // loops, so their only memory waits are for the next tile's loads
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  // Candidate stores go through a buffer descriptor over this workgroup's rows and are issued for
-  // every lane: lanes without a candidate use an out-of-range offset, which the hardware drops.
-  // With no branches around them, the number of stores per tile is fixed and the wait for the next
-  // tile's loads need not wait for them.
+  // Candidate stores go through a buffer descriptor over this workgroup's rows, each under its
+  // lane's pass bit (an exec mask: the selection an out-of-range offset would otherwise need costs
+  // a VALU instruction per score, the mask a few scalar ones).
   const BufRsrc crs = make_rsrc(a.cand + (seq * a.seq_rows + row0) * a.cap,
                                 static_cast<int64_t>(kRows) * a.cap * 8);
   const int r_off = my_local_a * a.cap * 8;
@@ -408,7 +407,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const u32x2_t v = {static_cast<uint32_t>(cb0 + 16 * q + e), __float_as_uint(c[q][e])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, crs, pass[q][e] && fits ? r_off + pos * 8 : 0x7fffffff, 0, 0);
+        if (pass[q][e] && fits) __builtin_amdgcn_raw_buffer_store_b64(v, crs, r_off + pos * 8, 0, 0);
         pos += static_cast<int>(pass[q][e]);
       }
       base += static_cast<int>((tot >> (8 * q)) & 0xffu);
@@ -418,9 +417,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
   // Per tile: all products first (LDS reads and MFMAs only), then the next tile's global loads,
   // then the appends (compares, LDS counters, candidate stores), then the staging of the next tile.
   // The loads are issued for every tile (past the last one they read zeros or unused blocks) and
-  // the tiles below every row's causal limit run in a loop of their own, so each loop body is
-  // straight-line code with a fixed number of stores after the loads: the staging waits for the
-  // loads only, not for the candidate stores behind them.
+  // the tiles below every row's causal limit run in a loop of their own, so the staging of the next
+  // tile waits for the loads only.
   auto tile = [&](int64_t t, bool check_causal) {
     const int buf = static_cast<int>(t & 1);
     const unsigned char* src = lds + buf * kTileBytes;
