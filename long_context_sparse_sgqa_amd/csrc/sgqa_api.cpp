@@ -48,8 +48,11 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 size_t dtype_size(int32_t dt) { return dt == SGQA_BF16 ? 2 : 4; }
 
 // Query tokens per chunk are bounded by a fixed budget of per-chunk selection state (stored score
-// rows on the split path, candidate lists on the fused path).
-constexpr size_t kForwardChunkBudget = size_t(8) << 30;   // 8 GiB
+// rows on the split path, candidate lists on the fused path).  17 GiB holds the candidate lists of
+// a whole 128K-token prefill with 8 groups (16.01 GiB), so it runs as one chunk: one filter launch
+// whose row tiles are all dispatched longest first, and one select launch, instead of three of each
+// with their launch tails; a small share of a GPU with 288 GB of HBM.
+constexpr size_t kForwardChunkBudget = size_t(17) << 30;   // 17 GiB
 
 struct Derived {
   sgqa::Dims d;
